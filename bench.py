@@ -1,0 +1,260 @@
+"""Benchmark of the FP8 runtime chain on one MI355X.
+
+Default workload (the prefill-shaped layer): X bf16 4096x8192 drawn as
+0.5 * Student-t(3), quantized per tensor with a current (dynamic) E4M3 scale;
+W bf16 29568x8192 ~ N(0, 0.02) quantized once at setup with a static
+per-tensor E4M3 scale; Y = s_x s_w (X8 W8^T) in bf16.  One step = the per-batch
+hot path: amax(X) -> scale -> saturating cast of X (with saturation/underflow
+counters) -> scaled GEMM with FP32 accumulation and bf16 output.  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
+
+Other workloads (--workload decode|delayed|block|block_mx) time their own
+chains; they are extra measurements, not the headline line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 quantize GB/s + scaled-GEMM TFLOP/s, as % of MI355X HBM/FP8 peak"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill",
+                   choices=["prefill", "decode", "delayed", "block", "block_mx"])
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU budget of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source (else None)."""
+    prof = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(prof):
+        return None
+    try:
+        d = json.load(open(prof))
+    except (OSError, ValueError):
+        return None
+    src = os.path.join(ROOT, d.get("source", ""))
+    if not os.path.exists(src) or src_hash(src) != d.get("source_sha256_16"):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream the library
+    launches on (the binding passes torch.cuda.current_stream())."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append([e, None])
+
+    def stop(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[name][-1][1] = e
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
+
+def cpu_baseline_prefill(x_bits, w_bits, M, N, K, budget_s):
+    """The oracle as it stands, single-threaded, on a bounded sample of the
+    same workload, extrapolated to one full step (TFLOP/s of the step).  All
+    oracle inputs come from the seeded generators and the oracle itself."""
+    import oracle
+
+    oracle.build(force=False)
+    # untimed setup: static weight scale and the codes of a sample of W rows
+    g = np.random.default_rng(7)
+    w_rows = np.sort(g.choice(N, size=256, replace=False))
+    s_w, _ = oracle.compute_scale(oracle.amax(w_bits), oracle.E4M3)
+    wq, _, _, _, _ = oracle.quantize(np.ascontiguousarray(w_bits[w_rows]), oracle.E4M3, (0, 0),
+                                     mode=oracle.GIVEN, scale=s_w)
+    # timed: full amax of X, then the cast of a sample of rows
+    t0 = time.perf_counter()
+    oracle.amax(x_bits)
+    t_amax = time.perf_counter() - t0
+    rows_done, tq, chunk = 0, 0.0, 64
+    while tq < budget_s * 0.25 and rows_done + chunk <= M:
+        t0 = time.perf_counter()
+        xq, s_x, _, _, _ = oracle.quantize(np.ascontiguousarray(x_bits[rows_done:rows_done + chunk]),
+                                           oracle.E4M3, (0, 0))
+        tq += time.perf_counter() - t0
+        rows_done += chunk
+    quant_full_s = t_amax + tq * (M / rows_done)
+    npts, tg = 0, 0.0
+    while tg < budget_s * 0.75:
+        m = g.integers(0, xq.shape[0], 256)
+        n = g.integers(0, wq.shape[0], 256)
+        t0 = time.perf_counter()
+        oracle.gemm_points(xq, oracle.E4M3, s_x, (0, 0), wq, oracle.E4M3, s_w, (0, 0), m, n)
+        tg += time.perf_counter() - t0
+        npts += 256
+    gemm_full_s = tg / npts * M * N
+    step_s = quant_full_s + gemm_full_s
+    return {"value": 2.0 * M * N * K / step_s / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": ("oracle amax of all of X (%.2f s), cast of %d of %d X rows (%.2f s) and %d "
+                       "GEMM dot products of K=%d (%.2f s), extrapolated to one full step: %.1f s"
+                       % (t_amax, rows_done, M, tq, npts, K, tg, step_s))}
+
+
+def bench_prefill(args, torch, rt, wl):
+    M, N, K = 4096, 29568, 8192
+    w = wl.C3Prefill()
+    t0 = time.time()
+    x_bits = w.make_x()
+    w_bits = w.make_w()
+    print("inputs generated in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
+    from_bits = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    x = from_bits(x_bits)
+    W = from_bits(w_bits)
+    dev = "cuda"
+    # setup (untimed): static weight scale from W's own amax, weight codes
+    aw = torch.empty((1, 1), device=dev)
+    rt.fp8_amax(W, (0, 0), aw)
+    s_w = torch.empty((1, 1), device=dev)
+    r_w = torch.empty((1, 1), device=dev)
+    rt.fp8_compute_scale(aw, rt.E4M3, 1e-12, False, s_w, r_w)
+    Wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    cnt_w = torch.zeros(2, dtype=torch.int64, device=dev)
+    am_w = torch.empty((1, 1), device=dev)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s_x = torch.empty((1, 1), device=dev)
+    r_x = torch.empty((1, 1), device=dev)
+    am_x = torch.empty((1, 1), device=dev)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    timer = Timer(torch)
+
+    def quant_w():
+        rt.fp8_quantize(W, (0, 0), rt.E4M3, rt.GIVEN, 1e-12, False, s_w, r_w, Wq, am_w, cnt_w)
+
+    def step(timed):
+        if timed:
+            timer.start("quant_x")
+        rt.fp8_quantize(x, (0, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, s_x, r_x, xq, am_x, cnt)
+        if timed:
+            timer.stop("quant_x")
+            timer.start("gemm")
+        rt.fp8_scaled_gemm(xq, rt.E4M3, (0, 0), s_x, Wq, rt.E4M3, (0, 0), s_w, y)
+        if timed:
+            timer.stop("gemm")
+
+    quant_w()
+    for _ in range(3):
+        timer.start("quant_w")
+        quant_w()
+        timer.stop("quant_w")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step(True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    ms_step = total_ms / args.steps
+    q_ms = float(np.mean(timer.ms("quant_x")))
+    g_ms = float(np.mean(timer.ms("gemm")))
+    qw_ms = float(np.mean(timer.ms("quant_w")))
+    flops = 2.0 * M * N * K
+    # algorithmic bytes: X read once (bf16) + codes written once + scale
+    q_bytes = M * K * 2 + M * K * 1 + 4
+    qw_bytes = N * K * 2 + N * K * 1 + 4
+    g_bytes = M * K + N * K + M * N * 2 + 8
+    g_tflops = flops / (g_ms * 1e-3) / 1e12
+    sat = cnt.cpu().tolist()
+    out = {
+        "metric": METRIC, "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic (seeded Philox; X = 0.5*t(3), W ~ N(0,0.02))",
+        "config": {"workload": "prefill MLP up-projection: X[4096x8192] bf16 per-tensor dynamic "
+                               "E4M3 x W[29568x8192] bf16 per-tensor static E4M3 -> Y bf16",
+                   "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "achieved": g_tflops, "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": g_tflops / FP8_PEAK_TFLOPS,
+                     "traffic": traffic_from_profile("gemm_prefill_traffic.json"),
+                     "kernel": "k_gemm (fp8 E4M3xE4M3, per-tensor scales, bf16 out)",
+                     "avg_launch_us": g_ms * 1e3},
+        "components": {
+            "quantize_x_dynamic_per_tensor": {
+                "us": q_ms * 1e3, "GB_s": q_bytes / (q_ms * 1e-3) / 1e9,
+                "frac_hbm": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_bytes": q_bytes, "kernels": "k_tensor_amax + k_tensor_cast + k_finish"},
+            "gemm": {"us": g_ms * 1e3, "TFLOP_s": g_tflops, "frac_fp8_peak": g_tflops / FP8_PEAK_TFLOPS,
+                     "algorithmic_bytes": g_bytes},
+            "quantize_w_given_per_tensor": {
+                "us": qw_ms * 1e3, "GB_s": qw_bytes / (qw_ms * 1e-3) / 1e9,
+                "frac_hbm": qw_bytes / (qw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_bytes": qw_bytes},
+            "quant_over_gemm": q_ms / g_ms,
+            "x_saturated_underflowed": sat,
+        },
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(x_bits, w_bits, M, N, K, args.cpu_seconds)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the FP8 chain is measured on a single MI355X "
+              "(multi-GPU sharding is described, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dynamic_scaling_scaled_amd as rt
+    import workloads as wl
+
+    rt.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "prefill":
+        out = bench_prefill(args, torch, rt, wl)
+    else:
+        import bench_extra
+
+        out = bench_extra.run(args, torch, rt, wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

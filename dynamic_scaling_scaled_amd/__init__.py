@@ -1,0 +1,171 @@
+"""Python binding of the gfx950 FP8 runtime chain (``libfp8rt.so``).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI of ``include/fp8rt.h`` and raises on a
+non-OK status.  All arithmetic runs in the library's HIP kernels; there is no
+CPU fallback: calling any function without the built library raises.
+
+Tensors are torch tensors on the GPU: inputs ``float32`` or ``bfloat16``,
+FP8 codes ``uint8``, scales ``float32``, counters ``int64`` (read as uint64).
+Granularities are ``(rows, cols)`` group extents, 0 meaning the whole
+dimension: per-tensor (0, 0), per-row (1, 0), per-group (1, 128),
+per-block (128, 128), MX-style (1, 32).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8rt.so")
+
+E4M3, E5M2 = 0, 1
+F32, BF16 = 0, 1
+DYNAMIC, GIVEN = 0, 1
+POW2_SCALES = 1
+FMAX = {E4M3: 448.0, E5M2: 57344.0}
+
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+
+
+class Fp8rtError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+class Gran(C.Structure):
+    _fields_ = [("rows", C.c_int32), ("cols", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the built library; raises if it is missing (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libfp8rt.so is not built: run __graft_entry__.build() "
+                              "or python dynamic_scaling_scaled_amd/_build.py")
+        L = C.CDLL(LIB_PATH)
+        P, I64, I32, F, U32 = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_uint32
+        L.fp8rt_status_string.restype = C.c_char_p
+        L.fp8rt_status_string.argtypes = [C.c_int]
+        L.fp8_amax.restype = C.c_int
+        L.fp8_amax.argtypes = [P, C.c_int, I64, I64, I64, Gran, P, P]
+        L.fp8_compute_scale.restype = C.c_int
+        L.fp8_compute_scale.argtypes = [P, I64, C.c_int, F, I32, P, P, P]
+        L.fp8_quantize.restype = C.c_int
+        L.fp8_quantize.argtypes = [P, C.c_int, I64, I64, I64, Gran, C.c_int, C.c_int, F, I32, P, P,
+                                   P, I64, P, P, P]
+        L.fp8_dequantize.restype = C.c_int
+        L.fp8_dequantize.argtypes = [P, C.c_int, I64, I64, I64, Gran, P, P, C.c_int, I64, P]
+        L.fp8_amax_history_update.restype = C.c_int
+        L.fp8_amax_history_update.argtypes = [P, I32, P, P, C.c_int, F, I32, P, P, P]
+        L.fp8_scaled_gemm.restype = C.c_int
+        L.fp8_scaled_gemm.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
+                                      I64, P, C.c_int, P, C.c_int, I64, U32, P]
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != OK:
+        raise Fp8rtError(fn, status, lib().fp8rt_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _mat(t: torch.Tensor):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D row-major tensor with unit column stride")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def ngroups(n: int, g: int) -> int:
+    return 1 if (g <= 0 or g >= n) else -(-n // g)
+
+
+def scale_shape(shape, gran):
+    return (ngroups(shape[0], gran[0]), ngroups(shape[1], gran[1]))
+
+
+def fp8_amax(x, gran, amax, stream=None):
+    rows, cols, ld = _mat(x)
+    _check("fp8_amax", lib().fp8_amax(_ptr(x), _dtype(x), rows, cols, ld, Gran(*gran), _ptr(amax),
+                                      _stream(stream)))
+
+
+def fp8_compute_scale(amax, fmt, eps, pow2_round_up, scale, inv_scale=None, stream=None):
+    _check("fp8_compute_scale", lib().fp8_compute_scale(_ptr(amax), amax.numel(), fmt, eps,
+                                                        int(pow2_round_up), _ptr(scale),
+                                                        _ptr(inv_scale), _stream(stream)))
+
+
+def fp8_quantize(x, gran, fmt, mode, eps, pow2_round_up, scale, inv_scale, q, amax_out=None,
+                 sat_underflow=None, stream=None):
+    rows, cols, ld = _mat(x)
+    _, _, ldq = _mat(q)
+    _check("fp8_quantize", lib().fp8_quantize(_ptr(x), _dtype(x), rows, cols, ld, Gran(*gran), fmt,
+                                              mode, eps, int(pow2_round_up), _ptr(scale),
+                                              _ptr(inv_scale), _ptr(q), ldq, _ptr(amax_out),
+                                              _ptr(sat_underflow), _stream(stream)))
+
+
+def fp8_dequantize(q, fmt, gran, scale, y, stream=None):
+    rows, cols, ldq = _mat(q)
+    _, _, ldy = _mat(y)
+    _check("fp8_dequantize", lib().fp8_dequantize(_ptr(q), fmt, rows, cols, ldq, Gran(*gran),
+                                                  _ptr(scale), _ptr(y), _dtype(y), ldy,
+                                                  _stream(stream)))
+
+
+def fp8_amax_history_update(history, head, amax_new, fmt, eps, pow2_round_up, scale_next,
+                            inv_scale_next=None, stream=None):
+    _check("fp8_amax_history_update",
+           lib().fp8_amax_history_update(_ptr(history), history.numel(), _ptr(head), _ptr(amax_new),
+                                         fmt, eps, int(pow2_round_up), _ptr(scale_next),
+                                         _ptr(inv_scale_next), _stream(stream)))
+
+
+def fp8_scaled_gemm(a, fa, ga, scale_a, b, fb, gb, scale_b, y, bias=None, flags=0, stream=None):
+    M, K, lda = _mat(a)
+    N, K2, ldb = _mat(b)
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    _, _, ldy = _mat(y)
+    bias_t = _dtype(bias) if bias is not None else F32
+    _check("fp8_scaled_gemm",
+           lib().fp8_scaled_gemm(_ptr(a), fa, lda, Gran(*ga), _ptr(scale_a), _ptr(b), fb, ldb,
+                                 Gran(*gb), _ptr(scale_b), M, N, K, _ptr(bias), bias_t, _ptr(y),
+                                 _dtype(y), ldy, flags, _stream(stream)))
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes arguments; returns the status."""
+    return getattr(lib(), name)(*args)
+
+
+__all__ = ["fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_dequantize",
+           "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
+           "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
+           "scale_shape"]

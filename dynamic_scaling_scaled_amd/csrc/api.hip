@@ -1,0 +1,203 @@
+// api.hip -- the C ABI of include/fp8rt.h: host-side argument validation and
+// dispatch to the gfx950 kernels.  Every check runs before anything is
+// enqueued; on an error nothing is written.
+#include <math.h>
+#include <stdint.h>
+
+#include "fp8rt.h"
+#include "internal.h"
+
+using namespace fp8rt;
+
+namespace {
+
+constexpr float kMinEps = 0x1p-96f;  // keeps r = F_max / eps finite for both formats
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool valid_fmt(int f) { return f == FP8RT_E4M3 || f == FP8RT_E5M2; }
+bool valid_dtype(int d) { return d == FP8RT_F32 || d == FP8RT_BF16; }
+bool valid_eps(float e) { return isfinite(e) && e >= kMinEps; }
+
+fp8rt_status from_hip(hipError_t e) { return e == hipSuccess ? FP8RT_OK : FP8RT_EHIP; }
+
+// Common checks of a [rows x cols] row-major operand with group extents g.
+fp8rt_status check_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld, fp8rt_gran g) {
+  if (!p) return FP8RT_EINVAL;
+  if (rows <= 0 || cols <= 0 || ld < cols) return FP8RT_EINVAL;
+  if (g.rows < 0 || g.cols < 0) return FP8RT_EINVAL;
+  if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return FP8RT_EINVAL;
+  if (cols % 16 != 0 || ld % 16 != 0) return FP8RT_EALIGN;
+  const int64_t ec = group_extent(cols, g.cols);
+  if (ec != cols && ec % 16 != 0) return FP8RT_EALIGN;
+  if (!aligned16(p)) return FP8RT_EALIGN;
+  return FP8RT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8rt_status_string(fp8rt_status s) {
+  switch (s) {
+    case FP8RT_OK: return "ok";
+    case FP8RT_EINVAL: return "invalid argument";
+    case FP8RT_EALIGN: return "misaligned size, leading dimension or pointer (16 required)";
+    case FP8RT_EUNSUPPORTED: return "unsupported format or scale-granularity combination";
+    case FP8RT_EHIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+fp8rt_status fp8_amax(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                      fp8rt_gran g, float* amax, hipStream_t stream) {
+  if (!valid_dtype(xt) || !amax) return FP8RT_EINVAL;
+  fp8rt_status st = check_matrix(x, rows, cols, ldx, g);
+  if (st != FP8RT_OK) return st;
+  if (!aligned4(amax)) return FP8RT_EALIGN;
+  QuantArgs a{};
+  a.x = x;
+  a.xt = xt;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.er = group_extent(rows, g.rows);
+  a.ec = group_extent(cols, g.cols);
+  a.fmt = FP8RT_E4M3;
+  a.mode = FP8RT_DYNAMIC;
+  a.eps = 1.0f;
+  a.ldq = cols;
+  a.amax_out = amax;
+  a.amax_only = true;
+  return from_hip(launch_quantize(a, stream));
+}
+
+fp8rt_status fp8_compute_scale(const float* amax, int64_t n, fp8rt_format f, float eps,
+                               int32_t pow2_round_up, float* scale, float* inv_scale,
+                               hipStream_t stream) {
+  if (!amax || !scale || n <= 0 || !valid_fmt(f) || !valid_eps(eps)) return FP8RT_EINVAL;
+  if (!aligned4(amax) || !aligned4(scale) || (inv_scale && !aligned4(inv_scale))) return FP8RT_EALIGN;
+  return from_hip(launch_compute_scale(amax, n, f, eps, pow2_round_up != 0, scale, inv_scale, stream));
+}
+
+fp8rt_status fp8_quantize(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,
+                          int64_t ldx, fp8rt_gran g, fp8rt_format f, fp8rt_mode mode,
+                          float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
+                          uint8_t* q, int64_t ldq, float* amax_out, uint64_t* sat_underflow,
+                          hipStream_t stream) {
+  if (!valid_dtype(xt) || !valid_fmt(f) || !scale || !q) return FP8RT_EINVAL;
+  if (mode != FP8RT_DYNAMIC && mode != FP8RT_GIVEN) return FP8RT_EINVAL;
+  if (mode == FP8RT_DYNAMIC && !valid_eps(eps)) return FP8RT_EINVAL;
+  fp8rt_status st = check_matrix(x, rows, cols, ldx, g);
+  if (st != FP8RT_OK) return st;
+  if (ldq < cols) return FP8RT_EINVAL;
+  if (ldq % 16 != 0 || !aligned16(q)) return FP8RT_EALIGN;
+  if (!aligned4(scale) || (inv_scale && !aligned4(inv_scale)) || (amax_out && !aligned4(amax_out)) ||
+      (sat_underflow && (reinterpret_cast<uintptr_t>(sat_underflow) & 7u)))
+    return FP8RT_EALIGN;
+  QuantArgs a{};
+  a.x = x;
+  a.xt = xt;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.er = group_extent(rows, g.rows);
+  a.ec = group_extent(cols, g.cols);
+  a.fmt = f;
+  a.mode = mode;
+  a.eps = mode == FP8RT_DYNAMIC ? eps : 1.0f;
+  a.pow2 = pow2_round_up != 0;
+  a.scale = scale;
+  a.inv_scale = inv_scale;
+  a.q = q;
+  a.ldq = ldq;
+  a.amax_out = amax_out;
+  a.counts = reinterpret_cast<unsigned long long*>(sat_underflow);
+  a.amax_only = false;
+  return from_hip(launch_quantize(a, stream));
+}
+
+fp8rt_status fp8_dequantize(const uint8_t* q, fp8rt_format f, int64_t rows, int64_t cols,
+                            int64_t ldq, fp8rt_gran g, const float* scale, void* y,
+                            fp8rt_dtype yt, int64_t ldy, hipStream_t stream) {
+  if (!valid_fmt(f) || !valid_dtype(yt) || !scale || !y) return FP8RT_EINVAL;
+  fp8rt_status st = check_matrix(q, rows, cols, ldq, g);
+  if (st != FP8RT_OK) return st;
+  if (ldy < cols) return FP8RT_EINVAL;
+  if (ldy % 16 != 0 || !aligned16(y) || !aligned4(scale)) return FP8RT_EALIGN;
+  return from_hip(launch_dequantize(q, f, rows, cols, ldq, group_extent(rows, g.rows),
+                                    group_extent(cols, g.cols), scale, y, yt, ldy, stream));
+}
+
+fp8rt_status fp8_amax_history_update(float* history, int32_t len, int32_t* head,
+                                     const float* amax_new, fp8rt_format f, float eps,
+                                     int32_t pow2_round_up, float* scale_next,
+                                     float* inv_scale_next, hipStream_t stream) {
+  if (!history || !head || !amax_new || !scale_next || !valid_fmt(f) || !valid_eps(eps))
+    return FP8RT_EINVAL;
+  if (len < 1 || len > 1024) return FP8RT_EINVAL;
+  if (!aligned4(history) || !aligned4(head) || !aligned4(amax_new) || !aligned4(scale_next) ||
+      (inv_scale_next && !aligned4(inv_scale_next)))
+    return FP8RT_EALIGN;
+  return from_hip(launch_history_update(history, len, head, amax_new, f, eps, pow2_round_up != 0,
+                                        scale_next, inv_scale_next, stream));
+}
+
+fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                             const float* scale_a, const uint8_t* b, fp8rt_format fb,
+                             int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
+                             int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
+                             void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
+                             hipStream_t stream) {
+  if (!a || !b || !scale_a || !scale_b || !y) return FP8RT_EINVAL;
+  if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_dtype(yt) || (bias && !valid_dtype(bias_t)))
+    return FP8RT_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || lda < K || ldb < K || ldy < N) return FP8RT_EINVAL;
+  if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
+  if (ga.rows < 0 || ga.cols < 0 || gb.rows < 0 || gb.cols < 0) return FP8RT_EINVAL;
+  if ((flags & ~FP8RT_POW2_SCALES) != 0) return FP8RT_EINVAL;
+  if (K % 16 != 0 || lda % 16 != 0 || ldb % 16 != 0) return FP8RT_EALIGN;
+  if (!aligned16(a) || !aligned16(b) || !aligned4(scale_a) || !aligned4(scale_b)) return FP8RT_EALIGN;
+  if ((yt == FP8RT_F32 && !aligned4(y)) || (yt == FP8RT_BF16 && (reinterpret_cast<uintptr_t>(y) & 1u)))
+    return FP8RT_EALIGN;
+  if (bias && !aligned4(bias)) return FP8RT_EALIGN;
+  if (!((fa == FP8RT_E4M3 && fb == FP8RT_E4M3) || (fa == FP8RT_E5M2 && fb == FP8RT_E4M3)))
+    return FP8RT_EUNSUPPORTED;
+
+  GemmArgs g{};
+  g.a = a;
+  g.fa = fa;
+  g.lda = lda;
+  g.era = group_extent(M, ga.rows);
+  g.eca = group_extent(K, ga.cols);
+  g.sa = scale_a;
+  g.b = b;
+  g.fb = fb;
+  g.ldb = ldb;
+  g.erb = group_extent(N, gb.rows);
+  g.ecb = group_extent(K, gb.cols);
+  g.sb = scale_b;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.bias = bias;
+  g.bias_t = bias_t;
+  g.y = y;
+  g.yt = yt;
+  g.ldy = ldy;
+  g.pow2_mx = false;
+  // Scale granularities the kernels implement.
+  const bool a_kblk = g.eca < K, b_kblk = g.ecb < K;
+  if (a_kblk && g.era != 1) return FP8RT_EUNSUPPORTED;  // A: tensor, row or {1, g}
+  if (g.eca == 32 && g.ecb == 32 && g.era == 1 && g.erb == 1) {
+    if (!(flags & FP8RT_POW2_SCALES)) return FP8RT_EUNSUPPORTED;
+    g.pow2_mx = true;
+  } else {
+    if (a_kblk && g.eca % 128 != 0) return FP8RT_EUNSUPPORTED;
+    if (b_kblk && g.ecb % 128 != 0) return FP8RT_EUNSUPPORTED;
+    if (a_kblk && b_kblk && g.eca != g.ecb) return FP8RT_EUNSUPPORTED;
+  }
+  return from_hip(launch_gemm(g, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,762 @@
+// quant_kernels.hip -- amax reduction, scale, saturating FP8 cast, dequantize
+// and the delayed-scaling history update for gfx950.
+//
+// Method ("FP8 formats and scaling for LLM inference"):
+//   section "How a scale fits a tensor into E4M3": a_max = max|X|,
+//     s = a_max / F_max, X_fp8 = cast(clip(X / s)), X_hat = s X_fp8;
+//   section "Per-channel and block scaling": one scale per row / block,
+//     s_g = a_g / F_max;
+//   section "Current scaling": reduce amax -> scale -> cast in the same step;
+//   section "Delayed scaling": s_{t+1} = f(a_t .. a_{t-h+1}) / F_max;
+//   section "What numerical validation looks at": saturation and underflow
+//     rates.
+// "FP8 production quantization guide", dynamic quantize listing: eps clamp of
+// amax, x * inv_scale, clamp to +-F_max, cast.
+//
+// Design (HBM-bound work): 16-byte loads of 8-element octets, exact integer
+// max on |x| bit patterns, one FP32 multiply, a clamp and the packed
+// v_cvt_pk_{fp8,bf8}_f32 convert per element; 8-byte code stores.  Group
+// maxima are reduced across lanes with shuffles and across a workgroup in LDS.
+// Cross-block results (per-tensor amax, counters) go through per-block
+// partials in per-call scratch and are combined by a second kernel, so no
+// result depends on atomics or on memory being pre-cleared.
+#include <float.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8rt {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+
+template <typename T> constexpr int oct_unroll() { return sizeof(T) == 2 ? 4 : 2; }
+
+// Block-wide max (all threads receive it).  Uses sh[kWaves].
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
+  v = wave_max_u32(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  uint32_t m = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = max(m, sh[i]);
+  return m;
+}
+
+// Writes this block's partial (wave-uniform counters already summed per wave
+// in sat_w / under_w; lane-level amax bits in mb).
+__device__ __forceinline__ void store_block_partial(BlockPartial* bp, uint32_t mb,
+                                                   unsigned long long sat_w,
+                                                   unsigned long long under_w) {
+  __shared__ uint32_t sh_m[kWaves];
+  __shared__ unsigned long long sh_s[kWaves], sh_u[kWaves];
+  mb = wave_max_u32(mb);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    sh_m[w] = mb;
+    sh_s[w] = sat_w;
+    sh_u[w] = under_w;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    unsigned long long s = 0, u = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      m = max(m, sh_m[i]);
+      s += sh_s[i];
+      u += sh_u[i];
+    }
+    bp[blockIdx.x].amax_bits = m;
+    bp[blockIdx.x].pad = 0;
+    bp[blockIdx.x].sat = s;
+    bp[blockIdx.x].under = u;
+  }
+}
+
+// Converts one octet with multiplier r; returns the 8 codes as two words and
+// adds the wave-wide saturation / underflow counts (wave-uniform values).
+template <typename T, int F, bool STATS>
+__device__ __forceinline__ u32x2 cast_octet(const Octet<T>& v, float r, bool nan_path,
+                                            unsigned long long& sat_w,
+                                            unsigned long long& under_w) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v.get(i) * r;
+  u32x2 out;
+  if (nan_path) {
+    out[0] = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+    out[1] = cvt4_nan<F>(f[4], f[5], f[6], f[7]);
+  } else {
+    out[0] = cvt4<F>(f[0], f[1], f[2], f[3]);
+    out[1] = cvt4<F>(f[4], f[5], f[6], f[7]);
+  }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sat_w += __popcll(__ballot(fabsf(f[i]) > Fmt<F>::kMax));
+      under_w += __popcll(__ballot(v.get(i) != 0.0f && fabsf(f[i]) <= Fmt<F>::kZeroEdge));
+    }
+  }
+  return out;
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor: pass 1 writes one amax partial per block.  The work is split in
+// segments of kBlock * U octets of one row.
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_tensor_amax(const T* __restrict__ x, int64_t rows,
+                                                        int64_t opr, int64_t ldx,
+                                                        int64_t segs_per_row,
+                                                        uint32_t* __restrict__ part) {
+  constexpr int U = oct_unroll<T>();
+  __shared__ uint32_t sh[kWaves];
+  uint32_t m = 0;
+  const int64_t nseg = rows * segs_per_row;
+  for (int64_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+    const int64_t r = sg / segs_per_row;
+    const int64_t s = sg - r * segs_per_row;
+    const T* xr = x + r * ldx;
+    Octet<T> v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = (s * U + u) * kBlock + threadIdx.x;
+      if (o < opr) v[u].load(xr + o * 8);
+      else v[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = max(m, v[u].absmax_bits());
+  }
+  m = block_max_u32(m, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+// Pass 2: every block combines the pass-1 partials itself (DYNAMIC) or reads
+// the given scale (GIVEN), then casts its segments.
+template <typename T, int F, bool GIVEN, bool STATS>
+__global__ __launch_bounds__(kBlock) void k_tensor_cast(
+    const T* __restrict__ x, int64_t rows, int64_t opr, int64_t ldx, int64_t segs_per_row,
+    uint8_t* __restrict__ q, int64_t ldq, const uint32_t* __restrict__ part, int nparts, float eps,
+    int pow2, const float* __restrict__ s_in, const float* __restrict__ r_in, float* s_out,
+    float* r_out, float* amax_out, BlockPartial* bpart) {
+  constexpr int U = oct_unroll<T>();
+  __shared__ uint32_t sh[kWaves];
+  float r;
+  if constexpr (!GIVEN) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += kBlock) m = max(m, part[i]);
+    m = block_max_u32(m, sh);
+    const float a = __uint_as_float(m);
+    float s;
+    scale_from_amax(a, Fmt<F>::kMax, eps, pow2 != 0, s, r);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      s_out[0] = s;
+      if (r_out) r_out[0] = r;
+      if (amax_out) amax_out[0] = a;
+    }
+  } else {
+    const float s = s_in[0];
+    r = r_in ? r_in[0] : 1.0f / s;
+  }
+  const bool r_bad = !(fabsf(r) <= FLT_MAX);
+  uint32_t mb = 0;
+  unsigned long long sat_w = 0, under_w = 0;
+  const int64_t nseg = rows * segs_per_row;
+  for (int64_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+    const int64_t rr = sg / segs_per_row;
+    const int64_t s = sg - rr * segs_per_row;
+    const T* xr = x + rr * ldx;
+    uint8_t* qr = q + rr * ldq;
+    Octet<T> v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = (s * U + u) * kBlock + threadIdx.x;
+      if (o < opr) v[u].load_nt(xr + o * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = (s * U + u) * kBlock + threadIdx.x;
+      if (o < opr) {
+        bool nan_path = r_bad;
+        if constexpr (GIVEN) {
+          const uint32_t omb = v[u].absmax_bits();
+          mb = max(mb, omb);
+          nan_path |= omb > kInfBits;
+        }
+        const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
+        *reinterpret_cast<u32x2*>(qr + o * 8) = c;
+      }
+    }
+  }
+  if constexpr (GIVEN || STATS) store_block_partial(bpart, mb, sat_w, under_w);
+}
+
+// Combines per-block partials into amax_out[0] (as binary32) and counts[0..1].
+__global__ __launch_bounds__(kBlock) void k_finish(const BlockPartial* __restrict__ bp, int n,
+                                                   float* amax_out,
+                                                   unsigned long long* counts) {
+  __shared__ uint32_t sh[kWaves];
+  __shared__ unsigned long long sh_s[kWaves], sh_u[kWaves];
+  uint32_t m = 0;
+  unsigned long long s = 0, u = 0;
+  for (int i = threadIdx.x; i < n; i += kBlock) {
+    m = max(m, bp[i].amax_bits);
+    s += bp[i].sat;
+    u += bp[i].under;
+  }
+  m = block_max_u32(m, sh);
+  s = wave_sum_u64(s);
+  u = wave_sum_u64(u);
+  if ((threadIdx.x & 63) == 0) {
+    sh_s[threadIdx.x >> 6] = s;
+    sh_u[threadIdx.x >> 6] = u;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long ts = 0, tu = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      ts += sh_s[i];
+      tu += sh_u[i];
+    }
+    if (amax_out) amax_out[0] = __uint_as_float(m);
+    if (counts) {
+      counts[0] = ts;
+      counts[1] = tu;
+    }
+  }
+}
+
+// Combines pass-1 amax partials into one binary32 amax (fp8_amax per tensor).
+__global__ __launch_bounds__(kBlock) void k_combine_amax(const uint32_t* __restrict__ part, int n,
+                                                         float* amax_out) {
+  __shared__ uint32_t sh[kWaves];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kBlock) m = max(m, part[i]);
+  m = block_max_u32(m, sh);
+  if (threadIdx.x == 0) amax_out[0] = __uint_as_float(m);
+}
+
+// ---------------------------------------------------------------------------
+// Row groups: groups of one row and L octets (8L elements, L a power of two,
+// 2 <= L <= 64).  Each row is padded to nCg * L octets so every group spans
+// exactly L lanes; padding and ragged tail octets load as zero and are not
+// stored.  A unit of kBlock * U padded octets holds kBlock * U / L groups:
+// lanes reduce their group's maximum with shuffles, one thread per group
+// computes (s, r) into LDS, then every lane casts its octets.
+
+template <typename T, int F, int L, bool GIVEN, bool STATS, bool AMAX_ONLY>
+__global__ __launch_bounds__(kBlock) void k_rowgroups(
+    const T* __restrict__ x, uint32_t rows, uint32_t oct_cols, int64_t ldx, FastDiv div_opr,
+    uint32_t nCg, uint32_t units, uint8_t* __restrict__ q, int64_t ldq, float eps, int pow2,
+    float* s_io, float* r_io, float* amax_out, BlockPartial* bpart) {
+  constexpr int U = sizeof(T) == 2 ? 8 : 4;
+  constexpr int GPU = kBlock * U / L;  // groups per unit
+  __shared__ uint32_t sh_amax[GPU];
+  __shared__ float sh_r[GPU];
+  const uint32_t opr = nCg * L;
+  const int t = threadIdx.x;
+  unsigned long long sat_w = 0, under_w = 0;
+  for (uint32_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const uint32_t base = unit * (kBlock * U);
+    Octet<T> v[U];
+    uint32_t omb[U];
+    uint32_t row[U], oc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t po = base + u * kBlock + t;
+      row[u] = div_opr.div(po);
+      oc[u] = po - row[u] * opr;
+      if (row[u] < rows && oc[u] < oct_cols) v[u].load_nt(x + static_cast<int64_t>(row[u]) * ldx + oc[u] * 8);
+      else v[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      omb[u] = v[u].absmax_bits();
+      const uint32_t gm = segment_max_u32<L>(omb[u]);
+      if ((t & (L - 1)) == 0) sh_amax[(u * kBlock + t) / L] = gm;
+    }
+    __syncthreads();
+    for (int gi = t; gi < GPU; gi += kBlock) {
+      const uint32_t po = base + gi * L;
+      const uint32_t gr = div_opr.div(po);
+      if (gr < rows) {
+        const uint32_t cg = (po - gr * opr) / L;
+        const int64_t g = static_cast<int64_t>(gr) * nCg + cg;
+        const float a = __uint_as_float(sh_amax[gi]);
+        if (amax_out) amax_out[g] = a;
+        if constexpr (!AMAX_ONLY) {
+          float s, r;
+          if constexpr (GIVEN) {
+            s = s_io[g];
+            r = r_io ? r_io[g] : 1.0f / s;
+          } else {
+            scale_from_amax(a, Fmt<F>::kMax, eps, pow2 != 0, s, r);
+            s_io[g] = s;
+            if (r_io) r_io[g] = r;
+          }
+          sh_r[gi] = r;
+        }
+      }
+    }
+    if constexpr (!AMAX_ONLY) {
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (row[u] < rows && oc[u] < oct_cols) {
+          const float r = sh_r[(u * kBlock + t) / L];
+          const bool nan_path = omb[u] > kInfBits || !(fabsf(r) <= FLT_MAX);
+          const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
+          *reinterpret_cast<u32x2*>(q + static_cast<int64_t>(row[u]) * ldq + oc[u] * 8) = c;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (STATS) store_block_partial(bpart, 0, sat_w, under_w);
+}
+
+// ---------------------------------------------------------------------------
+// Block tiles: one workgroup per group of er x ec elements (any extents; the
+// last group along each dimension may be short).  REG: the group fits in
+// registers (<= kBlock * U octets) and is read once; otherwise it is read
+// twice (max, then cast; the second read mostly hits L2).
+
+template <typename T, int F, bool GIVEN, bool STATS, bool AMAX_ONLY, bool REG>
+__global__ __launch_bounds__(kBlock) void k_blocktile(
+    const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int64_t er, int64_t ec,
+    int64_t nCg, int64_t ngroups, FastDiv div_full, FastDiv div_tail, uint8_t* __restrict__ q,
+    int64_t ldq, float eps, int pow2, float* s_io, float* r_io, float* amax_out,
+    BlockPartial* bpart) {
+  constexpr int U = sizeof(T) == 2 ? 8 : 4;
+  __shared__ uint32_t sh[kWaves];
+  __shared__ float sh_r;
+  const int t = threadIdx.x;
+  unsigned long long sat_w = 0, under_w = 0;
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const int64_t gi = g / nCg, gj = g - gi * nCg;
+    const int64_t r0 = gi * er, c0 = gj * ec;
+    const int64_t nr = min(er, rows - r0);
+    const int64_t ncol = min(ec, cols - c0);
+    const uint32_t oct_row = static_cast<uint32_t>(ncol / 8);
+    const FastDiv& dv = (ncol == ec) ? div_full : div_tail;
+    const uint32_t n_oct = static_cast<uint32_t>(nr) * oct_row;
+    const T* xg = x + r0 * ldx + c0;
+    uint8_t* qg = q + r0 * ldq + c0;
+    uint32_t mb = 0;
+    Octet<T> v[REG ? U : 1];
+    if constexpr (REG) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t o = u * kBlock + t;
+        if (o < n_oct) {
+          const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
+          v[u].load_nt(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
+        } else {
+          v[u].zero();
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) mb = max(mb, v[u].absmax_bits());
+    } else {
+      for (uint32_t o = t; o < n_oct; o += kBlock) {
+        const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
+        v[0].load(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
+        mb = max(mb, v[0].absmax_bits());
+      }
+    }
+    const uint32_t gmb = block_max_u32(mb, sh);
+    const float a = __uint_as_float(gmb);
+    if (t == 0) {
+      if (amax_out) amax_out[g] = a;
+      if constexpr (!AMAX_ONLY) {
+        float s, r;
+        if constexpr (GIVEN) {
+          s = s_io[g];
+          r = r_io ? r_io[g] : 1.0f / s;
+        } else {
+          scale_from_amax(a, Fmt<F>::kMax, eps, pow2 != 0, s, r);
+          s_io[g] = s;
+          if (r_io) r_io[g] = r;
+        }
+        sh_r = r;
+      }
+    }
+    if constexpr (!AMAX_ONLY) {
+      __syncthreads();
+      const float r = sh_r;
+      const bool r_bad = !(fabsf(r) <= FLT_MAX);
+      if constexpr (REG) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t o = u * kBlock + t;
+          if (o < n_oct) {
+            const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
+            const bool nan_path = r_bad || v[u].absmax_bits() > kInfBits;
+            const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
+            *reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8) = c;
+          }
+        }
+      } else {
+        for (uint32_t o = t; o < n_oct; o += kBlock) {
+          const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
+          v[0].load_nt(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
+          const bool nan_path = r_bad || v[0].absmax_bits() > kInfBits;
+          const u32x2 c = cast_octet<T, F, STATS>(v[0], r, nan_path, sat_w, under_w);
+          *reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8) = c;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (STATS) store_block_partial(bpart, 0, sat_w, under_w);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+
+namespace {
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <typename T, int F>
+hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
+  // A contiguous tensor is one long row for per-tensor work.
+  int64_t rows = a.rows, cols = a.cols;
+  if (a.ldx == a.cols && a.ldq == a.cols) {
+    cols = a.rows * a.cols;
+    rows = 1;
+  }
+  const int64_t opr = cols / 8;
+  constexpr int U = oct_unroll<T>();
+  const int64_t seg = static_cast<int64_t>(kBlock) * U;
+  const int64_t spr = ceil_div(opr, seg);
+  const int64_t nseg = rows * spr;
+  const int cus = device_cus();
+  const bool given = a.mode == FP8RT_GIVEN;
+  const bool stats = a.counts != nullptr;
+  const bool need_bp = (given && a.amax_out) || stats;
+
+  const int grid_amax = static_cast<int>(std::min<int64_t>(nseg, 2 * cus));
+  const int grid_cast = static_cast<int>(std::min<int64_t>(nseg, 8 * cus));
+  CallScratch scratch(st);
+  const size_t part_bytes = given ? 0 : sizeof(uint32_t) * grid_amax;
+  const size_t bp_bytes = need_bp ? sizeof(BlockPartial) * grid_cast : 0;
+  hipError_t e = scratch.alloc(part_bytes + bp_bytes + 16);
+  if (e != hipSuccess) return e;
+  uint32_t* part = static_cast<uint32_t*>(scratch.get());
+  BlockPartial* bp = reinterpret_cast<BlockPartial*>(static_cast<char*>(scratch.get()) +
+                                                     ((part_bytes + 15) / 16) * 16);
+  const T* x = static_cast<const T*>(a.x);
+  if (a.amax_only) {
+    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid_amax), dim3(kBlock), 0, st, x, rows, opr, a.ldx,
+                       spr, part);
+    hipLaunchKernelGGL(k_combine_amax, dim3(1), dim3(kBlock), 0, st, part, grid_amax, a.amax_out);
+    return hipGetLastError();
+  }
+  if (!given) {
+    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid_amax), dim3(kBlock), 0, st, x, rows, opr, a.ldx,
+                       spr, part);
+    if (stats)
+      hipLaunchKernelGGL((k_tensor_cast<T, F, false, true>), dim3(grid_cast), dim3(kBlock), 0, st,
+                         x, rows, opr, a.ldx, spr, a.q, a.ldq, part, grid_amax, a.eps, a.pow2,
+                         nullptr, nullptr, a.scale, a.inv_scale, a.amax_out, bp);
+    else
+      hipLaunchKernelGGL((k_tensor_cast<T, F, false, false>), dim3(grid_cast), dim3(kBlock), 0, st,
+                         x, rows, opr, a.ldx, spr, a.q, a.ldq, part, grid_amax, a.eps, a.pow2,
+                         nullptr, nullptr, a.scale, a.inv_scale, a.amax_out, bp);
+  } else {
+    if (stats)
+      hipLaunchKernelGGL((k_tensor_cast<T, F, true, true>), dim3(grid_cast), dim3(kBlock), 0, st, x,
+                         rows, opr, a.ldx, spr, a.q, a.ldq, nullptr, 0, a.eps, a.pow2, a.scale,
+                         a.inv_scale, nullptr, nullptr, nullptr, bp);
+    else
+      hipLaunchKernelGGL((k_tensor_cast<T, F, true, false>), dim3(grid_cast), dim3(kBlock), 0, st,
+                         x, rows, opr, a.ldx, spr, a.q, a.ldq, nullptr, 0, a.eps, a.pow2, a.scale,
+                         a.inv_scale, nullptr, nullptr, nullptr, bp);
+  }
+  if (need_bp)
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, bp, grid_cast,
+                       given ? a.amax_out : nullptr, a.counts);
+  return hipGetLastError();
+}
+
+template <typename T, int F, int L, bool GIVEN, bool STATS, bool AO>
+void launch_rowgroups_t(const QuantArgs& a, hipStream_t st, int grid, uint32_t units, FastDiv dv,
+                        uint32_t nCg, BlockPartial* bp) {
+  hipLaunchKernelGGL((k_rowgroups<T, F, L, GIVEN, STATS, AO>), dim3(grid), dim3(kBlock), 0, st,
+                     static_cast<const T*>(a.x), static_cast<uint32_t>(a.rows),
+                     static_cast<uint32_t>(a.cols / 8), a.ldx, dv, nCg, units, a.q, a.ldq, a.eps,
+                     a.pow2, a.scale, a.inv_scale, a.amax_out, bp);
+}
+
+template <typename T, int F, int L>
+void rowgroups_dispatch(const QuantArgs& a, hipStream_t st, int grid, uint32_t units, FastDiv dv,
+                        uint32_t nCg, BlockPartial* bp) {
+  const bool given = a.mode == FP8RT_GIVEN, stats = a.counts != nullptr;
+  if (a.amax_only) launch_rowgroups_t<T, F, L, false, false, true>(a, st, grid, units, dv, nCg, bp);
+  else if (given && stats) launch_rowgroups_t<T, F, L, true, true, false>(a, st, grid, units, dv, nCg, bp);
+  else if (given) launch_rowgroups_t<T, F, L, true, false, false>(a, st, grid, units, dv, nCg, bp);
+  else if (stats) launch_rowgroups_t<T, F, L, false, true, false>(a, st, grid, units, dv, nCg, bp);
+  else launch_rowgroups_t<T, F, L, false, false, false>(a, st, grid, units, dv, nCg, bp);
+}
+
+template <typename T, int F>
+hipError_t quant_rowgroups(const QuantArgs& a, int L, hipStream_t st) {
+  constexpr int U = sizeof(T) == 2 ? 8 : 4;
+  const int64_t nCg = ceil_div(a.cols, a.ec);
+  const int64_t padded = a.rows * nCg * L;
+  const uint32_t units = static_cast<uint32_t>(ceil_div(padded, static_cast<int64_t>(kBlock) * U));
+  const int grid = static_cast<int>(std::min<int64_t>(units, 8 * device_cus()));
+  const bool stats = a.counts != nullptr;
+  CallScratch scratch(st);
+  hipError_t e = scratch.alloc(stats ? sizeof(BlockPartial) * grid : 16);
+  if (e != hipSuccess) return e;
+  BlockPartial* bp = static_cast<BlockPartial*>(scratch.get());
+  const FastDiv dv(static_cast<uint32_t>(nCg * L));
+  const uint32_t ncg = static_cast<uint32_t>(nCg);
+  switch (L) {
+    case 2: rowgroups_dispatch<T, F, 2>(a, st, grid, units, dv, ncg, bp); break;
+    case 4: rowgroups_dispatch<T, F, 4>(a, st, grid, units, dv, ncg, bp); break;
+    case 8: rowgroups_dispatch<T, F, 8>(a, st, grid, units, dv, ncg, bp); break;
+    case 16: rowgroups_dispatch<T, F, 16>(a, st, grid, units, dv, ncg, bp); break;
+    case 32: rowgroups_dispatch<T, F, 32>(a, st, grid, units, dv, ncg, bp); break;
+    case 64: rowgroups_dispatch<T, F, 64>(a, st, grid, units, dv, ncg, bp); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (stats) hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, bp, grid, nullptr, a.counts);
+  return hipGetLastError();
+}
+
+template <typename T, int F, bool GIVEN, bool STATS, bool AO, bool REG>
+void launch_blocktile_t(const QuantArgs& a, hipStream_t st, int grid, int64_t nCg, int64_t ng,
+                        FastDiv df, FastDiv dt, BlockPartial* bp) {
+  hipLaunchKernelGGL((k_blocktile<T, F, GIVEN, STATS, AO, REG>), dim3(grid), dim3(kBlock), 0, st,
+                     static_cast<const T*>(a.x), a.rows, a.cols, a.ldx, a.er, a.ec, nCg, ng, df, dt,
+                     a.q, a.ldq, a.eps, a.pow2, a.scale, a.inv_scale, a.amax_out, bp);
+}
+
+template <typename T, int F, bool REG>
+void blocktile_dispatch(const QuantArgs& a, hipStream_t st, int grid, int64_t nCg, int64_t ng,
+                        FastDiv df, FastDiv dt, BlockPartial* bp) {
+  const bool given = a.mode == FP8RT_GIVEN, stats = a.counts != nullptr;
+  if (a.amax_only) launch_blocktile_t<T, F, false, false, true, REG>(a, st, grid, nCg, ng, df, dt, bp);
+  else if (given && stats) launch_blocktile_t<T, F, true, true, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
+  else if (given) launch_blocktile_t<T, F, true, false, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
+  else if (stats) launch_blocktile_t<T, F, false, true, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
+  else launch_blocktile_t<T, F, false, false, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
+}
+
+template <typename T, int F>
+hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
+  constexpr int U = sizeof(T) == 2 ? 8 : 4;
+  const int64_t nCg = ceil_div(a.cols, a.ec);
+  const int64_t ng = ceil_div(a.rows, a.er) * nCg;
+  const int grid = static_cast<int>(std::min<int64_t>(ng, 8 * device_cus()));
+  const bool stats = a.counts != nullptr;
+  CallScratch scratch(st);
+  hipError_t e = scratch.alloc(stats ? sizeof(BlockPartial) * grid : 16);
+  if (e != hipSuccess) return e;
+  BlockPartial* bp = static_cast<BlockPartial*>(scratch.get());
+  const int64_t tail = a.cols - (nCg - 1) * a.ec;
+  const FastDiv df(static_cast<uint32_t>(a.ec / 8)), dt(static_cast<uint32_t>(tail / 8));
+  const bool reg = a.er * (a.ec / 8) <= static_cast<int64_t>(kBlock) * U;
+  if (reg) blocktile_dispatch<T, F, true>(a, st, grid, nCg, ng, df, dt, bp);
+  else blocktile_dispatch<T, F, false>(a, st, grid, nCg, ng, df, dt, bp);
+  if (stats) hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, bp, grid, nullptr, a.counts);
+  return hipGetLastError();
+}
+
+template <typename T, int F>
+hipError_t quant_typed(const QuantArgs& a, hipStream_t st) {
+  if (a.er == a.rows && a.ec == a.cols) return quant_tensor<T, F>(a, st);
+  if (a.er == 1) {
+    const int64_t L = a.ec / 8;
+    // L is a power of two in [2, 64] and the padded octet space fits 31 bits
+    const bool pow2L = L >= 2 && L <= 64 && (L & (L - 1)) == 0;
+    if (pow2L && a.rows * ceil_div(a.cols, a.ec) * L < (int64_t(1) << 31) - 4096)
+      return quant_rowgroups<T, F>(a, static_cast<int>(L), st);
+  }
+  return quant_blocktile<T, F>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
+  if (a.xt == FP8RT_BF16) {
+    return a.fmt == FP8RT_E4M3 ? quant_typed<uint16_t, kE4M3>(a, st)
+                               : quant_typed<uint16_t, kE5M2>(a, st);
+  }
+  return a.fmt == FP8RT_E4M3 ? quant_typed<float, kE4M3>(a, st) : quant_typed<float, kE5M2>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Scale from amax, elementwise.
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_compute_scale(const float* __restrict__ amax, int64_t n,
+                                                          float eps, int pow2, float* s_out,
+                                                          float* r_out) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kBlock) {
+    float s, r;
+    scale_from_amax(amax[i], Fmt<F>::kMax, eps, pow2 != 0, s, r);
+    s_out[i] = s;
+    if (r_out) r_out[i] = r;
+  }
+}
+
+hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, float eps, int pow2,
+                                float* scale, float* inv_scale, hipStream_t st) {
+  const int grid = static_cast<int>(std::min<int64_t>(ceil_div(n, kBlock), 4 * device_cus()));
+  if (fmt == FP8RT_E4M3)
+    hipLaunchKernelGGL(k_compute_scale<kE4M3>, dim3(grid), dim3(kBlock), 0, st, amax, n, eps, pow2,
+                       scale, inv_scale);
+  else
+    hipLaunchKernelGGL(k_compute_scale<kE5M2>, dim3(grid), dim3(kBlock), 0, st, amax, n, eps, pow2,
+                       scale, inv_scale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: y = fl32(s_g * dec(code)); bf16 output rounds that binary32 to
+// nearest even (NaN -> 0x7FC0).  The hardware decode of one code is exact.
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & kAbsMask) > kInfBits) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int F>
+__device__ __forceinline__ void decode4(uint32_t w, float* out) {
+  if constexpr (F == kE4M3) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+  } else {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+  }
+}
+
+template <int F, bool BF16OUT>
+__global__ __launch_bounds__(kBlock) void k_dequantize(const uint8_t* __restrict__ q, int64_t rows,
+                                                       int64_t cols, int64_t ldq, int64_t er,
+                                                       FastDiv div_ec, int64_t nCg,
+                                                       const float* __restrict__ scale, void* y,
+                                                       int64_t ldy) {
+  const int64_t opr = cols / 8;
+  const int64_t total = rows * opr;
+  for (int64_t o = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; o < total;
+       o += static_cast<int64_t>(gridDim.x) * kBlock) {
+    const int64_t r = o / opr;
+    const int64_t c = (o - r * opr) * 8;
+    const u32x2 w = *reinterpret_cast<const u32x2*>(q + r * ldq + c);
+    const float s = scale[(r / er) * nCg + div_ec.div(static_cast<uint32_t>(c))];
+    float d[8];
+    decode4<F>(w[0], d);
+    decode4<F>(w[1], d + 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = s * d[i];
+    if constexpr (BF16OUT) {
+      u32x4 o4;
+      o4[0] = f32_to_bf16_bits(d[0]) | (f32_to_bf16_bits(d[1]) << 16);
+      o4[1] = f32_to_bf16_bits(d[2]) | (f32_to_bf16_bits(d[3]) << 16);
+      o4[2] = f32_to_bf16_bits(d[4]) | (f32_to_bf16_bits(d[5]) << 16);
+      o4[3] = f32_to_bf16_bits(d[6]) | (f32_to_bf16_bits(d[7]) << 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + r * ldy + c) = o4;
+    } else {
+      u32x4* yp = reinterpret_cast<u32x4*>(static_cast<float*>(y) + r * ldy + c);
+      yp[0] = u32x4{__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]), __float_as_uint(d[3])};
+      yp[1] = u32x4{__float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]), __float_as_uint(d[7])};
+    }
+  }
+}
+
+hipError_t launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
+                             int64_t er, int64_t ec, const float* scale, void* y, int yt,
+                             int64_t ldy, hipStream_t st) {
+  const int64_t total = rows * (cols / 8);
+  const int grid = static_cast<int>(std::min<int64_t>(ceil_div(total, kBlock), 8 * device_cus()));
+  const FastDiv dv(static_cast<uint32_t>(ec));
+  const int64_t nCg = ceil_div(cols, ec);
+  if (fmt == FP8RT_E4M3) {
+    if (yt == FP8RT_BF16)
+      hipLaunchKernelGGL((k_dequantize<kE4M3, true>), dim3(grid), dim3(kBlock), 0, st, q, rows, cols,
+                         ldq, er, dv, nCg, scale, y, ldy);
+    else
+      hipLaunchKernelGGL((k_dequantize<kE4M3, false>), dim3(grid), dim3(kBlock), 0, st, q, rows,
+                         cols, ldq, er, dv, nCg, scale, y, ldy);
+  } else {
+    if (yt == FP8RT_BF16)
+      hipLaunchKernelGGL((k_dequantize<kE5M2, true>), dim3(grid), dim3(kBlock), 0, st, q, rows, cols,
+                         ldq, er, dv, nCg, scale, y, ldy);
+    else
+      hipLaunchKernelGGL((k_dequantize<kE5M2, false>), dim3(grid), dim3(kBlock), 0, st, q, rows,
+                         cols, ldq, er, dv, nCg, scale, y, ldy);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Delayed scaling: one wave pushes a_t into the ring, takes the window
+// maximum (integer max of the binary32 patterns of non-negative entries, NaN
+// kept), and derives the next step's (s, r) on the device.
+
+template <int F>
+__global__ __launch_bounds__(64) void k_history_update(float* history, int32_t len, int32_t* head,
+                                                       const float* amax_new, float eps, int pow2,
+                                                       float* s_next, float* r_next) {
+  const int lane = threadIdx.x;
+  int32_t h = head[0];
+  h = ((h % len) + len) % len;
+  const float an = amax_new[0];
+  uint32_t m = 0;
+  for (int i = lane; i < len; i += 64) {
+    const float v = (i == h) ? an : history[i];
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t key = ((b & kAbsMask) > kInfBits) ? kQNaN : (v > 0.0f ? b : 0u);
+    m = max(m, key);
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) {
+    history[h] = an;
+    head[0] = (h + 1) % len;
+    float s, r;
+    scale_from_amax(__uint_as_float(m), Fmt<F>::kMax, eps, pow2 != 0, s, r);
+    s_next[0] = s;
+    if (r_next) r_next[0] = r;
+  }
+}
+
+hipError_t launch_history_update(float* history, int32_t len, int32_t* head, const float* amax_new,
+                                 int fmt, float eps, int pow2, float* scale_next,
+                                 float* inv_scale_next, hipStream_t st) {
+  if (fmt == FP8RT_E4M3)
+    hipLaunchKernelGGL(k_history_update<kE4M3>, dim3(1), dim3(64), 0, st, history, len, head,
+                       amax_new, eps, pow2, scale_next, inv_scale_next);
+  else
+    hipLaunchKernelGGL(k_history_update<kE5M2>, dim3(1), dim3(64), 0, st, history, len, head,
+                       amax_new, eps, pow2, scale_next, inv_scale_next);
+  return hipGetLastError();
+}
+
+}  // namespace fp8rt

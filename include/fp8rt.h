@@ -1,0 +1,166 @@
+/*
+ * fp8rt.h -- C ABI of the MI355X (gfx950) FP8 runtime chain:
+ *   amax reduction -> scale s = amax / F_max -> saturating round-to-nearest-
+ *   even cast to OCP E4M3 / E5M2 codes -> scaled GEMM with FP32 accumulation.
+ *
+ * Sources (page title, then section):
+ *  [P2] "FP8 formats and scaling for LLM inference" (charlestar.github.io)
+ *  [P4] "FP8 production quantization guide" (m.xxqk.cn)
+ *  [P5] "FP8 inference: E4M3/E5M2 and the NVIDIA FP8 ecosystem" (plumephp.com)
+ *  [P3] "Quantization W8A16" (datawhalechina llm-algo-leetcode ch.25)
+ *
+ * Conventions shared by every entry point
+ *  - Every array pointer is a caller-owned DEVICE pointer (HBM of the current
+ *    HIP device).  The library allocates nothing that outlives a call, keeps
+ *    no global state and is reentrant.  Work is enqueued on `stream` and the
+ *    call returns without synchronizing; results are valid once the stream
+ *    reaches that point.
+ *  - Matrices are row-major with a leading dimension in ELEMENTS (ldx >= cols).
+ *  - Arguments are validated on the host before anything is launched; on an
+ *    error nothing is written and nothing is enqueued.
+ *  - Non-finite data are not errors: a NaN in a group makes its amax, scale
+ *    and inverse scale NaN and its codes 0x7F; +-Inf saturates to the largest
+ *    finite code and is counted as saturated.
+ *  - Scale arrays are fp32, row-major [ceil(rows/gr)][ceil(cols/gc)] where
+ *    (gr, gc) is the granularity with 0 meaning "the whole dimension"; the last
+ *    group along a dimension may be short and is kept [P3, Step 2 granularity
+ *    table: per-group scale count out x ceil(in/group)].
+ *  - s is the DEQUANTIZATION scale stored with the codes (x ~ s * dec(code),
+ *    [P2 "How a scale fits a tensor into E4M3"]); r is the quantization
+ *    multiplier.  Dynamic scales: a_c = max(amax, eps), s = fl32(a_c / F_max),
+ *    r = fl32(F_max / a_c) [P2 same section; P4 dynamic quantize listing].
+ */
+#ifndef FP8RT_H
+#define FP8RT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8rt_status {
+    FP8RT_OK = 0,
+    FP8RT_EINVAL = 1,       /* null required pointer, dims <= 0, ld < cols, bad eps /
+                               history length / head, granularity not allowed for the op */
+    FP8RT_EALIGN = 2,       /* cols, K, a leading dimension or a group width not a multiple
+                               of 16, or a base pointer not 16-byte aligned ([P2 "Hardware
+                               support ..." notes dims divisible by 16 for FP8 linears) */
+    FP8RT_EUNSUPPORTED = 3, /* GEMM format pair / scale-granularity combination not built */
+    FP8RT_EHIP = 4          /* a HIP launch error */
+} fp8rt_status;
+
+/* [P2 "How the 8 bits are allocated"]: E4M3 max finite 448, E5M2 max finite
+ * 57344; [P5 "numeric properties"]: bias 7 and 15.  E4M3 is the OCP "fn"
+ * variant (no Inf, NaN = 0x7F/0xFF); E5M2 has IEEE-style Inf/NaN. */
+typedef enum fp8rt_format { FP8RT_E4M3 = 0, FP8RT_E5M2 = 1 } fp8rt_format;
+
+typedef enum fp8rt_dtype { FP8RT_F32 = 0, FP8RT_BF16 = 1 } fp8rt_dtype;
+
+/* Group extent of one scale [P2 "Per-channel and block scaling"]:
+ *   per-tensor {0,0} | per-row / per-token / per-output-channel {1,0} |
+ *   per-group along K {1,128} | per-block {128,128} | MX-style {1,32}. */
+typedef struct fp8rt_gran {
+    int32_t rows;
+    int32_t cols;
+} fp8rt_gran;
+
+/* Where the scale comes from [P2 "Current scaling", "Delayed scaling",
+ * "Weight scale and activation scale lifetimes"]. */
+typedef enum fp8rt_mode {
+    FP8RT_DYNAMIC = 0, /* current scaling: amax of this tensor -> s, r */
+    FP8RT_GIVEN = 1    /* static or delayed: s (and optionally r) supplied */
+} fp8rt_mode;
+
+/* fp8_scaled_gemm flags */
+#define FP8RT_POW2_SCALES 1u /* every scale is a power of two (enables 1x32 scaled MFMA) */
+
+/* Per-group amax a_g = max |x| over each group [P2 "How a scale fits a tensor
+ * into E4M3" (a_max = max|X|), "Per-channel and block scaling" (a_g)].
+ *   x     : [rows x cols] fp32 or bf16, leading dimension ldx (elements)
+ *   g     : granularity; amax receives ceil(rows/gr) * ceil(cols/gc) floats
+ * Exact (integer max on |x| bit patterns); NaN propagates. */
+fp8rt_status fp8_amax(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                      fp8rt_gran g, float* amax, hipStream_t stream);
+
+/* Scales from amax [P2 "How a scale fits a tensor into E4M3": s = a/F_max and
+ * the recipe option of power-of-two rounding; P4 dynamic quantize listing:
+ * eps clamp, scale and inv_scale].
+ *   amax[n] -> scale[n] = s, inv_scale[n] = r (inv_scale may be NULL).
+ *   eps: finite, >= 2^-96 (keeps r finite).  pow2_round_up != 0: s is rounded
+ *   up to 2^ceil(log2 s) and r = 1/s exactly. */
+fp8rt_status fp8_compute_scale(const float* amax, int64_t n, fp8rt_format f, float eps,
+                               int32_t pow2_round_up, float* scale, float* inv_scale,
+                               hipStream_t stream);
+
+/* Scale + saturating cast [P2 "How a scale fits a tensor into E4M3":
+ * X_fp8 = cast(clip(X/s)); P4 listing: x * inv_scale, clamp to +-F_max, cast;
+ * P2 "What numerical validation looks at": saturation and underflow rates].
+ *   x        : [rows x cols] fp32 / bf16 (ldx); q: [rows x cols] uint8 codes (ldq)
+ *   DYNAMIC  : per-group amax -> s, r written to scale / inv_scale (inv_scale
+ *              may be NULL); codes use r.
+ *   GIVEN    : scale is read (static calibration or delayed history); inv_scale
+ *              is read if non-NULL, else r = fl32(1/s).  eps / pow2 ignored.
+ *   amax_out : nullable; the observed per-group amax (for delayed scaling).
+ *   sat_underflow : nullable uint64[2], OVERWRITTEN with {#|fl32(x*r)| > F_max,
+ *              #(x != 0 and code is +-0)}.
+ *   v = fl32(x * r); code = RNE onto the OCP grid (subnormals included) of
+ *   clamp(v, -F_max, F_max); NaN -> 0x7F.
+ * Alignment: cols, ldx, ldq and the group width (if not whole-row) are
+ * multiples of 16, pointers 16-byte aligned.  Per-tensor DYNAMIC runs two
+ * kernels (amax, then cast); all other granularities run one fused pass. */
+fp8rt_status fp8_quantize(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,
+                          int64_t ldx, fp8rt_gran g, fp8rt_format f, fp8rt_mode mode,
+                          float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
+                          uint8_t* q, int64_t ldq, float* amax_out, uint64_t* sat_underflow,
+                          hipStream_t stream);
+
+/* Dequantize [P2 "How a scale fits a tensor into E4M3": X_hat = s * X_fp8;
+ * P5 dequantization example].  y = fl32(s_g * dec(code)); a bf16 output is
+ * that binary32 rounded to nearest even.  q: [rows x cols] (ldq), y (ldy). */
+fp8rt_status fp8_dequantize(const uint8_t* q, fp8rt_format f, int64_t rows, int64_t cols,
+                            int64_t ldq, fp8rt_gran g, const float* scale, void* y,
+                            fp8rt_dtype yt, int64_t ldy, hipStream_t stream);
+
+/* Delayed scaling step [P2 "Delayed scaling": s_{t+1} = f(a_t..a_{t-h+1})/F_max,
+ * f = window maximum].  One wave on the device:
+ *   history[*head] = *amax_new; *head = (*head + 1) % len;
+ *   a = max(history[0..len)); scale_next = s(a), inv_scale_next = r(a).
+ *   history: fp32[len] caller-owned ring, zero-initialised by the caller;
+ *   head: int32 device scalar in [0, len) (checked on the device: an out-of-
+ *   range head is reduced modulo len); len in [1, 1024].
+ * Cold start (no history yet): call fp8_amax on the first tensor, then this
+ * function, and quantize step 0 with the result (current scaling). */
+fp8rt_status fp8_amax_history_update(float* history, int32_t len, int32_t* head,
+                                     const float* amax_new, fp8rt_format f, float eps,
+                                     int32_t pow2_round_up, float* scale_next,
+                                     float* inv_scale_next, hipStream_t stream);
+
+/* Scaled GEMM on FP8 MFMA [P2 "The full precision contract of one FP8 GEMM":
+ * Y ~ s_x s_w (X8 W8), higher-precision accumulation, BF16/FP32 output, bias;
+ * P4 GEMM listing: scale_a, scale_b, out_dtype, bias].
+ *   Y[m,n] = sum_k s_a(m,k) s_b(n,k) dec(A[m,k]) dec(B[n,k]) + bias[n]
+ *   a : [M x K] codes (lda), format fa, scales scale_a with granularity ga
+ *   b : [N x K] codes (ldb) -- the nn.Linear weight layout, K contiguous
+ *   bias : nullable, [N] fp32 / bf16;  y : [M x N] fp32 / bf16 (ldy)
+ * Format pairs: E4M3 x E4M3 and E5M2 x E4M3.
+ * Granularities: A in {tensor, row {1,0}, K-group {1,g}}, B in {tensor, row,
+ * block {gr,g}} with g a multiple of 128 and equal for A and B when both are
+ * K-blocked; or {1,32} on both with FP8RT_POW2_SCALES (hardware-scaled MFMA).
+ * Accumulation is FP32 on the matrix cores; K-blocked scales are applied once
+ * per 128-deep K step.  Alignment: K, lda, ldb multiples of 16; M, N any. */
+fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                             const float* scale_a, const uint8_t* b, fp8rt_format fb,
+                             int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
+                             int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
+                             void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
+                             hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fp8rt_status_string(fp8rt_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8RT_H */

@@ -18,7 +18,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "fp8_oracle.c")
+_SRCS = [os.path.join(_HERE, "fp8_oracle.c"), os.path.join(_HERE, "fp8_dot_bound.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 E4M3, E5M2 = 0, 1
@@ -32,7 +32,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-std=c99", "-O2", "-Wall", "-fPIC", "-shared",
-                               "-o", tmp, _SRC, "-lm"])
+                               "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -71,6 +71,9 @@ def lib():
         L.orc_gemm_points.argtypes = gemm_args + [P]
         L.orc_gemm_points_exact.restype = I
         L.orc_gemm_points_exact.argtypes = gemm_args
+        L.orc_dot_truncation_bound.restype = I
+        L.orc_dot_truncation_bound.argtypes = [P, I, I64, I64, I64, P, P, I, I64, I64, I64, P, I64,
+                                               I64, I64, P, P, I64, P]
         L.orc_round_bf16.restype = C.c_uint16
         L.orc_round_bf16.argtypes = [D]
         L.orc_round_bf16_from_f32.restype = C.c_uint16
@@ -232,6 +235,25 @@ def gemm_full(a, fa, sa, ga, b, fb, sb, gb, bias=None):
     mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     y, S = gemm_points(a, fa, sa, ga, b, fb, sb, gb, mm.ravel(), nn.ravel(), bias)
     return y.reshape(M, N), S.reshape(M, N)
+
+
+def dot_truncation_bound(a, fa, sa, ga, b, fb, sb, gb, m_idx, n_idx):
+    """Tolerance term for the matrix-core FP8 dot product (see fp8_dot_bound.c)."""
+    a, b, M, N, K, sa, sb, _, _ = _gemm_common(a, fa, sa, ga, b, fb, sb, gb, None)
+    m_idx = np.ascontiguousarray(m_idx, np.int64)
+    n_idx = np.ascontiguousarray(n_idx, np.int64)
+    out = np.empty(m_idx.size, np.float64)
+    _check(lib().orc_dot_truncation_bound(_ptr(a), fa, K, ga[0], ga[1], _ptr(sa), _ptr(b), fb, K,
+                                          gb[0], gb[1], _ptr(sb), M, N, K, _ptr(m_idx),
+                                          _ptr(n_idx), m_idx.size, _ptr(out)),
+           "dot_truncation_bound")
+    return out
+
+
+def dot_truncation_bound_full(a, fa, sa, ga, b, fb, sb, gb):
+    M, N = a.shape[0], b.shape[0]
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    return dot_truncation_bound(a, fa, sa, ga, b, fb, sb, gb, mm.ravel(), nn.ravel()).reshape(M, N)
 
 
 def round_bf16(v) -> np.ndarray:

@@ -114,6 +114,14 @@ int orc_gemm_points_exact(const uint8_t* a, int fa, int64_t lda, int64_t gra, in
                           int64_t N, int64_t K, const void* bias, int bias_dtype,
                           const int64_t* m, const int64_t* n, int64_t npts, double* y);
 
+/* Tolerance helper (fp8_dot_bound.c): bound on the truncation error of the
+ * matrix-core FP8 dot product at points (m[i], n[i]); see that file. */
+int orc_dot_truncation_bound(const uint8_t* a, int fa, int64_t lda, int64_t gra, int64_t gca,
+                             const float* sa, const uint8_t* b, int fb, int64_t ldb,
+                             int64_t grb, int64_t gcb, const float* sb, int64_t M, int64_t N,
+                             int64_t K, const int64_t* m, const int64_t* n, int64_t npts,
+                             double* bound);
+
 /* Round a binary64 value to bfloat16 (nearest, ties to even); returns bits. */
 uint16_t orc_round_bf16(double v);
 

@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, and rejects bad arguments with the
+documented status before anything is launched.  Every call here is invalid on
+purpose, so none of them reaches a kernel."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8rt.h")
+
+
+@pytest.fixture(scope="module")
+def rt():
+    import dynamic_scaling_scaled_amd as rt
+    if not os.path.exists(rt.LIB_PATH):
+        from dynamic_scaling_scaled_amd import _build
+        _build.build()
+    rt.lib()
+    return rt
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:fp8rt_status|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_six_entry_points():
+    names = declared_functions()
+    for n in ("fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_dequantize",
+              "fp8_amax_history_update", "fp8_scaled_gemm", "fp8rt_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(rt):
+    L = rt.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(rt):
+    L = rt.lib()
+    for s in range(5):
+        assert len(L.fp8rt_status_string(s)) > 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+FAKE_ODD = 0x10004
+
+
+def q(rt, **kw):
+    a = dict(x=FAKE, xt=rt.BF16, rows=16, cols=64, ldx=64, gran=(0, 0), f=rt.E4M3, mode=rt.DYNAMIC,
+             eps=1e-12, pow2=0, scale=FAKE, inv=None, qq=FAKE, ldq=64, amax=None, cnt=None)
+    a.update(kw)
+    return rt.lib().fp8_quantize(a["x"], a["xt"], a["rows"], a["cols"], a["ldx"], rt.Gran(*a["gran"]),
+                                 a["f"], a["mode"], a["eps"], a["pow2"], a["scale"], a["inv"],
+                                 a["qq"], a["ldq"], a["amax"], a["cnt"], None)
+
+
+def test_quantize_validation(rt):
+    assert q(rt, x=None) == rt.EINVAL
+    assert q(rt, qq=None) == rt.EINVAL
+    assert q(rt, scale=None) == rt.EINVAL
+    assert q(rt, rows=0) == rt.EINVAL
+    assert q(rt, cols=-16) == rt.EINVAL
+    assert q(rt, ldx=48) == rt.EINVAL
+    assert q(rt, ldq=32) == rt.EINVAL
+    assert q(rt, eps=0.0) == rt.EINVAL
+    assert q(rt, eps=float("nan")) == rt.EINVAL
+    assert q(rt, eps=1e-35) == rt.EINVAL
+    assert q(rt, f=2) == rt.EINVAL
+    assert q(rt, xt=7) == rt.EINVAL
+    assert q(rt, mode=5) == rt.EINVAL
+    assert q(rt, gran=(-1, 0)) == rt.EINVAL
+    assert q(rt, cols=40, ldx=48, ldq=48) == rt.EALIGN
+    assert q(rt, ldx=72) == rt.EALIGN
+    assert q(rt, ldq=72) == rt.EALIGN
+    assert q(rt, gran=(1, 24)) == rt.EALIGN
+    assert q(rt, x=FAKE + 8) == rt.EALIGN
+    assert q(rt, qq=FAKE + 4) == rt.EALIGN
+    assert q(rt, scale=FAKE + 2) == rt.EALIGN
+    assert q(rt, cnt=FAKE_ODD) == rt.EALIGN
+
+
+def test_amax_scale_dequant_history_validation(rt):
+    L = rt.lib()
+    G = rt.Gran
+    assert L.fp8_amax(None, 1, 16, 64, 64, G(0, 0), FAKE, None) == rt.EINVAL
+    assert L.fp8_amax(FAKE, 1, 16, 64, 64, G(0, 0), None, None) == rt.EINVAL
+    assert L.fp8_amax(FAKE, 1, 16, 60, 64, G(0, 0), FAKE, None) == rt.EALIGN
+    assert L.fp8_compute_scale(FAKE, 0, 0, 1e-12, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_compute_scale(FAKE, 4, 0, -1.0, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_compute_scale(FAKE, 4, 3, 1e-12, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_compute_scale(FAKE + 1, 4, 0, 1e-12, 0, FAKE, None, None) == rt.EALIGN
+    assert L.fp8_dequantize(FAKE, 0, 16, 64, 64, G(0, 0), FAKE, None, 0, 64, None) == rt.EINVAL
+    assert L.fp8_dequantize(FAKE, 0, 16, 64, 64, G(0, 0), FAKE, FAKE, 0, 32, None) == rt.EINVAL
+    assert L.fp8_dequantize(FAKE, 0, 16, 64, 64, G(0, 0), FAKE, FAKE + 8, 0, 64, None) == rt.EALIGN
+    assert L.fp8_amax_history_update(FAKE, 0, FAKE, FAKE, 0, 1e-12, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_amax_history_update(FAKE, 2000, FAKE, FAKE, 0, 1e-12, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_amax_history_update(None, 16, FAKE, FAKE, 0, 1e-12, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_amax_history_update(FAKE, 16, None, FAKE, 0, 1e-12, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_amax_history_update(FAKE, 16, FAKE, FAKE, 0, 0.0, 0, FAKE, None, None) == rt.EINVAL
+    assert L.fp8_amax_history_update(FAKE + 2, 16, FAKE, FAKE, 0, 1e-12, 0, FAKE, None, None) == rt.EALIGN
+
+
+def g(rt, **kw):
+    a = dict(a=FAKE, fa=rt.E4M3, lda=128, ga=(0, 0), sa=FAKE, b=FAKE, fb=rt.E4M3, ldb=128, gb=(0, 0),
+             sb=FAKE, M=64, N=64, K=128, bias=None, bt=0, y=FAKE, yt=rt.BF16, ldy=64, flags=0)
+    a.update(kw)
+    return rt.lib().fp8_scaled_gemm(a["a"], a["fa"], a["lda"], rt.Gran(*a["ga"]), a["sa"], a["b"],
+                                    a["fb"], a["ldb"], rt.Gran(*a["gb"]), a["sb"], a["M"], a["N"],
+                                    a["K"], a["bias"], a["bt"], a["y"], a["yt"], a["ldy"],
+                                    a["flags"], None)
+
+
+def test_gemm_validation(rt):
+    assert g(rt, a=None) == rt.EINVAL
+    assert g(rt, sb=None) == rt.EINVAL
+    assert g(rt, y=None) == rt.EINVAL
+    assert g(rt, M=0) == rt.EINVAL
+    assert g(rt, lda=64) == rt.EINVAL
+    assert g(rt, ldy=32) == rt.EINVAL
+    assert g(rt, flags=4) == rt.EINVAL
+    assert g(rt, fa=9) == rt.EINVAL
+    assert g(rt, K=120, lda=128, ldb=128) == rt.EALIGN
+    assert g(rt, lda=136) == rt.EALIGN
+    assert g(rt, a=FAKE + 8) == rt.EALIGN
+    assert g(rt, fb=rt.E5M2) == rt.EUNSUPPORTED                       # E4M3 x E5M2 not built
+    assert g(rt, fa=rt.E5M2, fb=rt.E5M2) == rt.EUNSUPPORTED
+    assert g(rt, K=512, lda=512, ldb=512, ga=(1, 128), gb=(128, 256)) == rt.EUNSUPPORTED  # K-blocks differ
+    assert g(rt, K=256, lda=256, ldb=256, ga=(1, 64), gb=(0, 0)) == rt.EUNSUPPORTED       # not a multiple of 128
+    assert g(rt, K=256, lda=256, ldb=256, ga=(1, 32), gb=(1, 32)) == rt.EUNSUPPORTED      # 1x32 needs POW2 flag
+    assert g(rt, K=256, lda=256, ldb=256, ga=(2, 128), gb=(0, 0)) == rt.EUNSUPPORTED      # A blocks span rows

@@ -1,0 +1,136 @@
+"""Parity of the HIP scaled GEMM with the CPU oracle (binary64 reference) on
+every output element, at sizes that span several 128x128 tiles with ragged
+M, N and K tails.  Operands are FP8 codes and scales produced by the ORACLE's
+quantizer from seeded normal data (the GEMM under test never feeds its own
+inputs).  Acceptance: fp32 |y - y_ref| <= 1e-5 * sum_k |s_a s_b a_k b_k| + T_hw,
+bf16 within one bf16 ulp of the rounded reference (see gpu_helpers), where
+T_hw bounds the truncation of the matrix cores' FP8 dot product (measured:
+8-product groups aligned to their largest exponent sum keep 13 bits below
+it).  The count of elements that need T_hw is printed and bounded."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import check_gemm, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    import dynamic_scaling_scaled_amd as rt
+    rt.lib()
+    return rt
+
+
+def operands(orc, seed, M, N, K, fa, fb, ga, gb, pow2):
+    g = np.random.default_rng(seed)
+    xa = g.standard_normal((M, K)).astype(np.float32)
+    xb = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    a, sa, _, _, _ = orc.quantize(xa, fa, ga, pow2=pow2)
+    b, sb, _, _, _ = orc.quantize(xb, fb, gb, pow2=pow2)
+    return a, sa, b, sb
+
+
+def run_gemm(rt, a, fa, ga, sa, b, fb, gb, sb, out, bias=None, flags=0):
+    M, N = a.shape[0], b.shape[0]
+    y = torch.full((M, N), float("nan"), dtype=torch.float32 if out == "f32" else torch.bfloat16,
+                   device="cuda")
+    rt.fp8_scaled_gemm(dev(a), fa, ga, dev(sa), dev(b), fb, gb, dev(sb), y,
+                       bias=None if bias is None else dev(bias), flags=flags)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+SHAPES = [(200, 300, 320), (64, 256, 1024), (16, 512, 1024), (257, 129, 256)]
+SCALES = [((0, 0), (0, 0)), ((1, 0), (1, 0)), ((1, 128), (128, 128)), ((1, 128), (1, 0)),
+          ((0, 0), (128, 128))]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("fa", [0, 1])
+@pytest.mark.parametrize("grans", SCALES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_matches_oracle(rt, orc, shape, fa, grans, out):
+    M, N, K = shape
+    ga, gb = grans
+    a, sa, b, sb = operands(orc, hash((shape, fa, grans)) % 2 ** 31, M, N, K, fa, 0, ga, gb, False)
+    bias = None
+    if out == "bf16":
+        from workloads import to_bf16_bits
+        bias = to_bf16_bits((np.random.default_rng(1).standard_normal(N) * 0.1).astype(np.float32))
+    y = run_gemm(rt, a, fa, ga, sa, b, 0, gb, sb, out, bias)
+    yref, S = orc.gemm_full(a, fa, sa, ga, b, 0, sb, gb, bias=bias)
+    thw = orc.dot_truncation_bound_full(a, fa, sa, ga, b, 0, sb, gb)
+    bias_f = None if bias is None else orc.bf16_bits_to_f32(bias)
+    ok, st = check_gemm(y, yref, S, out == "bf16", orc, t_hw=thw,
+                        bias=None if bias is None else np.broadcast_to(bias_f, yref.shape))
+    print("gemm", shape, fa, grans, out, st)
+    assert ok, st
+    assert st["n_over_rel"] <= 1e-3 * st["n"], st
+
+
+@pytest.mark.parametrize("shape", [(200, 300, 320), (128, 256, 512)])
+@pytest.mark.parametrize("fa", [0, 1])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_mx32_pow2(rt, orc, shape, fa, out):
+    M, N, K = shape
+    ga = gb = (1, 32)
+    a, sa, b, sb = operands(orc, 3 + fa, M, N, K, fa, 0, ga, gb, True)
+    y = run_gemm(rt, a, fa, ga, sa, b, 0, gb, sb, out, flags=rt.POW2_SCALES)
+    yref, S = orc.gemm_full(a, fa, sa, ga, b, 0, sb, gb)
+    thw = orc.dot_truncation_bound_full(a, fa, sa, ga, b, 0, sb, gb)
+    ok, st = check_gemm(y, yref, S, out == "bf16", orc, t_hw=thw)
+    print("gemm mx32", shape, fa, out, st)
+    assert ok, st
+    assert st["n_over_rel"] <= 1e-3 * st["n"], st
+
+
+def test_gemm_fp32_bias_and_strided_output(rt, orc):
+    M, N, K = 96, 200, 384
+    a, sa, b, sb = operands(orc, 9, M, N, K, 0, 0, (1, 0), (1, 0), False)
+    bias = np.random.default_rng(2).standard_normal(N).astype(np.float32)
+    yb = torch.full((M, N + 56), float("nan"), device="cuda")
+    y = yb[:, :N]
+    rt.fp8_scaled_gemm(dev(a), 0, (1, 0), dev(sa), dev(b), 0, (1, 0), dev(sb), y, bias=dev(bias))
+    torch.cuda.synchronize()
+    yref, S = orc.gemm_full(a, 0, sa, (1, 0), b, 0, sb, (1, 0), bias=bias)
+    thw = orc.dot_truncation_bound_full(a, 0, sa, (1, 0), b, 0, sb, (1, 0))
+    ok, st = check_gemm(host(y), yref, S, False, orc, t_hw=thw, bias=np.broadcast_to(bias, yref.shape))
+    assert ok, st
+    assert np.all(np.isnan(host(yb)[:, N:]))          # nothing written past N
+
+
+def test_gemm_identity_weight_reproduces_dequantized_a(rt, orc):
+    M, K = 130, 256
+    g = np.random.default_rng(4)
+    a, sa, _, _, _ = orc.quantize(g.standard_normal((M, K)).astype(np.float32), 0, (1, 0))
+    b = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(b, 0x38)
+    sb = np.ones((1, 1), np.float32)
+    y = run_gemm(rt, a, 0, (1, 0), sa, b, 0, (0, 0), sb, "f32")
+    assert np.array_equal(y, orc.dequantize(a, 0, sa, (1, 0)))
+
+
+def test_fp8_dot_unit_truncation_model(rt, orc):
+    """Documents the matrix-core behaviour the tolerance term rests on: in a
+    row [X, d, 0, ...] times a column of ones, d survives when X / d <= 2^13
+    and is dropped when X / d >= 2^14 (same 8-product group); a d placed in
+    another group is kept."""
+    K = 128
+    rows = []
+    expect = []
+    for ex in range(-9, 9):
+        for ed in range(-9, ex + 1):
+            X, d = 2.0 ** ex, 2.0 ** ed
+            same = np.zeros(K, np.float32)
+            same[0], same[1] = X, d
+            other = np.zeros(K, np.float32)
+            other[0], other[8] = X, d
+            rows += [same, other]
+            expect += [X + d if ex - ed <= 13 else X, X + d]
+    A = np.array([[orc.encode(v, 0) for v in r] for r in rows], np.uint8)
+    B = np.full((16, K), 0x38, np.uint8)
+    one = np.ones((1, 1), np.float32)
+    y = run_gemm(rt, A, 0, (0, 0), one, B, 0, (0, 0), one, "f32")
+    assert np.array_equal(y[:, 0], np.array(expect, np.float32))
