@@ -9,8 +9,10 @@
 
 namespace fp8rt {
 
-// Per-block partial results of the quantize kernels (reduced by a finisher
-// kernel into amax_out and the saturation / underflow counters).
+// Per-block partial results of the quantize kernels, combined by the next
+// kernel on the stream (plain stores and loads: the kernel boundary orders
+// them; no device-scope fences or same-address atomics, which are slow on a
+// GPU whose L2 caches are per XCD).
 struct BlockPartial {
   uint32_t amax_bits;
   uint32_t pad;
@@ -18,26 +20,18 @@ struct BlockPartial {
   unsigned long long under;
 };
 
-// Stream-ordered scratch memory for one call (hipMallocAsync / hipFreeAsync
-// on the caller's stream, so concurrent calls never share it).
-class CallScratch {
- public:
-  explicit CallScratch(hipStream_t s) : stream_(s) {}
-  ~CallScratch() {
-    if (ptr_) (void)hipFreeAsync(ptr_, stream_);
-  }
-  CallScratch(const CallScratch&) = delete;
-  CallScratch& operator=(const CallScratch&) = delete;
-  hipError_t alloc(size_t bytes) {
-    if (bytes == 0) bytes = 256;
-    return hipMallocAsync(&ptr_, bytes, stream_);
-  }
-  void* get() const { return ptr_; }
+constexpr int kMaxBlocks = 8192;  // upper bound of every quantize grid
 
- private:
-  void* ptr_ = nullptr;
-  hipStream_t stream_;
+// Device workspace of one (device, stream) pair.  Calls on one stream are
+// ordered, so they never share it concurrently.
+struct DevWorkspace {
+  BlockPartial pass1[kMaxBlocks];  // per-tensor amax partials of the first pass
+  BlockPartial pass2[kMaxBlocks];  // per-block counters / observed amax of a cast pass
 };
+
+// Returns the workspace of (current device, stream), allocating and zeroing
+// it on first use (hipMalloc + hipMemset, outside any graph capture).
+hipError_t get_workspace(hipStream_t stream, DevWorkspace** ws);
 
 // Effective group extent of a granularity: 0 or >= n means the whole dimension.
 inline int64_t group_extent(int64_t n, int32_t g) { return (g <= 0 || g >= n) ? n : g; }
@@ -92,5 +86,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+bool gemm_big_eligible(const GemmArgs& g);
+hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace fp8rt

@@ -18,8 +18,10 @@
 // v_cvt_pk_{fp8,bf8}_f32 convert per element; 8-byte code stores.  Group
 // maxima are reduced across lanes with shuffles and across a workgroup in LDS.
 // Cross-block results (per-tensor amax, counters) go through per-block
-// partials in per-call scratch and are combined by a second kernel, so no
-// result depends on atomics or on memory being pre-cleared.
+// partials in a per-stream device workspace, written with plain stores and
+// combined by the next kernel on the stream.  Device-scope fences and
+// same-address atomics are avoided: with one L2 per XCD they cost more than
+// a small extra launch.
 #include <float.h>
 
 #include <algorithm>
@@ -47,8 +49,8 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
   return m;
 }
 
-// Writes this block's partial (wave-uniform counters already summed per wave
-// in sat_w / under_w; lane-level amax bits in mb).
+// Writes this block's partial: the block max of the lane amax bits mb and
+// the sums of the wave-uniform counters sat_w / under_w.
 __device__ __forceinline__ void store_block_partial(BlockPartial* bp, uint32_t mb,
                                                    unsigned long long sat_w,
                                                    unsigned long long under_w) {
@@ -106,14 +108,14 @@ __device__ __forceinline__ u32x2 cast_octet(const Octet<T>& v, float r, bool nan
 }
 
 // ---------------------------------------------------------------------------
-// Per-tensor: pass 1 writes one amax partial per block.  The work is split in
+// Per-tensor, pass 1: one amax partial per block.  The work is split in
 // segments of kBlock * U octets of one row.
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tensor_amax(const T* __restrict__ x, int64_t rows,
                                                         int64_t opr, int64_t ldx,
                                                         int64_t segs_per_row,
-                                                        uint32_t* __restrict__ part) {
+                                                        BlockPartial* __restrict__ part) {
   constexpr int U = oct_unroll<T>();
   __shared__ uint32_t sh[kWaves];
   uint32_t m = 0;
@@ -133,23 +135,25 @@ __global__ __launch_bounds__(kBlock) void k_tensor_amax(const T* __restrict__ x,
     for (int u = 0; u < U; ++u) m = max(m, v[u].absmax_bits());
   }
   m = block_max_u32(m, sh);
-  if (threadIdx.x == 0) part[blockIdx.x] = m;
+  if (threadIdx.x == 0) part[blockIdx.x].amax_bits = m;
 }
 
-// Pass 2: every block combines the pass-1 partials itself (DYNAMIC) or reads
-// the given scale (GIVEN), then casts its segments.
-template <typename T, int F, bool GIVEN, bool STATS>
+// Pass 2 of DYNAMIC (every block combines the pass-1 partials and derives
+// (s, r) itself; block 0 writes scale / inv_scale / amax_out) or the single
+// pass of GIVEN mode.  Counters and the observed amax go to per-block
+// partials for the finisher.
+template <typename T, int F, bool GIVEN, bool STATS, bool AMAX>
 __global__ __launch_bounds__(kBlock) void k_tensor_cast(
     const T* __restrict__ x, int64_t rows, int64_t opr, int64_t ldx, int64_t segs_per_row,
-    uint8_t* __restrict__ q, int64_t ldq, const uint32_t* __restrict__ part, int nparts, float eps,
-    int pow2, const float* __restrict__ s_in, const float* __restrict__ r_in, float* s_out,
-    float* r_out, float* amax_out, BlockPartial* bpart) {
+    uint8_t* __restrict__ q, int64_t ldq, const BlockPartial* __restrict__ part1, int nparts,
+    float eps, int pow2, const float* __restrict__ s_in, const float* __restrict__ r_in,
+    float* s_out, float* r_out, float* amax_out, BlockPartial* __restrict__ part2) {
   constexpr int U = oct_unroll<T>();
   __shared__ uint32_t sh[kWaves];
   float r;
   if constexpr (!GIVEN) {
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += kBlock) m = max(m, part[i]);
+    for (int i = threadIdx.x; i < nparts; i += kBlock) m = max(m, part1[i].amax_bits);
     m = block_max_u32(m, sh);
     const float a = __uint_as_float(m);
     float s;
@@ -185,18 +189,19 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
         bool nan_path = r_bad;
         if constexpr (GIVEN) {
           const uint32_t omb = v[u].absmax_bits();
-          mb = max(mb, omb);
+          if constexpr (AMAX) mb = max(mb, omb);
           nan_path |= omb > kInfBits;
         }
         const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
-        *reinterpret_cast<u32x2*>(qr + o * 8) = c;
+        __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qr + o * 8));
       }
     }
   }
-  if constexpr (GIVEN || STATS) store_block_partial(bpart, mb, sat_w, under_w);
+  if constexpr (STATS || AMAX) store_block_partial(part2, mb, sat_w, under_w);
 }
 
-// Combines per-block partials into amax_out[0] (as binary32) and counts[0..1].
+// Combines n block partials into amax_out[0] (as binary32, if non-null) and
+// counts[0..1] (if non-null).
 __global__ __launch_bounds__(kBlock) void k_finish(const BlockPartial* __restrict__ bp, int n,
                                                    float* amax_out,
                                                    unsigned long long* counts) {
@@ -231,16 +236,6 @@ __global__ __launch_bounds__(kBlock) void k_finish(const BlockPartial* __restric
   }
 }
 
-// Combines pass-1 amax partials into one binary32 amax (fp8_amax per tensor).
-__global__ __launch_bounds__(kBlock) void k_combine_amax(const uint32_t* __restrict__ part, int n,
-                                                         float* amax_out) {
-  __shared__ uint32_t sh[kWaves];
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < n; i += kBlock) m = max(m, part[i]);
-  m = block_max_u32(m, sh);
-  if (threadIdx.x == 0) amax_out[0] = __uint_as_float(m);
-}
-
 // ---------------------------------------------------------------------------
 // Row groups: groups of one row and L octets (8L elements, L a power of two,
 // 2 <= L <= 64).  Each row is padded to nCg * L octets so every group spans
@@ -253,7 +248,7 @@ template <typename T, int F, int L, bool GIVEN, bool STATS, bool AMAX_ONLY>
 __global__ __launch_bounds__(kBlock) void k_rowgroups(
     const T* __restrict__ x, uint32_t rows, uint32_t oct_cols, int64_t ldx, FastDiv div_opr,
     uint32_t nCg, uint32_t units, uint8_t* __restrict__ q, int64_t ldq, float eps, int pow2,
-    float* s_io, float* r_io, float* amax_out, BlockPartial* bpart) {
+    float* s_io, float* r_io, float* amax_out, DevWorkspace* ws, unsigned long long* counts) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;
   constexpr int GPU = kBlock * U / L;  // groups per unit
   __shared__ uint32_t sh_amax[GPU];
@@ -317,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
     }
     __syncthreads();
   }
-  if constexpr (STATS) store_block_partial(bpart, 0, sat_w, under_w);
+  if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_w, under_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,7 +326,7 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int64_t er, int64_t ec,
     int64_t nCg, int64_t ngroups, FastDiv div_full, FastDiv div_tail, uint8_t* __restrict__ q,
     int64_t ldq, float eps, int pow2, float* s_io, float* r_io, float* amax_out,
-    BlockPartial* bpart) {
+    DevWorkspace* ws, unsigned long long* counts) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;
   __shared__ uint32_t sh[kWaves];
   __shared__ float sh_r;
@@ -413,7 +408,7 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
     }
     __syncthreads();
   }
-  if constexpr (STATS) store_block_partial(bpart, 0, sat_w, under_w);
+  if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_w, under_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -451,70 +446,59 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   const int cus = device_cus();
   const bool given = a.mode == FP8RT_GIVEN;
   const bool stats = a.counts != nullptr;
-  const bool need_bp = (given && a.amax_out) || stats;
-
-  const int grid_amax = static_cast<int>(std::min<int64_t>(nseg, 2 * cus));
-  const int grid_cast = static_cast<int>(std::min<int64_t>(nseg, 8 * cus));
-  CallScratch scratch(st);
-  const size_t part_bytes = given ? 0 : sizeof(uint32_t) * grid_amax;
-  const size_t bp_bytes = need_bp ? sizeof(BlockPartial) * grid_cast : 0;
-  hipError_t e = scratch.alloc(part_bytes + bp_bytes + 16);
+  const bool am = a.amax_out != nullptr;
+  const int grid = static_cast<int>(std::min<int64_t>({nseg, int64_t(8) * cus, int64_t(kMaxBlocks)}));
+  const int grid1 = static_cast<int>(std::min<int64_t>({nseg, int64_t(4) * cus, int64_t(kMaxBlocks)}));
+  DevWorkspace* ws = nullptr;
+  hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
-  uint32_t* part = static_cast<uint32_t*>(scratch.get());
-  BlockPartial* bp = reinterpret_cast<BlockPartial*>(static_cast<char*>(scratch.get()) +
-                                                     ((part_bytes + 15) / 16) * 16);
   const T* x = static_cast<const T*>(a.x);
   if (a.amax_only) {
-    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid_amax), dim3(kBlock), 0, st, x, rows, opr, a.ldx,
-                       spr, part);
-    hipLaunchKernelGGL(k_combine_amax, dim3(1), dim3(kBlock), 0, st, part, grid_amax, a.amax_out);
+    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid1), dim3(kBlock), 0, st, x, rows, opr, a.ldx, spr,
+                       ws->pass1);
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass1, grid1, a.amax_out, nullptr);
     return hipGetLastError();
   }
+#define FP8RT_CAST(GV, ST, AM)                                                                        \
+  hipLaunchKernelGGL((k_tensor_cast<T, F, GV, ST, AM>), dim3(grid), dim3(kBlock), 0, st, x, rows, opr, \
+                     a.ldx, spr, a.q, a.ldq, ws->pass1, grid1, a.eps, a.pow2, a.scale, a.inv_scale,   \
+                     a.scale, a.inv_scale, a.amax_out, ws->pass2)
   if (!given) {
-    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid_amax), dim3(kBlock), 0, st, x, rows, opr, a.ldx,
-                       spr, part);
-    if (stats)
-      hipLaunchKernelGGL((k_tensor_cast<T, F, false, true>), dim3(grid_cast), dim3(kBlock), 0, st,
-                         x, rows, opr, a.ldx, spr, a.q, a.ldq, part, grid_amax, a.eps, a.pow2,
-                         nullptr, nullptr, a.scale, a.inv_scale, a.amax_out, bp);
-    else
-      hipLaunchKernelGGL((k_tensor_cast<T, F, false, false>), dim3(grid_cast), dim3(kBlock), 0, st,
-                         x, rows, opr, a.ldx, spr, a.q, a.ldq, part, grid_amax, a.eps, a.pow2,
-                         nullptr, nullptr, a.scale, a.inv_scale, a.amax_out, bp);
+    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid1), dim3(kBlock), 0, st, x, rows, opr, a.ldx, spr,
+                       ws->pass1);
+    if (stats) FP8RT_CAST(false, true, false);
+    else FP8RT_CAST(false, false, false);
   } else {
-    if (stats)
-      hipLaunchKernelGGL((k_tensor_cast<T, F, true, true>), dim3(grid_cast), dim3(kBlock), 0, st, x,
-                         rows, opr, a.ldx, spr, a.q, a.ldq, nullptr, 0, a.eps, a.pow2, a.scale,
-                         a.inv_scale, nullptr, nullptr, nullptr, bp);
-    else
-      hipLaunchKernelGGL((k_tensor_cast<T, F, true, false>), dim3(grid_cast), dim3(kBlock), 0, st,
-                         x, rows, opr, a.ldx, spr, a.q, a.ldq, nullptr, 0, a.eps, a.pow2, a.scale,
-                         a.inv_scale, nullptr, nullptr, nullptr, bp);
+    if (stats && am) FP8RT_CAST(true, true, true);
+    else if (stats) FP8RT_CAST(true, true, false);
+    else if (am) FP8RT_CAST(true, false, true);
+    else FP8RT_CAST(true, false, false);
   }
-  if (need_bp)
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, bp, grid_cast,
+#undef FP8RT_CAST
+  if (stats || (given && am))
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid,
                        given ? a.amax_out : nullptr, a.counts);
   return hipGetLastError();
 }
 
 template <typename T, int F, int L, bool GIVEN, bool STATS, bool AO>
 void launch_rowgroups_t(const QuantArgs& a, hipStream_t st, int grid, uint32_t units, FastDiv dv,
-                        uint32_t nCg, BlockPartial* bp) {
+                        uint32_t nCg, DevWorkspace* ws) {
   hipLaunchKernelGGL((k_rowgroups<T, F, L, GIVEN, STATS, AO>), dim3(grid), dim3(kBlock), 0, st,
                      static_cast<const T*>(a.x), static_cast<uint32_t>(a.rows),
                      static_cast<uint32_t>(a.cols / 8), a.ldx, dv, nCg, units, a.q, a.ldq, a.eps,
-                     a.pow2, a.scale, a.inv_scale, a.amax_out, bp);
+                     a.pow2, a.scale, a.inv_scale, a.amax_out, ws, a.counts);
 }
 
 template <typename T, int F, int L>
 void rowgroups_dispatch(const QuantArgs& a, hipStream_t st, int grid, uint32_t units, FastDiv dv,
-                        uint32_t nCg, BlockPartial* bp) {
+                        uint32_t nCg, DevWorkspace* ws) {
   const bool given = a.mode == FP8RT_GIVEN, stats = a.counts != nullptr;
-  if (a.amax_only) launch_rowgroups_t<T, F, L, false, false, true>(a, st, grid, units, dv, nCg, bp);
-  else if (given && stats) launch_rowgroups_t<T, F, L, true, true, false>(a, st, grid, units, dv, nCg, bp);
-  else if (given) launch_rowgroups_t<T, F, L, true, false, false>(a, st, grid, units, dv, nCg, bp);
-  else if (stats) launch_rowgroups_t<T, F, L, false, true, false>(a, st, grid, units, dv, nCg, bp);
-  else launch_rowgroups_t<T, F, L, false, false, false>(a, st, grid, units, dv, nCg, bp);
+  if (a.amax_only) launch_rowgroups_t<T, F, L, false, false, true>(a, st, grid, units, dv, nCg, ws);
+  else if (given && stats) launch_rowgroups_t<T, F, L, true, true, false>(a, st, grid, units, dv, nCg, ws);
+  else if (given) launch_rowgroups_t<T, F, L, true, false, false>(a, st, grid, units, dv, nCg, ws);
+  else if (stats) launch_rowgroups_t<T, F, L, false, true, false>(a, st, grid, units, dv, nCg, ws);
+  else launch_rowgroups_t<T, F, L, false, false, false>(a, st, grid, units, dv, nCg, ws);
 }
 
 template <typename T, int F>
@@ -523,44 +507,44 @@ hipError_t quant_rowgroups(const QuantArgs& a, int L, hipStream_t st) {
   const int64_t nCg = ceil_div(a.cols, a.ec);
   const int64_t padded = a.rows * nCg * L;
   const uint32_t units = static_cast<uint32_t>(ceil_div(padded, static_cast<int64_t>(kBlock) * U));
-  const int grid = static_cast<int>(std::min<int64_t>(units, 8 * device_cus()));
-  const bool stats = a.counts != nullptr;
-  CallScratch scratch(st);
-  hipError_t e = scratch.alloc(stats ? sizeof(BlockPartial) * grid : 16);
+  const int grid = static_cast<int>(std::min<int64_t>({int64_t(units), int64_t(8) * device_cus(),
+                                                       int64_t(kMaxBlocks)}));
+  DevWorkspace* ws = nullptr;
+  hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
-  BlockPartial* bp = static_cast<BlockPartial*>(scratch.get());
   const FastDiv dv(static_cast<uint32_t>(nCg * L));
   const uint32_t ncg = static_cast<uint32_t>(nCg);
   switch (L) {
-    case 2: rowgroups_dispatch<T, F, 2>(a, st, grid, units, dv, ncg, bp); break;
-    case 4: rowgroups_dispatch<T, F, 4>(a, st, grid, units, dv, ncg, bp); break;
-    case 8: rowgroups_dispatch<T, F, 8>(a, st, grid, units, dv, ncg, bp); break;
-    case 16: rowgroups_dispatch<T, F, 16>(a, st, grid, units, dv, ncg, bp); break;
-    case 32: rowgroups_dispatch<T, F, 32>(a, st, grid, units, dv, ncg, bp); break;
-    case 64: rowgroups_dispatch<T, F, 64>(a, st, grid, units, dv, ncg, bp); break;
+    case 2: rowgroups_dispatch<T, F, 2>(a, st, grid, units, dv, ncg, ws); break;
+    case 4: rowgroups_dispatch<T, F, 4>(a, st, grid, units, dv, ncg, ws); break;
+    case 8: rowgroups_dispatch<T, F, 8>(a, st, grid, units, dv, ncg, ws); break;
+    case 16: rowgroups_dispatch<T, F, 16>(a, st, grid, units, dv, ncg, ws); break;
+    case 32: rowgroups_dispatch<T, F, 32>(a, st, grid, units, dv, ncg, ws); break;
+    case 64: rowgroups_dispatch<T, F, 64>(a, st, grid, units, dv, ncg, ws); break;
     default: return hipErrorInvalidValue;
   }
-  if (stats) hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, bp, grid, nullptr, a.counts);
+  if (a.counts && !a.amax_only)
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid, nullptr, a.counts);
   return hipGetLastError();
 }
 
 template <typename T, int F, bool GIVEN, bool STATS, bool AO, bool REG>
 void launch_blocktile_t(const QuantArgs& a, hipStream_t st, int grid, int64_t nCg, int64_t ng,
-                        FastDiv df, FastDiv dt, BlockPartial* bp) {
+                        FastDiv df, FastDiv dt, DevWorkspace* ws) {
   hipLaunchKernelGGL((k_blocktile<T, F, GIVEN, STATS, AO, REG>), dim3(grid), dim3(kBlock), 0, st,
                      static_cast<const T*>(a.x), a.rows, a.cols, a.ldx, a.er, a.ec, nCg, ng, df, dt,
-                     a.q, a.ldq, a.eps, a.pow2, a.scale, a.inv_scale, a.amax_out, bp);
+                     a.q, a.ldq, a.eps, a.pow2, a.scale, a.inv_scale, a.amax_out, ws, a.counts);
 }
 
 template <typename T, int F, bool REG>
 void blocktile_dispatch(const QuantArgs& a, hipStream_t st, int grid, int64_t nCg, int64_t ng,
-                        FastDiv df, FastDiv dt, BlockPartial* bp) {
+                        FastDiv df, FastDiv dt, DevWorkspace* ws) {
   const bool given = a.mode == FP8RT_GIVEN, stats = a.counts != nullptr;
-  if (a.amax_only) launch_blocktile_t<T, F, false, false, true, REG>(a, st, grid, nCg, ng, df, dt, bp);
-  else if (given && stats) launch_blocktile_t<T, F, true, true, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
-  else if (given) launch_blocktile_t<T, F, true, false, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
-  else if (stats) launch_blocktile_t<T, F, false, true, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
-  else launch_blocktile_t<T, F, false, false, false, REG>(a, st, grid, nCg, ng, df, dt, bp);
+  if (a.amax_only) launch_blocktile_t<T, F, false, false, true, REG>(a, st, grid, nCg, ng, df, dt, ws);
+  else if (given && stats) launch_blocktile_t<T, F, true, true, false, REG>(a, st, grid, nCg, ng, df, dt, ws);
+  else if (given) launch_blocktile_t<T, F, true, false, false, REG>(a, st, grid, nCg, ng, df, dt, ws);
+  else if (stats) launch_blocktile_t<T, F, false, true, false, REG>(a, st, grid, nCg, ng, df, dt, ws);
+  else launch_blocktile_t<T, F, false, false, false, REG>(a, st, grid, nCg, ng, df, dt, ws);
 }
 
 template <typename T, int F>
@@ -568,18 +552,17 @@ hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;
   const int64_t nCg = ceil_div(a.cols, a.ec);
   const int64_t ng = ceil_div(a.rows, a.er) * nCg;
-  const int grid = static_cast<int>(std::min<int64_t>(ng, 8 * device_cus()));
-  const bool stats = a.counts != nullptr;
-  CallScratch scratch(st);
-  hipError_t e = scratch.alloc(stats ? sizeof(BlockPartial) * grid : 16);
+  const int grid = static_cast<int>(std::min<int64_t>({ng, int64_t(8) * device_cus(), int64_t(kMaxBlocks)}));
+  DevWorkspace* ws = nullptr;
+  hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
-  BlockPartial* bp = static_cast<BlockPartial*>(scratch.get());
   const int64_t tail = a.cols - (nCg - 1) * a.ec;
   const FastDiv df(static_cast<uint32_t>(a.ec / 8)), dt(static_cast<uint32_t>(tail / 8));
   const bool reg = a.er * (a.ec / 8) <= static_cast<int64_t>(kBlock) * U;
-  if (reg) blocktile_dispatch<T, F, true>(a, st, grid, nCg, ng, df, dt, bp);
-  else blocktile_dispatch<T, F, false>(a, st, grid, nCg, ng, df, dt, bp);
-  if (stats) hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, bp, grid, nullptr, a.counts);
+  if (reg) blocktile_dispatch<T, F, true>(a, st, grid, nCg, ng, df, dt, ws);
+  else blocktile_dispatch<T, F, false>(a, st, grid, nCg, ng, df, dt, ws);
+  if (a.counts && !a.amax_only)
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid, nullptr, a.counts);
   return hipGetLastError();
 }
 

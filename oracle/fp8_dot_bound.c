@@ -42,6 +42,15 @@ int orc_dot_truncation_bound(const uint8_t* a, int fa, int64_t lda, int64_t gra,
     const int64_t era = eff_extent(M, gra), eca = eff_extent(K, gca);
     const int64_t erb = eff_extent(N, grb), ecb = eff_extent(K, gcb);
     const int64_t nKa = (K + eca - 1) / eca, nKb = (K + ecb - 1) / ecb;
+    /* per-code tables: nonzero-and-finite flag and exponent */
+    int ea[256], eb[256], oka[256], okb[256];
+    for (unsigned c = 0; c < 256; ++c) {
+        const double va = orc_decode(c, fa), vb = orc_decode(c, fb);
+        oka[c] = va != 0.0 && isfinite(va);
+        okb[c] = vb != 0.0 && isfinite(vb);
+        ea[c] = code_exponent(c, fa);
+        eb[c] = code_exponent(c, fb);
+    }
     for (int64_t p = 0; p < npts; ++p) {
         const int64_t mi = m[p], ni = n[p];
         if (mi < 0 || mi >= M || ni < 0 || ni >= N) return 1;
@@ -50,9 +59,8 @@ int orc_dot_truncation_bound(const uint8_t* a, int fa, int64_t lda, int64_t gra,
             int emax = -100000, cnt = 0;
             for (int64_t k = k0; k < k0 + 8 && k < K; ++k) {
                 const unsigned ca = a[mi * lda + k], cb = b[ni * ldb + k];
-                const double va = orc_decode(ca, fa), vb = orc_decode(cb, fb);
-                if (va == 0.0 || vb == 0.0 || !isfinite(va) || !isfinite(vb)) continue;
-                const int e = code_exponent(ca, fa) + code_exponent(cb, fb);
+                if (!oka[ca] || !okb[cb]) continue;
+                const int e = ea[ca] + eb[cb];
                 if (e > emax) emax = e;
                 ++cnt;
             }

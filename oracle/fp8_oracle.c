@@ -309,22 +309,47 @@ static double bias_at(const void* bias, int dt, int64_t n) {
     return (double)orc_load(bias, dt == ORC_BF16 ? ORC_BF16 : ORC_F32, n);
 }
 
+/* orc_decode of every code, memoized (the same values, looked up). */
+static const double* decode_table(int fmt) {
+    static double tab[2][256];
+    static int ready[2] = {0, 0};
+    const int f = fmt == ORC_E4M3 ? 0 : 1;
+    if (!ready[f]) {
+        for (unsigned c = 0; c < 256; ++c) tab[f][c] = orc_decode(c, fmt);
+        ready[f] = 1;
+    }
+    return tab[f];
+}
+
 int orc_gemm_points(const uint8_t* a, int fa, int64_t lda, int64_t gra, int64_t gca,
                     const float* sa, const uint8_t* b, int fb, int64_t ldb,
                     int64_t grb, int64_t gcb, const float* sb, int64_t M, int64_t N,
                     int64_t K, const void* bias, int bias_dtype, const int64_t* m,
                     const int64_t* n, int64_t npts, double* y, double* S) {
     if (!a || !b || !sa || !sb || !m || !n || !y || M <= 0 || N <= 0 || K <= 0) return 1;
+    const double* da = decode_table(fa);
+    const double* db = decode_table(fb);
+    const int64_t ca = eff(K, gca), cb = eff(K, gcb);
     for (int64_t p = 0; p < npts; ++p) {
         const int64_t mi = m[p], ni = n[p];
         if (mi < 0 || mi >= M || ni < 0 || ni >= N) return 1;
+        const uint8_t* ar = a + mi * lda;
+        const uint8_t* br = b + ni * ldb;
         double acc = 0.0, absacc = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            const double t = (double)scale_at(sa, M, K, gra, gca, mi, k) *
-                             (double)scale_at(sb, N, K, grb, gcb, ni, k) *
-                             orc_decode(a[mi * lda + k], fa) * orc_decode(b[ni * ldb + k], fb);
-            acc += t;
-            absacc += fabs(t);
+        int64_t k = 0;
+        while (k < K) {
+            /* scales are constant up to the next K-block boundary of either operand */
+            int64_t end = (k / ca + 1) * ca;
+            const int64_t end_b = (k / cb + 1) * cb;
+            if (end_b < end) end = end_b;
+            if (K < end) end = K;
+            const double s1 = (double)scale_at(sa, M, K, gra, gca, mi, k);
+            const double s2 = (double)scale_at(sb, N, K, grb, gcb, ni, k);
+            for (; k < end; ++k) {
+                const double t = s1 * s2 * da[ar[k]] * db[br[k]];
+                acc += t;
+                absacc += fabs(t);
+            }
         }
         y[p] = acc + bias_at(bias, bias_dtype, ni);
         if (S) S[p] = absacc;
