@@ -7,32 +7,32 @@
 // scaling" for per-row scales.  Y[m,n] = s_a(m) s_b(n) sum_k dec(A[m,k]) dec(B[n,k]) + bias[n].
 //
 // Design for MI355X:
-//  - 256 x 256 output tile per workgroup of 8 waves (two per SIMD); each wave
-//    owns a 128 x 64 sub-tile: 4 x 2 v_mfma_f32_32x32x64_f8f6f4 per 64-deep K
-//    step, 128 FP32 accumulators per lane.  Per K step the workgroup reads
-//    96 KB of operand fragments from LDS for 8.4 MFLOP.
-//  - Operands move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging):
-//    each wave instruction fills 1 KB of LDS (16 rows of 64 bytes); every
-//    lane picks the global 16-byte chunk that belongs at its LDS slot, which
-//    implements an XOR swizzle of the 4 chunks of each row (conflict-free
-//    ds_read_b128 of the MFMA fragments).
-//  - Ping-pong between the two waves of each SIMD: waves 0-3 (rows 0-127)
-//    and waves 4-7 (rows 128-255) run the same alternation of a load phase
-//    (issue the next global->LDS loads, read the step's fragments from LDS)
-//    and a compute phase (8 MFMAs), half a step apart, with one s_barrier
-//    between phases.  In every phase one wave per SIMD feeds the MFMA pipe
-//    while the other one talks to LDS, and each wave needs a single register
-//    set of fragments.
-//  - Four LDS stages (8 x 16 KB arrays) in a ring: the loads of step k+3 are
-//    issued while step k is read.  Every barrier is preceded by an explicit
-//    wait that lets the two younger steps' loads stay outstanding (a fenced
-//    __syncthreads would drain them); scheduling barriers keep each phase's
-//    instructions on its side.
+//  - 256 x 256 output tile per workgroup of 4 waves (one per SIMD); each wave
+//    owns a 128 x 128 sub-tile: 4 x 4 v_mfma_f32_32x32x64_f8f6f4 per 64-deep
+//    K sub-step, 256 FP32 accumulators per lane held in AGPRs.
+//  - Two LDS stages of 128 K bytes (64 KB each).  A stage row is 128 bytes,
+//    a whole cache line, so every vector-memory request moves a full line
+//    (64-byte half rows doubled the L1->L2 request count and stalled the
+//    address path).  Operands move HBM -> LDS with global_load_lds_dwordx4
+//    (no VGPR staging): one instruction fills 8 rows; each lane picks the
+//    global chunk that belongs at its LDS slot, an XOR swizzle of the 8
+//    chunks of a row by (row / 2) that makes the ds_read_b128 fragment reads
+//    conflict-free on the 64-bank LDS.
+//  - Software pipeline over sub-steps, with two fragment register sets P/Q:
+//    even sub-step 2j multiplies P (stage j, K bytes 0-63) while it reads
+//    stage j, K bytes 64-127 into Q, then waits for stage j+1 and joins one
+//    s_barrier (stage j is then free); odd sub-step 2j+1 multiplies Q while
+//    it refills stage j's arrays with stage j+2 and reads stage j+1 into P.
+//    One barrier per 128-deep stage; scheduling groups interleave the LDS
+//    reads and the loads between the MFMAs.
 //  - Tile order: blocks are dealt round-robin to the 8 XCDs; each XCD gets a
 //    contiguous range of a grouped (GROUP_M M-tiles x all N-tiles) order, so
 //    the 32 CUs of an XCD share A and B slices in their own L2.
-//  - Epilogue: scales, bias and the bf16 / fp32 conversion, staged through
-//    LDS so global stores are 16-byte row chunks.
+//  - The MFMA computes the transposed tile (B as the first operand), so a
+//    lane ends with 4 consecutive output columns of one row: the epilogue
+//    applies the scales and bias with 4-wide LDS reads of the block's column
+//    vectors, converts with the hardware bf16 conversion (round to nearest
+//    even), stages 8- or 16-byte pieces in LDS and stores 16-byte row chunks.
 #include <float.h>
 
 #include <algorithm>
@@ -46,23 +46,26 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-constexpr int TM = 256, TN = 256, TK = 64;
-constexpr int kWaves = 8, WAVES_N = 4;            // 2 x 4 waves
+constexpr int TM = 256, TN = 256;
+constexpr int TKS = 128;                          // K bytes per LDS stage (full 128-byte rows)
+constexpr int TK = 64;                            // K per MFMA sub-step
+constexpr int kWaves = 4, WAVES_N = 2;            // 2 x 2 waves
 constexpr int kThreads = kWaves * 64;
 constexpr int WTM = TM / (kWaves / WAVES_N);      // 128 rows per wave
-constexpr int WTN = TN / WAVES_N;                 // 64 columns per wave
-constexpr int MI = WTM / 32, NJ = WTN / 32;       // 4 x 2 MFMA tiles of 32 x 32
-constexpr int kStageA = TM * TK, kStageB = TN * TK;  // 16 KB + 16 KB per stage
-constexpr int kDmaA = kStageA / 1024 / kWaves;    // 2 DMA instructions per wave
-constexpr int kDmaB = kStageB / 1024 / kWaves;    // 2
+constexpr int WTN = TN / WAVES_N;                 // 128 columns per wave
+constexpr int MI = WTM / 32, NJ = WTN / 32;       // 4 x 4 MFMA tiles of 32 x 32
+constexpr int kStageA = TM * TKS, kStageB = TN * TKS;  // 32 KB + 32 KB per stage
+constexpr int kDmaA = kStageA / 1024 / kWaves;    // 8 DMA instructions per wave
+constexpr int kDmaB = kStageB / 1024 / kWaves;    // 8
 constexpr int GROUP_M = 4;
 
-// Byte offset of 16-byte chunk c (0..3) of tile row r (64-byte rows); rows
-// r, r+4, r+8, r+12 use four different chunk positions.
-__device__ __forceinline__ int swz(int r, int c) { return r * TK + ((c ^ ((r >> 2) & 3)) << 4); }
+// Byte offset of 16-byte chunk c (0..7) of stage row r (128-byte rows).
+__device__ __forceinline__ int swz(int r, int c) { return r * TKS + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <int NDMA>
 __device__ __forceinline__ void dma_tile(const uint8_t* base, const uint32_t (&voff)[NDMA], uint8_t* lds,
@@ -73,11 +76,11 @@ __device__ __forceinline__ void dma_tile(const uint8_t* base, const uint32_t (&v
                                      16, 0, 0);
 }
 
-// 32x32x64 operand: lane l holds row (l % 32) and the 32 K bytes
-// [32 (l / 32), 32 (l / 32) + 32) of the step.
-__device__ __forceinline__ i32x8 frag(const uint8_t* lds, int row, int g) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz(row, 2 * g));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, 2 * g + 1));
+// 32x32x64 operand of sub-step h: lane l holds row (l % 32) and K bytes
+// [64 h + 32 (l / 32), +32).
+__device__ __forceinline__ i32x8 frag(const uint8_t* lds, int row, int c0) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz(row, c0));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, c0 + 1));
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
@@ -87,11 +90,11 @@ struct Frags {
 };
 
 __device__ __forceinline__ void read_frags(Frags& f, const uint8_t* la, const uint8_t* lb, int wm, int wn,
-                                           int fr, int fg) {
+                                           int fr, int c0) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) f.b[j] = frag(lb, wn * WTN + j * 32 + fr, fg);
+  for (int i = 0; i < MI; ++i) f.a[i] = frag(la, wm * WTM + i * 32 + fr, c0);
 #pragma unroll
-  for (int i = 0; i < MI; ++i) f.a[i] = frag(la, wm * WTM + i * 32 + fr, fg);
+  for (int j = 0; j < NJ; ++j) f.b[j] = frag(lb, wn * WTN + j * 32 + fr, c0);
 }
 
 template <int FA, int FB>
@@ -100,28 +103,22 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[MI][NJ])
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], FA, FB, 0, 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
 }
 
-// Wait until at most N of this wave's vector-memory operations (the LDS
-// loads of younger steps) are outstanding and all its LDS reads are done,
-// then join the workgroup barrier.  No memory fence: the younger loads keep
+// Wait until at most N of this wave's vector-memory operations (the loads of
+// the younger stage) are outstanding and all its LDS operations are done,
+// then join the workgroup barrier.  No memory fence: younger loads keep
 // flying across the barrier.
 template <int N>
 __device__ __forceinline__ void step_barrier() {
-  static_assert(N < 16, "vmcnt field");
+  static_assert(N < 64, "vmcnt field");
   __builtin_amdgcn_sched_barrier(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0070 | (N & 15));
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if ((u & kAbsMask) > kInfBits) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 template <int FA, int FB, bool BF16OUT>
@@ -132,14 +129,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
-  __shared__ __attribute__((aligned(16))) uint8_t sA2[kStageA];
-  __shared__ __attribute__((aligned(16))) uint8_t sA3[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB2[kStageB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB3[kStageB];
 
-  // ---- tile assignment: XCD-contiguous ranges of a grouped order
   const int T = tiles_m * tiles_n;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, loc = bid >> 3;
@@ -159,21 +151,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int fr = lane & 31, fg = lane >> 5;
 
-  // ---- per-lane DMA source offsets (rows past M / N are clamped: their
-  // products land in accumulators that are never stored)
+  // DMA j of a wave fills stage rows (wave * NDMA + j) * 8 + (lane / 8); the
+  // lane's LDS slot is chunk lane % 8 of that row, which holds global chunk
+  // slot ^ ((row >> 1) & 7).
   uint32_t voa[kDmaA], vob[kDmaB];
-  {
-    const int c = (lane & 3) ^ ((lane >> 4) & 3);  // chunk stored at this lane's LDS slot
 #pragma unroll
-    for (int j = 0; j < kDmaA; ++j) {
-      const int r = (wave * kDmaA + j) * 16 + (lane >> 2);
-      voa[j] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * lda + c * 16);
-    }
+  for (int j = 0; j < kDmaA; ++j) {
+    const int r = (wave * kDmaA + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    voa[j] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * lda + c * 16);
+  }
 #pragma unroll
-    for (int j = 0; j < kDmaB; ++j) {
-      const int r = (wave * kDmaB + j) * 16 + (lane >> 2);
-      vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
-    }
+  for (int j = 0; j < kDmaB; ++j) {
+    const int r = (wave * kDmaB + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
   }
   const uint8_t* a_base = A + m0 * lda;
   const uint8_t* b_base = B + n0 * ldb;
@@ -186,97 +178,134 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // K is a multiple of 4 * TK, so every iteration below runs four full
-  // steps.  Load phase of step k: issue the loads of step k+3 into stage
-  // (k+3) % 4 (read by both groups during step k-1, so free; the index is
-  // clamped to the last step, extra loads land in a stage nobody reads
-  // again), read step k's fragments.  Group 1 starts one phase late; every
-  // barrier waits for this wave's loads of step k+1 (two younger steps stay
-  // in flight), which both groups need before group 0's next load phase.
-  constexpr int kDmaStep = kDmaA + kDmaB;
-  const int nk = static_cast<int>(K / TK);
-  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
+  constexpr int kDmaStage = kDmaA + kDmaB;  // 16
+  const int ns = static_cast<int>(K / TKS);  // even
+  const int c_lo = 2 * fg, c_hi = 4 + 2 * fg;  // first chunk of sub-step 0 / 1
   dma_tile<kDmaA>(a_base, voa, sA0, wave);
   dma_tile<kDmaB>(b_base, vob, sB0, wave);
-  dma_tile<kDmaA>(a_base + TK, voa, sA1, wave);
-  dma_tile<kDmaB>(b_base + TK, vob, sB1, wave);
-  dma_tile<kDmaA>(a_base + 2 * TK, voa, sA2, wave);
-  dma_tile<kDmaB>(b_base + 2 * TK, vob, sB2, wave);
-  step_barrier<2 * kDmaStep>();
-  if (grp == 1) step_barrier<2 * kDmaStep>();
-  Frags f;
-#define FP8RT_STEP(RA, RB, DA, DB, K3)                                        \
+  dma_tile<kDmaA>(a_base + TKS, voa, sA1, wave);
+  dma_tile<kDmaB>(b_base + TKS, vob, sB1, wave);
+  step_barrier<kDmaStage>();  // stage 0 landed
+  Frags fp, fq;
+  read_frags(fp, sA0, sB0, wm, wn, fr, c_lo);
+  // Sub-step 2j: MFMAs on P (stage j, first half), read stage j second half
+  // into Q; then wait for stage j+1 and join the barrier (stage j is free).
+  // Sub-step 2j+1: MFMAs on Q, refill stage j's arrays with stage j+2, read
+  // stage j+1 first half into P.
+#define FP8RT_EVEN(LA, LB)                                                    \
   {                                                                           \
-    const int kn = min(K3, nk - 1);                                           \
-    dma_tile<kDmaA>(a_base + kn * TK, voa, DA, wave);                         \
-    dma_tile<kDmaB>(b_base + kn * TK, vob, DB, wave);                         \
-    read_frags(f, RA, RB, wm, wn, fr, fg);                                    \
-    step_barrier<2 * kDmaStep>();                                             \
-    mfma_step<FA, FB>(f, acc);                                                \
-    step_barrier<2 * kDmaStep>();                                             \
+    read_frags(fq, LA, LB, wm, wn, fr, c_hi);                                 \
+    mfma_step<FA, FB>(fp, acc);                                               \
+    for (int s = 0; s < 4; ++s) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
+    }                                                                         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                        \
+    step_barrier<0>();                                                        \
   }
-  for (int kt = 0; kt < nk; kt += 4) {
-    FP8RT_STEP(sA0, sB0, sA3, sB3, kt + 3)
-    FP8RT_STEP(sA1, sB1, sA0, sB0, kt + 4)
-    FP8RT_STEP(sA2, sB2, sA1, sB1, kt + 5)
-    FP8RT_STEP(sA3, sB3, sA2, sB2, kt + 6)
+#define FP8RT_ODD(DA, DB, KS, LA, LB)                                         \
+  {                                                                           \
+    const int kn = min(KS, ns - 1);                                           \
+    dma_tile<kDmaA>(a_base + kn * TKS, voa, DA, wave);                        \
+    dma_tile<kDmaB>(b_base + kn * TKS, vob, DB, wave);                        \
+    read_frags(fp, LA, LB, wm, wn, fr, c_lo);                                 \
+    mfma_step<FA, FB>(fq, acc);                                               \
+    for (int s = 0; s < 4; ++s) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
+    }                                                                         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                        \
+    __builtin_amdgcn_sched_barrier(0);                                        \
   }
-#undef FP8RT_STEP
-  if (grp == 0) step_barrier<2 * kDmaStep>();
+  for (int j = 0; j < ns; j += 2) {
+    FP8RT_EVEN(sA0, sB0)
+    FP8RT_ODD(sA0, sB0, j + 2, sA1, sB1)
+    FP8RT_EVEN(sA1, sB1)
+    FP8RT_ODD(sA1, sB1, j + 3, sA0, sB0)
+  }
+#undef FP8RT_EVEN
+#undef FP8RT_ODD
   step_barrier<0>();  // the clamped extra loads finish before the arrays are reused
 
-  // ---- epilogue: each wave stages 8 KB row bands of its 128 x 64 result in
-  // its own half of one stage array, then stores 16-byte row chunks.
-  uint8_t* arr = (wave >> 1) == 0 ? sA0 : (wave >> 1) == 1 ? sA1 : (wave >> 1) == 2 ? sA2 : sA3;
-  uint8_t* stage = arr + (wave & 1) * (kStageA / 2);
-  const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
-  float sbv[NJ], bv[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int64_t col = min(wcol0 + j * 32 + fr, N - 1);
-    sbv[j] = sb[col / erb];
-    bv[j] = 0.0f;
+  // ---- epilogue.  The MFMA computed the transposed tile, so lane l holds
+  // output row 32 i + (l % 32) and, per group g = e / 4, the 4 consecutive
+  // columns 32 j + 8 g + 4 (l / 32) + (e % 4).  Column scales and bias go
+  // through LDS once per block; each wave converts its 128 x 128 result,
+  // stages it in its own 32 KB of LDS (16-byte chunks XOR-swizzled by row)
+  // and stores 16-byte row chunks.
+  __shared__ __attribute__((aligned(16))) float sCol[2][TN];
+  {
+    const int64_t col = min(n0 + t, N - 1);
+    sCol[0][t] = sb[erb == 1 ? col : 0];
+    float bvv = 0.0f;
     if (bias)
-      bv[j] = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
-                        : static_cast<const float*>(bias)[col];
+      bvv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
+                      : static_cast<const float*>(bias)[col];
+    sCol[1][t] = bvv;
   }
+  __syncthreads();
+  uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
+  float sav[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) sav[i] = sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
   constexpr int ESZ = BF16OUT ? 2 : 4;
-  constexpr int ROWS = (kStageA / 2) / (WTN * ESZ);  // 64 (bf16) or 32 (fp32) rows per pass
-  constexpr int CHUNKS_PER_ROW = WTN * ESZ / 16;
-  constexpr int ELEMS_PER_CHUNK = 16 / ESZ;
+  constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
+  constexpr int ROWS = kStageA / RB;            // rows per pass: 128 or 64
+  constexpr int IPP = ROWS / 32;                // MFMA row tiles per pass: 4 or 2
+  constexpr int EPC = 16 / ESZ;                 // elements per chunk
 #pragma unroll
-  for (int pass = 0; pass < WTM / ROWS; ++pass) {
+  for (int pass = 0; pass < MI / IPP; ++pass) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      if (i * 32 + 32 <= pass * ROWS || i * 32 >= (pass + 1) * ROWS) continue;
+    for (int ii = 0; ii < IPP; ++ii) {
+      const int i = pass * IPP + ii;
+      const int lrow = ii * 32 + fr;            // row within the pass
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        // 32x32 output layout: lane l holds column l % 32 and rows
-        // 8 (e / 4) + 4 (l / 32) + (e % 4) of the sub-tile
-        const int lrow = i * 32 + 8 * (e >> 2) + 4 * fg + (e & 3);
-        const float sav = sa[min(wrow0 + lrow, M - 1) / era];
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const float v = acc[i][j][e] * (sav * sbv[j]) + bv[j];
-          const int off = ((lrow - pass * ROWS) * WTN + j * 32 + fr) * ESZ;
-          if constexpr (BF16OUT) *reinterpret_cast<uint16_t*>(stage + off) = static_cast<uint16_t>(bf16_rne(v));
-          else *reinterpret_cast<float*>(stage + off) = v;
+        for (int g = 0; g < 4; ++g) {
+          const int c = j * 32 + g * 8 + 4 * fg;  // first of 4 columns within the wave tile
+          const f32x4 scv = *reinterpret_cast<const f32x4*>(&sCol[0][wn * WTN + c]);
+          const f32x4 biv = *reinterpret_cast<const f32x4*>(&sCol[1][wn * WTN + c]);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * (sav[i] * scv[r]) + biv[r];
+          const int byte = c * ESZ;               // byte offset of the 4 values in the row
+          const int chunk = (byte >> 4) ^ (lrow & 15);
+          uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
+          if constexpr (BF16OUT) {
+            const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+            *reinterpret_cast<bf16x4*>(dst) = h;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          }
         }
-      }
     }
     __syncthreads();
-    for (int ch = lane; ch < ROWS * CHUNKS_PER_ROW; ch += 64) {
-      const int lrow = ch / CHUNKS_PER_ROW, cc = ch % CHUNKS_PER_ROW;
+    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
+      const int lrow = ch / CPR, cc = ch % CPR;
       const int64_t row = wrow0 + pass * ROWS + lrow;
-      const int64_t col = wcol0 + cc * ELEMS_PER_CHUNK;
+      const int64_t col = wcol0 + cc * EPC;
       if (row >= M || col >= N) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * WTN * ESZ + cc * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & 15)) << 4));
       char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
-      if (vec_store && col + ELEMS_PER_CHUNK <= N) {
+      if (vec_store && col + EPC <= N) {
         *reinterpret_cast<u32x4*>(dst) = v;
       } else {
         const char* src = reinterpret_cast<const char*>(&v);
-        for (int e = 0; e < ELEMS_PER_CHUNK && col + e < N; ++e)
+        for (int e = 0; e < EPC && col + e < N; ++e)
           for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
       }
     }
@@ -287,7 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
 }  // namespace
 
 bool gemm_big_eligible(const GemmArgs& g) {
-  return !g.pow2_mx && g.eca >= g.K && g.ecb >= g.K && g.K % (4 * TK) == 0 && g.M >= 128 &&
+  // per-tensor or per-row scales only (the epilogue selects, it does not divide)
+  const bool rows_ok = (g.era == 1 || g.era >= g.M) && (g.erb == 1 || g.erb >= g.N);
+  return rows_ok && !g.pow2_mx && g.eca >= g.K && g.ecb >= g.K && g.K % (2 * TKS) == 0 && g.M >= 128 &&
          g.N >= 128 && g.lda < (int64_t(1) << 23) && g.ldb < (int64_t(1) << 23);
 }
 
