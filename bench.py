@@ -8,8 +8,9 @@ hot path: amax(X) -> scale -> saturating cast of X (with saturation/underflow
 counters) -> scaled GEMM with FP32 accumulation and bf16 output.  Inputs are
 resident in HBM before the timed region.  Prints one JSON line.
 
-Other workloads (--workload decode|delayed|block|block_mx) time their own
-chains; they are extra measurements, not the headline line.
+The other workload shapes (decode, delayed-scaling backward, block-scaled)
+are parity-test cases; their quantize and GEMM kernels are timed as extra
+components of the same line.
 """
 from __future__ import annotations
 
@@ -35,11 +36,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "delayed", "block", "block_mx"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the other workload shapes' component timings")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain device copy of 1 GiB (read 1 GiB, write 1 GiB) three "
+                        "times: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -232,6 +236,126 @@ def bench_prefill(args, torch, rt, wl):
     return out
 
 
+def time_op(torch, fn, reps=10, scrub=None):
+    """Median microseconds of fn() over reps event-timed runs on the current
+    stream; scrub (untimed) runs before each repeat to evict the caches."""
+    fn()
+    out = []
+    for _ in range(reps):
+        if scrub is not None:
+            scrub()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(out))
+
+
+def hbm_entry(us, nbytes, kernels):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": us, "GB_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "kernels": kernels}
+
+
+def mfma_entry(us, flops, nbytes):
+    tf = flops / (us * 1e-6) / 1e12
+    return {"us": us, "TFLOP_s": tf, "frac_fp8_peak": tf / FP8_PEAK_TFLOPS, "algorithmic_bytes": nbytes}
+
+
+def extra_components(torch, rt, wl):
+    """Quantize and GEMM kernels of the other workload shapes, each timed alone
+    (median of 10, caches scrubbed between repeats by a 1 GiB fill)."""
+    dev = "cuda"
+    junk = torch.empty(2**28, dtype=torch.float32, device=dev)
+    scrub = lambda: junk.fill_(1.0)
+    from_bits = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
+    comp = {}
+
+    # decode-shaped linear: A 16x8192 per token, W 8192x8192 per output channel, bias, bf16 out
+    c2 = wl.C2Decode()
+    d = c2.make()
+    M, N, K = c2.M, c2.N, c2.K
+    A, W, bias = from_bits(d["a"]), from_bits(d["w"]), from_bits(d["bias"])
+    Aq, Wq = u8(M, K), u8(N, K)
+    sa, ra, sw, rw = f32(M, 1), f32(M, 1), f32(N, 1), f32(N, 1)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qa = lambda: rt.fp8_quantize(A, (1, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sa, ra, Aq)
+    qw = lambda: rt.fp8_quantize(W, (1, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sw, rw, Wq)
+    gm = lambda: rt.fp8_scaled_gemm(Aq, rt.E4M3, (1, 0), sa, Wq, rt.E4M3, (1, 0), sw, y, bias=bias)
+    qa(); qw()
+    comp["decode_quantize_a_per_token"] = hbm_entry(time_op(torch, qa, scrub=scrub), M * K * 3 + M * 4,
+                                                     "k_rowgroups")
+    comp["decode_quantize_w_per_channel"] = hbm_entry(time_op(torch, qw, scrub=scrub), N * K * 3 + N * 4,
+                                                       "k_rowgroups")
+    g_bytes = M * K + N * K + M * N * 2 + (M + N) * 4 + N * 2
+    e = hbm_entry(time_op(torch, gm, scrub=scrub), g_bytes, "k_gemm (small-M tiles)")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_gemm_bf16_bias"] = e
+    del A, W, bias, Aq, Wq, y, d
+
+    # delayed-scaling backward GEMM, one step: G 8192x8192 E5M2 with the scale of
+    # the history window, W 8192x8192 E4M3 per tensor, fp32 out
+    c4 = wl.C4Delayed()
+    M, N, K = c4.M, c4.N, c4.K
+    G = from_bits(c4.make_g(1))
+    W = from_bits(c4.make_w())
+    Gq, Wq = u8(M, K), u8(N, K)
+    hist = torch.zeros(c4.history, dtype=torch.float32, device=dev)
+    head = torch.zeros(1, dtype=torch.int32, device=dev)
+    sg, rg, am, sw, rw = f32(1, 1), f32(1, 1), f32(1, 1), f32(1, 1), f32(1, 1)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.DYNAMIC, 1e-12, False, sg, rg, Gq, am, cnt)
+    rt.fp8_amax_history_update(hist, head, am, rt.E5M2, 1e-12, False, sg, rg)
+    rt.fp8_quantize(W, (0, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sw, rw, Wq)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    qg = lambda: rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.GIVEN, 1e-12, False, sg, rg, Gq, am, cnt)
+    hu = lambda: rt.fp8_amax_history_update(hist, head, am, rt.E5M2, 1e-12, False, sg, rg)
+    gm = lambda: rt.fp8_scaled_gemm(Gq, rt.E5M2, (0, 0), sg, Wq, rt.E4M3, (0, 0), sw, y)
+    comp["delayed_quantize_g_given_e5m2"] = hbm_entry(time_op(torch, qg, scrub=scrub), M * K * 3 + 4,
+                                                       "k_tensor_cast (given, amax + counts) + k_finish")
+    comp["delayed_history_update_us"] = time_op(torch, hu)
+    comp["delayed_gemm_e5m2_e4m3_f32"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
+                                                    M * K + N * K + M * N * 4 + 8)
+    del G, W, Gq, Wq, y
+
+    # block-scaled GEMM: A 1x128 groups, W 128x128 blocks, bf16 out; variant 1x32 power-of-two
+    c5 = wl.C5Block()
+    M, N, K = c5.M, c5.N, c5.K
+    A = from_bits(c5.make_a())
+    W = from_bits(c5.make_w())
+    Aq, Wq = u8(M, K), u8(N, K)
+    sa, sw = f32(M, K // 128), f32(N // 128, K // 128)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qa = lambda: rt.fp8_quantize(A, (1, 128), rt.E4M3, rt.DYNAMIC, 1e-12, False, sa, None, Aq)
+    qw = lambda: rt.fp8_quantize(W, (128, 128), rt.E4M3, rt.DYNAMIC, 1e-12, False, sw, None, Wq)
+    gm = lambda: rt.fp8_scaled_gemm(Aq, rt.E4M3, (1, 128), sa, Wq, rt.E4M3, (128, 128), sw, y)
+    qa(); qw()
+    comp["block_quantize_a_1x128"] = hbm_entry(time_op(torch, qa, scrub=scrub),
+                                               M * K * 3 + sa.numel() * 4, "k_rowgroups")
+    comp["block_quantize_w_128x128"] = hbm_entry(time_op(torch, qw, scrub=scrub),
+                                                 N * K * 3 + sw.numel() * 4, "k_blocktile")
+    comp["block_gemm_bf16"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
+                                         M * K + N * K + M * N * 2 + (sa.numel() + sw.numel()) * 4)
+    sa32, sw32 = f32(M, K // 32), f32(N, K // 32)
+    qa = lambda: rt.fp8_quantize(A, (1, 32), rt.E4M3, rt.DYNAMIC, 1e-12, True, sa32, None, Aq)
+    qw = lambda: rt.fp8_quantize(W, (1, 32), rt.E4M3, rt.DYNAMIC, 1e-12, True, sw32, None, Wq)
+    gm = lambda: rt.fp8_scaled_gemm(Aq, rt.E4M3, (1, 32), sa32, Wq, rt.E4M3, (1, 32), sw32, y,
+                                    flags=rt.POW2_SCALES)
+    qa(); qw()
+    comp["block_mx_quantize_a_1x32_pow2"] = hbm_entry(time_op(torch, qa, scrub=scrub),
+                                                      M * K * 3 + sa32.numel() * 4, "k_rowgroups")
+    comp["block_mx_gemm_bf16"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
+                                            M * K + N * K + M * N * 2 + (sa32.numel() + sw32.numel()) * 4)
+    del A, W, Aq, Wq, y, junk
+    torch.cuda.empty_cache()
+    return comp
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -247,12 +371,21 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    if args.workload == "prefill":
-        out = bench_prefill(args, torch, rt, wl)
-    else:
-        import bench_extra
-
-        out = bench_extra.run(args, torch, rt, wl)
+    if args.calibrate_copy:
+        src = torch.ones(2**28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "repeats": 3}), flush=True)
+        return
+    out = bench_prefill(args, torch, rt, wl)
+    if not args.no_extra:
+        out["components"].update(extra_components(torch, rt, wl))
+        fr = [v["frac_hbm"] for k, v in out["components"].items()
+              if isinstance(v, dict) and "frac_hbm" in v and "quantize" in k and "decode_quantize_a" not in k]
+        out["components"]["quantize_min_frac_hbm_large"] = min(fr)
     print(json.dumps(out), flush=True)
 
 
