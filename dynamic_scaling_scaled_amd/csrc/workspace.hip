@@ -1,7 +1,7 @@
-// workspace.hip -- per-(device, stream) device workspace for cross-block
-// results of the quantize kernels (block partials, a last-block counter and
-// the per-tensor amax / scale handoff).  Allocated and zeroed once per pair
-// on first use and kept for the life of the process.
+// workspace.hip -- per-(device, stream) device workspace for the cross-block
+// results of the quantize kernels (the per-block partials of an amax pass and
+// of a cast pass).  Allocated and zeroed once per pair on first use and kept
+// for the life of the process.
 #include <mutex>
 #include <utility>
 #include <map>

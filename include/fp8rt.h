@@ -11,9 +11,13 @@
  *
  * Conventions shared by every entry point
  *  - Every array pointer is a caller-owned DEVICE pointer (HBM of the current
- *    HIP device).  The library allocates nothing that outlives a call, keeps
- *    no global state and is reentrant.  Work is enqueued on `stream` and the
- *    call returns without synchronizing; results are valid once the stream
+ *    HIP device).  The only memory the library owns is one device workspace
+ *    of 384 KB per (device, stream) pair that the quantize entry points use
+ *    for per-block partial results; it is allocated and zeroed (with a device
+ *    synchronization) on the first such call on that pair and kept until the
+ *    process ends.  Calls on one stream are ordered and share it; calls on
+ *    different streams never do.  Work is enqueued on `stream` and the call
+ *    returns without synchronizing; results are valid once the stream
  *    reaches that point.
  *  - Matrices are row-major with a leading dimension in ELEMENTS (ldx >= cols).
  *  - Arguments are validated on the host before anything is launched; on an
