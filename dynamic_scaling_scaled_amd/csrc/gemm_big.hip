@@ -76,11 +76,14 @@ __device__ __forceinline__ void dma_tile(const uint8_t* base, const uint32_t (&v
                                      16, 0, 0);
 }
 
-// 32x32x64 operand of sub-step h: lane l holds row (l % 32) and K bytes
-// [64 h + 32 (l / 32), +32).
+// 32x32x64 operand of sub-step h: lane l holds row (l % 32); the matrix
+// core reads the lane's first 16 bytes as K [16 g, 16 g + 16) and the last 16
+// as K [32 + 16 g, 48 + 16 g) of the sub-step, g = l / 32, so the lane loads
+// chunks 4 h + g and 4 h + g + 2 and K order in LDS equals the hardware's
+// (which the 32-element scale blocks of the MX path rely on).
 __device__ __forceinline__ i32x8 frag(const uint8_t* lds, int row, int c0) {
   const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz(row, c0));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, c0 + 1));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, c0 + 2));
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
@@ -97,13 +100,22 @@ __device__ __forceinline__ void read_frags(Frags& f, const uint8_t* la, const ui
   for (int j = 0; j < NJ; ++j) f.b[j] = frag(lb, wn * WTN + j * 32 + fr, c0);
 }
 
-template <int FA, int FB>
-__device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[MI][NJ]) {
+// One 64-deep sub-step of MFMAs.  The first operand is B, so the result is
+// the transposed tile.  With MX, each lane passes the E8M0 scales of its own
+// row and 32-element K block; OPSEL picks the byte of the sub-step.
+template <int FA, int FB, bool MX, int OPSEL>
+__device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[MI][NJ], const uint32_t (&xa)[MI],
+                                          const uint32_t (&xb)[NJ]) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (MX)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, OPSEL,
+                                                                    xb[j], OPSEL, xa[i]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    }
 }
 
 // Wait until at most N of this wave's vector-memory operations (the loads of
@@ -121,12 +133,16 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FA, int FB, bool BF16OUT>
+// MX: power-of-two 1x32 scales applied inside the MFMA.  xpa / xpb hold the
+// E8M0 exponents repacked by k_pack_e8m0 as [row / 32][stage][row % 32] dwords
+// (byte b = K block 4 stage + b).
+template <int FA, int FB, bool BF16OUT, bool MX>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
-    void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store) {
+    void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store,
+    const uint32_t* __restrict__ xpa, const uint32_t* __restrict__ xpb) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
@@ -180,22 +196,58 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
 
   constexpr int kDmaStage = kDmaA + kDmaB;  // 16
   const int ns = static_cast<int>(K / TKS);  // even
-  const int c_lo = 2 * fg, c_hi = 4 + 2 * fg;  // first chunk of sub-step 0 / 1
+  const int c_lo = fg, c_hi = 4 + fg;  // first chunk of sub-step 0 / 1
+  // MX: per stage the workgroup needs the E8M0 dwords of 8 A and 8 B row
+  // groups (256 bytes each, 4 KB): each wave copies 1 KB of them into LDS
+  // with one DMA (waves 0/1: A groups 0-3 / 4-7, waves 2/3: B).  Lane l of
+  // an MFMA reads the dword of its row and K-half l / 32, whose bytes 0 and 2
+  // are the blocks of sub-steps 0 and 1.
+  __shared__ __attribute__((aligned(16))) uint32_t sX0[2][8 * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t sX1[2][8 * 64];
+  uint32_t xa0[MI] = {}, xb0[NJ] = {}, xa1[MI] = {}, xb1[NJ] = {};  // even / odd stages
+  const uint32_t* xsrc = nullptr;
+  uint32_t xoff = 0;
+  if constexpr (MX) {
+    // lane l copies 16 bytes of row group 4 (wave & 1) + l / 16
+    const bool opb = wave >= 2;
+    const int64_t gmax = (opb ? (N - 1) : (M - 1)) / 32;
+    const int64_t g = min((opb ? n0 : m0) / 32 + 4 * (wave & 1) + (lane >> 4), gmax);
+    xsrc = opb ? xpb : xpa;
+    xoff = static_cast<uint32_t>(g * ns * 64 + (lane & 15) * 4);
+  }
+  auto sc_dma = [&](int st, uint32_t (&dst)[2][8 * 64]) {
+    if constexpr (MX) {
+      const int64_t stc = min(st, ns - 1);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(xsrc + xoff + stc * 64),
+                                       (lds_void*)(&dst[wave >> 1][(wave & 1) * 256]), 16, 0, 0);
+    }
+  };
+  auto sc_read = [&](const uint32_t (&src)[2][8 * 64], uint32_t (&xa)[MI], uint32_t (&xb)[NJ]) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) xa[i] = src[0][(wm * MI + i) * 64 + fg * 32 + fr];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) xb[j] = src[1][(wn * NJ + j) * 64 + fg * 32 + fr];
+    }
+  };
+  sc_dma(0, sX0);
+  sc_dma(1, sX1);
   dma_tile<kDmaA>(a_base, voa, sA0, wave);
   dma_tile<kDmaB>(b_base, vob, sB0, wave);
   dma_tile<kDmaA>(a_base + TKS, voa, sA1, wave);
   dma_tile<kDmaB>(b_base + TKS, vob, sB1, wave);
-  step_barrier<kDmaStage>();  // stage 0 landed
+  step_barrier<kDmaStage>();  // stage 0 (and the scales, issued first) landed
   Frags fp, fq;
   read_frags(fp, sA0, sB0, wm, wn, fr, c_lo);
+  sc_read(sX0, xa0, xb0);
   // Sub-step 2j: MFMAs on P (stage j, first half), read stage j second half
   // into Q; then wait for stage j+1 and join the barrier (stage j is free).
   // Sub-step 2j+1: MFMAs on Q, refill stage j's arrays with stage j+2, read
   // stage j+1 first half into P.
-#define FP8RT_EVEN(LA, LB)                                                    \
+#define FP8RT_EVEN(LA, LB, XA, XB)                                            \
   {                                                                           \
     read_frags(fq, LA, LB, wm, wn, fr, c_hi);                                 \
-    mfma_step<FA, FB>(fp, acc);                                               \
+    mfma_step<FA, FB, MX, 0>(fp, acc, XA, XB);                                \
     for (int s = 0; s < 4; ++s) {                                             \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
@@ -207,13 +259,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                        \
     step_barrier<0>();                                                        \
   }
-#define FP8RT_ODD(DA, DB, KS, LA, LB)                                         \
+#define FP8RT_ODD(DA, DB, DX, KS, LA, LB, LX, XA, XB, NXA, NXB)              \
   {                                                                           \
+    sc_read(LX, NXA, NXB);                                                    \
     const int kn = min(KS, ns - 1);                                           \
     dma_tile<kDmaA>(a_base + kn * TKS, voa, DA, wave);                        \
     dma_tile<kDmaB>(b_base + kn * TKS, vob, DB, wave);                        \
+    sc_dma(KS, DX);                                                           \
     read_frags(fp, LA, LB, wm, wn, fr, c_lo);                                 \
-    mfma_step<FA, FB>(fq, acc);                                               \
+    mfma_step<FA, FB, MX, 2>(fq, acc, XA, XB);                                \
     for (int s = 0; s < 4; ++s) {                                             \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                      \
@@ -229,10 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     __builtin_amdgcn_sched_barrier(0);                                        \
   }
   for (int j = 0; j < ns; j += 2) {
-    FP8RT_EVEN(sA0, sB0)
-    FP8RT_ODD(sA0, sB0, j + 2, sA1, sB1)
-    FP8RT_EVEN(sA1, sB1)
-    FP8RT_ODD(sA1, sB1, j + 3, sA0, sB0)
+    FP8RT_EVEN(sA0, sB0, xa0, xb0)
+    FP8RT_ODD(sA0, sB0, sX0, j + 2, sA1, sB1, sX1, xa0, xb0, xa1, xb1)
+    FP8RT_EVEN(sA1, sB1, xa1, xb1)
+    FP8RT_ODD(sA1, sB1, sX1, j + 3, sA0, sB0, sX0, xa1, xb1, xa0, xb0)
   }
 #undef FP8RT_EVEN
 #undef FP8RT_ODD
@@ -247,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   __shared__ __attribute__((aligned(16))) float sCol[2][TN];
   {
     const int64_t col = min(n0 + t, N - 1);
-    sCol[0][t] = sb[erb == 1 ? col : 0];
+    sCol[0][t] = MX ? 1.0f : sb[erb == 1 ? col : 0];  // MX scales were applied by the MFMA
     float bvv = 0.0f;
     if (bias)
       bvv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
@@ -259,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
   float sav[MI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) sav[i] = sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
+  for (int i = 0; i < MI; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
   constexpr int ESZ = BF16OUT ? 2 : 4;
   constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
@@ -313,12 +367,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   }
 }
 
+// Repack power-of-two 1x32 scales (fp32, [rows][K / 32]) as E8M0 exponent
+// bytes for the MFMA: dword [row / 32][stage][half][row % 32] holds in bytes 0
+// and 2 the exponents of K blocks 4 stage + half and 4 stage + half + 2 (the
+// blocks that lane half `half` of an MFMA covers in the stage's two
+// sub-steps).  Rows past the end get exponent 127 (scale 1); their products
+// are never stored.
+__global__ __launch_bounds__(256) void k_pack_e8m0(const float* __restrict__ s, int64_t rows, int64_t nblk,
+                                                   int64_t ngroups, int64_t nstage, uint32_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= ngroups * nstage * 64) return;
+  const int64_t rr = idx & 31, half = (idx >> 5) & 1, gs = idx >> 6;
+  const int64_t st = gs % nstage, g = gs / nstage;
+  const int64_t row = g * 32 + rr;
+  uint32_t w = 0x007F007Fu;
+  if (row < rows) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(s + row * nblk + st * 4 + half);
+    w = ((src[0] >> 23) & 0xFFu) | (((src[2] >> 23) & 0xFFu) << 16);
+  }
+  out[idx] = w;
+}
+
 }  // namespace
 
 bool gemm_big_eligible(const GemmArgs& g) {
   // per-tensor or per-row scales only (the epilogue selects, it does not divide)
   const bool rows_ok = (g.era == 1 || g.era >= g.M) && (g.erb == 1 || g.erb >= g.N);
-  return rows_ok && !g.pow2_mx && g.eca >= g.K && g.ecb >= g.K && g.K % (2 * TKS) == 0 && g.M >= 128 &&
+  const bool scales_ok = g.pow2_mx ? (g.era == 1 && g.erb == 1 && g.eca == 32 && g.ecb == 32)
+                                   : (g.eca >= g.K && g.ecb >= g.K);
+  return rows_ok && scales_ok && g.K % (2 * TKS) == 0 && g.M >= 128 &&
          g.N >= 128 && g.lda < (int64_t(1) << 23) && g.ldb < (int64_t(1) << 23);
 }
 
@@ -329,16 +406,33 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
   const int vec = ((g.ldy * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(g.y) & 15u) == 0);
   const dim3 grid(tiles_m * tiles_n);
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
-#define FP8RT_BIG(FA, FB, OUT)                                                                         \
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
-                     g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec)
-  if (g.fa == FP8RT_E4M3) {
-    if (g.yt == FP8RT_BF16) FP8RT_BIG(0, 0, true);
-    else FP8RT_BIG(0, 0, false);
-  } else {
-    if (g.yt == FP8RT_BF16) FP8RT_BIG(1, 0, true);
-    else FP8RT_BIG(1, 0, false);
+  uint32_t* xpa = nullptr;
+  uint32_t* xpb = nullptr;
+  if (g.pow2_mx) {
+    const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
+    void* p = nullptr;
+    hipError_t e = get_scratch(st, static_cast<size_t>((ga + gb) * ns * 64) * 4, &p);
+    if (e != hipSuccess) return e;
+    xpa = static_cast<uint32_t*>(p);
+    xpb = xpa + ga * ns * 64;
+    hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((ga * ns * 64 + 255) / 256)), dim3(256), 0, st,
+                       g.sa, g.M, g.K / 32, ga, ns, xpa);
+    hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((gb * ns * 64 + 255) / 256)), dim3(256), 0, st,
+                       g.sb, g.N, g.K / 32, gb, ns, xpb);
   }
+#define FP8RT_BIG(FA, FB, OUT, MXV)                                                                         \
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT, MXV>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
+                     g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec, \
+                     xpa, xpb)
+#define FP8RT_BIG_OUT(FA, FB, MXV)          \
+  if (g.yt == FP8RT_BF16) FP8RT_BIG(FA, FB, true, MXV); \
+  else FP8RT_BIG(FA, FB, false, MXV);
+  if (g.fa == FP8RT_E4M3) {
+    if (g.pow2_mx) { FP8RT_BIG_OUT(0, 0, true) } else { FP8RT_BIG_OUT(0, 0, false) }
+  } else {
+    if (g.pow2_mx) { FP8RT_BIG_OUT(1, 0, true) } else { FP8RT_BIG_OUT(1, 0, false) }
+  }
+#undef FP8RT_BIG_OUT
 #undef FP8RT_BIG
   return hipGetLastError();
 }

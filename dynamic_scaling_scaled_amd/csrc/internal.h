@@ -33,6 +33,12 @@ struct DevWorkspace {
 // it on first use (hipMalloc + hipMemset, outside any graph capture).
 hipError_t get_workspace(hipStream_t stream, DevWorkspace** ws);
 
+// Returns a scratch buffer of at least `bytes` for (current device, stream).
+// It grows on demand (the stream is synchronized before an old buffer is
+// freed) and is kept for the life of the process; its contents do not
+// persist between calls.
+hipError_t get_scratch(hipStream_t stream, size_t bytes, void** ptr);
+
 // Effective group extent of a granularity: 0 or >= n means the whole dimension.
 inline int64_t group_extent(int64_t n, int32_t g) { return (g <= 0 || g >= n) ? n : g; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

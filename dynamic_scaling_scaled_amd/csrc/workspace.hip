@@ -1,7 +1,8 @@
 // workspace.hip -- per-(device, stream) device workspace for the cross-block
 // results of the quantize kernels (the per-block partials of an amax pass and
 // of a cast pass).  Allocated and zeroed once per pair on first use and kept
-// for the life of the process.
+// for the life of the process.  Also a growable per-pair scratch buffer for
+// the GEMM's repacked block scales.
 #include <mutex>
 #include <utility>
 #include <map>
@@ -34,6 +35,35 @@ hipError_t get_workspace(hipStream_t stream, DevWorkspace** ws) {
   }
   *ws = static_cast<DevWorkspace*>(p);
   table.emplace(key, *ws);
+  return hipSuccess;
+}
+
+hipError_t get_scratch(hipStream_t stream, size_t bytes, void** ptr) {
+  static std::mutex mu;
+  static std::map<std::pair<int, uintptr_t>, std::pair<void*, size_t>> table;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(stream));
+  std::lock_guard<std::mutex> lock(mu);
+  auto& slot = table[key];
+  if (slot.second >= bytes) {
+    *ptr = slot.first;
+    return hipSuccess;
+  }
+  if (slot.first) {
+    e = hipStreamSynchronize(stream);  // earlier work on this stream may still read it
+    if (e != hipSuccess) return e;
+    e = hipFree(slot.first);
+    slot = {nullptr, 0};
+    if (e != hipSuccess) return e;
+  }
+  const size_t want = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);  // whole MiB
+  void* p = nullptr;
+  e = hipMalloc(&p, want);
+  if (e != hipSuccess) return e;
+  slot = {p, want};
+  *ptr = p;
   return hipSuccess;
 }
 

@@ -71,7 +71,7 @@ def test_gemm_matches_oracle(rt, orc, shape, fa, grans, out):
     assert st["n_over_rel"] <= 1e-3 * st["n"], st
 
 
-@pytest.mark.parametrize("shape", [(200, 300, 320), (128, 256, 512)])
+@pytest.mark.parametrize("shape", [(200, 300, 320), (128, 256, 512), (300, 520, 512), (520, 776, 1024)])
 @pytest.mark.parametrize("fa", [0, 1])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_mx32_pow2(rt, orc, shape, fa, out):
