@@ -17,6 +17,7 @@ namespace fp8rt {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;
@@ -77,6 +78,12 @@ template <> struct Octet<uint16_t> {  // bf16 carried as raw bits
   // Cached load (the data is read again soon).
   __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const u32x4*>(p); }
   __device__ __forceinline__ void zero() { raw = u32x4{0u, 0u, 0u, 0u}; }
+  // Zero the octet unless valid (a select, not a branch: guarded loads are
+  // issued unconditionally from a clamped address so they all stay in flight).
+  __device__ __forceinline__ void keep_if(bool valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = valid ? raw[j] : 0u;
+  }
   // Exact widening: a bf16 is the top half of a binary32.
   __device__ __forceinline__ float get(int i) const {
     const uint32_t w = raw[i >> 1];
@@ -85,13 +92,14 @@ template <> struct Octet<uint16_t> {  // bf16 carried as raw bits
   // max over the 8 elements of the |x| bit pattern (as binary32 bits); NaN
   // patterns exceed Inf, so NaN propagates.
   __device__ __forceinline__ uint32_t absmax_bits() const {
-    uint32_t m = 0;
+    // 16-bit lane-wise max of the |bf16| patterns (v_pk_max_u16), then the
+    // larger half widened to binary32 bits.  Computed on the raw words so it
+    // shares no value with the widening of get().
+    u16x2 m = u16x2{0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = raw[j] & 0x7FFF7FFFu;
-      m = max(m, max(w << 16, w & 0xFFFF0000u));
-    }
-    return m;
+    for (int j = 0; j < 4; ++j)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, raw[j] & 0x7FFF7FFFu));
+    return static_cast<uint32_t>(max(m[0], m[1])) << 16;
   }
 };
 
@@ -108,6 +116,13 @@ template <> struct Octet<float> {
   __device__ __forceinline__ void zero() {
     raw0 = u32x4{0u, 0u, 0u, 0u};
     raw1 = raw0;
+  }
+  __device__ __forceinline__ void keep_if(bool valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      raw0[j] = valid ? raw0[j] : 0u;
+      raw1[j] = valid ? raw1[j] : 0u;
+    }
   }
   __device__ __forceinline__ float get(int i) const {
     return __uint_as_float(i < 4 ? raw0[i] : raw1[i - 4]);

@@ -50,13 +50,13 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
 }
 
 // Writes this block's partial: the block max of the lane amax bits mb and
-// the sums of the wave-uniform counters sat_w / under_w.
-__device__ __forceinline__ void store_block_partial(BlockPartial* bp, uint32_t mb,
-                                                   unsigned long long sat_w,
-                                                   unsigned long long under_w) {
+// the block sums of the per-lane counters sat_l / under_l.
+__device__ __forceinline__ void store_block_partial(BlockPartial* bp, uint32_t mb, uint32_t sat_l,
+                                                   uint32_t under_l) {
   __shared__ uint32_t sh_m[kWaves];
   __shared__ unsigned long long sh_s[kWaves], sh_u[kWaves];
   mb = wave_max_u32(mb);
+  const unsigned long long sat_w = wave_sum_u64(sat_l), under_w = wave_sum_u64(under_l);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
@@ -81,11 +81,10 @@ __device__ __forceinline__ void store_block_partial(BlockPartial* bp, uint32_t m
 }
 
 // Converts one octet with multiplier r; returns the 8 codes as two words and
-// adds the wave-wide saturation / underflow counts (wave-uniform values).
+// adds this lane's saturation / underflow counts.
 template <typename T, int F, bool STATS>
-__device__ __forceinline__ u32x2 cast_octet(const Octet<T>& v, float r, bool nan_path,
-                                            unsigned long long& sat_w,
-                                            unsigned long long& under_w) {
+__device__ __forceinline__ u32x2 cast_octet(const Octet<T>& v, float r, bool nan_path, uint32_t& sat_l,
+                                            uint32_t& under_l) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = v.get(i) * r;
@@ -100,8 +99,8 @@ __device__ __forceinline__ u32x2 cast_octet(const Octet<T>& v, float r, bool nan
   if constexpr (STATS) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sat_w += __popcll(__ballot(fabsf(f[i]) > Fmt<F>::kMax));
-      under_w += __popcll(__ballot(v.get(i) != 0.0f && fabsf(f[i]) <= Fmt<F>::kZeroEdge));
+      sat_l += fabsf(f[i]) > Fmt<F>::kMax ? 1u : 0u;
+      under_l += (v.get(i) != 0.0f && fabsf(f[i]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
     }
   }
   return out;
@@ -128,8 +127,8 @@ __global__ __launch_bounds__(kBlock) void k_tensor_amax(const T* __restrict__ x,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (s * U + u) * kBlock + threadIdx.x;
-      if (o < opr) v[u].load(xr + o * 8);
-      else v[u].zero();
+      v[u].load_nt(xr + min(o, opr - 1) * 8);
+      v[u].keep_if(o < opr);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) m = max(m, v[u].absmax_bits());
@@ -169,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
   }
   const bool r_bad = !(fabsf(r) <= FLT_MAX);
   uint32_t mb = 0;
-  unsigned long long sat_w = 0, under_w = 0;
+  uint32_t sat_l = 0, under_l = 0;
   const int64_t nseg = rows * segs_per_row;
   for (int64_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
     const int64_t rr = sg / segs_per_row;
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (s * U + u) * kBlock + threadIdx.x;
-      if (o < opr) v[u].load_nt(xr + o * 8);
+      v[u].load_nt(xr + min(o, opr - 1) * 8);  // clamped: every load stays in flight
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -192,12 +191,12 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
           if constexpr (AMAX) mb = max(mb, omb);
           nan_path |= omb > kInfBits;
         }
-        const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
+        const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_l, under_l);
         __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qr + o * 8));
       }
     }
   }
-  if constexpr (STATS || AMAX) store_block_partial(part2, mb, sat_w, under_w);
+  if constexpr (STATS || AMAX) store_block_partial(part2, mb, sat_l, under_l);
 }
 
 // Combines n block partials into amax_out[0] (as binary32, if non-null) and
@@ -255,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
   __shared__ float sh_r[GPU];
   const uint32_t opr = nCg * L;
   const int t = threadIdx.x;
-  unsigned long long sat_w = 0, under_w = 0;
+  uint32_t sat_l = 0, under_l = 0;
   for (uint32_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const uint32_t base = unit * (kBlock * U);
     Octet<T> v[U];
@@ -266,8 +265,9 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
       const uint32_t po = base + u * kBlock + t;
       row[u] = div_opr.div(po);
       oc[u] = po - row[u] * opr;
-      if (row[u] < rows && oc[u] < oct_cols) v[u].load_nt(x + static_cast<int64_t>(row[u]) * ldx + oc[u] * 8);
-      else v[u].zero();
+      const bool ok = row[u] < rows && oc[u] < oct_cols;
+      v[u].load_nt(x + static_cast<int64_t>(min(row[u], rows - 1)) * ldx + min(oc[u], oct_cols - 1) * 8);
+      v[u].keep_if(ok);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -305,14 +305,14 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
         if (row[u] < rows && oc[u] < oct_cols) {
           const float r = sh_r[(u * kBlock + t) / L];
           const bool nan_path = omb[u] > kInfBits || !(fabsf(r) <= FLT_MAX);
-          const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
-          *reinterpret_cast<u32x2*>(q + static_cast<int64_t>(row[u]) * ldq + oc[u] * 8) = c;
+          const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_l, under_l);
+          __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + static_cast<int64_t>(row[u]) * ldq + oc[u] * 8));
         }
       }
     }
     __syncthreads();
   }
-  if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_w, under_w);
+  if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_l, under_l);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
   __shared__ uint32_t sh[kWaves];
   __shared__ float sh_r;
   const int t = threadIdx.x;
-  unsigned long long sat_w = 0, under_w = 0;
+  uint32_t sat_l = 0, under_l = 0;
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
     const int64_t gi = g / nCg, gj = g - gi * nCg;
     const int64_t r0 = gi * er, c0 = gj * ec;
@@ -348,12 +348,10 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t o = u * kBlock + t;
-        if (o < n_oct) {
-          const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
-          v[u].load_nt(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
-        } else {
-          v[u].zero();
-        }
+        const uint32_t oc = min(o, n_oct - 1);
+        const uint32_t rr = dv.div(oc), cc = oc - rr * oct_row;
+        v[u].load_nt(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
+        v[u].keep_if(o < n_oct);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) mb = max(mb, v[u].absmax_bits());
@@ -392,8 +390,8 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
           if (o < n_oct) {
             const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
             const bool nan_path = r_bad || v[u].absmax_bits() > kInfBits;
-            const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_w, under_w);
-            *reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8) = c;
+            const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_l, under_l);
+            __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8));
           }
         }
       } else {
@@ -401,14 +399,14 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
           const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
           v[0].load_nt(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
           const bool nan_path = r_bad || v[0].absmax_bits() > kInfBits;
-          const u32x2 c = cast_octet<T, F, STATS>(v[0], r, nan_path, sat_w, under_w);
-          *reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8) = c;
+          const u32x2 c = cast_octet<T, F, STATS>(v[0], r, nan_path, sat_l, under_l);
+          __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8));
         }
       }
     }
     __syncthreads();
   }
-  if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_w, under_w);
+  if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_l, under_l);
 }
 
 // ---------------------------------------------------------------------------
