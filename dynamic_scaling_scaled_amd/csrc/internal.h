@@ -94,5 +94,7 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 bool gemm_big_eligible(const GemmArgs& g);
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream);
+bool gemm_skinny_eligible(const GemmArgs& g);
+hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace fp8rt

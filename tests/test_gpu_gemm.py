@@ -42,7 +42,7 @@ def run_gemm(rt, a, fa, ga, sa, b, fb, gb, sb, out, bias=None, flags=0):
     return host(y)
 
 
-SHAPES = [(200, 300, 320), (64, 256, 1024), (16, 512, 1024), (257, 129, 256), (300, 520, 512),
+SHAPES = [(200, 300, 320), (64, 256, 1024), (16, 512, 1024), (5, 200, 2048), (257, 129, 256), (300, 520, 512),
           (520, 776, 1024)]
 SCALES = [((0, 0), (0, 0)), ((1, 0), (1, 0)), ((1, 128), (128, 128)), ((1, 128), (1, 0)),
           ((0, 0), (128, 128))]
