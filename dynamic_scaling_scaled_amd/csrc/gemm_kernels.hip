@@ -241,6 +241,7 @@ static void launch_formats(const GemmArgs& g, hipStream_t st) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (gemm_skinny_eligible(g)) return launch_gemm_skinny(g, st);
   if (gemm_big_eligible(g)) return launch_gemm_big(g, st);
+  if (gemm_kblock_eligible(g)) return launch_gemm_kblock(g, st);
   if (g.fa == FP8RT_E4M3 && g.fb == FP8RT_E4M3) launch_formats<0, 0>(g, st);
   else if (g.fa == FP8RT_E5M2 && g.fb == FP8RT_E4M3) launch_formats<1, 0>(g, st);
   else return hipErrorInvalidValue;

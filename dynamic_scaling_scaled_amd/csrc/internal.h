@@ -94,6 +94,8 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 bool gemm_big_eligible(const GemmArgs& g);
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream);
+bool gemm_kblock_eligible(const GemmArgs& g);
+hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t stream);
 bool gemm_skinny_eligible(const GemmArgs& g);
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream);
 
