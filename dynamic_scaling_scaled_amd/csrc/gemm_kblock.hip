@@ -9,8 +9,9 @@
 // along K (per tensor, per row) is applied once in the epilogue instead.
 //
 // Design for MI355X:
-//  - 256 x 128 output tile per workgroup of 4 waves (one per SIMD); each wave
-//    owns 128 x 64 as 8 x 4 tiles of v_mfma_f32_16x16x128_f8f6f4.  One
+//  - 256 x 256 output tile per workgroup of 8 waves (two per SIMD, which
+//    hide each other's LDS and promotion latency); each wave owns 128 x 64
+//    as 8 x 4 tiles of v_mfma_f32_16x16x128_f8f6f4.  One
 //    128-deep LDS stage is exactly one scale block and one MFMA per tile, so
 //    each tile's block partial comes out of a single MFMA started from zero
 //    and is promoted into the FP32 accumulator right away with one FMA per
@@ -18,13 +19,13 @@
 //    MFMA results in VGPRs (-amdgpu-mfma-vgpr-form) so the FMA reads them
 //    directly; the result is the transposed tile, so a lane's 4 elements of
 //    a tile share one output row and one factor.
-//  - Operands move HBM -> LDS with global_load_lds_dwordx4 into two 48 KB
+//  - Operands move HBM -> LDS with global_load_lds_dwordx4 into two 64 KB
 //    stages with 128-byte rows (full cache lines, XOR-swizzled by row / 2);
 //    the loads of stage g+1 fly while stage g multiplies; B's fragments are
 //    read at the stage start, A's one row tile ahead.  One s_barrier per stage.
 //  - A's group scales are transposed once per call (k_transpose_scales) so a
-//    stage's row scales are contiguous; B's block scale is one scalar per
-//    workgroup and stage.
+//    stage's row scales are contiguous; B's block scales (two 128-column
+//    blocks per tile) sit in LDS for all stages, one scalar per wave and stage.
 //  - Tile order as in the per-tensor kernel (XCD-grouped); the epilogue
 //    stages the result through LDS and stores 16-byte row chunks with the
 //    hardware bf16 rounding.
@@ -45,15 +46,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-constexpr int TM = 256, TN = 128;
+constexpr int TM = 256, TN = 256;
 constexpr int TKS = 128;                          // K bytes per LDS stage = one scale block
-constexpr int kWaves = 4, WAVES_N = 2;            // 2 x 2 waves
+constexpr int kWaves = 8, WAVES_N = 4;            // 2 x 4 waves, two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int WTM = TM / (kWaves / WAVES_N);      // 128 rows per wave
 constexpr int WTN = TN / WAVES_N;                 // 64 columns per wave
 constexpr int MI = WTM / 16, NJ = WTN / 16;       // 8 x 4 MFMA tiles of 16 x 16
-constexpr int kStageA = TM * TKS, kStageB = TN * TKS;  // 32 KB + 16 KB per stage
-constexpr int kDmaA = kStageA / 1024 / kWaves;    // 8 DMA instructions per wave
+constexpr int kStageA = TM * TKS, kStageB = TN * TKS;  // 32 KB + 32 KB per stage
+constexpr int kDmaA = kStageA / 1024 / kWaves;    // 4 DMA instructions per wave
 constexpr int kDmaB = kStageB / 1024 / kWaves;    // 4
 constexpr int GROUP_M = 4;
 constexpr int kMaxStages = 2048;  // K / 128 limit (B block scales of a tile live in LDS)
@@ -95,7 +96,7 @@ __device__ __forceinline__ void step_barrier() {
 // along K, taken from sa in the epilogue).  sbk: B's block scales
 // [ceil(N / erb)][K / 128] (null: constant along K, from sb in the epilogue).
 template <int FA, int FB, bool BF16OUT, bool AKB, bool BKB>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_kblock(
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sat, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sbk, const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias,
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_kblock(
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) float sSa0[TM];   // A row scales of the stage in sA0
   __shared__ __attribute__((aligned(16))) float sSa1[TM];
-  __shared__ float sSb[kMaxStages];                         // B block scales of every stage
+  __shared__ float sSb[2][kMaxStages];                      // B block scales of every stage (2 blocks)
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
@@ -153,8 +154,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_kblock(
   const int fr = lane & 15, fq = lane >> 4;
   // B block scales of this tile's block row for every stage, once, in LDS.
   if constexpr (BKB) {
-    const float* sbk_row = sbk + (n0 / erb) * ns;
-    for (int i = t; i < ns; i += kThreads) sSb[i] = sbk_row[i];
+    for (int hb = 0; hb < 2; ++hb) {
+      const float* sbk_row = sbk + (min(n0 + hb * 128, N - 1) / erb) * ns;
+      for (int i = t; i < ns; i += kThreads) sSb[hb][i] = sbk_row[i];
+    }
   }
   // A row scales of a stage: one DMA of the 256 contiguous row scales of the
   // transposed, row-padded table (every wave issues it; the copies carry the
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_kblock(
   // partial is a single MFMA from zero, promoted at once.
   auto stage_mma = [&](const uint8_t* la, const uint8_t* lb, const float* ssa, int st) {
     float f[MI];
-    const float fb = BKB ? sSb[st] : 1.0f;
+    const float fb = BKB ? sSb[(wn * WTN) / 128][st] : 1.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) f[i] = (AKB ? ssa[wm * WTM + i * 16 + fr] : 1.0f) * fb;
     i32x8 bfr[NJ];
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_kblock(
     sCol[1][t] = bvv;
   }
   __syncthreads();
-  uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA0 + kStageA / 2 : wave == 2 ? sA1 : sA1 + kStageA / 2;
+  uint8_t* stage = (wave < 4 ? sA0 : sA1) + (wave & 3) * (kStageA / 4);
   const int64_t wcol0 = n0 + wn * WTN;
   float sav[MI];
 #pragma unroll
@@ -233,8 +236,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_kblock(
   constexpr int ESZ = BF16OUT ? 2 : 4;
   constexpr int RB = WTN * ESZ;                 // staged row bytes: 128 or 256
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8 or 16
-  constexpr int ROWS = (kStageA / 2) / RB;      // rows per pass: 128 or 64
-  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass: 8 or 4
+  constexpr int ROWS = (kStageA / 4) / RB;      // rows per pass: 64 or 32
+  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass: 4 or 2
   constexpr int EPC = 16 / ESZ;
 #pragma unroll
   for (int pass = 0; pass < MI / IPP; ++pass) {
@@ -308,7 +311,7 @@ bool gemm_kblock_eligible(const GemmArgs& g) {
   const bool a_kb = g.eca < g.K, b_kb = g.ecb < g.K;
   if (!a_kb && !b_kb) return false;
   if (a_kb && !(g.era == 1 && g.eca == TKS)) return false;
-  if (b_kb && !(g.erb % TN == 0 && g.ecb == TKS)) return false;
+  if (b_kb && !(g.erb % 128 == 0 && g.ecb == TKS)) return false;
   if (!a_kb && !(g.era == 1 || g.era >= g.M)) return false;
   if (!b_kb && !(g.erb == 1 || g.erb >= g.N)) return false;
   return true;
