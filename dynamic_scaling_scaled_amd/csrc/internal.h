@@ -39,6 +39,9 @@ hipError_t get_workspace(hipStream_t stream, DevWorkspace** ws);
 // persist between calls.
 hipError_t get_scratch(hipStream_t stream, size_t bytes, void** ptr);
 
+// Compute units of the current device (256 on MI355X).
+int device_cus();
+
 // Effective group extent of a granularity: 0 or >= n means the whole dimension.
 inline int64_t group_extent(int64_t n, int32_t g) { return (g <= 0 || g >= n) ? n : g; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -414,20 +414,6 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
 
 namespace {
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <typename T, int F>
 hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   // A contiguous tensor is one long row for per-tensor work.

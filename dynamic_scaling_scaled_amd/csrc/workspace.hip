@@ -2,7 +2,7 @@
 // results of the quantize kernels (the per-block partials of an amax pass and
 // of a cast pass).  Allocated and zeroed once per pair on first use and kept
 // for the life of the process.  Also a growable per-pair scratch buffer for
-// the GEMM's repacked block scales.
+// the GEMM's repacked block scales, and the compute-unit count of a device.
 #include <mutex>
 #include <utility>
 #include <map>
@@ -65,6 +65,20 @@ hipError_t get_scratch(hipStream_t stream, size_t bytes, void** ptr) {
   slot = {p, want};
   *ptr = p;
   return hipSuccess;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 }  // namespace fp8rt
