@@ -11,14 +11,20 @@
  *
  * Conventions shared by every entry point
  *  - Every array pointer is a caller-owned DEVICE pointer (HBM of the current
- *    HIP device).  The only memory the library owns is one device workspace
- *    of 384 KB per (device, stream) pair that the quantize entry points use
- *    for per-block partial results; it is allocated and zeroed (with a device
- *    synchronization) on the first such call on that pair and kept until the
- *    process ends.  Calls on one stream are ordered and share it; calls on
- *    different streams never do.  Work is enqueued on `stream` and the call
- *    returns without synchronizing; results are valid once the stream
- *    reaches that point.
+ *    HIP device).  The library owns two kinds of device memory, both per
+ *    (device, stream) pair and kept until the process ends:
+ *      * a workspace of 384 KB that the quantize entry points use for
+ *        per-block partial results; it is allocated and zeroed (with a device
+ *        synchronization) on the first such call on that pair;
+ *      * a GEMM scratch buffer for repacked block scales, used by
+ *        fp8_scaled_gemm with 1x32 power-of-two scales ((ceil(M/32) +
+ *        ceil(N/32)) * K/128 * 256 bytes) and with 1x128 A groups on large
+ *        shapes (ceil(M/256) * 256 * K/128 * 4 bytes).  It grows on demand;
+ *        before a smaller buffer is freed the stream is synchronized.
+ *    Calls on one stream are ordered and share them; calls on different
+ *    streams never do.  Work is enqueued on `stream` and the call returns
+ *    without synchronizing (apart from the allocations above); results are
+ *    valid once the stream reaches that point.
  *  - Matrices are row-major with a leading dimension in ELEMENTS (ldx >= cols).
  *  - Arguments are validated on the host before anything is launched; on an
  *    error nothing is written and nothing is enqueued.
