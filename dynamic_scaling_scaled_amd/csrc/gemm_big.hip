@@ -133,6 +133,82 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Tile (tile_m, tile_n) of position `logical` in the grouped order: groups of
+// GROUP_M M-tiles by all N-tiles, M-tile fastest inside a group.
+__device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, int& tile_m, int& tile_n) {
+  const int group = GROUP_M * tiles_n;
+  const int gidx = logical / group;
+  const int first_m = gidx * GROUP_M;
+  const int gm = min(GROUP_M, tiles_m - first_m);
+  const int within = logical - gidx * group;
+  tile_m = first_m + within % gm;
+  tile_n = within / gm;
+}
+
+// Epilogue of one block: lane l holds output row 32 i + (l % 32) and, per
+// group g = e / 4, the 4 consecutive columns 32 j + 8 g + 4 (l / 32) + (e % 4)
+// of its wave tile (the MFMA computed the transposed tile).  Values are
+// scaled (row factor sav, column vectors scol / bias from LDS), converted,
+// staged in the wave's 32 KB of LDS (16-byte chunks XOR-swizzled by row) and
+// stored as 16-byte row chunks; rows / columns at or past (M, N) are skipped.
+template <bool OUTBF16>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t* stage, const float* scol,
+                                           const float* sbias, const float (&sav)[MI], int64_t wrow0, int64_t wcol0,
+                                           int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
+                                           int wn, int fr, int fg, int lane) {
+  constexpr int ESZ = OUTBF16 ? 2 : 4;
+  constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
+  constexpr int ROWS = kStageA / RB;            // rows per pass: 128 or 64
+  constexpr int IPP = ROWS / 32;                // MFMA row tiles per pass: 4 or 2
+  constexpr int EPC = 16 / ESZ;                 // elements per chunk
+#pragma unroll
+  for (int pass = 0; pass < MI / IPP; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < IPP; ++ii) {
+      const int i = pass * IPP + ii;
+      const int lrow = ii * 32 + fr;            // row within the pass
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = j * 32 + g * 8 + 4 * fg;  // first of 4 columns within the wave tile
+          const f32x4 scv = *reinterpret_cast<const f32x4*>(&scol[wn * WTN + c]);
+          const f32x4 biv = *reinterpret_cast<const f32x4*>(&sbias[wn * WTN + c]);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * (sav[i] * scv[r]) + biv[r];
+          const int byte = c * ESZ;               // byte offset of the 4 values in the row
+          const int chunk = (byte >> 4) ^ (lrow & 15);
+          uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
+          if constexpr (OUTBF16) {
+            const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+            *reinterpret_cast<bf16x4*>(dst) = h;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          }
+        }
+    }
+    __syncthreads();
+    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
+      const int lrow = ch / CPR, cc = ch % CPR;
+      const int64_t row = wrow0 + pass * ROWS + lrow;
+      const int64_t col = wcol0 + cc * EPC;
+      if (row >= M || col >= N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & 15)) << 4));
+      char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
+      if (vec_store && col + EPC <= N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const char* src = reinterpret_cast<const char*>(&v);
+        for (int e = 0; e < EPC && col + e < N; ++e)
+          for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // MX: power-of-two 1x32 scales applied inside the MFMA.  xpa / xpb hold the
 // E8M0 exponents repacked by k_pack_e8m0 as [row / 32][stage][row % 32] dwords
 // (byte b = K block 4 stage + b).
@@ -142,24 +218,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
     void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store,
-    const uint32_t* __restrict__ xpa, const uint32_t* __restrict__ xpb) {
+    const uint32_t* __restrict__ xpa, const uint32_t* __restrict__ xpb, int t_main, int split, int ns_part,
+    float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
 
-  const int T = tiles_m * tiles_n;
+  // Blocks below t_main take whole tiles [0, t_main) of the grouped order;
+  // the rest are split-K units: unit u computes K stages
+  // [(u % split) ns_part, +ns_part) of tile t_main + u / split and writes its
+  // raw FP32 sums to part[u] (k_split_reduce finishes those tiles).
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int q = T >> 3, rem = T & 7;
-  const int logical = xcd * q + min(xcd, rem) + loc;
-  const int group = GROUP_M * tiles_n;
-  const int gidx = logical / group;
-  const int first_m = gidx * GROUP_M;
-  const int gm = min(GROUP_M, tiles_m - first_m);
-  const int within = logical - gidx * group;
-  const int tile_m = first_m + within % gm;
-  const int tile_n = within / gm;
+  const bool unit = bid >= t_main;
+  int logical, s0 = 0;
+  if (!unit) {
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int q = t_main >> 3, rem = t_main & 7;
+    logical = xcd * q + min(xcd, rem) + loc;
+  } else {
+    const int u = bid - t_main;
+    logical = t_main + u / split;
+    s0 = (u % split) * ns_part;
+  }
+  int tile_m, tile_n;
+  tile_of(logical, tiles_m, tiles_n, tile_m, tile_n);
   const int64_t m0 = static_cast<int64_t>(tile_m) * TM, n0 = static_cast<int64_t>(tile_n) * TN;
 
   const int t = threadIdx.x;
@@ -183,8 +266,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
   }
-  const uint8_t* a_base = A + m0 * lda;
-  const uint8_t* b_base = B + n0 * ldb;
+  const uint8_t* a_base = A + m0 * lda + static_cast<int64_t>(s0) * TKS;
+  const uint8_t* b_base = B + n0 * ldb + static_cast<int64_t>(s0) * TKS;
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -195,7 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   constexpr int kDmaStage = kDmaA + kDmaB;  // 16
-  const int ns = static_cast<int>(K / TKS);  // even
+  const int ns_all = static_cast<int>(K / TKS);  // even
+  const int ns = unit ? ns_part : ns_all;         // stages this block runs (even)
   const int c_lo = fg, c_hi = 4 + fg;  // first chunk of sub-step 0 / 1
   // MX: per stage the workgroup needs the E8M0 dwords of 8 A and 8 B row
   // groups (256 bytes each, 4 KB): each wave copies 1 KB of them into LDS
@@ -213,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     const int64_t gmax = (opb ? (N - 1) : (M - 1)) / 32;
     const int64_t g = min((opb ? n0 : m0) / 32 + 4 * (wave & 1) + (lane >> 4), gmax);
     xsrc = opb ? xpb : xpa;
-    xoff = static_cast<uint32_t>(g * ns * 64 + (lane & 15) * 4);
+    xoff = static_cast<uint32_t>((g * ns_all + s0) * 64 + (lane & 15) * 4);
   }
   auto sc_dma = [&](int st, uint32_t (&dst)[2][8 * 64]) {
     if constexpr (MX) {
@@ -299,7 +383,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   // stages it in its own 32 KB of LDS (16-byte chunks XOR-swizzled by row)
   // and stores 16-byte row chunks.
   __shared__ __attribute__((aligned(16))) float sCol[2][TN];
-  {
+  if (unit) {
+    sCol[0][t] = 1.0f;
+    sCol[1][t] = 0.0f;
+  } else {
     const int64_t col = min(n0 + t, N - 1);
     sCol[0][t] = MX ? 1.0f : sb[erb == 1 ? col : 0];  // MX scales were applied by the MFMA
     float bvv = 0.0f;
@@ -310,60 +397,69 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   }
   __syncthreads();
   uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
-  const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
   float sav[MI];
+  if (unit) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
-  constexpr int ESZ = BF16OUT ? 2 : 4;
-  constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
-  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
-  constexpr int ROWS = kStageA / RB;            // rows per pass: 128 or 64
-  constexpr int IPP = ROWS / 32;                // MFMA row tiles per pass: 4 or 2
-  constexpr int EPC = 16 / ESZ;                 // elements per chunk
+    for (int i = 0; i < MI; ++i) sav[i] = 1.0f;
+    float* dst = part + static_cast<int64_t>(bid - t_main) * (TM * TN);
+    store_tile<false>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1, wn, fr, fg,
+                      lane);
+  } else {
+    const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
 #pragma unroll
-  for (int pass = 0; pass < MI / IPP; ++pass) {
+    for (int i = 0; i < MI; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
+    store_tile<BF16OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr,
+                        fg, lane);
+  }
+}
+
+// Finishes the split-K tiles: tile t_main + k sums its `split` FP32 partials
+// part[k split + p] in the order p = 0, 1, ..., applies s_a(row) s_b(col) and
+// the bias, rounds and stores; one thread per 4 consecutive columns.
+template <bool OUTBF16>
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int t_main, int split,
+                                                      int tiles_m, int tiles_n, int64_t M, int64_t N,
+                                                      const float* __restrict__ sa, int64_t era,
+                                                      const float* __restrict__ sb, int64_t erb,
+                                                      const void* __restrict__ bias, int bias_bf16,
+                                                      void* __restrict__ Y, int64_t ldy, int vec_store) {
+  const int k = blockIdx.y;
+  int tile_m, tile_n;
+  tile_of(t_main + k, tiles_m, tiles_n, tile_m, tile_n);
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // quad index in the tile
+  const int r = idx / (TN / 4), c = (idx % (TN / 4)) * 4;
+  const int64_t row = static_cast<int64_t>(tile_m) * TM + r, col = static_cast<int64_t>(tile_n) * TN + c;
+  if (row >= M || col >= N) return;
+  const float* p = part + static_cast<int64_t>(k) * split * (TM * TN) + r * TN + c;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(p);
+  for (int q = 1; q < split; ++q) acc += *reinterpret_cast<const f32x4*>(p + static_cast<int64_t>(q) * (TM * TN));
+  const float sav = sa[era == 1 ? row : 0];
+  float v[4];
 #pragma unroll
-    for (int ii = 0; ii < IPP; ++ii) {
-      const int i = pass * IPP + ii;
-      const int lrow = ii * 32 + fr;            // row within the pass
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = j * 32 + g * 8 + 4 * fg;  // first of 4 columns within the wave tile
-          const f32x4 scv = *reinterpret_cast<const f32x4*>(&sCol[0][wn * WTN + c]);
-          const f32x4 biv = *reinterpret_cast<const f32x4*>(&sCol[1][wn * WTN + c]);
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * (sav[i] * scv[r]) + biv[r];
-          const int byte = c * ESZ;               // byte offset of the 4 values in the row
-          const int chunk = (byte >> 4) ^ (lrow & 15);
-          uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
-          if constexpr (BF16OUT) {
-            const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
-            *reinterpret_cast<bf16x4*>(dst) = h;
-          } else {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-          }
-        }
+  for (int e = 0; e < 4; ++e) {
+    const int64_t cc = min(col + e, N - 1);
+    float bv = 0.0f;
+    if (bias)
+      bv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[cc]) << 16)
+                     : static_cast<const float*>(bias)[cc];
+    v[e] = acc[e] * (sav * sb[erb == 1 ? cc : 0]) + bv;
+  }
+  if constexpr (OUTBF16) {
+    const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+    uint16_t* dst = static_cast<uint16_t*>(Y) + row * ldy + col;
+    if (vec_store && col + 4 <= N) {
+      *reinterpret_cast<bf16x4*>(dst) = h;
+    } else {
+      const u32x2 hb = __builtin_bit_cast(u32x2, h);  // 4 bf16 as 2 words
+      for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = static_cast<uint16_t>(hb[e >> 1] >> (16 * (e & 1)));
     }
-    __syncthreads();
-    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
-      const int lrow = ch / CPR, cc = ch % CPR;
-      const int64_t row = wrow0 + pass * ROWS + lrow;
-      const int64_t col = wcol0 + cc * EPC;
-      if (row >= M || col >= N) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & 15)) << 4));
-      char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
-      if (vec_store && col + EPC <= N) {
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
-        const char* src = reinterpret_cast<const char*>(&v);
-        for (int e = 0; e < EPC && col + e < N; ++e)
-          for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
-      }
+  } else {
+    float* dst = static_cast<float*>(Y) + row * ldy + col;
+    if (vec_store && col + 4 <= N) {
+      *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = v[e];
     }
-    __syncthreads();
   }
 }
 
@@ -404,8 +500,33 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
   const int tiles_n = static_cast<int>((g.N + TN - 1) / TN);
   const int esz = g.yt == FP8RT_BF16 ? 2 : 4;
   const int vec = ((g.ldy * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(g.y) & 15u) == 0);
-  const dim3 grid(tiles_m * tiles_n);
+  const int T = tiles_m * tiles_n;
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
+  // Ragged last wave: when the tiles fill the CUs a whole number of times
+  // plus a last wave at most half full (the 4096 x 29568 up-projection: 7
+  // waves + 64 tiles), each last-wave tile is split along K into up to 4
+  // units so the last wave fills the CUs; k_split_reduce adds the parts.
+  int t_main = T, split = 1, ns_part = 0;
+  float* part = nullptr;
+  {
+    const int cus = device_cus();
+    const int rem = T % cus;
+    const int64_t ns = g.K / TKS;
+    if (!g.pow2_mx && T > cus && rem > 0 && 2 * rem <= cus) {
+      int sp = std::min(cus / rem, 4);
+      while (sp > 1 && ns % (2 * sp) != 0) --sp;  // every part an even number of stages
+      if (sp > 1) {
+        void* p = nullptr;
+        hipError_t e = get_scratch(st, static_cast<size_t>(rem) * sp * TM * TN * sizeof(float), &p);
+        if (e != hipSuccess) return e;
+        part = static_cast<float*>(p);
+        split = sp;
+        t_main = T - rem;
+        ns_part = static_cast<int>(ns / sp);
+      }
+    }
+  }
+  const dim3 grid(static_cast<unsigned>(t_main + (T - t_main) * split));
   uint32_t* xpa = nullptr;
   uint32_t* xpb = nullptr;
   if (g.pow2_mx) {
@@ -423,7 +544,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
 #define FP8RT_BIG(FA, FB, OUT, MXV)                                                                         \
   hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT, MXV>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
                      g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec, \
-                     xpa, xpb)
+                     xpa, xpb, t_main, split, ns_part, part)
 #define FP8RT_BIG_OUT(FA, FB, MXV)          \
   if (g.yt == FP8RT_BF16) FP8RT_BIG(FA, FB, true, MXV); \
   else FP8RT_BIG(FA, FB, false, MXV);
@@ -434,6 +555,15 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
   }
 #undef FP8RT_BIG_OUT
 #undef FP8RT_BIG
+  if (split > 1) {
+    const dim3 rgrid(TM * TN / 4 / 256, static_cast<unsigned>(T - t_main));
+    if (g.yt == FP8RT_BF16)
+      hipLaunchKernelGGL(k_split_reduce<true>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M,
+                         g.N, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+    else
+      hipLaunchKernelGGL(k_split_reduce<false>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M,
+                         g.N, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+  }
   return hipGetLastError();
 }
 

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
       if (vec_store && nb + 4 <= N) {
         *reinterpret_cast<bf16x4*>(dst) = h;
       } else {
-        for (int e = 0; e < 4 && nb + e < N; ++e) dst[e] = __builtin_bit_cast(uint16_t, h[e]);
+        const u32x2 hb = __builtin_bit_cast(u32x2, h);  // 4 bf16 as 2 words
+        for (int e = 0; e < 4 && nb + e < N; ++e) dst[e] = static_cast<uint16_t>(hb[e >> 1] >> (16 * (e & 1)));
       }
     } else {
       float* dst = static_cast<float*>(Y) + m * ldy + nb;

@@ -42,8 +42,8 @@ def run_gemm(rt, a, fa, ga, sa, b, fb, gb, sb, out, bias=None, flags=0):
     return host(y)
 
 
-SHAPES = [(200, 300, 320), (64, 256, 1024), (16, 512, 1024), (5, 200, 2048), (257, 129, 256), (300, 520, 512),
-          (520, 776, 1024)]
+SHAPES = [(200, 300, 320), (64, 256, 1024), (16, 512, 1024), (5, 200, 2048), (7, 203, 1024), (257, 129, 256),
+          (300, 520, 512), (520, 776, 1024)]
 SCALES = [((0, 0), (0, 0)), ((1, 0), (1, 0)), ((1, 128), (128, 128)), ((1, 128), (1, 0)),
           ((0, 0), (128, 128))]
 
@@ -135,3 +135,33 @@ def test_fp8_dot_unit_truncation_model(rt, orc):
     one = np.ones((1, 1), np.float32)
     y = run_gemm(rt, A, 0, (0, 0), one, B, 0, (0, 0), one, "f32")
     assert np.array_equal(y[:, 0], np.array(expect, np.float32))
+
+
+@pytest.mark.parametrize("fa", [0, 1])
+@pytest.mark.parametrize("grans", [((0, 0), (0, 0)), ((1, 0), (1, 0))])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_split_last_wave(rt, orc, fa, grans, out):
+    """4096 x 4300 x 1024: 16 x 17 = 272 tiles of 256 x 256 on 256 CUs, so the
+    last 16 tiles run as K-split units plus a reduction.  Whole rows and
+    columns through the split tiles (rows 3072-4095, columns 3328-4299) and
+    through whole tiles, plus random points, against the oracle."""
+    M, N, K = 4096, 4300, 1024
+    ga, gb = grans
+    a, sa, b, sb = operands(orc, 11 + fa, M, N, K, fa, 0, ga, gb, False)
+    bias = None
+    if out == "bf16":
+        from workloads import to_bf16_bits
+        bias = to_bf16_bits((np.random.default_rng(2).standard_normal(N) * 0.1).astype(np.float32))
+    y = run_gemm(rt, a, fa, ga, sa, b, 0, gb, sb, out, bias)
+    rows = np.array([3072, 3583, 4095, 17])
+    cols = np.array([3328, 3999, 4299, 5])
+    g = np.random.default_rng(5)
+    m = np.concatenate([np.repeat(rows, N), np.repeat(np.arange(M), len(cols)), g.integers(0, M, 8192)])
+    n = np.concatenate([np.tile(np.arange(N), len(rows)), np.tile(cols, M), g.integers(0, N, 8192)])
+    yref, S = orc.gemm_points(a, fa, sa, ga, b, 0, sb, gb, m, n, bias=bias)
+    thw = orc.dot_truncation_bound(a, fa, sa, ga, b, 0, sb, gb, m, n)
+    bias_f = None if bias is None else orc.bf16_bits_to_f32(bias)[n]
+    ok, st = check_gemm(y[m, n], yref, S, out == "bf16", orc, t_hw=thw, bias=bias_f)
+    print("split", fa, grans, out, st)
+    assert ok, st
+    assert st["n_over_rel"] <= 1e-3 * st["n"], st
