@@ -61,6 +61,9 @@ def lib():
         L.orc_compute_scale.argtypes = [P, I64, I, F, I, P, P]
         L.orc_quantize.restype = I
         L.orc_quantize.argtypes = [P, I, I64, I64, I64, I64, I64, I, I, F, I, P, P, P, I64, P, P]
+        L.orc_quantize_transpose.restype = I
+        L.orc_quantize_transpose.argtypes = [P, I, I64, I64, I64, I64, I64, I, I, F, I, P, P, P, I64, P,
+                                             I64, P, P]
         L.orc_dequantize.restype = I
         L.orc_dequantize.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, I, I64]
         L.orc_history_update.restype = I
@@ -165,6 +168,32 @@ def quantize(x: np.ndarray, fmt: int, gran=(0, 0), mode: int = DYNAMIC, eps: flo
     if r is None:
         r = (1.0 / s.astype(np.float64)).astype(np.float32)
     return q, s, r, am, cnt
+
+
+def quantize_transpose(x: np.ndarray, fmt: int, gran=(0, 0), mode: int = DYNAMIC,
+                       eps: float = 1e-12, pow2: bool = False, scale: np.ndarray | None = None,
+                       inv_scale: np.ndarray | None = None):
+    """Cast-transpose: returns (codes [rows x cols], codes transposed [cols x rows],
+    scale, inv_scale, amax, counts[sat, under])."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    G = (ngroups(rows, gran[0]), ngroups(cols, gran[1]))
+    q = np.empty((rows, cols), np.uint8)
+    qt = np.empty((cols, rows), np.uint8)
+    am = np.empty(G, np.float32)
+    cnt = np.zeros(2, np.uint64)
+    if mode == DYNAMIC:
+        s = np.empty(G, np.float32)
+        r = np.empty(G, np.float32)
+    else:
+        s = np.ascontiguousarray(scale, dtype=np.float32).reshape(G)
+        r = None if inv_scale is None else np.ascontiguousarray(inv_scale, np.float32).reshape(G)
+    _check(lib().orc_quantize_transpose(_ptr(x), _dtype_code(x), rows, cols, cols, gran[0], gran[1],
+                                        fmt, mode, eps, int(pow2), _ptr(s), _ptr(r), _ptr(q), cols,
+                                        _ptr(qt), rows, _ptr(am), _ptr(cnt)), "quantize_transpose")
+    if r is None:
+        r = (1.0 / s.astype(np.float64)).astype(np.float32)
+    return q, qt, s, r, am, cnt
 
 
 def dequantize(q: np.ndarray, fmt: int, scale: np.ndarray, gran=(0, 0), out_dtype: int = F32):

@@ -238,6 +238,26 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
     return 0;
 }
 
+/* Cast-transpose.  "FP8 formats and scaling for LLM inference", section "How
+ * the 8 bits are allocated": the hybrid recipe keeps E4M3 for the forward
+ * pass and E5M2 for the backward gradients, and a backward GEMM reads the
+ * operand in the other orientation; "FP8 inference: E4M3/E5M2 and the NVIDIA
+ * FP8 ecosystem", QAT section: forward and backward both run through FP8.
+ * Definition: the quantize above (same groups, scales and counters), with
+ * every code also written transposed, qt[j][i] = q[i][j]. */
+int orc_quantize_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t gr, int64_t gc, int fmt, int mode, float eps, int pow2,
+                           float* s, float* r, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                           float* amax_out, uint64_t* counts) {
+    if (!qt || ldqt < rows) return 1;
+    const int rc = orc_quantize(x, dtype, rows, cols, ldx, gr, gc, fmt, mode, eps, pow2, s, r, q, ldq,
+                                amax_out, counts);
+    if (rc) return rc;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) qt[j * ldqt + i] = q[i * ldq + j];
+    return 0;
+}
+
 /* Dequantize.  "FP8 formats and scaling for LLM inference", section "How a
  * scale fits a tensor into E4M3": X_hat = s * X_fp8.  "FP8 inference:
  * E4M3/E5M2 and the NVIDIA FP8 ecosystem", dequantization example.

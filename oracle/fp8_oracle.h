@@ -82,6 +82,13 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
                  float* s, float* r, uint8_t* q, int64_t ldq,
                  float* amax_out, uint64_t* counts);
 
+/* Cast-transpose: orc_quantize, plus qt[j * ldqt + i] = q[i * ldq + j]
+ * (the codes also written K-major).  Requires ldqt >= rows. */
+int orc_quantize_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t gr, int64_t gc, int fmt, int mode, float eps, int pow2,
+                           float* s, float* r, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                           float* amax_out, uint64_t* counts);
+
 /* y = fl32(s * dec(code)); out_dtype ORC_BF16 rounds that binary32 to bf16. */
 int orc_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
                    int64_t gr, int64_t gc, const float* s, void* y, int out_dtype,
