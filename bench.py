@@ -321,7 +321,19 @@ def extra_components(torch, rt, wl):
     comp["delayed_history_update_us"] = time_op(torch, hu)
     comp["delayed_gemm_e5m2_e4m3_f32"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
                                                     M * K + N * K + M * N * 4 + 8)
-    del G, W, Gq, Wq, y
+    # cast-transpose of the same G (the backward reads it in both orientations):
+    # codes row-major and K-major in one pass, per-tensor GIVEN (+ amax, counters),
+    # and per-column DYNAMIC (column amax pass, scales, then the pass)
+    Gt = u8(K, M)
+    ct = lambda: rt.fp8_quantize_transpose(G, (0, 0), rt.E5M2, rt.GIVEN, 1e-12, False, sg, rg, Gq, Gt, am, cnt)
+    comp["cast_transpose_g_e5m2_given"] = hbm_entry(time_op(torch, ct, scrub=scrub), M * K * 4 + 4,
+                                                    "k_cast_transpose + k_finish")
+    sgc, rgc = f32(1, K), f32(1, K)
+    ctc = lambda: rt.fp8_quantize_transpose(G, (0, 1), rt.E5M2, rt.DYNAMIC, 1e-12, False, sgc, rgc, Gq, Gt)
+    comp["cast_transpose_g_e5m2_per_column_dynamic"] = hbm_entry(
+        time_op(torch, ctc, scrub=scrub), M * K * 4 + K * 8,
+        "k_col_amax + k_col_amax_finish + k_compute_scale + k_cast_transpose")
+    del G, W, Gq, Wq, y, Gt
 
     # block-scaled GEMM: A 1x128 groups, W 128x128 blocks, bf16 out; variant 1x32 power-of-two
     c5 = wl.C5Block()

@@ -61,6 +61,9 @@ def lib():
         L.fp8_quantize.restype = C.c_int
         L.fp8_quantize.argtypes = [P, C.c_int, I64, I64, I64, Gran, C.c_int, C.c_int, F, I32, P, P,
                                    P, I64, P, P, P]
+        L.fp8_quantize_transpose.restype = C.c_int
+        L.fp8_quantize_transpose.argtypes = [P, C.c_int, I64, I64, I64, Gran, C.c_int, C.c_int, F, I32,
+                                             P, P, P, I64, P, I64, P, P, P]
         L.fp8_dequantize.restype = C.c_int
         L.fp8_dequantize.argtypes = [P, C.c_int, I64, I64, I64, Gran, P, P, C.c_int, I64, P]
         L.fp8_amax_history_update.restype = C.c_int
@@ -131,6 +134,20 @@ def fp8_quantize(x, gran, fmt, mode, eps, pow2_round_up, scale, inv_scale, q, am
                                               _ptr(sat_underflow), _stream(stream)))
 
 
+def fp8_quantize_transpose(x, gran, fmt, mode, eps, pow2_round_up, scale, inv_scale, q, qt,
+                           amax_out=None, sat_underflow=None, stream=None):
+    rows, cols, ld = _mat(x)
+    _, _, ldq = _mat(q)
+    qr, qc, ldqt = _mat(qt)
+    if (qr, qc) != (cols, rows):
+        raise ValueError("qt must be [cols x rows]")
+    _check("fp8_quantize_transpose",
+           lib().fp8_quantize_transpose(_ptr(x), _dtype(x), rows, cols, ld, Gran(*gran), fmt, mode, eps,
+                                        int(pow2_round_up), _ptr(scale), _ptr(inv_scale), _ptr(q), ldq,
+                                        _ptr(qt), ldqt, _ptr(amax_out), _ptr(sat_underflow),
+                                        _stream(stream)))
+
+
 def fp8_dequantize(q, fmt, gran, scale, y, stream=None):
     rows, cols, ldq = _mat(q)
     _, _, ldy = _mat(y)
@@ -165,7 +182,7 @@ def raw_call(name: str, *args) -> int:
     return getattr(lib(), name)(*args)
 
 
-__all__ = ["fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_dequantize",
+__all__ = ["fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
            "scale_shape"]

@@ -117,6 +117,51 @@ fp8rt_status fp8_quantize(const void* x, fp8rt_dtype xt, int64_t rows, int64_t c
   return from_hip(launch_quantize(a, stream));
 }
 
+fp8rt_status fp8_quantize_transpose(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,
+                                    int64_t ldx, fp8rt_gran g, fp8rt_format f, fp8rt_mode mode,
+                                    float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
+                                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                    float* amax_out, uint64_t* sat_underflow, hipStream_t stream) {
+  if (!valid_dtype(xt) || !valid_fmt(f) || !scale || !q || !qt) return FP8RT_EINVAL;
+  if (mode != FP8RT_DYNAMIC && mode != FP8RT_GIVEN) return FP8RT_EINVAL;
+  if (mode == FP8RT_DYNAMIC && !valid_eps(eps)) return FP8RT_EINVAL;
+  // one-column groups are read whole by this kernel: the 16-wide group rule
+  // of the quantize kernels does not apply to them
+  fp8rt_gran gc = g;
+  if (g.cols == 1 && group_extent(rows, g.rows) == rows) gc.cols = 0;
+  fp8rt_status st = check_matrix(x, rows, cols, ldx, gc);
+  if (st != FP8RT_OK) return st;
+  if (ldq < cols || ldqt < rows) return FP8RT_EINVAL;
+  if (rows % 16 != 0 || ldq % 16 != 0 || ldqt % 16 != 0 || !aligned16(q) || !aligned16(qt))
+    return FP8RT_EALIGN;
+  if (!aligned4(scale) || (inv_scale && !aligned4(inv_scale)) || (amax_out && !aligned4(amax_out)) ||
+      (sat_underflow && (reinterpret_cast<uintptr_t>(sat_underflow) & 7u)))
+    return FP8RT_EALIGN;
+  const int64_t er = group_extent(rows, g.rows), ec = group_extent(cols, g.cols);
+  const bool tensor = er == rows && ec == cols, row = er == 1 && ec == cols, col = er == rows && ec == 1;
+  if (!tensor && !row && !col) return FP8RT_EUNSUPPORTED;
+  QuantArgs a{};
+  a.x = x;
+  a.xt = xt;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.er = er;
+  a.ec = ec;
+  a.fmt = f;
+  a.mode = mode;
+  a.eps = mode == FP8RT_DYNAMIC ? eps : 1.0f;
+  a.pow2 = pow2_round_up != 0;
+  a.scale = scale;
+  a.inv_scale = inv_scale;
+  a.q = q;
+  a.ldq = ldq;
+  a.amax_out = amax_out;
+  a.counts = reinterpret_cast<unsigned long long*>(sat_underflow);
+  a.amax_only = false;
+  return from_hip(launch_quantize_transpose(a, qt, ldqt, stream));
+}
+
 fp8rt_status fp8_dequantize(const uint8_t* q, fp8rt_format f, int64_t rows, int64_t cols,
                             int64_t ldq, fp8rt_gran g, const float* scale, void* y,
                             fp8rt_dtype yt, int64_t ldy, hipStream_t stream) {

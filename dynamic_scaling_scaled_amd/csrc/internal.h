@@ -65,6 +65,9 @@ struct QuantArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// Cast-transpose: the quantize of a (tensor, row or column groups), codes also
+// written transposed to qt [cols x rows] (ldqt).
+hipError_t launch_quantize_transpose(const QuantArgs& a, uint8_t* qt, int64_t ldqt, hipStream_t stream);
 hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, float eps, int pow2,
                                 float* scale, float* inv_scale, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,

@@ -409,6 +409,152 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
   if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_l, under_l);
 }
 
+
+// ---------------------------------------------------------------------------
+// Cast-transpose: the cast of the quantize kernels, with every code written
+// twice: row-major to q and transposed (K-major) to qt.  GIVEN scales only
+// (the host runs the amax and scale kernels first in DYNAMIC mode).  Groups:
+// GK 0 tensor, 1 row, 2 column.  128 x 128 tiles: 16-byte loads of 8
+// elements, 8-byte row-major code stores, byte writes into an LDS tile kept
+// transposed (132-byte pitch: lanes of one write instruction fall in
+// different banks), 16-byte K-major stores of whole 128-byte lines.
+
+constexpr int kCtR = 128, kCtC = 128, kCtW = 132;
+
+template <typename T, int F, bool STATS>
+__device__ __forceinline__ u32x2 cast_octet_r8(const Octet<T>& v, const float (&r)[8], bool nan_path,
+                                               uint32_t& sat_l, uint32_t& under_l) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v.get(i) * r[i];
+  u32x2 out;
+  if (nan_path) {
+    out[0] = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+    out[1] = cvt4_nan<F>(f[4], f[5], f[6], f[7]);
+  } else {
+    out[0] = cvt4<F>(f[0], f[1], f[2], f[3]);
+    out[1] = cvt4<F>(f[4], f[5], f[6], f[7]);
+  }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sat_l += fabsf(f[i]) > Fmt<F>::kMax ? 1u : 0u;
+      under_l += (v.get(i) != 0.0f && fabsf(f[i]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+    }
+  }
+  return out;
+}
+
+template <typename T, int F, int GK, bool STATS, bool AMAX>
+__global__ __launch_bounds__(kBlock) void k_cast_transpose(
+    const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, const float* __restrict__ s_in,
+    const float* __restrict__ r_in, uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qt,
+    int64_t ldqt, int tiles_c, int ntiles, BlockPartial* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t tl[kCtC * kCtW];  // [tile column][tile row]
+  auto rmul = [&](int64_t g) { return r_in ? r_in[g] : 1.0f / s_in[g]; };
+  const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  uint32_t mb = 0, sat_l = 0, under_l = 0;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int tr = tile / tiles_c, tc = tile - tr * tiles_c;
+    const int64_t r0 = static_cast<int64_t>(tr) * kCtR, c0 = static_cast<int64_t>(tc) * kCtC;
+    const int64_t col = c0 + cg * 8;
+    const bool col_ok = col < cols;
+    const int64_t colc = min(col, cols - 8);
+    float rv[8];
+    bool rbad_c = false;
+    if constexpr (GK == 0) {
+      const float r = rmul(0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rv[k] = r;
+    } else if constexpr (GK == 2) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rv[k] = rmul(colc + k);
+    }
+    if constexpr (GK != 1) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rbad_c |= !(fabsf(rv[k]) <= FLT_MAX);
+    }
+    Octet<T> v[kCtR / 16];
+#pragma unroll
+    for (int i = 0; i < kCtR / 16; ++i) {
+      const int64_t row = r0 + i * 16 + rl;
+      v[i].load_nt(x + min(row, rows - 1) * ldx + colc);  // clamped: every load stays in flight
+      v[i].keep_if(col_ok && row < rows);
+    }
+    if (tile != static_cast<int>(blockIdx.x)) __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < kCtR / 16; ++i) {
+      const int lr = i * 16 + rl;
+      const int64_t row = r0 + lr;
+      float rr[8];
+      bool rbad = rbad_c;
+      if constexpr (GK == 1) {
+        const float r = rmul(min(row, rows - 1));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rr[k] = r;
+        rbad = !(fabsf(r) <= FLT_MAX);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rr[k] = rv[k];
+      }
+      const uint32_t omb = v[i].absmax_bits();
+      if constexpr (AMAX) mb = max(mb, omb);
+      const u32x2 c = cast_octet_r8<T, F, STATS>(v[i], rr, rbad || omb > kInfBits, sat_l, under_l);
+      if (col_ok && row < rows) __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + row * ldq + col));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tl[(cg * 8 + k) * kCtW + lr] = static_cast<uint8_t>(c[k >> 2] >> (8 * (k & 3)));
+    }
+    __syncthreads();
+    // qt row c0 + qc holds tile column qc: 8 parts of 16 codes (tile rows)
+#pragma unroll
+    for (int j = 0; j < kCtR * kCtC / 16 / kBlock; ++j) {
+      const int id = j * kBlock + threadIdx.x;
+      const int qc = id >> 3, pc = id & 7;
+      const int64_t orow = c0 + qc, ocol = r0 + pc * 16;
+      if (orow < cols && ocol < rows) {  // rows is a multiple of 16: a part is whole or absent
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(tl + qc * kCtW + pc * 16);
+        __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
+                                    reinterpret_cast<u32x4*>(qt + orow * ldqt + ocol));
+      }
+    }
+  }
+  if constexpr (STATS || AMAX) store_block_partial(part, mb, sat_l, under_l);
+}
+
+// Column maxima, pass 1: block (bx, by) takes columns [2048 bx, +2048) of
+// rows [by rpc, +rpc); one partial per (row chunk, column) as binary32 bits
+// of |x| (NaN patterns exceed Inf, so NaN propagates).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_col_amax(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                     int64_t ldx, int64_t rpc, uint32_t* __restrict__ part) {
+  const int64_t col = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * 8;
+  if (col >= cols) return;
+  const int64_t rb0 = static_cast<int64_t>(blockIdx.y) * rpc, rb1 = min(rb0 + rpc, rows);
+  uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t r = rb0; r < rb1; r += 4) {
+    Octet<T> v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u].load_nt(x + min(r + u, rb1 - 1) * ldx + col);  // clamped: repeats the last row (max unchanged)
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m[k] = max(m[k], __float_as_uint(v[u].get(k)) & kAbsMask);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) part[blockIdx.y * cols + col + k] = m[k];
+}
+
+__global__ __launch_bounds__(kBlock) void k_col_amax_finish(const uint32_t* __restrict__ part, int64_t nchunk,
+                                                            int64_t cols, float* __restrict__ amax) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (c >= cols) return;
+  uint32_t m = 0;
+  for (int64_t k = 0; k < nchunk; ++k) m = max(m, part[k * cols + c]);
+  amax[c] = __uint_as_float(m);
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 
@@ -563,6 +709,81 @@ hipError_t quant_typed(const QuantArgs& a, hipStream_t st) {
   return quant_blocktile<T, F>(a, st);
 }
 
+
+// ---------------------------------------------------------------------------
+// Cast-transpose launcher.
+
+template <typename T, int F, int GK, bool STATS, bool AM>
+void launch_ct_t(const QuantArgs& a, const float* r, uint8_t* qt, int64_t ldqt, int grid, int tiles_c,
+                 int ntiles, DevWorkspace* ws, hipStream_t st) {
+  hipLaunchKernelGGL((k_cast_transpose<T, F, GK, STATS, AM>), dim3(grid), dim3(kBlock), 0, st,
+                     static_cast<const T*>(a.x), a.rows, a.cols, a.ldx, a.scale, r, a.q, a.ldq, qt, ldqt,
+                     tiles_c, ntiles, ws->pass2);
+}
+
+template <typename T, int F>
+hipError_t quant_transpose_typed(const QuantArgs& a, uint8_t* qt, int64_t ldqt, hipStream_t st) {
+  const int gk = (a.er == a.rows && a.ec == a.cols) ? 0 : (a.er == 1 && a.ec == a.cols) ? 1 : 2;
+  const int64_t G = gk == 0 ? 1 : gk == 1 ? a.rows : a.cols;
+  const bool dynamic = a.mode == FP8RT_DYNAMIC;
+  const bool need_amax = dynamic || (a.amax_out && gk != 0);
+  DevWorkspace* ws = nullptr;
+  hipError_t e = get_workspace(st, &ws);
+  if (e != hipSuccess) return e;
+  // scratch: amax [G] (when amax_out is null), r [G] (when inv_scale is null),
+  // column partials [nchunk][cols]
+  const int64_t colblocks = ceil_div(a.cols, static_cast<int64_t>(kBlock) * 8);
+  const int64_t nchunk = gk == 2 ? std::min<int64_t>(a.rows, ceil_div(8 * device_cus(), colblocks)) : 0;
+  const int64_t rpc = gk == 2 ? ceil_div(a.rows, nchunk) : 0;
+  void* scr = nullptr;
+  e = get_scratch(st, static_cast<size_t>(2 * G + nchunk * a.cols) * 4 + 256, &scr);
+  if (e != hipSuccess) return e;
+  float* amax = a.amax_out ? a.amax_out : static_cast<float*>(scr);
+  float* rbuf = static_cast<float*>(scr) + G;
+  uint32_t* cpart = reinterpret_cast<uint32_t*>(static_cast<float*>(scr) + 2 * G);
+  if (need_amax) {
+    if (gk == 2) {
+      hipLaunchKernelGGL(k_col_amax<T>, dim3(static_cast<unsigned>(colblocks), static_cast<unsigned>(nchunk)),
+                         dim3(kBlock), 0, st, static_cast<const T*>(a.x), a.rows, a.cols, a.ldx, rpc, cpart);
+      hipLaunchKernelGGL(k_col_amax_finish, dim3(static_cast<unsigned>(ceil_div(a.cols, kBlock))), dim3(kBlock),
+                         0, st, cpart, nchunk, a.cols, amax);
+    } else {
+      QuantArgs b = a;
+      b.amax_only = true;
+      b.amax_out = amax;
+      b.counts = nullptr;
+      e = launch_quantize(b, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  const float* r = a.inv_scale;
+  if (dynamic) {
+    float* rw = a.inv_scale ? a.inv_scale : rbuf;
+    e = launch_compute_scale(amax, G, a.fmt, a.eps, a.pow2 != 0, a.scale, rw, st);
+    if (e != hipSuccess) return e;
+    r = rw;
+  }
+  const bool stats = a.counts != nullptr;
+  const bool am = gk == 0 && !dynamic && a.amax_out != nullptr;  // observed per-tensor amax
+  const int tiles_c = static_cast<int>(ceil_div(a.cols, kCtC));
+  const int64_t nt = ceil_div(a.rows, kCtR) * tiles_c;
+  if (nt > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int ntiles = static_cast<int>(nt);
+  const int grid = static_cast<int>(std::min<int64_t>({nt, int64_t(8) * device_cus(), int64_t(kMaxBlocks)}));
+#define FP8RT_CT(GK)                                                                                         \
+  if (stats && am) launch_ct_t<T, F, GK, true, true>(a, r, qt, ldqt, grid, tiles_c, ntiles, ws, st);       \
+  else if (stats) launch_ct_t<T, F, GK, true, false>(a, r, qt, ldqt, grid, tiles_c, ntiles, ws, st);       \
+  else if (am) launch_ct_t<T, F, GK, false, true>(a, r, qt, ldqt, grid, tiles_c, ntiles, ws, st);          \
+  else launch_ct_t<T, F, GK, false, false>(a, r, qt, ldqt, grid, tiles_c, ntiles, ws, st);
+  if (gk == 0) { FP8RT_CT(0) }
+  else if (gk == 1) { FP8RT_CT(1) }
+  else { FP8RT_CT(2) }
+#undef FP8RT_CT
+  if (stats || am)
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid, am ? a.amax_out : nullptr,
+                       a.counts);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
@@ -571,6 +792,15 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
                                : quant_typed<uint16_t, kE5M2>(a, st);
   }
   return a.fmt == FP8RT_E4M3 ? quant_typed<float, kE4M3>(a, st) : quant_typed<float, kE5M2>(a, st);
+}
+
+hipError_t launch_quantize_transpose(const QuantArgs& a, uint8_t* qt, int64_t ldqt, hipStream_t st) {
+  if (a.xt == FP8RT_BF16) {
+    return a.fmt == FP8RT_E4M3 ? quant_transpose_typed<uint16_t, kE4M3>(a, qt, ldqt, st)
+                               : quant_transpose_typed<uint16_t, kE5M2>(a, qt, ldqt, st);
+  }
+  return a.fmt == FP8RT_E4M3 ? quant_transpose_typed<float, kE4M3>(a, qt, ldqt, st)
+                             : quant_transpose_typed<float, kE5M2>(a, qt, ldqt, st);
 }
 
 // ---------------------------------------------------------------------------

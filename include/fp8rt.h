@@ -126,6 +126,26 @@ fp8rt_status fp8_quantize(const void* x, fp8rt_dtype xt, int64_t rows, int64_t c
                           uint8_t* q, int64_t ldq, float* amax_out, uint64_t* sat_underflow,
                           hipStream_t stream);
 
+/* Cast-transpose [P2 "How the 8 bits are allocated": the hybrid recipe runs
+ * the forward pass in E4M3 and the backward gradients in E5M2, and a backward
+ * GEMM reads the operand in the other orientation; P5 QAT section: forward
+ * and backward both through FP8].  Exactly fp8_quantize (same scales, codes,
+ * amax_out and counters), with every code also written transposed:
+ *   qt[j * ldqt + i] = q[i * ldq + j],  qt : [cols x rows] codes (ldqt >= rows).
+ * Granularities: tensor {0,0}, row {1,0}, column {0,1} (one scale per column:
+ * the row scale of the K-major copy); others return FP8RT_EUNSUPPORTED.
+ * DYNAMIC runs an amax kernel (per-column: two), the scale kernel, then one
+ * fused cast-transpose pass; GIVEN runs the pass alone (plus an amax pass
+ * when amax_out is requested for row or column groups).
+ * Alignment: rows, cols, ldx, ldq and ldqt multiples of 16; pointers 16-byte
+ * aligned.  Scratch: the per-stream GEMM scratch buffer holds the amax and
+ * r arrays when amax_out / inv_scale are NULL, and the per-column partials. */
+fp8rt_status fp8_quantize_transpose(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,
+                                    int64_t ldx, fp8rt_gran g, fp8rt_format f, fp8rt_mode mode,
+                                    float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
+                                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                    float* amax_out, uint64_t* sat_underflow, hipStream_t stream);
+
 /* Dequantize [P2 "How a scale fits a tensor into E4M3": X_hat = s * X_fp8;
  * P5 dequantization example].  y = fl32(s_g * dec(code)); a bf16 output is
  * that binary32 rounded to nearest even.  q: [rows x cols] (ldq), y (ldy). */

@@ -133,3 +133,26 @@ def test_gemm_validation(rt):
     assert g(rt, K=256, lda=256, ldb=256, ga=(1, 64), gb=(0, 0)) == rt.EUNSUPPORTED       # not a multiple of 128
     assert g(rt, K=256, lda=256, ldb=256, ga=(1, 32), gb=(1, 32)) == rt.EUNSUPPORTED      # 1x32 needs POW2 flag
     assert g(rt, K=256, lda=256, ldb=256, ga=(2, 128), gb=(0, 0)) == rt.EUNSUPPORTED      # A blocks span rows
+
+
+def qtr(rt, **kw):
+    a = dict(x=FAKE, xt=rt.BF16, rows=32, cols=64, ldx=64, gran=(0, 0), f=rt.E4M3, mode=rt.DYNAMIC,
+             eps=1e-12, pow2=0, scale=FAKE, inv=None, qq=FAKE, ldq=64, qt=FAKE, ldqt=32, amax=None,
+             cnt=None)
+    a.update(kw)
+    return rt.lib().fp8_quantize_transpose(a["x"], a["xt"], a["rows"], a["cols"], a["ldx"],
+                                           rt.Gran(*a["gran"]), a["f"], a["mode"], a["eps"], a["pow2"],
+                                           a["scale"], a["inv"], a["qq"], a["ldq"], a["qt"], a["ldqt"],
+                                           a["amax"], a["cnt"], None)
+
+
+def test_quantize_transpose_validation(rt):
+    assert qtr(rt, qt=None) == rt.EINVAL
+    assert qtr(rt, x=None) == rt.EINVAL
+    assert qtr(rt, ldqt=16) == rt.EINVAL          # ldqt < rows
+    assert qtr(rt, rows=24, ldqt=32) == rt.EALIGN  # rows not a multiple of 16
+    assert qtr(rt, ldqt=40) == rt.EALIGN
+    assert qtr(rt, qt=FAKE_ODD) == rt.EALIGN
+    assert qtr(rt, gran=(1, 32)) == rt.EUNSUPPORTED
+    assert qtr(rt, gran=(16, 16)) == rt.EUNSUPPORTED
+    assert qtr(rt, mode=rt.DYNAMIC, eps=float("nan")) == rt.EINVAL
