@@ -13,11 +13,13 @@ namespace fp8rt {
 // kernel on the stream (plain stores and loads: the kernel boundary orders
 // them; no device-scope fences or same-address atomics, which are slow on a
 // GPU whose L2 caches are per XCD).
+// 16 bytes, moved as one vector; a block handles fewer than 2^32 elements, so
+// its counts fit 32 bits (the finisher sums them in 64).
 struct BlockPartial {
   uint32_t amax_bits;
+  uint32_t sat;
+  uint32_t under;
   uint32_t pad;
-  unsigned long long sat;
-  unsigned long long under;
 };
 
 constexpr int kMaxBlocks = 8192;  // upper bound of every quantize grid

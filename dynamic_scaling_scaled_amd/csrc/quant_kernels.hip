@@ -73,10 +73,8 @@ __device__ __forceinline__ void store_block_partial(BlockPartial* bp, uint32_t m
       s += sh_s[i];
       u += sh_u[i];
     }
-    bp[blockIdx.x].amax_bits = m;
-    bp[blockIdx.x].pad = 0;
-    bp[blockIdx.x].sat = s;
-    bp[blockIdx.x].under = u;
+    *reinterpret_cast<u32x4*>(&bp[blockIdx.x]) =
+        u32x4{m, static_cast<uint32_t>(s), static_cast<uint32_t>(u), 0u};
   }
 }
 
@@ -152,7 +150,13 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
   float r;
   if constexpr (!GIVEN) {
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += kBlock) m = max(m, part1[i].amax_bits);
+    for (int i = threadIdx.x; i < nparts; i += 4 * kBlock) {  // four partials in flight per thread
+      uint32_t b[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[k] = part1[min(i + k * kBlock, nparts - 1)].amax_bits;  // clamped: a repeat
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, b[k]);
+    }
     m = block_max_u32(m, sh);
     const float a = __uint_as_float(m);
     float s;
@@ -200,34 +204,45 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
 }
 
 // Combines n block partials into amax_out[0] (as binary32, if non-null) and
-// counts[0..1] (if non-null).
-__global__ __launch_bounds__(kBlock) void k_finish(const BlockPartial* __restrict__ bp, int n,
-                                                   float* amax_out,
-                                                   unsigned long long* counts) {
-  __shared__ uint32_t sh[kWaves];
-  __shared__ unsigned long long sh_s[kWaves], sh_u[kWaves];
+// counts[0..1] (if non-null).  One workgroup of 1024 threads, four partials
+// (16-byte loads) in flight per thread.
+constexpr int kFinThreads = 1024;
+__global__ __launch_bounds__(kFinThreads) void k_finish(const BlockPartial* __restrict__ bp, int n,
+                                                        float* amax_out, unsigned long long* counts) {
+  __shared__ uint32_t sh_m[kFinThreads / 64];
+  __shared__ unsigned long long sh_s[kFinThreads / 64], sh_u[kFinThreads / 64];
   uint32_t m = 0;
   unsigned long long s = 0, u = 0;
-  for (int i = threadIdx.x; i < n; i += kBlock) {
-    m = max(m, bp[i].amax_bits);
-    s += bp[i].sat;
-    u += bp[i].under;
+  for (int i = threadIdx.x; i < n; i += 4 * kFinThreads) {
+    u32x4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = *reinterpret_cast<const u32x4*>(&bp[min(i + k * kFinThreads, n - 1)]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool in = i + k * kFinThreads < n;  // the clamped repeats add no counts
+      m = max(m, w[k][0]);
+      s += in ? w[k][1] : 0u;
+      u += in ? w[k][2] : 0u;
+    }
   }
-  m = block_max_u32(m, sh);
+  m = wave_max_u32(m);
   s = wave_sum_u64(s);
   u = wave_sum_u64(u);
   if ((threadIdx.x & 63) == 0) {
+    sh_m[threadIdx.x >> 6] = m;
     sh_s[threadIdx.x >> 6] = s;
     sh_u[threadIdx.x >> 6] = u;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    uint32_t tm = 0;
     unsigned long long ts = 0, tu = 0;
-    for (int i = 0; i < kWaves; ++i) {
+    for (int i = 0; i < kFinThreads / 64; ++i) {
+      tm = max(tm, sh_m[i]);
       ts += sh_s[i];
       tu += sh_u[i];
     }
-    if (amax_out) amax_out[0] = __uint_as_float(m);
+    if (amax_out) amax_out[0] = __uint_as_float(tm);
     if (counts) {
       counts[0] = ts;
       counts[1] = tu;
@@ -427,14 +442,12 @@ __device__ __forceinline__ u32x2 cast_octet_r8(const Octet<T>& v, const float (&
   float f[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = v.get(i) * r[i];
+  // the NaN fix-up as selects, not a branch (a branch here keeps both paths'
+  // values live and halves the occupancy of the cast-transpose kernel)
+  (void)nan_path;
   u32x2 out;
-  if (nan_path) {
-    out[0] = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
-    out[1] = cvt4_nan<F>(f[4], f[5], f[6], f[7]);
-  } else {
-    out[0] = cvt4<F>(f[0], f[1], f[2], f[3]);
-    out[1] = cvt4<F>(f[4], f[5], f[6], f[7]);
-  }
+  out[0] = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+  out[1] = cvt4_nan<F>(f[4], f[5], f[6], f[7]);
   if constexpr (STATS) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -450,7 +463,9 @@ __global__ __launch_bounds__(kBlock) void k_cast_transpose(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, const float* __restrict__ s_in,
     const float* __restrict__ r_in, uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qt,
     int64_t ldqt, int tiles_c, int ntiles, BlockPartial* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint8_t tl[kCtC * kCtW];  // [tile column][tile row]
+  // [tile column][tile row] codes; a thread owns 4 consecutive tile rows of 8
+  // columns per pass, so each column's 4 codes go to LDS as one word
+  __shared__ __attribute__((aligned(16))) uint32_t tl[kCtC * kCtW / 4];
   auto rmul = [&](int64_t g) { return r_in ? r_in[g] : 1.0f / s_in[g]; };
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
   uint32_t mb = 0, sat_l = 0, under_l = 0;
@@ -474,35 +489,50 @@ __global__ __launch_bounds__(kBlock) void k_cast_transpose(
 #pragma unroll
       for (int k = 0; k < 8; ++k) rbad_c |= !(fabsf(rv[k]) <= FLT_MAX);
     }
-    Octet<T> v[kCtR / 16];
-#pragma unroll
-    for (int i = 0; i < kCtR / 16; ++i) {
-      const int64_t row = r0 + i * 16 + rl;
-      v[i].load_nt(x + min(row, rows - 1) * ldx + colc);  // clamped: every load stays in flight
-      v[i].keep_if(col_ok && row < rows);
-    }
     if (tile != static_cast<int>(blockIdx.x)) __syncthreads();  // the previous tile's LDS reads are done
+    // tile row of pass p, row u of the thread: 64 p + 4 rl + u
 #pragma unroll
-    for (int i = 0; i < kCtR / 16; ++i) {
-      const int lr = i * 16 + rl;
-      const int64_t row = r0 + lr;
-      float rr[8];
-      bool rbad = rbad_c;
-      if constexpr (GK == 1) {
-        const float r = rmul(min(row, rows - 1));
+    for (int p = 0; p < 2; ++p) {
+      Octet<T> v[1][4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) rr[k] = r;
-        rbad = !(fabsf(r) <= FLT_MAX);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) rr[k] = rv[k];
+      for (int u = 0; u < 4; ++u) {
+        const int64_t row = r0 + 64 * p + 4 * rl + u;
+        v[0][u].load_nt(x + min(row, rows - 1) * ldx + colc);  // clamped: every load stays in flight
+        v[0][u].keep_if(col_ok && row < rows);
       }
-      const uint32_t omb = v[i].absmax_bits();
-      if constexpr (AMAX) mb = max(mb, omb);
-      const u32x2 c = cast_octet_r8<T, F, STATS>(v[i], rr, rbad || omb > kInfBits, sat_l, under_l);
-      if (col_ok && row < rows) __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + row * ldq + col));
+      u32x2 c[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) tl[(cg * 8 + k) * kCtW + lr] = static_cast<uint8_t>(c[k >> 2] >> (8 * (k & 3)));
+      for (int u = 0; u < 4; ++u) {
+        const int64_t row = r0 + 64 * p + 4 * rl + u;
+        float rr[8];
+        bool rbad = rbad_c;
+        if constexpr (GK == 1) {
+          const float r = rmul(min(row, rows - 1));
+#pragma unroll
+          for (int k = 0; k < 8; ++k) rr[k] = r;
+          rbad = !(fabsf(r) <= FLT_MAX);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) rr[k] = rv[k];
+        }
+        const uint32_t omb = v[0][u].absmax_bits();
+        if constexpr (AMAX) mb = max(mb, omb);
+        c[u] = cast_octet_r8<T, F, STATS>(v[0][u], rr, rbad || omb > kInfBits, sat_l, under_l);
+        if (col_ok && row < rows) __builtin_nontemporal_store(c[u], reinterpret_cast<u32x2*>(q + row * ldq + col));
+        // the counters pass through an opaque copy per octet: otherwise the
+        // 64 increments of a tile are reassociated into one tree that keeps
+        // every product of the tile live (141 VGPRs, 3 waves per SIMD)
+        if constexpr (STATS) asm volatile("" : "+v"(sat_l), "+v"(under_l));
+      }
+      // column k's codes of the 4 rows, packed row-ascending into one word
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sh = 8 * (k & 3), wd = k >> 2;
+        const uint32_t w = ((c[0][wd] >> sh) & 0xFFu) | (((c[1][wd] >> sh) & 0xFFu) << 8) |
+                           (((c[2][wd] >> sh) & 0xFFu) << 16) | (((c[3][wd] >> sh) & 0xFFu) << 24);
+        tl[(cg * 8 + k) * (kCtW / 4) + 16 * p + rl] = w;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the next pass's loads here (registers)
     }
     __syncthreads();
     // qt row c0 + qc holds tile column qc: 8 parts of 16 codes (tile rows)
@@ -512,7 +542,7 @@ __global__ __launch_bounds__(kBlock) void k_cast_transpose(
       const int qc = id >> 3, pc = id & 7;
       const int64_t orow = c0 + qc, ocol = r0 + pc * 16;
       if (orow < cols && ocol < rows) {  // rows is a multiple of 16: a part is whole or absent
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(tl + qc * kCtW + pc * 16);
+        const uint32_t* src = tl + qc * (kCtW / 4) + pc * 4;
         __builtin_nontemporal_store(u32x4{src[0], src[1], src[2], src[3]},
                                     reinterpret_cast<u32x4*>(qt + orow * ldqt + ocol));
       }
@@ -521,29 +551,37 @@ __global__ __launch_bounds__(kBlock) void k_cast_transpose(
   if constexpr (STATS || AMAX) store_block_partial(part, mb, sat_l, under_l);
 }
 
-// Column maxima, pass 1: block (bx, by) takes columns [2048 bx, +2048) of
-// rows [by rpc, +rpc); one partial per (row chunk, column) as binary32 bits
-// of |x| (NaN patterns exceed Inf, so NaN propagates).
+// Column maxima, pass 1: block (bx, by) takes columns [128 bx, +128) of rows
+// [by rpc, +rpc): 16 x 16 threads (8 columns by every 16th row each, four
+// rows in flight), reduced over the row lanes in LDS; one partial per (row
+// chunk, column) as binary32 bits of |x| (NaN patterns exceed Inf).
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_col_amax(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                      int64_t ldx, int64_t rpc, uint32_t* __restrict__ part) {
-  const int64_t col = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * 8;
-  if (col >= cols) return;
+  __shared__ uint32_t sh[16][129];
+  const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int64_t colc = min(c0 + cg * 8, cols - 8);
   const int64_t rb0 = static_cast<int64_t>(blockIdx.y) * rpc, rb1 = min(rb0 + rpc, rows);
   uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t r = rb0; r < rb1; r += 4) {
+  for (int64_t r = rb0 + rl; r < rb1; r += 64) {
     Octet<T> v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v[u].load_nt(x + min(r + u, rb1 - 1) * ldx + col);  // clamped: repeats the last row (max unchanged)
-    }
+    for (int u = 0; u < 4; ++u) v[u].load_nt(x + min(r + 16 * u, rb1 - 1) * ldx + colc);  // clamped: a repeat
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int k = 0; k < 8; ++k) m[k] = max(m[k], __float_as_uint(v[u].get(k)) & kAbsMask);
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) part[blockIdx.y * cols + col + k] = m[k];
+  for (int k = 0; k < 8; ++k) sh[rl][cg * 8 + k] = m[k];
+  __syncthreads();
+  if (threadIdx.x < 128 && c0 + threadIdx.x < cols) {
+    uint32_t mm = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mm = max(mm, sh[i][threadIdx.x]);
+    part[blockIdx.y * cols + c0 + threadIdx.x] = mm;
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void k_col_amax_finish(const uint32_t* __restrict__ part, int64_t nchunk,
@@ -586,7 +624,7 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   if (a.amax_only) {
     hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid1), dim3(kBlock), 0, st, x, rows, opr, a.ldx, spr,
                        ws->pass1);
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass1, grid1, a.amax_out, nullptr);
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass1, grid1, a.amax_out, nullptr);
     return hipGetLastError();
   }
 #define FP8RT_CAST(GV, ST, AM)                                                                        \
@@ -606,7 +644,7 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   }
 #undef FP8RT_CAST
   if (stats || (given && am))
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid,
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid,
                        given ? a.amax_out : nullptr, a.counts);
   return hipGetLastError();
 }
@@ -654,7 +692,7 @@ hipError_t quant_rowgroups(const QuantArgs& a, int L, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   if (a.counts && !a.amax_only)
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid, nullptr, a.counts);
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid, nullptr, a.counts);
   return hipGetLastError();
 }
 
@@ -692,7 +730,7 @@ hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
   if (reg) blocktile_dispatch<T, F, true>(a, st, grid, nCg, ng, df, dt, ws);
   else blocktile_dispatch<T, F, false>(a, st, grid, nCg, ng, df, dt, ws);
   if (a.counts && !a.amax_only)
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid, nullptr, a.counts);
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid, nullptr, a.counts);
   return hipGetLastError();
 }
 
@@ -732,8 +770,10 @@ hipError_t quant_transpose_typed(const QuantArgs& a, uint8_t* qt, int64_t ldqt, 
   if (e != hipSuccess) return e;
   // scratch: amax [G] (when amax_out is null), r [G] (when inv_scale is null),
   // column partials [nchunk][cols]
-  const int64_t colblocks = ceil_div(a.cols, static_cast<int64_t>(kBlock) * 8);
-  const int64_t nchunk = gk == 2 ? std::min<int64_t>(a.rows, ceil_div(8 * device_cus(), colblocks)) : 0;
+  const int64_t colblocks = ceil_div(a.cols, 128);
+  const int64_t nchunk =
+      gk == 2 ? std::max<int64_t>(1, std::min<int64_t>(ceil_div(a.rows, 64), ceil_div(8 * device_cus(), colblocks)))
+              : 0;
   const int64_t rpc = gk == 2 ? ceil_div(a.rows, nchunk) : 0;
   void* scr = nullptr;
   e = get_scratch(st, static_cast<size_t>(2 * G + nchunk * a.cols) * 4 + 256, &scr);
@@ -769,7 +809,7 @@ hipError_t quant_transpose_typed(const QuantArgs& a, uint8_t* qt, int64_t ldqt, 
   const int64_t nt = ceil_div(a.rows, kCtR) * tiles_c;
   if (nt > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int ntiles = static_cast<int>(nt);
-  const int grid = static_cast<int>(std::min<int64_t>({nt, int64_t(8) * device_cus(), int64_t(kMaxBlocks)}));
+  const int grid = static_cast<int>(std::min<int64_t>(nt, int64_t(kMaxBlocks)));
 #define FP8RT_CT(GK)                                                                                         \
   if (stats && am) launch_ct_t<T, F, GK, true, true>(a, r, qt, ldqt, grid, tiles_c, ntiles, ws, st);       \
   else if (stats) launch_ct_t<T, F, GK, true, false>(a, r, qt, ldqt, grid, tiles_c, ntiles, ws, st);       \
@@ -780,7 +820,7 @@ hipError_t quant_transpose_typed(const QuantArgs& a, uint8_t* qt, int64_t ldqt, 
   else { FP8RT_CT(2) }
 #undef FP8RT_CT
   if (stats || am)
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, ws->pass2, grid, am ? a.amax_out : nullptr,
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid, am ? a.amax_out : nullptr,
                        a.counts);
   return hipGetLastError();
 }

@@ -13,7 +13,7 @@
  *  - Every array pointer is a caller-owned DEVICE pointer (HBM of the current
  *    HIP device).  The library owns two kinds of device memory, both per
  *    (device, stream) pair and kept until the process ends:
- *      * a workspace of 384 KB that the quantize entry points use for
+ *      * a workspace of 256 KB that the quantize entry points use for
  *        per-block partial results; it is allocated and zeroed (with a device
  *        synchronization) on the first such call on that pair;
  *      * a GEMM scratch buffer for repacked block scales, used by
