@@ -173,6 +173,17 @@ def bench_prefill(args, torch, rt, wl):
         if timed:
             timer.stop("gemm")
 
+    # the same GEMM with the output requantized to E4M3 in the epilogue (an
+    # output scale given, as a delayed scale would be), amax of Y and counters
+    s_y = torch.full((1, 1), 0.05, device=dev)
+    am_y = torch.empty((1, 1), device=dev)
+    cnt_y = torch.zeros(2, dtype=torch.int64, device=dev)
+    yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+
+    def gemm_fp8out():
+        rt.fp8_scaled_gemm_fp8out(xq, rt.E4M3, (0, 0), s_x, Wq, rt.E4M3, (0, 0), s_w, yq, rt.E4M3, s_y, None,
+                                  am_y, cnt_y)
+
     quant_w()
     for _ in range(3):
         timer.start("quant_w")
@@ -192,6 +203,15 @@ def bench_prefill(args, torch, rt, wl):
     wall = time.perf_counter() - t0
     total_ms = ev0.elapsed_time(ev1)
     ms_step = total_ms / args.steps
+    gemm_fp8out()
+    for _ in range(3):
+        timer.start("gemm_fp8out")
+        gemm_fp8out()
+        timer.stop("gemm_fp8out")
+    torch.cuda.synchronize()
+    go_ms = float(np.mean(timer.ms("gemm_fp8out")))
+    fp8out = mfma_entry(go_ms * 1e3, 2.0 * M * N * K, M * K + N * K + M * N + 8)
+    fp8out["kernels"] = "k_gemm_big (E4M3 out, whole tiles) + k_finish"
     q_ms = float(np.mean(timer.ms("quant_x")))
     g_ms = float(np.mean(timer.ms("gemm")))
     qw_ms = float(np.mean(timer.ms("quant_w")))
@@ -226,6 +246,7 @@ def bench_prefill(args, torch, rt, wl):
                 "us": qw_ms * 1e3, "GB_s": qw_bytes / (qw_ms * 1e-3) / 1e9,
                 "frac_hbm": qw_bytes / (qw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes": qw_bytes},
+            "gemm_fp8_out_e4m3": fp8out,
             "quant_over_gemm": q_ms / g_ms,
             "x_saturated_underflowed": sat,
         },

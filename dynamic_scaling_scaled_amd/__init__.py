@@ -71,6 +71,9 @@ def lib():
         L.fp8_scaled_gemm.restype = C.c_int
         L.fp8_scaled_gemm.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                       I64, P, C.c_int, P, C.c_int, I64, U32, P]
+        L.fp8_scaled_gemm_fp8out.restype = C.c_int
+        L.fp8_scaled_gemm_fp8out.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
+                                             I64, P, C.c_int, C.c_int, P, P, P, I64, P, P, U32, P]
         _lib = L
     return _lib
 
@@ -182,7 +185,24 @@ def raw_call(name: str, *args) -> int:
     return getattr(lib(), name)(*args)
 
 
-__all__ = ["fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
+def fp8_scaled_gemm_fp8out(a, fa, ga, scale_a, b, fb, gb, scale_b, yq, fy, scale_y, inv_scale_y=None,
+                           amax_y=None, sat_underflow=None, bias=None, flags=0, stream=None):
+    M, K, lda = _mat(a)
+    N, K2, ldb = _mat(b)
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    My, Ny, ldy = _mat(yq)
+    if (My, Ny) != (M, N) or yq.dtype != torch.uint8:
+        raise ValueError("yq must be uint8 [M x N]")
+    bt = F32 if bias is None else _dtype(bias)
+    _check("fp8_scaled_gemm_fp8out",
+           lib().fp8_scaled_gemm_fp8out(_ptr(a), fa, lda, Gran(*ga), _ptr(scale_a), _ptr(b), fb, ldb, Gran(*gb),
+                                        _ptr(scale_b), M, N, K, _ptr(bias), bt, fy, _ptr(scale_y),
+                                        _ptr(inv_scale_y), _ptr(yq), ldy, _ptr(amax_y), _ptr(sat_underflow),
+                                        flags, _stream(stream)))
+
+
+__all__ = ["fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
            "scale_shape"]

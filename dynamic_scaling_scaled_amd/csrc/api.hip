@@ -188,28 +188,25 @@ fp8rt_status fp8_amax_history_update(float* history, int32_t len, int32_t* head,
                                         scale_next, inv_scale_next, stream));
 }
 
-fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
-                             const float* scale_a, const uint8_t* b, fp8rt_format fb,
-                             int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
-                             int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
-                             void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
-                             hipStream_t stream) {
-  if (!a || !b || !scale_a || !scale_b || !y) return FP8RT_EINVAL;
-  if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_dtype(yt) || (bias && !valid_dtype(bias_t)))
-    return FP8RT_EINVAL;
+namespace {
+
+// Validation shared by the two GEMM entry points; fills g (output fields
+// excepted) and returns FP8RT_OK, or the status to return.
+fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga, const float* scale_a,
+                        const uint8_t* b, fp8rt_format fb, int64_t ldb, fp8rt_gran gb, const float* scale_b,
+                        int64_t M, int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t, int64_t ldy,
+                        uint32_t flags, GemmArgs& g) {
+  if (!a || !b || !scale_a || !scale_b) return FP8RT_EINVAL;
+  if (!valid_fmt(fa) || !valid_fmt(fb) || (bias && !valid_dtype(bias_t))) return FP8RT_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0 || lda < K || ldb < K || ldy < N) return FP8RT_EINVAL;
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
   if (ga.rows < 0 || ga.cols < 0 || gb.rows < 0 || gb.cols < 0) return FP8RT_EINVAL;
   if ((flags & ~FP8RT_POW2_SCALES) != 0) return FP8RT_EINVAL;
   if (K % 16 != 0 || lda % 16 != 0 || ldb % 16 != 0) return FP8RT_EALIGN;
   if (!aligned16(a) || !aligned16(b) || !aligned4(scale_a) || !aligned4(scale_b)) return FP8RT_EALIGN;
-  if ((yt == FP8RT_F32 && !aligned4(y)) || (yt == FP8RT_BF16 && (reinterpret_cast<uintptr_t>(y) & 1u)))
-    return FP8RT_EALIGN;
   if (bias && !aligned4(bias)) return FP8RT_EALIGN;
   if (!((fa == FP8RT_E4M3 && fb == FP8RT_E4M3) || (fa == FP8RT_E5M2 && fb == FP8RT_E4M3)))
     return FP8RT_EUNSUPPORTED;
-
-  GemmArgs g{};
   g.a = a;
   g.fa = fa;
   g.lda = lda;
@@ -227,8 +224,6 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
   g.K = K;
   g.bias = bias;
   g.bias_t = bias_t;
-  g.y = y;
-  g.yt = yt;
   g.ldy = ldy;
   g.pow2_mx = false;
   // Scale granularities the kernels implement.
@@ -242,6 +237,56 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
     if (b_kblk && g.ecb % 128 != 0) return FP8RT_EUNSUPPORTED;
     if (a_kblk && b_kblk && g.eca != g.ecb) return FP8RT_EUNSUPPORTED;
   }
+  return FP8RT_OK;
+}
+
+}  // namespace
+
+fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                             const float* scale_a, const uint8_t* b, fp8rt_format fb,
+                             int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
+                             int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
+                             void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
+                             hipStream_t stream) {
+  if (!y || !valid_dtype(yt)) return FP8RT_EINVAL;
+  GemmArgs g{};
+  const fp8rt_status st =
+      gemm_setup(a, fa, lda, ga, scale_a, b, fb, ldb, gb, scale_b, M, N, K, bias, bias_t, ldy, flags, g);
+  if (st != FP8RT_OK) return st;
+  if ((yt == FP8RT_F32 && !aligned4(y)) || (yt == FP8RT_BF16 && (reinterpret_cast<uintptr_t>(y) & 1u)))
+    return FP8RT_EALIGN;
+  g.y = y;
+  g.yt = yt;
+  return from_hip(launch_gemm(g, stream));
+}
+
+fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                                    const float* scale_a, const uint8_t* b, fp8rt_format fb, int64_t ldb,
+                                    fp8rt_gran gb, const float* scale_b, int64_t M, int64_t N, int64_t K,
+                                    const void* bias, fp8rt_dtype bias_t, fp8rt_format fy,
+                                    const float* scale_y, const float* inv_scale_y, uint8_t* yq,
+                                    int64_t ldy, float* amax_y, uint64_t* sat_underflow, uint32_t flags,
+                                    hipStream_t stream) {
+  if (!yq || !scale_y || !valid_fmt(fy)) return FP8RT_EINVAL;
+  GemmArgs g{};
+  const fp8rt_status st =
+      gemm_setup(a, fa, lda, ga, scale_a, b, fb, ldb, gb, scale_b, M, N, K, bias, bias_t, ldy, flags, g);
+  if (st != FP8RT_OK) return st;
+  if (!aligned4(scale_y) || (inv_scale_y && !aligned4(inv_scale_y)) || (amax_y && !aligned4(amax_y)) ||
+      (sat_underflow && (reinterpret_cast<uintptr_t>(sat_underflow) & 7u)))
+    return FP8RT_EALIGN;
+  // one per-block partial per 128 x 128 output tile at most
+  if (ceil_div(M, 128) * ceil_div(N, 128) > kMaxBlocks) return FP8RT_EUNSUPPORTED;
+  DevWorkspace* ws = nullptr;
+  if (get_workspace(stream, &ws) != hipSuccess) return FP8RT_EHIP;
+  g.y = yq;
+  g.yt = FP8RT_F32;  // unused with yq_fmt set
+  g.yq_fmt = fy;
+  g.sy = scale_y;
+  g.ry = inv_scale_y;
+  g.amax_y = amax_y;
+  g.counts_y = reinterpret_cast<unsigned long long*>(sat_underflow);
+  g.part = ws->pass2;
   return from_hip(launch_gemm(g, stream));
 }
 

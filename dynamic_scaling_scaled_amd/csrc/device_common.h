@@ -198,6 +198,34 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return v;
 }
 
+// Block-wide max of m and sums of s and u over NW waves; thread 0 writes
+// {m, s, u, 0} to dst (16 bytes).  Called by every thread of the block.
+template <int NW>
+__device__ __forceinline__ void block_stats_store(u32x4* dst, uint32_t m, uint32_t s, uint32_t u) {
+  __shared__ uint32_t sh_st[3][NW];
+  m = wave_max_u32(m);
+  s = static_cast<uint32_t>(wave_sum_u64(s));
+  u = static_cast<uint32_t>(wave_sum_u64(u));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    sh_st[0][w] = m;
+    sh_st[1][w] = s;
+    sh_st[2][w] = u;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tm = 0, ts = 0, tu = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      tm = max(tm, sh_st[0][i]);
+      ts += sh_st[1][i];
+      tu += sh_st[2][i];
+    }
+    *dst = u32x4{tm, ts, tu, 0u};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Division of a 32-bit unsigned by a run-time invariant divisor d >= 1:
 // q = (mulhi(n, m) + n) >> l with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.

@@ -151,15 +151,20 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
 // scaled (row factor sav, column vectors scol / bias from LDS), converted,
 // staged in the wave's 32 KB of LDS (16-byte chunks XOR-swizzled by row) and
 // stored as 16-byte row chunks; rows / columns at or past (M, N) are skipped.
-template <bool OUTBF16>
+// FP8 output (OUT kOutE4M3 / kOutE5M2): codes of v * rq with the quantize
+// kernels' saturating RNE cast; the lane's max |v| and counters accumulate
+// into mb / sat_l / under_l.
+template <int OUT>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t* stage, const float* scol,
                                            const float* sbias, const float (&sav)[MI], int64_t wrow0, int64_t wcol0,
                                            int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
-                                           int wn, int fr, int fg, int lane) {
-  constexpr int ESZ = OUTBF16 ? 2 : 4;
-  constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
-  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
-  constexpr int ROWS = kStageA / RB;            // rows per pass: 128 or 64
+                                           int wn, int fr, int fg, int lane, float rq, uint32_t& mb, uint32_t& sat_l,
+                                           uint32_t& under_l) {
+  constexpr int ESZ = OUT == kOutF32 ? 4 : OUT == kOutBF16 ? 2 : 1;
+  constexpr int RB = WTN * ESZ;                 // staged row bytes: 128, 256 or 512
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8, 16 or 32
+  constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // chunk swizzle mask
+  constexpr int ROWS = kStageA / RB < WTM ? kStageA / RB : WTM;  // rows per pass: 128 or 64
   constexpr int IPP = ROWS / 32;                // MFMA row tiles per pass: 4 or 2
   constexpr int EPC = 16 / ESZ;                 // elements per chunk
 #pragma unroll
@@ -179,13 +184,31 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * (sav[i] * scv[r]) + biv[r];
           const int byte = c * ESZ;               // byte offset of the 4 values in the row
-          const int chunk = (byte >> 4) ^ (lrow & 15);
+          const int chunk = (byte >> 4) ^ (lrow & SWM);
           uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
-          if constexpr (OUTBF16) {
+          if constexpr (OUT == kOutBF16) {
             const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
             *reinterpret_cast<bf16x4*>(dst) = h;
-          } else {
+          } else if constexpr (OUT == kOutF32) {
             *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
+            // statistics of stored outputs only: the tile's rows / columns
+            // past (M, N) hold clamped or unscaled padding
+            const bool row_in = wrow0 + pass * ROWS + lrow < M;
+            float f[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              f[r] = v[r] * rq;
+              const bool in = row_in && wcol0 + c + r < N;
+              mb = max(mb, in ? (__float_as_uint(v[r]) & kAbsMask) : 0u);
+              sat_l += (in && fabsf(f[r]) > Fmt<F>::kMax) ? 1u : 0u;
+              under_l += (in && v[r] != 0.0f && fabsf(f[r]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+            }
+            *reinterpret_cast<uint32_t*>(dst) = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+            // opaque per group: otherwise the tile's 256 updates are
+            // reassociated into trees that keep every accumulator live
+            asm volatile("" : "+v"(mb), "+v"(sat_l), "+v"(under_l));
           }
         }
     }
@@ -195,7 +218,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
       const int64_t row = wrow0 + pass * ROWS + lrow;
       const int64_t col = wcol0 + cc * EPC;
       if (row >= M || col >= N) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & 15)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & SWM)) << 4));
       char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
       if (vec_store && col + EPC <= N) {
         *reinterpret_cast<u32x4*>(dst) = v;
@@ -212,14 +235,15 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
 // MX: power-of-two 1x32 scales applied inside the MFMA.  xpa / xpb hold the
 // E8M0 exponents repacked by k_pack_e8m0 as [row / 32][stage][row % 32] dwords
 // (byte b = K block 4 stage + b).
-template <int FA, int FB, bool BF16OUT, bool MX>
+template <int FA, int FB, int OUT, bool MX>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
     void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store,
     const uint32_t* __restrict__ xpa, const uint32_t* __restrict__ xpb, int t_main, int split, int ns_part,
-    float* __restrict__ part) {
+    float* __restrict__ part, const float* __restrict__ sy, const float* __restrict__ ry,
+    BlockPartial* __restrict__ ypart) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
@@ -398,19 +422,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   __syncthreads();
   uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
   float sav[MI];
+  uint32_t mb = 0, sat_l = 0, under_l = 0;
   if (unit) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) sav[i] = 1.0f;
     float* dst = part + static_cast<int64_t>(bid - t_main) * (TM * TN);
-    store_tile<false>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1, wn, fr, fg,
-                      lane);
+    store_tile<kOutF32>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1, wn, fr,
+                        fg, lane, 1.0f, mb, sat_l, under_l);
   } else {
     const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
 #pragma unroll
     for (int i = 0; i < MI; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
-    store_tile<BF16OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr,
-                        fg, lane);
+    float rq = 1.0f;
+    if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
+    store_tile<OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr, fg,
+                    lane, rq, mb, sat_l, under_l);
   }
+  // FP8 output: this tile's max |y| and counters (blocks run whole tiles in
+  // this mode; the host does not split the last wave)
+  if constexpr (OUT >= kOutE4M3)
+    block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
 }
 
 // Finishes the split-K tiles: tile t_main + k sums its `split` FP32 partials
@@ -498,7 +529,8 @@ bool gemm_big_eligible(const GemmArgs& g) {
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = static_cast<int>((g.M + TM - 1) / TM);
   const int tiles_n = static_cast<int>((g.N + TN - 1) / TN);
-  const int esz = g.yt == FP8RT_BF16 ? 2 : 4;
+  const int okind = gemm_out_kind(g);
+  const int esz = okind == kOutF32 ? 4 : okind == kOutBF16 ? 2 : 1;
   const int vec = ((g.ldy * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(g.y) & 15u) == 0);
   const int T = tiles_m * tiles_n;
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
@@ -512,7 +544,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
     const int cus = device_cus();
     const int rem = T % cus;
     const int64_t ns = g.K / TKS;
-    if (!g.pow2_mx && T > cus && rem > 0 && 2 * rem <= cus) {
+    if (!g.pow2_mx && okind < kOutE4M3 && T > cus && rem > 0 && 2 * rem <= cus) {
       int sp = std::min(cus / rem, 4);
       while (sp > 1 && ns % (2 * sp) != 0) --sp;  // every part an even number of stages
       if (sp > 1) {
@@ -544,10 +576,14 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
 #define FP8RT_BIG(FA, FB, OUT, MXV)                                                                         \
   hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT, MXV>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
                      g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec, \
-                     xpa, xpb, t_main, split, ns_part, part)
-#define FP8RT_BIG_OUT(FA, FB, MXV)          \
-  if (g.yt == FP8RT_BF16) FP8RT_BIG(FA, FB, true, MXV); \
-  else FP8RT_BIG(FA, FB, false, MXV);
+                     xpa, xpb, t_main, split, ns_part, part, g.sy, g.ry, g.part)
+#define FP8RT_BIG_OUT(FA, FB, MXV)                                  \
+  switch (okind) {                                                  \
+    case kOutBF16: FP8RT_BIG(FA, FB, kOutBF16, MXV); break;         \
+    case kOutE4M3: FP8RT_BIG(FA, FB, kOutE4M3, MXV); break;         \
+    case kOutE5M2: FP8RT_BIG(FA, FB, kOutE5M2, MXV); break;         \
+    default: FP8RT_BIG(FA, FB, kOutF32, MXV); break;                \
+  }
   if (g.fa == FP8RT_E4M3) {
     if (g.pow2_mx) { FP8RT_BIG_OUT(0, 0, true) } else { FP8RT_BIG_OUT(0, 0, false) }
   } else {

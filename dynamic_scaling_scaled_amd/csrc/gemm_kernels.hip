@@ -41,13 +41,13 @@ enum ScaleMode { kScaleEpilogue = 0, kScaleKBlock = 1, kScaleMX32 = 2 };
 // Byte offset of 16-byte chunk c (0..7) of tile row r in the swizzled LDS tile.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 
-template <int FA, int FB, int MODE, bool BF16OUT>
+template <int FA, int FB, int MODE, int OUT>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era, int64_t nKa,
     int64_t eca, const float* __restrict__ sb, int64_t erb, int64_t nKb, int64_t ecb,
     const void* __restrict__ bias, int bias_bf16, void* __restrict__ Y, int64_t ldy,
-    int tiles_n) {
+    int tiles_n, const float* __restrict__ sy, const float* __restrict__ ry, BlockPartial* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];  // [buf][A|B]
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -180,6 +180,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   }
 
   // Epilogue: scales (per-tensor / per-row modes), bias, convert, store.
+  // FP8 output: code = cast(y * r_y) with the quantize kernels' saturating
+  // RNE cast; max |y| and the counters go to this block's partial.
+  float rq = 1.0f;
+  if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
+  uint32_t mb = 0, sat_l = 0, under_l = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t col = n0 + wn * 64 + j * 16 + fr;
@@ -199,17 +204,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
         float v = acc[i][j][r];
         if constexpr (MODE == kScaleEpilogue) v = v * (sa[(row / era) * nKa] * sbv);
         v = v + bv;
-        if constexpr (BF16OUT) {
+        if constexpr (OUT == kOutBF16) {
           const uint32_t u = __float_as_uint(v);
           const uint16_t h = ((u & kAbsMask) > kInfBits) ? 0x7FC0u
                                                           : static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
           static_cast<uint16_t*>(Y)[row * ldy + col] = h;
-        } else {
+        } else if constexpr (OUT == kOutF32) {
           static_cast<float*>(Y)[row * ldy + col] = v;
+        } else {
+          constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
+          const float f = v * rq;
+          mb = max(mb, __float_as_uint(v) & kAbsMask);
+          sat_l += fabsf(f) > Fmt<F>::kMax ? 1u : 0u;
+          under_l += (v != 0.0f && fabsf(f) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+          static_cast<uint8_t*>(Y)[row * ldy + col] = static_cast<uint8_t>(cvt4_nan<F>(f, 0.f, 0.f, 0.f));
         }
       }
     }
   }
+  if constexpr (OUT >= kOutE4M3)
+    block_stats_store<kGemmThreads / 64>(reinterpret_cast<u32x4*>(&part[blockIdx.x]), mb, sat_l, under_l);
 }
 
 template <int FA, int FB, int MODE>
@@ -217,16 +231,17 @@ static void launch_mode(const GemmArgs& g, hipStream_t st, int nKa, int nKb) {
   const int tiles_m = static_cast<int>((g.M + BM - 1) / BM);
   const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
   const dim3 grid(tiles_m * tiles_n);
-  if (g.yt == FP8RT_BF16)
-    hipLaunchKernelGGL((k_gemm<FA, FB, MODE, true>), grid, dim3(kGemmThreads), 0, st, g.a, g.lda,
-                       g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, (int64_t)nKa, g.eca, g.sb, g.erb,
-                       (int64_t)nKb, g.ecb, g.bias, g.bias_t == FP8RT_BF16 ? 1 : 0, g.y, g.ldy,
-                       tiles_n);
-  else
-    hipLaunchKernelGGL((k_gemm<FA, FB, MODE, false>), grid, dim3(kGemmThreads), 0, st, g.a, g.lda,
-                       g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, (int64_t)nKa, g.eca, g.sb, g.erb,
-                       (int64_t)nKb, g.ecb, g.bias, g.bias_t == FP8RT_BF16 ? 1 : 0, g.y, g.ldy,
-                       tiles_n);
+#define FP8RT_GEN(OUT)                                                                                   \
+  hipLaunchKernelGGL((k_gemm<FA, FB, MODE, OUT>), grid, dim3(kGemmThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
+                     g.M, g.N, g.K, g.sa, g.era, (int64_t)nKa, g.eca, g.sb, g.erb, (int64_t)nKb, g.ecb,   \
+                     g.bias, g.bias_t == FP8RT_BF16 ? 1 : 0, g.y, g.ldy, tiles_n, g.sy, g.ry, g.part)
+  switch (gemm_out_kind(g)) {
+    case kOutBF16: FP8RT_GEN(kOutBF16); break;
+    case kOutE4M3: FP8RT_GEN(kOutE4M3); break;
+    case kOutE5M2: FP8RT_GEN(kOutE5M2); break;
+    default: FP8RT_GEN(kOutF32); break;
+  }
+#undef FP8RT_GEN
 }
 
 template <int FA, int FB>
@@ -238,14 +253,28 @@ static void launch_formats(const GemmArgs& g, hipStream_t st) {
   else launch_mode<FA, FB, kScaleEpilogue>(g, st, nKa, nKb);
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
-  if (gemm_skinny_eligible(g)) return launch_gemm_skinny(g, st);
-  if (gemm_big_eligible(g)) return launch_gemm_big(g, st);
-  if (gemm_kblock_eligible(g)) return launch_gemm_kblock(g, st);
+static hipError_t launch_generic(const GemmArgs& g, hipStream_t st) {
   if (g.fa == FP8RT_E4M3 && g.fb == FP8RT_E4M3) launch_formats<0, 0>(g, st);
   else if (g.fa == FP8RT_E5M2 && g.fb == FP8RT_E4M3) launch_formats<1, 0>(g, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  if (g.yq_fmt >= 0) {
+    // FP8 output: the large kernel (whole tiles, no split of the last wave)
+    // or the general one; then the partials of max |y| and the counters.
+    const bool big = gemm_big_eligible(g);
+    hipError_t e = big ? launch_gemm_big(g, st) : launch_generic(g, st);
+    if (e != hipSuccess) return e;
+    const int64_t nb = big ? ceil_div(g.M, 256) * ceil_div(g.N, 256) : ceil_div(g.M, BM) * ceil_div(g.N, BN);
+    if (g.amax_y || g.counts_y) return launch_finish(g.part, static_cast<int>(nb), g.amax_y, g.counts_y, st);
+    return hipSuccess;
+  }
+  if (gemm_skinny_eligible(g)) return launch_gemm_skinny(g, st);
+  if (gemm_big_eligible(g)) return launch_gemm_big(g, st);
+  if (gemm_kblock_eligible(g)) return launch_gemm_kblock(g, st);
+  return launch_generic(g, st);
 }
 
 }  // namespace fp8rt

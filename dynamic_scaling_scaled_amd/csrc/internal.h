@@ -97,7 +97,27 @@ struct GemmArgs {
   int yt;
   int64_t ldy;
   bool pow2_mx;  // 1x32 power-of-two scales through the scaled MFMA
+  // FP8 output (fp8_scaled_gemm_fp8out) when yq_fmt >= 0: y then holds codes
+  // of y_fp32 * r_y, r_y = ry[0] or fl32(1 / sy[0]); per-block partials of
+  // max |y| and the saturation / underflow counts go to part.
+  int yq_fmt = -1;
+  const float* sy = nullptr;
+  const float* ry = nullptr;
+  float* amax_y = nullptr;
+  unsigned long long* counts_y = nullptr;
+  BlockPartial* part = nullptr;
 };
+
+// Output kinds of the GEMM kernels' epilogues.
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2, kOutE5M2 = 3;
+inline int gemm_out_kind(const GemmArgs& g) {
+  if (g.yq_fmt >= 0) return g.yq_fmt == FP8RT_E4M3 ? kOutE4M3 : kOutE5M2;
+  return g.yt == FP8RT_BF16 ? kOutBF16 : kOutF32;
+}
+
+// Combines n per-block partials into amax_out[0] / counts[0..1] (nullable).
+hipError_t launch_finish(const BlockPartial* part, int n, float* amax_out, unsigned long long* counts,
+                         hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 bool gemm_big_eligible(const GemmArgs& g);

@@ -834,6 +834,12 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   return a.fmt == FP8RT_E4M3 ? quant_typed<float, kE4M3>(a, st) : quant_typed<float, kE5M2>(a, st);
 }
 
+hipError_t launch_finish(const BlockPartial* part, int n, float* amax_out, unsigned long long* counts,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, part, n, amax_out, counts);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_transpose(const QuantArgs& a, uint8_t* qt, int64_t ldqt, hipStream_t st) {
   if (a.xt == FP8RT_BF16) {
     return a.fmt == FP8RT_E4M3 ? quant_transpose_typed<uint16_t, kE4M3>(a, qt, ldqt, st)

@@ -187,6 +187,31 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
                              void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
                              hipStream_t stream);
 
+/* Scaled GEMM with an FP8 output [P2 "The full precision contract of one FP8
+ * GEMM": the contract names the output scale / requantization when the next
+ * op consumes FP8, applied in the epilogue instead of a BF16 write and a
+ * separate cast].  y = the fp8_scaled_gemm result in binary32 (scales, FP32
+ * accumulation, bias), then exactly the GIVEN-mode cast of fp8_quantize:
+ *   yq[m, n] = RNE_fy(clamp(fl32(y * r_y), -F_max, F_max)),  NaN -> 0x7F,
+ *   r_y = inv_scale_y[0], or fl32(1 / scale_y[0]) when inv_scale_y is NULL;
+ *   amax_y (nullable, [1]): max |y| over the output (binary32, before the
+ *   cast) -- the amax a delayed output scale pushes into its history;
+ *   sat_underflow (nullable, [2]): |fl32(y r_y)| > F_max, and y != 0 cast to
+ *   a zero code.
+ * Operands, granularities and alignment as fp8_scaled_gemm; yq : [M x N]
+ * codes (ldy).  The large-shape kernel (per-tensor, per-row and 1x32
+ * power-of-two scales) runs it without splitting its last wave of tiles;
+ * other shapes run on the general kernel.  Limit: ceil(M/128) ceil(N/128)
+ * <= 8192 (one per-block partial per output tile), else
+ * FP8RT_EUNSUPPORTED. */
+fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                                    const float* scale_a, const uint8_t* b, fp8rt_format fb, int64_t ldb,
+                                    fp8rt_gran gb, const float* scale_b, int64_t M, int64_t N, int64_t K,
+                                    const void* bias, fp8rt_dtype bias_t, fp8rt_format fy,
+                                    const float* scale_y, const float* inv_scale_y, uint8_t* yq,
+                                    int64_t ldy, float* amax_y, uint64_t* sat_underflow, uint32_t flags,
+                                    hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp8rt_status_string(fp8rt_status s);
 

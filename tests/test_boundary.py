@@ -156,3 +156,23 @@ def test_quantize_transpose_validation(rt):
     assert qtr(rt, gran=(1, 32)) == rt.EUNSUPPORTED
     assert qtr(rt, gran=(16, 16)) == rt.EUNSUPPORTED
     assert qtr(rt, mode=rt.DYNAMIC, eps=float("nan")) == rt.EINVAL
+
+
+def test_gemm_fp8out_validation(rt):
+    L = rt.lib()
+    G = rt.Gran
+
+    def call(**kw):
+        a = dict(a=FAKE, lda=64, sa=FAKE, b=FAKE, ldb=64, sb=FAKE, M=32, N=32, K=64, fy=rt.E4M3, sy=FAKE,
+                 yq=FAKE, ldy=32, flags=0)
+        a.update(kw)
+        return L.fp8_scaled_gemm_fp8out(a["a"], rt.E4M3, a["lda"], G(0, 0), a["sa"], a["b"], rt.E4M3, a["ldb"],
+                                        G(0, 0), a["sb"], a["M"], a["N"], a["K"], None, rt.F32, a["fy"], a["sy"],
+                                        None, a["yq"], a["ldy"], None, None, a["flags"], None)
+    assert call(yq=None) == rt.EINVAL
+    assert call(sy=None) == rt.EINVAL
+    assert call(fy=7) == rt.EINVAL
+    assert call(ldy=16) == rt.EINVAL
+    assert call(K=48, lda=48, ldb=48) == rt.EALIGN or call(K=40, lda=48, ldb=48) == rt.EALIGN
+    assert call(sy=FAKE + 2) == rt.EALIGN
+    assert call(M=128 * 8193, N=128, ldy=128) == rt.EUNSUPPORTED
