@@ -438,60 +438,94 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     store_tile<OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr, fg,
                     lane, rq, mb, sat_l, under_l);
   }
-  // FP8 output: this tile's max |y| and counters (blocks run whole tiles in
-  // this mode; the host does not split the last wave)
+  // FP8 output: a whole tile's max |y| and counters (split-K units hold raw
+  // partial sums; k_split_reduce takes the statistics of their tiles)
   if constexpr (OUT >= kOutE4M3)
-    block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
+    if (!unit) block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
 }
 
 // Finishes the split-K tiles: tile t_main + k sums its `split` FP32 partials
 // part[k split + p] in the order p = 0, 1, ..., applies s_a(row) s_b(col) and
-// the bias, rounds and stores; one thread per 4 consecutive columns.
-template <bool OUTBF16>
+// the bias, rounds and stores.  A block covers kRedQ x 256 quads (4
+// consecutive columns each) of one tile, thread t the quads t, t + 256, ...
+// FP8 output: codes of y * rq, and the block's max |y| and counters go to
+// ypart[t_main + k kRedBlocks + blockIdx.x].
+constexpr int kRedQ = 4;
+constexpr int kRedBlocks = TM * TN / 4 / 256 / kRedQ;  // blocks per split tile
+template <int OUT>
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int t_main, int split,
                                                       int tiles_m, int tiles_n, int64_t M, int64_t N,
                                                       const float* __restrict__ sa, int64_t era,
                                                       const float* __restrict__ sb, int64_t erb,
                                                       const void* __restrict__ bias, int bias_bf16,
-                                                      void* __restrict__ Y, int64_t ldy, int vec_store) {
+                                                      void* __restrict__ Y, int64_t ldy, int vec_store,
+                                                      const float* __restrict__ sy, const float* __restrict__ ry,
+                                                      BlockPartial* __restrict__ ypart) {
   const int k = blockIdx.y;
   int tile_m, tile_n;
   tile_of(t_main + k, tiles_m, tiles_n, tile_m, tile_n);
-  const int idx = blockIdx.x * 256 + threadIdx.x;  // quad index in the tile
-  const int r = idx / (TN / 4), c = (idx % (TN / 4)) * 4;
-  const int64_t row = static_cast<int64_t>(tile_m) * TM + r, col = static_cast<int64_t>(tile_n) * TN + c;
-  if (row >= M || col >= N) return;
-  const float* p = part + static_cast<int64_t>(k) * split * (TM * TN) + r * TN + c;
-  f32x4 acc = *reinterpret_cast<const f32x4*>(p);
-  for (int q = 1; q < split; ++q) acc += *reinterpret_cast<const f32x4*>(p + static_cast<int64_t>(q) * (TM * TN));
-  const float sav = sa[era == 1 ? row : 0];
-  float v[4];
+  float rq = 1.0f;
+  if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
+  uint32_t mb = 0, sat_l = 0, under_l = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t cc = min(col + e, N - 1);
-    float bv = 0.0f;
-    if (bias)
-      bv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[cc]) << 16)
-                     : static_cast<const float*>(bias)[cc];
-    v[e] = acc[e] * (sav * sb[erb == 1 ? cc : 0]) + bv;
-  }
-  if constexpr (OUTBF16) {
-    const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
-    uint16_t* dst = static_cast<uint16_t*>(Y) + row * ldy + col;
-    if (vec_store && col + 4 <= N) {
-      *reinterpret_cast<bf16x4*>(dst) = h;
-    } else {
-      const u32x2 hb = __builtin_bit_cast(u32x2, h);  // 4 bf16 as 2 words
-      for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = static_cast<uint16_t>(hb[e >> 1] >> (16 * (e & 1)));
+  for (int qi = 0; qi < kRedQ; ++qi) {
+    const int idx = (blockIdx.x * kRedQ + qi) * 256 + threadIdx.x;  // quad index in the tile
+    const int r = idx / (TN / 4), c = (idx % (TN / 4)) * 4;
+    const int64_t row = static_cast<int64_t>(tile_m) * TM + r, col = static_cast<int64_t>(tile_n) * TN + c;
+    if (row >= M || col >= N) continue;
+    const float* p = part + static_cast<int64_t>(k) * split * (TM * TN) + r * TN + c;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(p);
+    for (int q = 1; q < split; ++q) acc += *reinterpret_cast<const f32x4*>(p + static_cast<int64_t>(q) * (TM * TN));
+    const float sav = sa[era == 1 ? row : 0];
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t cc = min(col + e, N - 1);
+      float bv = 0.0f;
+      if (bias)
+        bv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[cc]) << 16)
+                       : static_cast<const float*>(bias)[cc];
+      v[e] = acc[e] * (sav * sb[erb == 1 ? cc : 0]) + bv;
     }
-  } else {
-    float* dst = static_cast<float*>(Y) + row * ldy + col;
-    if (vec_store && col + 4 <= N) {
-      *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    if constexpr (OUT == kOutBF16) {
+      const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+      uint16_t* dst = static_cast<uint16_t*>(Y) + row * ldy + col;
+      if (vec_store && col + 4 <= N) {
+        *reinterpret_cast<bf16x4*>(dst) = h;
+      } else {
+        const u32x2 hb = __builtin_bit_cast(u32x2, h);  // 4 bf16 as 2 words
+        for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = static_cast<uint16_t>(hb[e >> 1] >> (16 * (e & 1)));
+      }
+    } else if constexpr (OUT == kOutF32) {
+      float* dst = static_cast<float*>(Y) + row * ldy + col;
+      if (vec_store && col + 4 <= N) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = v[e];
+      }
     } else {
-      for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = v[e];
+      constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = v[e] * rq;
+        const bool in = col + e < N;
+        mb = max(mb, in ? (__float_as_uint(v[e]) & kAbsMask) : 0u);
+        sat_l += (in && fabsf(f[e]) > Fmt<F>::kMax) ? 1u : 0u;
+        under_l += (in && v[e] != 0.0f && fabsf(f[e]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+      }
+      const uint32_t w = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+      uint8_t* dst = static_cast<uint8_t*>(Y) + row * ldy + col;
+      if (vec_store && col + 4 <= N) {
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+        for (int e = 0; e < 4 && col + e < N; ++e) dst[e] = static_cast<uint8_t>(w >> (8 * e));
+      }
     }
   }
+  if constexpr (OUT >= kOutE4M3)
+    block_stats_store<4>(reinterpret_cast<u32x4*>(&ypart[t_main + k * kRedBlocks + blockIdx.x]), mb, sat_l,
+                         under_l);
 }
 
 // Repack power-of-two 1x32 scales (fp32, [rows][K / 32]) as E8M0 exponent
@@ -526,7 +560,7 @@ bool gemm_big_eligible(const GemmArgs& g) {
          g.N >= 128 && g.lda < (int64_t(1) << 23) && g.ldb < (int64_t(1) << 23);
 }
 
-hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
+hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
   const int tiles_m = static_cast<int>((g.M + TM - 1) / TM);
   const int tiles_n = static_cast<int>((g.N + TN - 1) / TN);
   const int okind = gemm_out_kind(g);
@@ -544,7 +578,9 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
     const int cus = device_cus();
     const int rem = T % cus;
     const int64_t ns = g.K / TKS;
-    if (!g.pow2_mx && okind < kOutE4M3 && T > cus && rem > 0 && 2 * rem <= cus) {
+    // FP8 output: one statistics slot per whole tile and per reduce block
+    const bool slots_ok = okind < kOutE4M3 || (T - rem) + rem * kRedBlocks <= kMaxBlocks;
+    if (!g.pow2_mx && slots_ok && T > cus && rem > 0 && 2 * rem <= cus) {
       int sp = std::min(cus / rem, 4);
       while (sp > 1 && ns % (2 * sp) != 0) --sp;  // every part an even number of stages
       if (sp > 1) {
@@ -592,14 +628,19 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st) {
 #undef FP8RT_BIG_OUT
 #undef FP8RT_BIG
   if (split > 1) {
-    const dim3 rgrid(TM * TN / 4 / 256, static_cast<unsigned>(T - t_main));
-    if (g.yt == FP8RT_BF16)
-      hipLaunchKernelGGL(k_split_reduce<true>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M,
-                         g.N, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
-    else
-      hipLaunchKernelGGL(k_split_reduce<false>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M,
-                         g.N, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+    const dim3 rgrid(kRedBlocks, static_cast<unsigned>(T - t_main));
+#define FP8RT_RED(OUT)                                                                                          \
+  hipLaunchKernelGGL(k_split_reduce<OUT>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M, \
+                     g.N, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec, g.sy, g.ry, g.part)
+    switch (okind) {
+      case kOutBF16: FP8RT_RED(kOutBF16); break;
+      case kOutE4M3: FP8RT_RED(kOutE4M3); break;
+      case kOutE5M2: FP8RT_RED(kOutE5M2); break;
+      default: FP8RT_RED(kOutF32); break;
+    }
+#undef FP8RT_RED
   }
+  if (nparts) *nparts = split > 1 ? t_main + (T - t_main) * kRedBlocks : T;
   return hipGetLastError();
 }
 

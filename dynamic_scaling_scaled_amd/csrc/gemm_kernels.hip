@@ -262,13 +262,18 @@ static hipError_t launch_generic(const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.yq_fmt >= 0) {
-    // FP8 output: the large kernel (whole tiles, no split of the last wave)
-    // or the general one; then the partials of max |y| and the counters.
-    const bool big = gemm_big_eligible(g);
-    hipError_t e = big ? launch_gemm_big(g, st) : launch_generic(g, st);
+    // FP8 output: the large kernel or the general one, then the partials of
+    // max |y| and the counters (one per tile, or per split-K reduce block).
+    int nb = 0;
+    hipError_t e;
+    if (gemm_big_eligible(g)) {
+      e = launch_gemm_big(g, st, &nb);
+    } else {
+      e = launch_generic(g, st);
+      nb = static_cast<int>(ceil_div(g.M, BM) * ceil_div(g.N, BN));
+    }
     if (e != hipSuccess) return e;
-    const int64_t nb = big ? ceil_div(g.M, 256) * ceil_div(g.N, 256) : ceil_div(g.M, BM) * ceil_div(g.N, BN);
-    if (g.amax_y || g.counts_y) return launch_finish(g.part, static_cast<int>(nb), g.amax_y, g.counts_y, st);
+    if (g.amax_y || g.counts_y) return launch_finish(g.part, nb, g.amax_y, g.counts_y, st);
     return hipSuccess;
   }
   if (gemm_skinny_eligible(g)) return launch_gemm_skinny(g, st);

@@ -121,7 +121,9 @@ hipError_t launch_finish(const BlockPartial* part, int n, float* amax_out, unsig
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 bool gemm_big_eligible(const GemmArgs& g);
-hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream);
+// nparts (nullable) receives the number of FP8-output statistics partials
+// written to g.part.
+hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream, int* nparts = nullptr);
 bool gemm_kblock_eligible(const GemmArgs& g);
 hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t stream);
 bool gemm_skinny_eligible(const GemmArgs& g);

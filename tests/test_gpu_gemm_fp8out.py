@@ -50,6 +50,19 @@ CASES = [  # (shape, ga, gb, pow2)
 @pytest.mark.parametrize("fy", [0, 1])
 @pytest.mark.parametrize("with_inv", [True, False])
 def test_fp8_output_within_tolerance(rt, orc, case, fy, with_inv):
+    check_fp8out(rt, orc, case, fy, with_inv)
+
+
+@pytest.mark.parametrize("fy,with_inv", [(0, False), (1, True)])
+def test_fp8_output_split_last_wave(rt, orc, fy, with_inv):
+    """520 x 22000 x 512: 3 x 86 = 258 tiles of 256 x 256 on 256 CUs, so the
+    last two tiles (columns 21760-21999, rows 256-519, the second ragged in
+    both dimensions) run as K-split units; the reduction kernel requantizes
+    them and supplies their statistics partials."""
+    check_fp8out(rt, orc, ((520, 22000, 512), (1, 0), (1, 0), False), fy, with_inv)
+
+
+def check_fp8out(rt, orc, case, fy, with_inv):
     (M, N, K), ga, gb, pow2 = case
     fa = 0
     a, sa, b, sb = operands(orc, hash((case, fy)) % 2 ** 31, M, N, K, fa, ga, gb, pow2)
