@@ -200,10 +200,10 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
  *   a zero code.
  * Operands, granularities and alignment as fp8_scaled_gemm; yq : [M x N]
  * codes (ldy).  The large-shape kernel (per-tensor, per-row and 1x32
- * power-of-two scales) runs it without splitting its last wave of tiles;
- * other shapes run on the general kernel.  Limit: ceil(M/128) ceil(N/128)
- * <= 8192 (one per-block partial per output tile), else
- * FP8RT_EUNSUPPORTED. */
+ * power-of-two scales) runs it, a ragged last wave of tiles split along K
+ * with the requantization in the reduction kernel; other shapes run on the
+ * general kernel.  Limit: ceil(M/128) ceil(N/128) <= 8192 (one per-block
+ * statistics partial per output tile), else FP8RT_EUNSUPPORTED. */
 fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
                                     const float* scale_a, const uint8_t* b, fp8rt_format fb, int64_t ldb,
                                     fp8rt_gran gb, const float* scale_b, int64_t M, int64_t N, int64_t K,
