@@ -74,6 +74,9 @@ def lib():
         L.orc_gemm_points.argtypes = gemm_args + [P]
         L.orc_gemm_points_exact.restype = I
         L.orc_gemm_points_exact.argtypes = gemm_args
+        L.orc_wonly_gemm_points.restype = I
+        L.orc_wonly_gemm_points.argtypes = [P, I, I64, P, I, I64, I64, I64, P, I64, I64, I64, P, I,
+                                            P, P, I64, P, P]
         L.orc_dot_truncation_bound.restype = I
         L.orc_dot_truncation_bound.argtypes = [P, I, I64, I64, I64, P, P, I, I64, I64, I64, P, I64,
                                                I64, I64, P, P, I64, P]
@@ -256,6 +259,38 @@ def gemm_points_exact(a, fa, sa, ga, b, fb, sb, gb, m_idx, n_idx, bias=None):
                                        _ptr(m_idx), _ptr(n_idx), m_idx.size, _ptr(y)),
            "gemm_points_exact")
     return y
+
+
+def wonly_gemm_points(x, w, fw, sw, gw, m_idx, n_idx, bias=None):
+    """Weight-only FP8 reference at points (m_idx[i], n_idx[i]):
+    y = sum_k x[m,k] s_w(n,k) dec(W[n,k]) + bias[n] and S = sum_k |term|, in
+    binary64.  x: [M, K] float32 or bf16 bits (uint16); w: [N, K] codes."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w, np.uint8)
+    M, K = x.shape
+    N, K2 = w.shape
+    assert K == K2
+    sw = np.ascontiguousarray(sw, np.float32)
+    bt = F32
+    if bias is not None:
+        bias = np.ascontiguousarray(bias)
+        bt = _dtype_code(bias)
+    m_idx = np.ascontiguousarray(m_idx, np.int64)
+    n_idx = np.ascontiguousarray(n_idx, np.int64)
+    y = np.empty(m_idx.size, np.float64)
+    S = np.empty(m_idx.size, np.float64)
+    _check(lib().orc_wonly_gemm_points(_ptr(x), _dtype_code(x), K, _ptr(w), fw, K, gw[0], gw[1],
+                                       _ptr(sw), M, N, K, _ptr(bias), bt, _ptr(m_idx), _ptr(n_idx),
+                                       m_idx.size, _ptr(y), _ptr(S)), "wonly_gemm_points")
+    return y, S
+
+
+def wonly_gemm_full(x, w, fw, sw, gw, bias=None):
+    """Every output point of the weight-only GEMM; (y [M,N], S [M,N])."""
+    M, N = x.shape[0], w.shape[0]
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    y, S = wonly_gemm_points(x, w, fw, sw, gw, mm.ravel(), nn.ravel(), bias)
+    return y.reshape(M, N), S.reshape(M, N)
 
 
 def gemm_full(a, fa, sa, ga, b, fb, sb, gb, bias=None):

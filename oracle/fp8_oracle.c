@@ -377,6 +377,35 @@ int orc_gemm_points(const uint8_t* a, int fa, int64_t lda, int64_t gra, int64_t 
     return 0;
 }
 
+/* Weight-only FP8 ("FP8 formats and scaling for LLM inference", section
+ * "Weight-only FP8 and W8A8 FP8": weights stored as FP8 with their scales,
+ * activations kept in BF16, the weight restored inside the GEMM).  The
+ * restored weight is the exact real value s_w * dec(code); every product
+ * x * s_w * dec is exact in binary64 (8 + 24 + 4 significant bits), and the
+ * products are summed in k order. */
+int orc_wonly_gemm_points(const void* x, int xdtype, int64_t ldx, const uint8_t* w, int fw,
+                          int64_t ldw, int64_t grw, int64_t gcw, const float* sw, int64_t M,
+                          int64_t N, int64_t K, const void* bias, int bias_dtype,
+                          const int64_t* m, const int64_t* n, int64_t npts, double* y,
+                          double* S) {
+    if (!x || !w || !sw || !m || !n || !y || M <= 0 || N <= 0 || K <= 0) return 1;
+    const double* dw = decode_table(fw);
+    for (int64_t p = 0; p < npts; ++p) {
+        const int64_t mi = m[p], ni = n[p];
+        if (mi < 0 || mi >= M || ni < 0 || ni >= N) return 1;
+        double acc = 0.0, absacc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double xv = (double)orc_load(x, xdtype, mi * ldx + k);
+            const double t = xv * (double)scale_at(sw, N, K, grw, gcw, ni, k) * dw[w[ni * ldw + k]];
+            acc += t;
+            absacc += fabs(t);
+        }
+        y[p] = acc + bias_at(bias, bias_dtype, ni);
+        if (S) S[p] = absacc;
+    }
+    return 0;
+}
+
 /* Integer value of a code in units of the format's smallest subnormal
  * (2^-9 for E4M3, 2^-16 for E5M2); returns 0 and sets *bad for NaN/Inf. */
 static int64_t code_units(unsigned code, int fmt, int* bad) {

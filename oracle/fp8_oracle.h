@@ -15,7 +15,8 @@
  *      s = amax/F_max), "Per-channel and block scaling" (s_g = a_g/F_max),
  *      "Delayed scaling" (s_{t+1} = f(a_t..a_{t-h+1})/F_max),
  *      "The full precision contract of one FP8 GEMM" (Y ~ s_x s_w X8 W8),
- *      "What numerical validation looks at" (saturation / underflow rates).
+ *      "What numerical validation looks at" (saturation / underflow rates),
+ *      "Weight-only FP8 and W8A8 FP8" (FP8 weights with BF16 activations).
  *  - "FP8 production quantization guide" (m.xxqk.cn): the dynamic per-tensor
  *      quantize listing (amax clamp, scale, inverse scale, clamp, cast).
  *  - "FP8 inference: E4M3/E5M2 and the NVIDIA FP8 ecosystem" (plumephp.com):
@@ -110,6 +111,16 @@ int orc_gemm_points(const uint8_t* a, int fa, int64_t lda, int64_t gra, int64_t 
                     int64_t grb, int64_t gcb, const float* sb, int64_t M, int64_t N,
                     int64_t K, const void* bias, int bias_dtype, const int64_t* m,
                     const int64_t* n, int64_t npts, double* y, double* S);
+
+/* Weight-only FP8 GEMM reference at points (m[i], n[i]):
+ *   y[i] = sum_k x[m,k] s_w(n,k) dec(W[n,k]) + bias[n],  S[i] = sum_k |term|
+ * x: [M x K] bf16 / fp32 activations (ldx, elements); W: [N x K] codes (ldw);
+ * s_w: [ceil(N/grw)][ceil(K/gcw)].  Accumulation in binary64. */
+int orc_wonly_gemm_points(const void* x, int xdtype, int64_t ldx, const uint8_t* w, int fw,
+                          int64_t ldw, int64_t grw, int64_t gcw, const float* sw, int64_t M,
+                          int64_t N, int64_t K, const void* bias, int bias_dtype,
+                          const int64_t* m, const int64_t* n, int64_t npts, double* y,
+                          double* S);
 
 /* Exact inner sums: for point i and every maximal K-run on which both scales
  * are constant, the sum of dec*dec products as an exact integer multiple of
