@@ -314,10 +314,18 @@ def extra_components(torch, rt, wl):
     comp["decode_quantize_w_per_channel"] = hbm_entry(time_op(torch, qw, scrub=scrub), N * K * 3 + N * 4,
                                                        "k_rowgroups")
     g_bytes = M * K + N * K + M * N * 2 + (M + N) * 4 + N * 2
-    e = hbm_entry(time_op(torch, gm, scrub=scrub), g_bytes, "k_gemm (small-M tiles)")
+    e = hbm_entry(time_op(torch, gm, scrub=scrub), g_bytes, "k_gemm_skinny")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_gemm_bf16_bias"] = e
-    del A, W, bias, Aq, Wq, y, d
+    # weight-only FP8: the same per-channel E4M3 weight codes, bf16 activations
+    yw = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wo = lambda: rt.fp8_weight_only_gemm(A, Wq, rt.E4M3, (1, 0), sw, yw, bias=bias)
+    wo()
+    wo_bytes = M * K * 2 + N * K + M * N * 2 + N * 4 + N * 2
+    e = hbm_entry(time_op(torch, wo, scrub=scrub), wo_bytes, "k_gemm_wonly")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_weight_only_gemm_bf16_bias"] = e
+    del A, W, bias, Aq, Wq, y, yw, d
 
     # delayed-scaling backward GEMM, one step: G 8192x8192 E5M2 with the scale of
     # the history window, W 8192x8192 E4M3 per tensor, fp32 out

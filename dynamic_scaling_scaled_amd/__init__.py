@@ -71,6 +71,9 @@ def lib():
         L.fp8_scaled_gemm.restype = C.c_int
         L.fp8_scaled_gemm.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                       I64, P, C.c_int, P, C.c_int, I64, U32, P]
+        L.fp8_weight_only_gemm.restype = C.c_int
+        L.fp8_weight_only_gemm.argtypes = [P, C.c_int, I64, P, C.c_int, I64, Gran, P, I64, I64, I64, P,
+                                           C.c_int, P, C.c_int, I64, P]
         L.fp8_scaled_gemm_fp8out.restype = C.c_int
         L.fp8_scaled_gemm_fp8out.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                              I64, P, C.c_int, C.c_int, P, P, P, I64, P, P, U32, P]
@@ -202,7 +205,20 @@ def fp8_scaled_gemm_fp8out(a, fa, ga, scale_a, b, fb, gb, scale_b, yq, fy, scale
                                         flags, _stream(stream)))
 
 
-__all__ = ["fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
+def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, stream=None):
+    """y = x (s_w o dec(w))^T + bias: x [M, K] bf16, w [N, K] uint8 codes."""
+    M, K, ldx = _mat(x)
+    N, K2, ldw = _mat(w)
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    _, _, ldy = _mat(y)
+    bt = F32 if bias is None else _dtype(bias)
+    _check("fp8_weight_only_gemm",
+           lib().fp8_weight_only_gemm(_ptr(x), _dtype(x), ldx, _ptr(w), fw, ldw, Gran(*gw), _ptr(scale_w),
+                                      M, N, K, _ptr(bias), bt, _ptr(y), _dtype(y), ldy, _stream(stream)))
+
+
+__all__ = ["fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
            "scale_shape"]

@@ -290,4 +290,41 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
   return from_hip(launch_gemm(g, stream));
 }
 
+fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, const uint8_t* w, fp8rt_format fw,
+                                  int64_t ldw, fp8rt_gran gw, const float* scale_w, int64_t M, int64_t N,
+                                  int64_t K, const void* bias, fp8rt_dtype bias_t, void* y, fp8rt_dtype yt,
+                                  int64_t ldy, hipStream_t stream) {
+  if (!x || !w || !scale_w || !y) return FP8RT_EINVAL;
+  if (!valid_dtype(xt) || !valid_fmt(fw) || !valid_dtype(yt) || (bias && !valid_dtype(bias_t)))
+    return FP8RT_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || ldx < K || ldw < K || ldy < N || gw.rows < 0 || gw.cols < 0)
+    return FP8RT_EINVAL;
+  if (M > int64_t(16) * 65535 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
+  if (xt != FP8RT_BF16) return FP8RT_EUNSUPPORTED;  // activations stay BF16
+  if (K % 16 != 0 || ldx % 8 != 0 || ldw % 16 != 0) return FP8RT_EALIGN;
+  if (!aligned16(x) || !aligned16(w) || !aligned4(scale_w) || (bias && !aligned4(bias))) return FP8RT_EALIGN;
+  if ((yt == FP8RT_F32 && !aligned4(y)) || (yt == FP8RT_BF16 && (reinterpret_cast<uintptr_t>(y) & 1u)))
+    return FP8RT_EALIGN;
+  WonlyArgs g;
+  g.erw = group_extent(N, gw.rows);
+  g.ecw = group_extent(K, gw.cols);
+  if (g.ecw < K && g.ecw % 128 != 0) return FP8RT_EUNSUPPORTED;  // K groups: whole 128-deep steps
+  if (ceil_div(N, g.erw) * ceil_div(K, g.ecw) >= (int64_t(1) << 31)) return FP8RT_EUNSUPPORTED;
+  g.x = static_cast<const uint16_t*>(x);
+  g.ldx = ldx;
+  g.w = w;
+  g.fw = fw;
+  g.ldw = ldw;
+  g.sw = scale_w;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.bias = bias;
+  g.bias_t = bias_t;
+  g.y = y;
+  g.yt = yt;
+  g.ldy = ldy;
+  return from_hip(launch_gemm_wonly(g, stream));
+}
+
 }  // extern "C"

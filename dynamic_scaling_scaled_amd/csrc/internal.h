@@ -127,6 +127,26 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream, int* nparts = 
 bool gemm_kblock_eligible(const GemmArgs& g);
 hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t stream);
 bool gemm_skinny_eligible(const GemmArgs& g);
+
+// Weight-only FP8 GEMM (gemm_wonly.hip): bf16 activations x [M x K] (ldx in
+// elements), FP8 weights w [N x K] (ldw bytes) with fp32 scales
+// [ceil(N/erw)][ceil(K/ecw)]; ecw >= K or a multiple of 128.
+struct WonlyArgs {
+  const uint16_t* x = nullptr;
+  int64_t ldx = 0;
+  const uint8_t* w = nullptr;
+  int fw = 0;
+  int64_t ldw = 0;
+  const float* sw = nullptr;
+  int64_t erw = 1, ecw = 1;
+  int64_t M = 0, N = 0, K = 0;
+  const void* bias = nullptr;
+  int bias_t = 0;
+  void* y = nullptr;
+  int yt = 0;
+  int64_t ldy = 0;
+};
+hipError_t launch_gemm_wonly(const WonlyArgs& g, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace fp8rt

@@ -212,6 +212,30 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
                                     int64_t ldy, float* amax_y, uint64_t* sat_underflow, uint32_t flags,
                                     hipStream_t stream);
 
+/* Weight-only FP8 GEMM ["FP8 formats and scaling for LLM inference", section
+ * "Weight-only FP8 and W8A8 FP8": weights stored as FP8, activations kept in
+ * BF16, the weight converted inside the kernel; section "Per-channel and
+ * block scaling" for the weight's scale groups].
+ *   Y[m,n] = sum_k x[m,k] s_w(n,k) dec(W[n,k]) + bias[n]
+ *   x : [M x K] bf16 activations (ldx in elements); xt must be FP8RT_BF16
+ *       (FP8RT_F32 returns FP8RT_EUNSUPPORTED)
+ *   w : [N x K] FP8 codes (ldw bytes), format fw (E4M3 or E5M2)
+ *   scale_w : fp32 [ceil(N/gw.rows)][ceil(K/gw.cols)]; gw.cols 0 / >= K
+ *       (tensor, channel, row blocks) or a multiple of 128 (K groups), else
+ *       FP8RT_EUNSUPPORTED
+ *   bias : nullable [N] fp32 / bf16;  y : [M x N] fp32 / bf16 (ldy)
+ * Every FP8 value is exactly a bf16 value: the products x dec(W) are exact,
+ * accumulated in FP32; the scale multiplies each K group's partial sum in
+ * FP32.  Built for decode shapes (W streamed once per 16 activation rows;
+ * larger M re-reads W per 16 rows).  Limits: M <= 16 * 65535.
+ * Alignment: K a multiple of 16, ldx a multiple of 8, ldw of 16; x and w
+ * 16-byte aligned, scales and fp32 bias / y 4-byte aligned. */
+fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, const uint8_t* w,
+                                  fp8rt_format fw, int64_t ldw, fp8rt_gran gw, const float* scale_w,
+                                  int64_t M, int64_t N, int64_t K, const void* bias,
+                                  fp8rt_dtype bias_t, void* y, fp8rt_dtype yt, int64_t ldy,
+                                  hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp8rt_status_string(fp8rt_status s);
 

@@ -176,3 +176,34 @@ def test_gemm_fp8out_validation(rt):
     assert call(K=48, lda=48, ldb=48) == rt.EALIGN or call(K=40, lda=48, ldb=48) == rt.EALIGN
     assert call(sy=FAKE + 2) == rt.EALIGN
     assert call(M=128 * 8193, N=128, ldy=128) == rt.EUNSUPPORTED
+
+
+def test_weight_only_gemm_validation(rt):
+    L = rt.lib()
+    G = rt.Gran
+
+    def call(**kw):
+        a = dict(x=FAKE, xt=rt.BF16, ldx=256, w=FAKE, fw=rt.E4M3, ldw=256, gw=(1, 0), sw=FAKE, M=16, N=64,
+                 K=256, bias=None, bt=rt.F32, y=FAKE, yt=rt.BF16, ldy=64)
+        a.update(kw)
+        return L.fp8_weight_only_gemm(a["x"], a["xt"], a["ldx"], a["w"], a["fw"], a["ldw"], G(*a["gw"]), a["sw"],
+                                      a["M"], a["N"], a["K"], a["bias"], a["bt"], a["y"], a["yt"], a["ldy"], None)
+    assert call(x=None) == rt.EINVAL
+    assert call(w=None) == rt.EINVAL
+    assert call(sw=None) == rt.EINVAL
+    assert call(y=None) == rt.EINVAL
+    assert call(fw=5) == rt.EINVAL
+    assert call(yt=9) == rt.EINVAL
+    assert call(M=0) == rt.EINVAL
+    assert call(ldx=128) == rt.EINVAL            # ldx < K
+    assert call(ldy=32) == rt.EINVAL             # ldy < N
+    assert call(gw=(-1, 0)) == rt.EINVAL
+    assert call(M=16 * 65536) == rt.EINVAL
+    assert call(xt=rt.F32) == rt.EUNSUPPORTED    # activations stay bf16
+    assert call(K=248, ldx=248, ldw=256) == rt.EALIGN
+    assert call(ldx=260) == rt.EALIGN            # 520-byte rows
+    assert call(ldw=264) == rt.EALIGN
+    assert call(x=FAKE + 8) == rt.EALIGN
+    assert call(sw=FAKE + 2) == rt.EALIGN
+    assert call(gw=(1, 64)) == rt.EUNSUPPORTED   # K groups are whole 128-deep steps
+    assert call(gw=(1, 192)) == rt.EUNSUPPORTED
