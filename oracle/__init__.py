@@ -74,6 +74,8 @@ def lib():
         L.orc_gemm_points.argtypes = gemm_args + [P]
         L.orc_gemm_points_exact.restype = I
         L.orc_gemm_points_exact.argtypes = gemm_args
+        L.orc_history_update_recipe.restype = I
+        L.orc_history_update_recipe.argtypes = [P, I, P, F, I, I, I, F, I, P, P]
         L.orc_wonly_gemm_points.restype = I
         L.orc_wonly_gemm_points.argtypes = [P, I, I64, P, I, I64, I64, I64, P, I64, I64, I64, P, I,
                                             P, P, I64, P, P]
@@ -218,6 +220,24 @@ def history_update(hist: np.ndarray, head: int, amax_new: float, fmt: int, eps: 
     r = np.empty(1, np.float32)
     _check(lib().orc_history_update(_ptr(hist), hist.size, C.byref(h), float(amax_new), fmt,
                                     eps, int(pow2), _ptr(s), _ptr(r)), "history_update")
+    return h.value, s[0], r[0]
+
+
+HIST_MAX, HIST_LATEST = 0, 1
+
+
+def history_update_recipe(hist: np.ndarray, head: int, amax_new: float, fmt: int, fn: int = HIST_MAX,
+                          margin: int = 0, eps: float = 1e-12, pow2: bool = False):
+    """Recipe variant of history_update (history function fn, margin m: the
+    scale is derived from f * 2^m).  Updates ``hist`` in place; returns
+    (new_head, s_next, r_next)."""
+    assert hist.dtype == np.float32 and hist.flags.c_contiguous
+    h = C.c_int(head)
+    s = np.empty(1, np.float32)
+    r = np.empty(1, np.float32)
+    _check(lib().orc_history_update_recipe(_ptr(hist), hist.size, C.byref(h), float(amax_new), fmt, fn,
+                                           margin, eps, int(pow2), _ptr(s), _ptr(r)),
+           "history_update_recipe")
     return h.value, s[0], r[0]
 
 

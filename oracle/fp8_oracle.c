@@ -307,6 +307,34 @@ int orc_history_update(float* hist, int len, int* head, float amax_new, int fmt,
     return orc_compute_scale(&a, 1, fmt, eps, pow2, s_next, r_next);
 }
 
+/* Delayed-scaling recipe variants (same section: the history function may be
+ * the most recent value, the window maximum or another rule; real recipes add
+ * a margin).  fn ORC_HIST_MAX is orc_history_update's window maximum;
+ * ORC_HIST_LATEST uses a_t alone (a non-positive a_t counts as 0, NaN
+ * propagates).  Reading of the margin m (0..16): the amax the scale is derived
+ * from is a * 2^m, so s grows by exactly 2^m (an overflow to Inf gives NaN s
+ * and r, as any non-finite amax does). */
+int orc_history_update_recipe(float* hist, int len, int* head, float amax_new, int fmt, int fn,
+                              int margin, float eps, int pow2, float* s_next, float* r_next) {
+    if (!hist || !head || len <= 0 || *head < 0 || *head >= len || !s_next) return 1;
+    if ((fn != ORC_HIST_MAX && fn != ORC_HIST_LATEST) || margin < 0 || margin > 16) return 1;
+    hist[*head] = amax_new;
+    *head = (*head + 1) % len;
+    float a = 0.0f;
+    if (fn == ORC_HIST_LATEST) {
+        a = isnan(amax_new) ? NAN : (amax_new > 0.0f ? amax_new : 0.0f);
+    } else {
+        int nan = 0;
+        for (int i = 0; i < len; ++i) {
+            if (isnan(hist[i])) nan = 1;
+            else if (hist[i] > a) a = hist[i];
+        }
+        if (nan) a = NAN;
+    }
+    a = (float)ldexp((double)a, margin);
+    return orc_compute_scale(&a, 1, fmt, eps, pow2, s_next, r_next);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scaled GEMM.  "FP8 formats and scaling for LLM inference", section "The full
  * precision contract of one FP8 GEMM": X ~ s_x X8, W ~ s_w W8,

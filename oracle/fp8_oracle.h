@@ -100,6 +100,14 @@ int orc_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_
 int orc_history_update(float* hist, int len, int* head, float amax_new, int fmt,
                        float eps, int pow2, float* s_next, float* r_next);
 
+/* Delayed-scaling recipe variants: the history function fn (ORC_HIST_MAX =
+ * window maximum, ORC_HIST_LATEST = a_t alone) and a margin m in [0, 16]:
+ * the scale is derived from f * 2^m.  The ring and head advance as in
+ * orc_history_update. */
+enum { ORC_HIST_MAX = 0, ORC_HIST_LATEST = 1 };
+int orc_history_update_recipe(float* hist, int len, int* head, float amax_new, int fmt, int fn,
+                              int margin, float eps, int pow2, float* s_next, float* r_next);
+
 /* Scaled GEMM reference at selected output points (m[i], n[i]):
  *   y[i] = sum_k s_a(m,k) s_b(n,k) dec(A[m,k]) dec(B[n,k]) + bias[n]
  *   S[i] = sum_k |s_a(m,k) s_b(n,k) dec(A[m,k]) dec(B[n,k])|
