@@ -71,6 +71,8 @@ def lib():
         L.fp8_scaled_gemm.restype = C.c_int
         L.fp8_scaled_gemm.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                       I64, P, C.c_int, P, C.c_int, I64, U32, P]
+        L.fp8_delayed_scale_update.restype = C.c_int
+        L.fp8_delayed_scale_update.argtypes = [P, I32, P, P, C.c_int, C.c_int, I32, F, I32, P, P, P]
         L.fp8_weight_only_gemm.restype = C.c_int
         L.fp8_weight_only_gemm.argtypes = [P, C.c_int, I64, P, C.c_int, I64, Gran, P, I64, I64, I64, P,
                                            C.c_int, P, C.c_int, I64, P]
@@ -205,6 +207,21 @@ def fp8_scaled_gemm_fp8out(a, fa, ga, scale_a, b, fb, gb, scale_b, yq, fy, scale
                                         flags, _stream(stream)))
 
 
+HIST_MAX, HIST_LATEST = 0, 1
+
+
+def fp8_delayed_scale_update(history, head, amax_new, fmt, fn, margin, eps, pow2, scale_next,
+                             inv_scale_next=None, stream=None):
+    """Delayed-scaling recipe step: push amax_new into the ring, derive the
+    next (s, r) from f * 2^margin (f = window max or latest amax)."""
+    if history.dtype != torch.float32 or history.dim() != 1 or not history.is_contiguous():
+        raise ValueError("history must be a contiguous float32 vector")
+    _check("fp8_delayed_scale_update",
+           lib().fp8_delayed_scale_update(_ptr(history), history.numel(), _ptr(head), _ptr(amax_new), fmt, fn,
+                                          margin, eps, int(pow2), _ptr(scale_next), _ptr(inv_scale_next),
+                                          _stream(stream)))
+
+
 def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, stream=None):
     """y = x (s_w o dec(w))^T + bias: x [M, K] bf16, w [N, K] uint8 codes."""
     M, K, ldx = _mat(x)
@@ -218,7 +235,7 @@ def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, stream=None):
                                       M, N, K, _ptr(bias), bt, _ptr(y), _dtype(y), ldy, _stream(stream)))
 
 
-__all__ = ["fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
+__all__ = ["fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
            "scale_shape"]

@@ -184,8 +184,24 @@ fp8rt_status fp8_amax_history_update(float* history, int32_t len, int32_t* head,
   if (!aligned4(history) || !aligned4(head) || !aligned4(amax_new) || !aligned4(scale_next) ||
       (inv_scale_next && !aligned4(inv_scale_next)))
     return FP8RT_EALIGN;
-  return from_hip(launch_history_update(history, len, head, amax_new, f, eps, pow2_round_up != 0,
+  return from_hip(launch_history_update(history, len, head, amax_new, f, eps, pow2_round_up != 0, 0, 0,
                                         scale_next, inv_scale_next, stream));
+}
+
+fp8rt_status fp8_delayed_scale_update(float* history, int32_t len, int32_t* head, const float* amax_new,
+                                      fp8rt_format f, fp8rt_history_fn fn, int32_t margin, float eps,
+                                      int32_t pow2_round_up, float* scale_next, float* inv_scale_next,
+                                      hipStream_t stream) {
+  if (!history || !head || !amax_new || !scale_next || !valid_fmt(f) || !valid_eps(eps))
+    return FP8RT_EINVAL;
+  if (len < 1 || len > 1024) return FP8RT_EINVAL;
+  if ((fn != FP8RT_HIST_MAX && fn != FP8RT_HIST_LATEST) || margin < 0 || margin > 16) return FP8RT_EINVAL;
+  if (!aligned4(history) || !aligned4(head) || !aligned4(amax_new) || !aligned4(scale_next) ||
+      (inv_scale_next && !aligned4(inv_scale_next)))
+    return FP8RT_EALIGN;
+  return from_hip(launch_history_update(history, len, head, amax_new, f, eps, pow2_round_up != 0,
+                                        fn == FP8RT_HIST_LATEST ? 1 : 0, margin, scale_next, inv_scale_next,
+                                        stream));
 }
 
 namespace {

@@ -75,8 +75,9 @@ hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, float eps
 hipError_t launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
                              int64_t er, int64_t ec, const float* scale, void* y, int yt,
                              int64_t ldy, hipStream_t stream);
+// fn: 0 = window maximum, 1 = latest amax; margin: scale from f * 2^margin.
 hipError_t launch_history_update(float* history, int32_t len, int32_t* head, const float* amax_new,
-                                 int fmt, float eps, int pow2, float* scale_next,
+                                 int fmt, float eps, int pow2, int fn, int margin, float* scale_next,
                                  float* inv_scale_next, hipStream_t stream);
 
 struct GemmArgs {

@@ -964,41 +964,49 @@ hipError_t launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t co
 // maximum (integer max of the binary32 patterns of non-negative entries, NaN
 // kept), and derives the next step's (s, r) on the device.
 
+// Recipe variants (same section: the history function may be the latest
+// value or the window maximum; recipes add a margin): fn 1 takes a_t alone
+// (the ring still advances), and the scale is derived from f * 2^margin
+// (v_ldexp_f32: exact, or Inf -> NaN scale on overflow).
 template <int F>
 __global__ __launch_bounds__(64) void k_history_update(float* history, int32_t len, int32_t* head,
-                                                       const float* amax_new, float eps, int pow2,
-                                                       float* s_next, float* r_next) {
+                                                       const float* amax_new, float eps, int pow2, int fn,
+                                                       int margin, float* s_next, float* r_next) {
   const int lane = threadIdx.x;
   int32_t h = head[0];
   h = ((h % len) + len) % len;
   const float an = amax_new[0];
-  uint32_t m = 0;
-  for (int i = lane; i < len; i += 64) {
-    const float v = (i == h) ? an : history[i];
+  // ordering key: NaN above everything, non-positive values as zero
+  auto key_of = [](float v) {
     const uint32_t b = __float_as_uint(v);
-    const uint32_t key = ((b & kAbsMask) > kInfBits) ? kQNaN : (v > 0.0f ? b : 0u);
-    m = max(m, key);
+    return ((b & kAbsMask) > kInfBits) ? kQNaN : (v > 0.0f ? b : 0u);
+  };
+  uint32_t m = 0;
+  if (fn == 0) {
+    for (int i = lane; i < len; i += 64) m = max(m, key_of((i == h) ? an : history[i]));
+    m = wave_max_u32(m);
+  } else {
+    m = key_of(an);
   }
-  m = wave_max_u32(m);
   if (lane == 0) {
     history[h] = an;
     head[0] = (h + 1) % len;
     float s, r;
-    scale_from_amax(__uint_as_float(m), Fmt<F>::kMax, eps, pow2 != 0, s, r);
+    scale_from_amax(ldexpf(__uint_as_float(m), margin), Fmt<F>::kMax, eps, pow2 != 0, s, r);
     s_next[0] = s;
     if (r_next) r_next[0] = r;
   }
 }
 
 hipError_t launch_history_update(float* history, int32_t len, int32_t* head, const float* amax_new,
-                                 int fmt, float eps, int pow2, float* scale_next,
+                                 int fmt, float eps, int pow2, int fn, int margin, float* scale_next,
                                  float* inv_scale_next, hipStream_t st) {
   if (fmt == FP8RT_E4M3)
     hipLaunchKernelGGL(k_history_update<kE4M3>, dim3(1), dim3(64), 0, st, history, len, head,
-                       amax_new, eps, pow2, scale_next, inv_scale_next);
+                       amax_new, eps, pow2, fn, margin, scale_next, inv_scale_next);
   else
     hipLaunchKernelGGL(k_history_update<kE5M2>, dim3(1), dim3(64), 0, st, history, len, head,
-                       amax_new, eps, pow2, scale_next, inv_scale_next);
+                       amax_new, eps, pow2, fn, margin, scale_next, inv_scale_next);
   return hipGetLastError();
 }
 

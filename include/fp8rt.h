@@ -167,6 +167,28 @@ fp8rt_status fp8_amax_history_update(float* history, int32_t len, int32_t* head,
                                      int32_t pow2_round_up, float* scale_next,
                                      float* inv_scale_next, hipStream_t stream);
 
+/* History function of a delayed-scaling recipe. */
+typedef enum fp8rt_history_fn {
+  FP8RT_HIST_MAX = 0,    /* window maximum over the history ring */
+  FP8RT_HIST_LATEST = 1  /* the newest amax alone */
+} fp8rt_history_fn;
+
+/* Delayed-scaling recipe variants ["FP8 formats and scaling for LLM
+ * inference", section "Delayed scaling": the history function may be the
+ * most recent value or the window maximum; section "How a scale fits a
+ * tensor into E4M3": real recipes add a margin].  As
+ * fp8_amax_history_update (same ring, head, eps and pow2 semantics), with
+ *   f = window maximum (FP8RT_HIST_MAX) or a_t alone (FP8RT_HIST_LATEST;
+ *       a non-positive a_t counts as 0, NaN propagates), and
+ *   the scale derived from f * 2^margin, margin in [0, 16]: s_next grows by
+ *       exactly 2^margin (an overflow to Inf gives NaN s and r).
+ * FP8RT_HIST_MAX with margin 0 is fp8_amax_history_update.  Bad fn or
+ * margin: FP8RT_EINVAL. */
+fp8rt_status fp8_delayed_scale_update(float* history, int32_t len, int32_t* head,
+                                      const float* amax_new, fp8rt_format f, fp8rt_history_fn fn,
+                                      int32_t margin, float eps, int32_t pow2_round_up,
+                                      float* scale_next, float* inv_scale_next, hipStream_t stream);
+
 /* Scaled GEMM on FP8 MFMA [P2 "The full precision contract of one FP8 GEMM":
  * Y ~ s_x s_w (X8 W8), higher-precision accumulation, BF16/FP32 output, bias;
  * P4 GEMM listing: scale_a, scale_b, out_dtype, bias].

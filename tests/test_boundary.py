@@ -207,3 +207,22 @@ def test_weight_only_gemm_validation(rt):
     assert call(sw=FAKE + 2) == rt.EALIGN
     assert call(gw=(1, 64)) == rt.EUNSUPPORTED   # K groups are whole 128-deep steps
     assert call(gw=(1, 192)) == rt.EUNSUPPORTED
+
+
+def test_delayed_scale_update_validation(rt):
+    L = rt.lib()
+
+    def call(**kw):
+        a = dict(h=FAKE, n=16, head=FAKE, a=FAKE, f=rt.E4M3, fn=rt.HIST_MAX, m=0, eps=1e-12, s=FAKE)
+        a.update(kw)
+        return L.fp8_delayed_scale_update(a["h"], a["n"], a["head"], a["a"], a["f"], a["fn"], a["m"], a["eps"], 0,
+                                          a["s"], None, None)
+    assert call(h=None) == rt.EINVAL
+    assert call(s=None) == rt.EINVAL
+    assert call(n=0) == rt.EINVAL
+    assert call(n=1025) == rt.EINVAL
+    assert call(fn=2) == rt.EINVAL
+    assert call(m=-1) == rt.EINVAL
+    assert call(m=17) == rt.EINVAL
+    assert call(eps=float("inf")) == rt.EINVAL
+    assert call(head=FAKE + 2) == rt.EALIGN
