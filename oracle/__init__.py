@@ -74,6 +74,8 @@ def lib():
         L.orc_gemm_points.argtypes = gemm_args + [P]
         L.orc_gemm_points_exact.restype = I
         L.orc_gemm_points_exact.argtypes = gemm_args
+        L.orc_quant_error.restype = I
+        L.orc_quant_error.argtypes = [P, I, I64, I64, I64, P, I, I64, I64, I64, P, P, I64, I64, P]
         L.orc_history_update_recipe.restype = I
         L.orc_history_update_recipe.argtypes = [P, I, P, F, I, I, I, F, I, P, P]
         L.orc_wonly_gemm_points.restype = I
@@ -221,6 +223,26 @@ def history_update(hist: np.ndarray, head: int, amax_new: float, fmt: int, eps: 
     _check(lib().orc_history_update(_ptr(hist), hist.size, C.byref(h), float(amax_new), fmt,
                                     eps, int(pow2), _ptr(s), _ptr(r)), "history_update")
     return h.value, s[0], r[0]
+
+
+def quant_error(w, q, fmt, scale, gran, x=None):
+    """Ledger statistics of a quantized weight (binary64): sum e^2, sum w^2,
+    max |e|, sum d^2, sum y_ref^2, sum y_q^2, sum y_ref y_q (see the C
+    header); x is bf16 bits [M, K] or None."""
+    w = np.ascontiguousarray(w)
+    q = np.ascontiguousarray(q, np.uint8)
+    N, K = w.shape
+    assert q.shape == (N, K)
+    s = np.ascontiguousarray(scale, np.float32)
+    M = 0
+    if x is not None:
+        x = np.ascontiguousarray(x, np.uint16)
+        M = x.shape[0]
+        assert x.shape[1] == K
+    st = np.empty(7, np.float64)
+    _check(lib().orc_quant_error(_ptr(w), _dtype_code(w), N, K, K, _ptr(q), fmt, K, gran[0], gran[1],
+                                 _ptr(s), _ptr(x), M, K, _ptr(st)), "quant_error")
+    return st
 
 
 HIST_MAX, HIST_LATEST = 0, 1

@@ -434,6 +434,59 @@ int orc_wonly_gemm_points(const void* x, int xdtype, int64_t ldx, const uint8_t*
     return 0;
 }
 
+/* Reconstruction error of a quantized weight, for the granularity ledger
+ * ("Quantization W8A16", the granularity comparison: per granularity the
+ * scale count and bytes, the restored weight's mean squared error, and the
+ * layer output's squared error and cosine against the unquantized weight).
+ * The restored weight is the dequantization fl32(s * dec(q)); e = w_hat - w
+ * exactly (binary64).  With inputs x [M x K]: y_ref = x W^T and
+ * y_q = x W_hat^T in binary64, d = y_q - y_ref = x e^T.
+ * stats[0] = sum e^2, [1] = sum w^2, [2] = max |e|, [3] = sum d^2,
+ * [4] = sum y_ref^2, [5] = sum y_q^2, [6] = sum y_ref y_q (3..6 zero when
+ * x is NULL). */
+int orc_quant_error(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw, const uint8_t* q,
+                    int fmt, int64_t ldq, int64_t gr, int64_t gc, const float* scale, const void* x,
+                    int64_t M, int64_t ldx, double* stats) {
+    if (!w || !q || !scale || !stats || N <= 0 || K <= 0 || ldw < K || ldq < K) return 1;
+    if (x && (M <= 0 || ldx < K)) return 1;
+    const int64_t er = eff(N, gr), ec = eff(K, gc);
+    const int64_t nC = orc_ngroups(K, gc);
+    double* e = (double*)malloc(sizeof(double) * (size_t)K);
+    double* wv = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!e || !wv) { free(e); free(wv); return 1; }
+    for (int i = 0; i < 7; ++i) stats[i] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const double sv = (double)scale[(n / er) * nC + (k / ec)];
+            const float wh = (float)(sv * orc_decode(q[n * ldq + k], fmt));
+            wv[k] = (double)orc_load(w, wdtype, n * ldw + k);
+            e[k] = (double)wh - wv[k];
+            stats[0] += e[k] * e[k];
+            stats[1] += wv[k] * wv[k];
+            const double ae = fabs(e[k]);
+            if (isnan(ae)) stats[2] = NAN;                 /* NaN propagates */
+            else if (ae > stats[2]) stats[2] = ae;         /* false once stats[2] is NaN */
+        }
+        if (!x) continue;
+        for (int64_t m = 0; m < M; ++m) {
+            double d = 0.0, yr = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double xv = (double)orc_load(x, ORC_BF16, m * ldx + k);
+                d += xv * e[k];
+                yr += xv * wv[k];
+            }
+            const double yq = yr + d;
+            stats[3] += d * d;
+            stats[4] += yr * yr;
+            stats[5] += yq * yq;
+            stats[6] += yr * yq;
+        }
+    }
+    free(e);
+    free(wv);
+    return 0;
+}
+
 /* Integer value of a code in units of the format's smallest subnormal
  * (2^-9 for E4M3, 2^-16 for E5M2); returns 0 and sets *bad for NaN/Inf. */
 static int64_t code_units(unsigned code, int fmt, int* bad) {

@@ -17,6 +17,8 @@
  *      "The full precision contract of one FP8 GEMM" (Y ~ s_x s_w X8 W8),
  *      "What numerical validation looks at" (saturation / underflow rates),
  *      "Weight-only FP8 and W8A8 FP8" (FP8 weights with BF16 activations).
+ *  - "Quantization W8A16" (datawhalechina llm-algo-leetcode): the granularity
+ *      comparison (scale count and bytes against reconstruction error).
  *  - "FP8 production quantization guide" (m.xxqk.cn): the dynamic per-tensor
  *      quantize listing (amax clamp, scale, inverse scale, clamp, cast).
  *  - "FP8 inference: E4M3/E5M2 and the NVIDIA FP8 ecosystem" (plumephp.com):
@@ -129,6 +131,16 @@ int orc_wonly_gemm_points(const void* x, int xdtype, int64_t ldx, const uint8_t*
                           int64_t N, int64_t K, const void* bias, int bias_dtype,
                           const int64_t* m, const int64_t* n, int64_t npts, double* y,
                           double* S);
+
+/* Reconstruction error of a quantized weight (granularity ledger):
+ * w [N x K] fp32 / bf16 (ldw), codes q (ldq) with scales [ceil(N/gr)][ceil(K/gc)],
+ * optional bf16 inputs x [M x K] (ldx).  w_hat = fl32(s dec(q)), e = w_hat - w.
+ * stats[7] = {sum e^2, sum w^2, max |e|, sum d^2, sum y_ref^2, sum y_q^2,
+ * sum y_ref y_q} with y_ref = x W^T, y_q = x W_hat^T, d = y_q - y_ref, all in
+ * binary64 (3..6 zero without x). */
+int orc_quant_error(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw, const uint8_t* q,
+                    int fmt, int64_t ldq, int64_t gr, int64_t gc, const float* scale, const void* x,
+                    int64_t M, int64_t ldx, double* stats);
 
 /* Exact inner sums: for point i and every maximal K-run on which both scales
  * are constant, the sum of dec*dec products as an exact integer multiple of
