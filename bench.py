@@ -325,7 +325,15 @@ def extra_components(torch, rt, wl):
     e = hbm_entry(time_op(torch, wo, scrub=scrub), wo_bytes, "k_gemm_wonly")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_weight_only_gemm_bf16_bias"] = e
-    del A, W, bias, Aq, Wq, y, yw, d
+    # granularity ledger: error statistics of the per-channel weight codes
+    # against the bf16 weight, with the 16 activation rows
+    stats = torch.empty(7, dtype=torch.float64, device=dev)
+    le = lambda: rt.fp8_quant_error(W, Wq, rt.E4M3, (1, 0), sw, stats, x=A)
+    le()
+    e = hbm_entry(time_op(torch, le, scrub=scrub), N * K * 3 + N * 4 + M * K * 2, "k_quant_error + k_ledger_finish")
+    e["TFLOP_s"] = 4.0 * M * N * K / (e["us"] * 1e-6) / 1e12  # x.e and x.w per (m, n, k)
+    comp["ledger_quant_error_w_per_channel_x16"] = e
+    del A, W, bias, Aq, Wq, y, yw, d, stats
 
     # delayed-scaling backward GEMM, one step: G 8192x8192 E5M2 with the scale of
     # the history window, W 8192x8192 E4M3 per tensor, fp32 out

@@ -40,6 +40,18 @@ class Gran(C.Structure):
     _fields_ = [("rows", C.c_int32), ("cols", C.c_int32)]
 
 
+class LedgerSpec(C.Structure):
+    _fields_ = [("gran", Gran), ("pow2_round_up", C.c_int32)]
+
+
+class LedgerRow(C.Structure):
+    _fields_ = [("gran", Gran), ("pow2_round_up", C.c_int32), ("qparam_count", C.c_int64),
+                ("qparam_bytes", C.c_int64), ("quantized_weight_bytes", C.c_int64),
+                ("total_state_bytes", C.c_int64), ("weight_mse", C.c_double),
+                ("weight_max_abs_err", C.c_double), ("output_mse", C.c_double),
+                ("output_cosine", C.c_double), ("saturated", C.c_uint64), ("underflowed", C.c_uint64)]
+
+
 _lib = None
 
 
@@ -71,6 +83,11 @@ def lib():
         L.fp8_scaled_gemm.restype = C.c_int
         L.fp8_scaled_gemm.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                       I64, P, C.c_int, P, C.c_int, I64, U32, P]
+        L.fp8_quant_error.restype = C.c_int
+        L.fp8_quant_error.argtypes = [P, C.c_int, I64, I64, I64, P, C.c_int, I64, Gran, P, P, I64, I64, P, P]
+        L.fp8_granularity_ledger.restype = C.c_int
+        L.fp8_granularity_ledger.argtypes = [P, C.c_int, I64, I64, I64, P, I64, I64, C.c_int, F,
+                                             C.POINTER(LedgerSpec), I32, C.POINTER(LedgerRow), P]
         L.fp8_delayed_scale_update.restype = C.c_int
         L.fp8_delayed_scale_update.argtypes = [P, I32, P, P, C.c_int, C.c_int, I32, F, I32, P, P, P]
         L.fp8_weight_only_gemm.restype = C.c_int
@@ -210,6 +227,47 @@ def fp8_scaled_gemm_fp8out(a, fa, ga, scale_a, b, fb, gb, scale_b, yq, fy, scale
 HIST_MAX, HIST_LATEST = 0, 1
 
 
+def fp8_quant_error(w, q, fmt, gran, scale, stats, x=None, stream=None):
+    """stats (float64[7] on the device) <- the quantization error sums of w
+    restored from (q, scale); x: optional bf16 inputs [M, K]."""
+    N, K, ldw = _mat(w)
+    Nq, Kq, ldq = _mat(q)
+    if (Nq, Kq) != (N, K) or q.dtype != torch.uint8:
+        raise ValueError("q must be uint8 [N x K]")
+    if stats.dtype != torch.float64 or stats.numel() < 7:
+        raise ValueError("stats must be float64 with 7 entries")
+    M, ldx = 0, 0
+    if x is not None:
+        M, Kx, ldx = _mat(x)
+        if Kx != K:
+            raise ValueError("x and w disagree on K")
+    _check("fp8_quant_error",
+           lib().fp8_quant_error(_ptr(w), _dtype(w), N, K, ldw, _ptr(q), fmt, ldq, Gran(*gran), _ptr(scale),
+                                 _ptr(x), M, ldx, _ptr(stats), _stream(stream)))
+
+
+def fp8_granularity_ledger(w, fmt, specs, x=None, eps=1e-12, stream=None):
+    """Quantizes w at each (gran, pow2) spec and returns the ledger rows as
+    dicts (scale count and bytes, weight / output error, counters)."""
+    N, K, ldw = _mat(w)
+    M, ldx = 0, 0
+    if x is not None:
+        M, Kx, ldx = _mat(x)
+        if Kx != K:
+            raise ValueError("x and w disagree on K")
+    sp = (LedgerSpec * len(specs))(*[LedgerSpec(Gran(*g), int(p)) for g, p in specs])
+    rows = (LedgerRow * len(specs))()
+    _check("fp8_granularity_ledger",
+           lib().fp8_granularity_ledger(_ptr(w), _dtype(w), N, K, ldw, _ptr(x), M, ldx, fmt, eps, sp, len(specs),
+                                        rows, _stream(stream)))
+    out = []
+    for r in rows:
+        d = {k: getattr(r, k) for k, _ in LedgerRow._fields_ if k != "gran"}
+        d["gran"] = (r.gran.rows, r.gran.cols)
+        out.append(d)
+    return out
+
+
 def fp8_delayed_scale_update(history, head, amax_new, fmt, fn, margin, eps, pow2, scale_next,
                              inv_scale_next=None, stream=None):
     """Delayed-scaling recipe step: push amax_new into the ring, derive the
@@ -235,7 +293,7 @@ def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, stream=None):
                                       M, N, K, _ptr(bias), bt, _ptr(y), _dtype(y), ldy, _stream(stream)))
 
 
-__all__ = ["fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
+__all__ = ["fp8_quant_error", "fp8_granularity_ledger", "LedgerSpec", "LedgerRow", "fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
            "scale_shape"]

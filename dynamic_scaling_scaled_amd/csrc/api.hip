@@ -4,6 +4,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cmath>
+#include <limits>
+
 #include "fp8rt.h"
 #include "internal.h"
 
@@ -341,6 +345,115 @@ fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, co
   g.yt = yt;
   g.ldy = ldy;
   return from_hip(launch_gemm_wonly(g, stream));
+}
+
+namespace {
+
+// Validation shared by the two ledger entry points; fills g (q / scale /
+// stats excepted).
+fp8rt_status quant_error_setup(const void* w, fp8rt_dtype wt, int64_t N, int64_t K, int64_t ldw, const void* x,
+                               int64_t M, int64_t ldx, fp8rt_format f, QuantErrorArgs& g) {
+  if (!w || !valid_dtype(wt) || !valid_fmt(f)) return FP8RT_EINVAL;
+  if (N <= 0 || K <= 0 || ldw < K || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
+  if (x && (M <= 0 || ldx < K)) return FP8RT_EINVAL;
+  if (K % 16 != 0 || ldw % 8 != 0 || (x && ldx % 8 != 0)) return FP8RT_EALIGN;
+  if (!aligned16(w) || (x && !aligned16(x))) return FP8RT_EALIGN;
+  g.w = w;
+  g.wt = wt;
+  g.ldw = ldw;
+  g.f = f;
+  g.N = N;
+  g.K = K;
+  g.x = static_cast<const uint16_t*>(x);
+  g.M = x ? M : 0;
+  g.ldx = ldx;
+  return FP8RT_OK;
+}
+
+}  // namespace
+
+fp8rt_status fp8_quant_error(const void* w, fp8rt_dtype wt, int64_t N, int64_t K, int64_t ldw, const uint8_t* q,
+                             fp8rt_format f, int64_t ldq, fp8rt_gran g, const float* scale, const void* x,
+                             int64_t M, int64_t ldx, double* stats, hipStream_t stream) {
+  QuantErrorArgs a;
+  fp8rt_status st = quant_error_setup(w, wt, N, K, ldw, x, M, ldx, f, a);
+  if (st != FP8RT_OK) return st;
+  if (!q || !scale || !stats || ldq < K || g.rows < 0 || g.cols < 0) return FP8RT_EINVAL;
+  if (ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(q) & 7u) || !aligned4(scale) ||
+      (reinterpret_cast<uintptr_t>(stats) & 7u))
+    return FP8RT_EALIGN;
+  a.q = q;
+  a.ldq = ldq;
+  a.scale = scale;
+  a.er = group_extent(N, g.rows);
+  a.ec = group_extent(K, g.cols);
+  if (a.ec < K && a.ec % 8 != 0) return FP8RT_EUNSUPPORTED;  // a lane's 8 elements share one scale
+  a.stats = stats;
+  void* part = nullptr;
+  if (get_scratch(stream, quant_error_partials_bytes(N), &part) != hipSuccess) return FP8RT_EHIP;
+  return from_hip(launch_quant_error(a, part, stream));
+}
+
+fp8rt_status fp8_granularity_ledger(const void* w, fp8rt_dtype wt, int64_t N, int64_t K, int64_t ldw,
+                                    const void* x, int64_t M, int64_t ldx, fp8rt_format f, float eps,
+                                    const fp8rt_ledger_spec* specs, int32_t n_specs, fp8rt_ledger_row* rows,
+                                    hipStream_t stream) {
+  QuantErrorArgs a;
+  fp8rt_status st = quant_error_setup(w, wt, N, K, ldw, x, M, ldx, f, a);
+  if (st != FP8RT_OK) return st;
+  if (!specs || !rows || n_specs < 1 || n_specs > 64 || !valid_eps(eps)) return FP8RT_EINVAL;
+  // one scratch buffer: codes [N x K], the largest scale array, 7 stats, 2 counters, partials
+  int64_t max_scales = 1;
+  for (int i = 0; i < n_specs; ++i) {
+    if (specs[i].gran.rows < 0 || specs[i].gran.cols < 0) return FP8RT_EINVAL;
+    max_scales = std::max(max_scales, ceil_div(N, group_extent(N, specs[i].gran.rows)) *
+                                          ceil_div(K, group_extent(K, specs[i].gran.cols)));
+  }
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  const int64_t off_s = up(N * K), off_st = off_s + up(max_scales * 4), off_c = off_st + 256,
+                off_p = off_c + 256;
+  void* scr = nullptr;
+  if (get_scratch(stream, static_cast<size_t>(off_p) + quant_error_partials_bytes(N), &scr) != hipSuccess)
+    return FP8RT_EHIP;
+  uint8_t* base = static_cast<uint8_t*>(scr);
+  uint8_t* codes = base;
+  float* scales = reinterpret_cast<float*>(base + off_s);
+  double* stats = reinterpret_cast<double*>(base + off_st);
+  uint64_t* counts = reinterpret_cast<uint64_t*>(base + off_c);
+  for (int i = 0; i < n_specs; ++i) {
+    const fp8rt_gran gr = specs[i].gran;
+    st = fp8_quantize(w, wt, N, K, ldw, gr, f, FP8RT_DYNAMIC, eps, specs[i].pow2_round_up, scales, nullptr,
+                      codes, K, nullptr, counts, stream);
+    if (st != FP8RT_OK) return st;
+    a.q = codes;
+    a.ldq = K;
+    a.scale = scales;
+    a.er = group_extent(N, gr.rows);
+    a.ec = group_extent(K, gr.cols);
+    a.stats = stats;
+    if (launch_quant_error(a, base + off_p, stream) != hipSuccess) return FP8RT_EHIP;
+    double hs[7];
+    uint64_t hc[2];
+    if (hipMemcpyAsync(hs, stats, sizeof(hs), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(hc, counts, sizeof(hc), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return FP8RT_EHIP;
+    fp8rt_ledger_row& r = rows[i];
+    r.gran = gr;
+    r.pow2_round_up = specs[i].pow2_round_up;
+    r.qparam_count = ceil_div(N, a.er) * ceil_div(K, a.ec);
+    r.qparam_bytes = r.qparam_count * static_cast<int64_t>(sizeof(float));
+    r.quantized_weight_bytes = N * K;
+    r.total_state_bytes = r.quantized_weight_bytes + r.qparam_bytes;
+    r.weight_mse = hs[0] / static_cast<double>(N * K);
+    r.weight_max_abs_err = hs[2];
+    const double nan = std::numeric_limits<double>::quiet_NaN();
+    r.output_mse = x ? hs[3] / (static_cast<double>(M) * static_cast<double>(N)) : nan;
+    r.output_cosine = x ? hs[6] / std::max(std::sqrt(hs[4]) * std::sqrt(hs[5]), 1e-8) : nan;
+    r.saturated = hc[0];
+    r.underflowed = hc[1];
+  }
+  return FP8RT_OK;
 }
 
 }  // extern "C"

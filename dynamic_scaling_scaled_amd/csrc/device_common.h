@@ -168,6 +168,20 @@ __device__ __forceinline__ uint32_t cvt4_nan(float a, float b, float c, float d)
   return (w & ~m) | (0x7F7F7F7Fu & m);
 }
 
+// Exact decode of 4 FP8 codes (one dword, byte i = element i) to binary32.
+template <int F>
+__device__ __forceinline__ void decode4(uint32_t w, float* out) {
+  if constexpr (F == kE4M3) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+  } else {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Reductions (wave64).
 

@@ -148,6 +148,26 @@ struct WonlyArgs {
   int64_t ldy = 0;
 };
 hipError_t launch_gemm_wonly(const WonlyArgs& g, hipStream_t stream);
+
+// Quantization error statistics (ledger.hip): w [N x K] (fp32 / bf16, ldw),
+// codes q (ldq) with scales [ceil(N/er)][ceil(K/ec)], optional bf16 x [M x K]
+// (ldx); stats: 7 device doubles.  partials: quant_error_partials_bytes(N).
+struct QuantErrorArgs {
+  const void* w = nullptr;
+  int wt = 0;
+  int64_t ldw = 0;
+  const uint8_t* q = nullptr;
+  int f = 0;
+  int64_t ldq = 0;
+  int64_t N = 0, K = 0;
+  const float* scale = nullptr;
+  int64_t er = 1, ec = 1;
+  const uint16_t* x = nullptr;
+  int64_t M = 0, ldx = 0;
+  double* stats = nullptr;
+};
+size_t quant_error_partials_bytes(int64_t N);
+hipError_t launch_quant_error(const QuantErrorArgs& g, void* partials, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace fp8rt

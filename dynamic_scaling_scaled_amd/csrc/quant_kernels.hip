@@ -887,19 +887,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int F>
-__device__ __forceinline__ void decode4(uint32_t w, float* out) {
-  if constexpr (F == kE4M3) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
-  } else {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
-    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
-  }
-}
-
 template <int F, bool BF16OUT>
 __global__ __launch_bounds__(kBlock) void k_dequantize(const uint8_t* __restrict__ q, int64_t rows,
                                                        int64_t cols, int64_t ldq, int64_t er,

@@ -258,6 +258,66 @@ fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, co
                                   fp8rt_dtype bias_t, void* y, fp8rt_dtype yt, int64_t ldy,
                                   hipStream_t stream);
 
+/* Quantization error of a weight, for the granularity ledger ["Quantization
+ * W8A16" (datawhalechina llm-algo-leetcode): the granularity comparison
+ * reports each granularity's restored-weight mean squared error and the layer
+ * output's error against the unquantized weight].
+ *   w : [N x K] fp32 / bf16 (ldw elements, a multiple of 8), the weight;
+ *   q : [N x K] codes (ldq bytes, a multiple of 8) with scales [ceil(N/g.rows)]
+ *       [ceil(K/g.cols)] (group widths a multiple of 8 or the whole row);
+ *   x : nullable bf16 inputs [M x K] (ldx elements, a multiple of 8);
+ *   stats : device double[7], OVERWRITTEN:
+ *     {sum e^2, sum w^2, max |e|, sum d^2, sum y_ref^2, sum y_q^2, sum y_ref y_q}
+ *     with w_hat = fl32(s dec(q)) (the dequantization), e = w_hat - w (exact),
+ *     y_ref = x W^T, y_q = x W_hat^T, d = y_q - y_ref (FP32 products over
+ *     8-element runs, combined in binary64; 3..6 are 0 when x is NULL).
+ *     NaN propagates (max |e| is NaN when any e is).
+ * K a multiple of 16; w and x 16-byte aligned, q and stats 8-byte aligned.
+ * Scratch: the per-stream GEMM scratch buffer holds per-block partials. */
+fp8rt_status fp8_quant_error(const void* w, fp8rt_dtype wt, int64_t N, int64_t K, int64_t ldw,
+                             const uint8_t* q, fp8rt_format f, int64_t ldq, fp8rt_gran g,
+                             const float* scale, const void* x, int64_t M, int64_t ldx,
+                             double* stats, hipStream_t stream);
+
+/* One granularity of the ledger: the scale groups and the power-of-two
+ * round-up of the scales (MX-style 1x32 blocks use {1, 32} with 1). */
+typedef struct fp8rt_ledger_spec {
+  fp8rt_gran gran;
+  int32_t pow2_round_up;
+} fp8rt_ledger_spec;
+
+/* One row of the ledger (host memory). */
+typedef struct fp8rt_ledger_row {
+  fp8rt_gran gran;
+  int32_t pow2_round_up;
+  int64_t qparam_count;            /* number of fp32 scales */
+  int64_t qparam_bytes;            /* 4 * qparam_count */
+  int64_t quantized_weight_bytes;  /* N * K code bytes */
+  int64_t total_state_bytes;       /* codes + scales */
+  double weight_mse;               /* sum e^2 / (N K) */
+  double weight_max_abs_err;       /* max |e| */
+  double output_mse;               /* sum d^2 / (M N); NaN without inputs */
+  double output_cosine;            /* <y_ref, y_q> / max(|y_ref| |y_q|, 1e-8); NaN without inputs */
+  uint64_t saturated, underflowed; /* the quantization's counters */
+} fp8rt_ledger_row;
+
+/* The FP8 granularity ledger ["Quantization W8A16", the granularity
+ * comparison: for one weight and one set of inputs, each granularity's scale
+ * count and bytes against the restored weight's and the output's error;
+ * "FP8 formats and scaling for LLM inference", section "Per-channel and block
+ * scaling": finer groups buy precision with scale metadata].  For each of
+ * n_specs (1..64) specs: fp8_quantize(w, spec.gran, f, DYNAMIC, eps,
+ * spec.pow2_round_up) into library scratch, then fp8_quant_error, and
+ * rows[i] is filled on the host.  Synchronous: the stream is synchronized
+ * once per spec.  Arguments as fp8_quant_error; a spec that fp8_quantize
+ * rejects returns that status (rows before it are filled).  Scratch: the
+ * per-stream GEMM scratch buffer holds the codes (N K bytes), the scales and
+ * the partials. */
+fp8rt_status fp8_granularity_ledger(const void* w, fp8rt_dtype wt, int64_t N, int64_t K, int64_t ldw,
+                                    const void* x, int64_t M, int64_t ldx, fp8rt_format f, float eps,
+                                    const fp8rt_ledger_spec* specs, int32_t n_specs,
+                                    fp8rt_ledger_row* rows, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp8rt_status_string(fp8rt_status s);
 

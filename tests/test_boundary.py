@@ -226,3 +226,44 @@ def test_delayed_scale_update_validation(rt):
     assert call(m=17) == rt.EINVAL
     assert call(eps=float("inf")) == rt.EINVAL
     assert call(head=FAKE + 2) == rt.EALIGN
+
+
+def test_quant_error_and_ledger_validation(rt):
+    L = rt.lib()
+    G = rt.Gran
+
+    def qe(**kw):
+        a = dict(w=FAKE, wt=rt.BF16, N=32, K=64, ldw=64, q=FAKE, f=rt.E4M3, ldq=64, g=(1, 0), s=FAKE, x=None, M=0,
+                 ldx=0, st=FAKE)
+        a.update(kw)
+        return L.fp8_quant_error(a["w"], a["wt"], a["N"], a["K"], a["ldw"], a["q"], a["f"], a["ldq"], G(*a["g"]),
+                                 a["s"], a["x"], a["M"], a["ldx"], a["st"], None)
+    assert qe(w=None) == rt.EINVAL
+    assert qe(q=None) == rt.EINVAL
+    assert qe(st=None) == rt.EINVAL
+    assert qe(N=0) == rt.EINVAL
+    assert qe(ldq=32) == rt.EINVAL
+    assert qe(x=FAKE, M=0, ldx=64) == rt.EINVAL
+    assert qe(x=FAKE, M=4, ldx=32) == rt.EINVAL
+    assert qe(K=40, ldw=40, ldq=40) == rt.EALIGN
+    assert qe(ldw=68) == rt.EALIGN
+    assert qe(q=FAKE + 4) == rt.EALIGN
+    assert qe(st=FAKE + 4) == rt.EALIGN
+    assert qe(g=(1, 12)) == rt.EUNSUPPORTED
+
+    spec = (rt.LedgerSpec * 1)(rt.LedgerSpec(G(1, 0), 0))
+    rows = (rt.LedgerRow * 1)()
+
+    def led(**kw):
+        a = dict(w=FAKE, N=32, K=64, ldw=64, specs=spec, n=1, rows=rows, eps=1e-12)
+        a.update(kw)
+        return L.fp8_granularity_ledger(a["w"], rt.BF16, a["N"], a["K"], a["ldw"], None, 0, 0, rt.E4M3, a["eps"],
+                                        a["specs"], a["n"], a["rows"], None)
+    assert led(w=None) == rt.EINVAL
+    assert led(n=0) == rt.EINVAL
+    assert led(n=65) == rt.EINVAL
+    assert led(specs=None) == rt.EINVAL
+    assert led(rows=None) == rt.EINVAL
+    assert led(eps=float("nan")) == rt.EINVAL
+    assert led(K=40, ldw=40) == rt.EALIGN
+    assert C.sizeof(rt.LedgerRow) == 96 and C.sizeof(rt.LedgerSpec) == 12
