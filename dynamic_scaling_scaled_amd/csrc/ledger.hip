@@ -18,13 +18,15 @@
 // 8-element runs and combined in binary64; cosine = <y_ref, y_q> /
 // max(|y_ref| |y_q|, 1e-8).
 //
-// Design for MI355X: one wave per weight row (grid-stride), lane l taking 8
-// consecutive elements of every 512-wide K chunk, so W, its codes and each
-// activation row are read with 16-, 8- and 16-byte loads.  The weight sums
-// are binary64 (e is exact there); each output dot product keeps one FP32
-// partial per lane per activation row (16 rows per pass), reduced across the
-// wave in a fixed butterfly.  Per-block partials go to a finisher that adds
-// them in a fixed order: the result does not depend on scheduling.
+// Design for MI355X: a wave takes 4 weight rows (grid-stride), lane l taking
+// 8 consecutive elements of every 512-wide K chunk, so W, its codes and each
+// activation row are read with 16-, 8- and 16-byte loads, and one activation
+// load serves the 4 rows (the activations are re-read from L2 once per 4
+// weight rows).  The weight sums are binary64 (e is exact there); each output
+// dot product keeps one FP32 partial per lane (8 activation rows per pass),
+// reduced across the wave in a fixed butterfly.  Per-block partials go to a
+// finisher that adds them in a fixed order: the result does not depend on
+// scheduling.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -41,7 +43,8 @@ namespace {
 
 constexpr int kLgWaves = 4;
 constexpr int kLgThreads = kLgWaves * 64;
-constexpr int kLgM = 16;       // activation rows per pass
+constexpr int kLgM = 8;        // activation rows per pass
+constexpr int kLgR = 4;        // weight rows per wave
 constexpr int kLgMaxBlocks = 4096;
 
 // {sum e^2, sum w^2, max |e|, sum d^2, sum y_ref^2, sum y_q^2, sum y_ref y_q, any NaN e}
@@ -81,35 +84,51 @@ __global__ __launch_bounds__(kLgThreads) void k_quant_error(const WT* __restrict
   uint32_t nan = 0;
   const int64_t nchunks = (K + 511) / 512;
   const int npass = X ? static_cast<int>((M + kLgM - 1) / kLgM) : 1;
-  for (int64_t n = static_cast<int64_t>(blockIdx.x) * kLgWaves + wave; n < N; n += nwaves) {
-    const WT* wrow = W + n * ldw;
-    const uint8_t* qrow = Q + n * ldq;
-    const float* srow = S + (n / er) * nc;
-    for (int p = 0; p < npass; ++p) {
-      float ad[kLgM], ay[kLgM];
+  // kLgR weight rows per wave: each activation octet loaded serves all of them
+  for (int64_t n0 = (static_cast<int64_t>(blockIdx.x) * kLgWaves + wave) * kLgR; n0 < N; n0 += nwaves * kLgR) {
+    const WT* wrow[kLgR];
+    const uint8_t* qrow[kLgR];
+    const float* srow[kLgR];
+    bool live[kLgR];
 #pragma unroll
-      for (int mm = 0; mm < kLgM; ++mm) ad[mm] = ay[mm] = 0.0f;
+    for (int i = 0; i < kLgR; ++i) {
+      live[i] = n0 + i < N;
+      const int64_t n = live[i] ? n0 + i : N - 1;  // clamped: loads stay in bounds, results unused
+      wrow[i] = W + n * ldw;
+      qrow[i] = Q + n * ldq;
+      srow[i] = S + (n / er) * nc;
+    }
+    for (int p = 0; p < npass; ++p) {
+      float ad[kLgR][kLgM], ay[kLgR][kLgM];
+#pragma unroll
+      for (int i = 0; i < kLgR; ++i)
+#pragma unroll
+        for (int mm = 0; mm < kLgM; ++mm) ad[i][mm] = ay[i][mm] = 0.0f;
       for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t k0 = c * 512 + 8 * lane;
         if (k0 >= K) continue;  // K is a multiple of 8: a started octet is whole
-        Octet<WT> wo;
-        wo.load(wrow + k0);
-        const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow + k0);
-        const float sv = srow[k0 / ec];
-        float dq[8], e[8], wv[8];
-        decode4<F>(qv[0], dq);
-        decode4<F>(qv[1], dq + 4);
+        float e[kLgR][8], wv[kLgR][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float wh = sv * dq[i];  // the dequantization fl32(s dec(q))
-          wv[i] = wo.get(i);
-          e[i] = wh - wv[i];
-          if (p == 0) {
-            const double ed = static_cast<double>(wh) - static_cast<double>(wv[i]);  // exact
-            se += ed * ed;
-            sw += static_cast<double>(wv[i]) * static_cast<double>(wv[i]);
-            nan |= (ed != ed) ? 1u : 0u;
-            emax = fmax(emax, fabs(ed));
+        for (int i = 0; i < kLgR; ++i) {
+          Octet<WT> wo;
+          wo.load(wrow[i] + k0);
+          const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow[i] + k0);
+          const float sv = srow[i][k0 / ec];
+          float dq[8];
+          decode4<F>(qv[0], dq);
+          decode4<F>(qv[1], dq + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float wh = sv * dq[j];  // the dequantization fl32(s dec(q))
+            wv[i][j] = wo.get(j);
+            e[i][j] = wh - wv[i][j];
+            if (p == 0 && live[i]) {
+              const double ed = static_cast<double>(wh) - static_cast<double>(wv[i][j]);  // exact
+              se += ed * ed;
+              sw += static_cast<double>(wv[i][j]) * static_cast<double>(wv[i][j]);
+              nan |= (ed != ed) ? 1u : 0u;
+              emax = fmax(emax, fabs(ed));
+            }
           }
         }
         if (X) {
@@ -119,32 +138,37 @@ __global__ __launch_bounds__(kLgThreads) void k_quant_error(const WT* __restrict
             if (m >= M) break;
             Octet<uint16_t> xo;
             xo.load(X + m * ldx + k0);
-            float pd = 0.0f, py = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              pd += xo.get(i) * e[i];
-              py += xo.get(i) * wv[i];
+            for (int i = 0; i < kLgR; ++i) {
+              float pd = 0.0f, py = 0.0f;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                pd += xo.get(j) * e[i][j];
+                py += xo.get(j) * wv[i][j];
+              }
+              ad[i][mm] += pd;
+              ay[i][mm] += py;
             }
-            ad[mm] += pd;
-            ay[mm] += py;
           }
         }
       }
       if (X) {
 #pragma unroll
-        for (int mm = 0; mm < kLgM; ++mm) {
-          const int64_t m = static_cast<int64_t>(p) * kLgM + mm;
-          if (m >= M) break;
-          const double dd = static_cast<double>(wave_sum_f32(ad[mm]));
-          const double yr = static_cast<double>(wave_sum_f32(ay[mm]));
-          if (lane == 0) {
-            const double yq = yr + dd;
-            sd += dd * dd;
-            syr += yr * yr;
-            syq += yq * yq;
-            syrq += yr * yq;
+        for (int i = 0; i < kLgR; ++i)
+#pragma unroll
+          for (int mm = 0; mm < kLgM; ++mm) {
+            const int64_t m = static_cast<int64_t>(p) * kLgM + mm;
+            if (m >= M) break;
+            const double dd = static_cast<double>(wave_sum_f32(ad[i][mm]));
+            const double yr = static_cast<double>(wave_sum_f32(ay[i][mm]));
+            if (lane == 0 && live[i]) {
+              const double yq = yr + dd;
+              sd += dd * dd;
+              syr += yr * yr;
+              syq += yq * yq;
+              syrq += yr * yq;
+            }
           }
-        }
       }
     }
   }
@@ -199,12 +223,13 @@ __global__ __launch_bounds__(256) void k_ledger_finish(const LedgerPartial* __re
 }  // namespace
 
 size_t quant_error_partials_bytes(int64_t N) {
-  const int64_t nb = std::min<int64_t>((N + kLgWaves - 1) / kLgWaves, kLgMaxBlocks);
+  const int64_t nb = std::min<int64_t>((N + kLgWaves * kLgR - 1) / (kLgWaves * kLgR), kLgMaxBlocks);
   return static_cast<size_t>(nb) * sizeof(LedgerPartial);
 }
 
 hipError_t launch_quant_error(const QuantErrorArgs& g, void* partials, hipStream_t st) {
-  const int nb = static_cast<int>(std::min<int64_t>((g.N + kLgWaves - 1) / kLgWaves, kLgMaxBlocks));
+  const int nb = static_cast<int>(
+      std::min<int64_t>((g.N + kLgWaves * kLgR - 1) / (kLgWaves * kLgR), kLgMaxBlocks));
   LedgerPartial* part = static_cast<LedgerPartial*>(partials);
   const int64_t nc = (g.K + g.ec - 1) / g.ec;
 #define FP8RT_QE(WT, F)                                                                                      \
