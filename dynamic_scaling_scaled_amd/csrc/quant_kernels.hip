@@ -147,6 +147,19 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
     float* s_out, float* r_out, float* amax_out, BlockPartial* __restrict__ part2) {
   constexpr int U = oct_unroll<T>();
   __shared__ uint32_t sh[kWaves];
+  const int64_t nseg = rows * segs_per_row;
+  Octet<T> v[U];
+  auto load_seg = [&](int64_t sg) {
+    const int64_t rr = sg / segs_per_row;
+    const int64_t sr = sg - rr * segs_per_row;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = (sr * U + u) * kBlock + threadIdx.x;
+      v[u].load_nt(x + rr * ldx + min(o, opr - 1) * 8);  // clamped: every load stays in flight
+    }
+  };
+  // the first segment's loads fly while the scale is derived from the partials
+  if (blockIdx.x < nseg) load_seg(blockIdx.x);
   float r;
   if constexpr (!GIVEN) {
     uint32_t m = 0;
@@ -173,18 +186,11 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
   const bool r_bad = !(fabsf(r) <= FLT_MAX);
   uint32_t mb = 0;
   uint32_t sat_l = 0, under_l = 0;
-  const int64_t nseg = rows * segs_per_row;
   for (int64_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
     const int64_t rr = sg / segs_per_row;
     const int64_t s = sg - rr * segs_per_row;
-    const T* xr = x + rr * ldx;
     uint8_t* qr = q + rr * ldq;
-    Octet<T> v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t o = (s * U + u) * kBlock + threadIdx.x;
-      v[u].load_nt(xr + min(o, opr - 1) * 8);  // clamped: every load stays in flight
-    }
+    if (sg != blockIdx.x) load_seg(sg);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (s * U + u) * kBlock + threadIdx.x;
