@@ -1,8 +1,10 @@
 """Parity of the HIP quantization-error statistics (fp8_quant_error) and the
 granularity ledger (fp8_granularity_ledger) with the CPU oracle.
 
-The weight sums (sum e^2, sum w^2) are binary64 sums of exact terms: equal to
-the oracle's within 1e-12 relative; max |e| is bit-exact.  The output sums
+The weight sums (sum e^2, sum w^2) are binary64 sums of N K nonnegative
+terms, added in different orders on the two sides: each within (n - 1) 2^-53
+of the exact sum, so they agree within 2 N K 2^-53 relative; max |e| is
+bit-exact.  The output sums
 use FP32 dot products (8-element runs, a per-lane chain over the K chunks, a
 64-lane butterfly), so each d and y_ref is within
 gamma * sum_k |x e| (resp. |x w|) of the exact value, gamma = (chunks + 16)
@@ -65,6 +67,11 @@ def bounds(orc, w, q, s, fmt, gran, x):
     return np.array(tol)
 
 
+def sum_rtol(N, K):
+    """Two binary64 sums of N K nonnegative terms in different orders."""
+    return 2.0 * N * K * 2.0 ** -53
+
+
 def run_quant_error(rt, w, q, s, fmt, gran, x):
     st = torch.full((7,), float("nan"), dtype=torch.float64, device="cuda")
     rt.fp8_quant_error(dev(w), dev(q), fmt, gran, dev(s), st, x=None if x is None else dev(x))
@@ -89,7 +96,7 @@ def test_quant_error_matches_oracle(rt, orc, case):
     ref = orc.quant_error(w, q, fmt, s, gran, x)
     got = run_quant_error(rt, w, q, s, fmt, gran, x)
     print("quant_error", case, got, ref)
-    assert np.allclose(got[:2], ref[:2], rtol=1e-12, atol=0)
+    assert np.allclose(got[:2], ref[:2], rtol=sum_rtol(N, K), atol=0)
     assert got[2] == ref[2]
     if x is None:
         assert not got[3:].any()
@@ -123,7 +130,7 @@ def test_ledger_rows(rt, orc, dtype):
         assert r["qparam_count"] == s.size and r["qparam_bytes"] == 4 * s.size
         assert r["quantized_weight_bytes"] == N * K and r["total_state_bytes"] == N * K + 4 * s.size
         assert (r["saturated"], r["underflowed"]) == (int(cnt[0]), int(cnt[1]))
-        assert np.isclose(r["weight_mse"], st[0] / (N * K), rtol=1e-12, atol=0)
+        assert np.isclose(r["weight_mse"], st[0] / (N * K), rtol=sum_rtol(N, K), atol=0)
         assert r["weight_max_abs_err"] == st[2]
         tol = bounds(orc, w, q, s, fmt, gran, x) + 1e-12 * np.abs(st[3:])
         assert abs(r["output_mse"] - st[3] / (M * N)) <= tol[0] / (M * N)
