@@ -237,10 +237,12 @@ def bench_prefill(args, torch, rt, wl):
                      "avg_launch_us": g_ms * 1e3},
         "components": {
             "quantize_x_dynamic_per_tensor": {
-                "us": q_ms * 1e3, "GB_s": q_bytes / (q_ms * 1e-3) / 1e9,
+                "us": q_ms * 1e3, "p95_us": float(np.percentile(timer.ms("quant_x"), 95)) * 1e3,
+                "GB_s": q_bytes / (q_ms * 1e-3) / 1e9,
                 "frac_hbm": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes": q_bytes, "kernels": "k_tensor_amax + k_tensor_cast + k_finish"},
-            "gemm": {"us": g_ms * 1e3, "TFLOP_s": g_tflops, "frac_fp8_peak": g_tflops / FP8_PEAK_TFLOPS,
+            "gemm": {"us": g_ms * 1e3, "p95_us": float(np.percentile(timer.ms("gemm"), 95)) * 1e3,
+                     "TFLOP_s": g_tflops, "frac_fp8_peak": g_tflops / FP8_PEAK_TFLOPS,
                      "algorithmic_bytes": g_bytes},
             "quantize_w_given_per_tensor": {
                 "us": qw_ms * 1e3, "GB_s": qw_bytes / (qw_ms * 1e-3) / 1e9,
@@ -257,10 +259,21 @@ def bench_prefill(args, torch, rt, wl):
     return out
 
 
-def time_op(torch, fn, reps=10, scrub=None):
-    """Median microseconds of fn() over reps event-timed runs on the current
-    stream; scrub (untimed) runs before each repeat to evict the caches."""
-    fn()
+class Timing(float):
+    """Median microseconds, carrying the 95th percentile as .p95."""
+
+    def __new__(cls, med, p95):
+        t = super().__new__(cls, med)
+        t.p95 = p95
+        return t
+
+
+def time_op(torch, fn, reps=20, warmup=3, scrub=None):
+    """Median and 95th percentile (linear interpolation) of fn() over reps
+    event-timed runs on the current stream after warmup untimed calls; scrub
+    (untimed) runs before each repeat to evict the caches."""
+    for _ in range(warmup):
+        fn()
     out = []
     for _ in range(reps):
         if scrub is not None:
@@ -272,23 +285,30 @@ def time_op(torch, fn, reps=10, scrub=None):
         e1.record()
         e1.synchronize()
         out.append(e0.elapsed_time(e1) * 1e3)
-    return float(np.median(out))
+    return Timing(float(np.median(out)), float(np.percentile(out, 95)))
 
 
 def hbm_entry(us, nbytes, kernels):
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"us": us, "GB_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
-            "kernels": kernels}
+    e = {"us": float(us), "GB_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+         "kernels": kernels}
+    if hasattr(us, "p95"):
+        e["p95_us"] = us.p95
+    return e
 
 
 def mfma_entry(us, flops, nbytes):
     tf = flops / (us * 1e-6) / 1e12
-    return {"us": us, "TFLOP_s": tf, "frac_fp8_peak": tf / FP8_PEAK_TFLOPS, "algorithmic_bytes": nbytes}
+    e = {"us": float(us), "TFLOP_s": tf, "frac_fp8_peak": tf / FP8_PEAK_TFLOPS, "algorithmic_bytes": nbytes}
+    if hasattr(us, "p95"):
+        e["p95_us"] = us.p95
+    return e
 
 
 def extra_components(torch, rt, wl):
     """Quantize and GEMM kernels of the other workload shapes, each timed alone
-    (median of 10, caches scrubbed between repeats by a 1 GiB fill)."""
+    (3 untimed calls, then median and 95th percentile of 20, caches scrubbed
+    between repeats by a 1 GiB fill)."""
     dev = "cuda"
     junk = torch.empty(2**28, dtype=torch.float32, device=dev)
     scrub = lambda: junk.fill_(1.0)
@@ -355,7 +375,7 @@ def extra_components(torch, rt, wl):
     gm = lambda: rt.fp8_scaled_gemm(Gq, rt.E5M2, (0, 0), sg, Wq, rt.E4M3, (0, 0), sw, y)
     comp["delayed_quantize_g_given_e5m2"] = hbm_entry(time_op(torch, qg, scrub=scrub), M * K * 3 + 4,
                                                        "k_tensor_cast (given, amax + counts) + k_finish")
-    comp["delayed_history_update_us"] = time_op(torch, hu)
+    comp["delayed_history_update_us"] = float(time_op(torch, hu))
     comp["delayed_gemm_e5m2_e4m3_f32"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
                                                     M * K + N * K + M * N * 4 + 8)
     # cast-transpose of the same G (the backward reads it in both orientations):
