@@ -153,13 +153,17 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
 // stored as 16-byte row chunks; rows / columns at or past (M, N) are skipped.
 // FP8 output (OUT kOutE4M3 / kOutE5M2): codes of v * rq with the quantize
 // kernels' saturating RNE cast; the lane's max |v| and counters accumulate
-// into mb / sat_l / under_l.
-template <int OUT>
+// into mb / sat_l / under_l, with one chain per position r of a group of 4
+// (four independent chains per statistic: the epilogue runs one wave per
+// SIMD, so nothing else hides a serial chain's latency).  EDGE: the wave
+// tile may reach past (M, N), so elements are tested before they count.
+template <int OUT, bool EDGE = true>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t* stage, const float* scol,
                                            const float* sbias, const float (&sav)[MI], int64_t wrow0, int64_t wcol0,
                                            int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
                                            int wn, int fr, int fg, int lane, float rq, uint32_t& mb, uint32_t& sat_l,
                                            uint32_t& under_l) {
+  uint32_t mb4[4] = {0u, 0u, 0u, 0u}, sat4[4] = {0u, 0u, 0u, 0u}, und4[4] = {0u, 0u, 0u, 0u};
   constexpr int ESZ = OUT == kOutF32 ? 4 : OUT == kOutBF16 ? 2 : 1;
   constexpr int RB = WTN * ESZ;                 // staged row bytes: 128, 256 or 512
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8, 16 or 32
@@ -195,20 +199,21 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
             constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
             // statistics of stored outputs only: the tile's rows / columns
             // past (M, N) hold clamped or unscaled padding
-            const bool row_in = wrow0 + pass * ROWS + lrow < M;
+            const bool row_in = !EDGE || wrow0 + pass * ROWS + lrow < M;
             float f[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               f[r] = v[r] * rq;
-              const bool in = row_in && wcol0 + c + r < N;
-              mb = max(mb, in ? (__float_as_uint(v[r]) & kAbsMask) : 0u);
-              sat_l += (in && fabsf(f[r]) > Fmt<F>::kMax) ? 1u : 0u;
-              under_l += (in && v[r] != 0.0f && fabsf(f[r]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+              const bool in = !EDGE || (row_in && wcol0 + c + r < N);
+              mb4[r] = max(mb4[r], in ? (__float_as_uint(v[r]) & kAbsMask) : 0u);
+              sat4[r] += (in && fabsf(f[r]) > Fmt<F>::kMax) ? 1u : 0u;
+              und4[r] += (in && v[r] != 0.0f && fabsf(f[r]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
             }
             *reinterpret_cast<uint32_t*>(dst) = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
             // opaque per group: otherwise the tile's 256 updates are
             // reassociated into trees that keep every accumulator live
-            asm volatile("" : "+v"(mb), "+v"(sat_l), "+v"(under_l));
+            asm volatile("" : "+v"(mb4[0]), "+v"(mb4[1]), "+v"(mb4[2]), "+v"(mb4[3]), "+v"(sat4[0]), "+v"(sat4[1]),
+                         "+v"(sat4[2]), "+v"(sat4[3]), "+v"(und4[0]), "+v"(und4[1]), "+v"(und4[2]), "+v"(und4[3]));
           }
         }
     }
@@ -230,6 +235,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
     }
     __syncthreads();
   }
+  mb = max(mb, max(max(mb4[0], mb4[1]), max(mb4[2], mb4[3])));
+  sat_l += (sat4[0] + sat4[1]) + (sat4[2] + sat4[3]);
+  under_l += (und4[0] + und4[1]) + (und4[2] + und4[3]);
 }
 
 // MX: power-of-two 1x32 scales applied inside the MFMA.  xpa / xpb hold the
@@ -435,8 +443,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     for (int i = 0; i < MI; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
     float rq = 1.0f;
     if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
-    store_tile<OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr, fg,
-                    lane, rq, mb, sat_l, under_l);
+    // the whole block tile inside (M, N): every wave takes the same branch
+    // (store_tile holds barriers)
+    if (OUT >= kOutE4M3 && m0 + TM <= M && n0 + TN <= N)
+      store_tile<OUT, false>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn,
+                             fr, fg, lane, rq, mb, sat_l, under_l);
+    else
+      store_tile<OUT, true>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn,
+                            fr, fg, lane, rq, mb, sat_l, under_l);
   }
   // FP8 output: a whole tile's max |y| and counters (split-K units hold raw
   // partial sums; k_split_reduce takes the statistics of their tiles)
