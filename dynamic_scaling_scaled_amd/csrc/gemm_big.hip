@@ -153,17 +153,32 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
 // stored as 16-byte row chunks; rows / columns at or past (M, N) are skipped.
 // FP8 output (OUT kOutE4M3 / kOutE5M2): codes of v * rq with the quantize
 // kernels' saturating RNE cast; the lane's max |v| and counters accumulate
-// into mb / sat_l / under_l, with one chain per position r of a group of 4
-// (four independent chains per statistic: the epilogue runs one wave per
-// SIMD, so nothing else hides a serial chain's latency).  EDGE: the wave
-// tile may reach past (M, N), so elements are tested before they count.
+// into mb / sat_l / under_l.  Saturation, underflow and NaN are rare, so a
+// group of 4 is screened first (its max and min |v| against conservative
+// thresholds, one unordered compare per pair) and the exact per-element work
+// runs only for a group that may need it.  EDGE: the wave tile may reach past
+// (M, N), so elements are tested before they count.
 template <int OUT, bool EDGE = true>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t* stage, const float* scol,
                                            const float* sbias, const float (&sav)[MI], int64_t wrow0, int64_t wcol0,
                                            int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
                                            int wn, int fr, int fg, int lane, float rq, uint32_t& mb, uint32_t& sat_l,
                                            uint32_t& under_l) {
-  uint32_t mb4[4] = {0u, 0u, 0u, 0u}, sat4[4] = {0u, 0u, 0u, 0u}, und4[4] = {0u, 0u, 0u, 0u};
+  // Screen thresholds on |v| bit patterns.  |f| = fl(|v| |rq|) is monotonic
+  // in |v|: no element with |v| <= kMax / |rq| (two ulps below, absorbing the
+  // quotient's rounding) saturates, and none with |v| > kZeroEdge / |rq| (two
+  // ulps above) underflows.  NaN patterns exceed every finite threshold; a
+  // zero, infinite or NaN rq screens nothing.
+  uint32_t thr_sat = 0u, thr_und = ~0u;
+  if constexpr (OUT >= kOutE4M3) {
+    constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
+    const float arq = fabsf(rq);
+    if (arq > 0.0f && arq <= FLT_MAX) {
+      const uint32_t ts = __float_as_uint(Fmt<F>::kMax / arq), tu = __float_as_uint(Fmt<F>::kZeroEdge / arq);
+      thr_sat = ts > 2u ? ts - 2u : 0u;
+      thr_und = tu + 2u;
+    }
+  }
   constexpr int ESZ = OUT == kOutF32 ? 4 : OUT == kOutBF16 ? 2 : 1;
   constexpr int RB = WTN * ESZ;                 // staged row bytes: 128, 256 or 512
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8, 16 or 32
@@ -201,19 +216,30 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
             // past (M, N) hold clamped or unscaled padding
             const bool row_in = !EDGE || wrow0 + pass * ROWS + lrow < M;
             float f[4];
+            uint32_t ab[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               f[r] = v[r] * rq;
               const bool in = !EDGE || (row_in && wcol0 + c + r < N);
-              mb4[r] = max(mb4[r], in ? (__float_as_uint(v[r]) & kAbsMask) : 0u);
-              sat4[r] += (in && fabsf(f[r]) > Fmt<F>::kMax) ? 1u : 0u;
-              und4[r] += (in && v[r] != 0.0f && fabsf(f[r]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+              ab[r] = in ? (__float_as_uint(v[r]) & kAbsMask) : 0u;  // 0: not counted
             }
-            *reinterpret_cast<uint32_t*>(dst) = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
-            // opaque per group: otherwise the tile's 256 updates are
+            const uint32_t gmax = max(max(ab[0], ab[1]), max(ab[2], ab[3]));
+            const uint32_t gmin = min(min(ab[0], ab[1]), min(ab[2], ab[3]));
+            mb = max(mb, gmax);
+            if (gmax > thr_sat || gmin <= thr_und) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                sat_l += (ab[r] != 0u && fabsf(f[r]) > Fmt<F>::kMax) ? 1u : 0u;
+                under_l += (ab[r] != 0u && fabsf(f[r]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+              }
+            }
+            uint32_t w = cvt4<F>(f[0], f[1], f[2], f[3]);
+            if (__builtin_isunordered(f[0], f[1]) || __builtin_isunordered(f[2], f[3]))
+              w = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+            *reinterpret_cast<uint32_t*>(dst) = w;
+            // opaque per group: otherwise the tile's updates are
             // reassociated into trees that keep every accumulator live
-            asm volatile("" : "+v"(mb4[0]), "+v"(mb4[1]), "+v"(mb4[2]), "+v"(mb4[3]), "+v"(sat4[0]), "+v"(sat4[1]),
-                         "+v"(sat4[2]), "+v"(sat4[3]), "+v"(und4[0]), "+v"(und4[1]), "+v"(und4[2]), "+v"(und4[3]));
+            asm volatile("" : "+v"(mb), "+v"(sat_l), "+v"(under_l));
           }
         }
     }
@@ -235,9 +261,6 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
     }
     __syncthreads();
   }
-  mb = max(mb, max(max(mb4[0], mb4[1]), max(mb4[2], mb4[3])));
-  sat_l += (sat4[0] + sat4[1]) + (sat4[2] + sat4[3]);
-  under_l += (und4[0] + und4[1]) + (und4[2] + und4[3]);
 }
 
 // MX: power-of-two 1x32 scales applied inside the MFMA.  xpa / xpb hold the
