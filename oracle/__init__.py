@@ -74,6 +74,8 @@ def lib():
         L.orc_gemm_points.argtypes = gemm_args + [P]
         L.orc_gemm_points_exact.restype = I
         L.orc_gemm_points_exact.argtypes = gemm_args
+        L.orc_pack_weights16.restype = I
+        L.orc_pack_weights16.argtypes = [P, I64, I64, I64, P]
         L.orc_quant_error.restype = I
         L.orc_quant_error.argtypes = [P, I, I64, I64, I64, P, I, I64, I64, I64, P, P, I64, I64, P]
         L.orc_history_update_recipe.restype = I
@@ -243,6 +245,16 @@ def quant_error(w, q, fmt, scale, gran, x=None):
     _check(lib().orc_quant_error(_ptr(w), _dtype_code(w), N, K, K, _ptr(q), fmt, K, gran[0], gran[1],
                                  _ptr(s), _ptr(x), M, K, _ptr(st)), "quant_error")
     return st
+
+
+def pack_weights16(q):
+    """Fragment-ordered layout of codes q [N, K] (K % 128 == 0): a flat uint8
+    array of ceil(N/16) * 16 * K bytes."""
+    q = np.ascontiguousarray(q, np.uint8)
+    N, K = q.shape
+    out = np.empty(((N + 15) // 16) * 16 * K, np.uint8)
+    _check(lib().orc_pack_weights16(_ptr(q), N, K, K, _ptr(out)), "pack_weights16")
+    return out
 
 
 HIST_MAX, HIST_LATEST = 0, 1

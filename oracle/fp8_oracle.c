@@ -487,6 +487,26 @@ int orc_quant_error(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw
     return 0;
 }
 
+/* Fragment-ordered weight codes (a layout of the same codes, no arithmetic):
+ * rows in groups of 16, K in steps of 128; the 2048 bytes of (group G, step s)
+ * hold at byte h * 1024 + l * 16 + b (h in {0,1}, lane l in 0..63, b in 0..15)
+ * the code W[16 G + l % 16][128 s + 32 (l / 16) + 16 h + b], or 0 past the
+ * last row.  Requires K % 128 == 0; qp holds ceil(N/16) * 16 * K bytes. */
+int orc_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp) {
+    if (!q || !qp || N <= 0 || K <= 0 || K % 128 != 0 || ldq < K) return 1;
+    const int64_t steps = K / 128, groups = (N + 15) / 16;
+    for (int64_t G = 0; G < groups; ++G)
+        for (int64_t st = 0; st < steps; ++st)
+            for (int h = 0; h < 2; ++h)
+                for (int l = 0; l < 64; ++l)
+                    for (int b = 0; b < 16; ++b) {
+                        const int64_t row = 16 * G + l % 16;
+                        const int64_t col = 128 * st + 32 * (l / 16) + 16 * h + b;
+                        qp[(G * steps + st) * 2048 + h * 1024 + l * 16 + b] = row < N ? q[row * ldq + col] : 0;
+                    }
+    return 0;
+}
+
 /* Integer value of a code in units of the format's smallest subnormal
  * (2^-9 for E4M3, 2^-16 for E5M2); returns 0 and sets *bad for NaN/Inf. */
 static int64_t code_units(unsigned code, int fmt, int* bad) {

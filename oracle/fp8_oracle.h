@@ -142,6 +142,10 @@ int orc_quant_error(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw
                     int fmt, int64_t ldq, int64_t gr, int64_t gc, const float* scale, const void* x,
                     int64_t M, int64_t ldx, double* stats);
 
+/* Fragment-ordered weight layout (16-row groups x 128-byte K steps, 2 KB
+ * each, lane-major halves); see fp8_oracle.c.  Zero codes past row N. */
+int orc_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp);
+
 /* Exact inner sums: for point i and every maximal K-run on which both scales
  * are constant, the sum of dec*dec products as an exact integer multiple of
  * the product quantum (2^-18 E4M3xE4M3, 2^-25 E5M2xE4M3, 2^-32 E5M2xE5M2),
