@@ -345,6 +345,22 @@ def extra_components(torch, rt, wl):
     e = hbm_entry(time_op(torch, wo, scrub=scrub), wo_bytes, "k_gemm_wonly")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_weight_only_gemm_bf16_bias"] = e
+    # the same two GEMMs on the fragment-ordered image of the weight codes
+    # (packed once, as a weight is laid out offline; the pack is timed alone)
+    P = rt.fp8_pack_weights16(Wq)
+    pk = lambda: rt.fp8_pack_weights16(Wq, out=P.data)
+    comp["decode_pack_weights16"] = hbm_entry(time_op(torch, pk, scrub=scrub), 2 * N * K, "k_pack_weights16")
+    gmp = lambda: rt.fp8_scaled_gemm(Aq, rt.E4M3, (1, 0), sa, P, rt.E4M3, (1, 0), sw, y, bias=bias)
+    gmp()
+    e = hbm_entry(time_op(torch, gmp, scrub=scrub), g_bytes, "k_gemm_skinny (packed B)")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_gemm_bf16_bias_packed_w"] = e
+    wop = lambda: rt.fp8_weight_only_gemm(A, P, rt.E4M3, (1, 0), sw, yw, bias=bias)
+    wop()
+    e = hbm_entry(time_op(torch, wop, scrub=scrub), wo_bytes, "k_gemm_wonly (packed W)")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_weight_only_gemm_bf16_bias_packed_w"] = e
+    del P
     # granularity ledger: error statistics of the per-channel weight codes
     # against the bf16 weight, with the 16 activation rows
     stats = torch.empty(7, dtype=torch.float64, device=dev)

@@ -25,6 +25,7 @@ E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
 DYNAMIC, GIVEN = 0, 1
 POW2_SCALES = 1
+B_PACKED16 = 2
 FMAX = {E4M3: 448.0, E5M2: 57344.0}
 
 OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
@@ -92,7 +93,9 @@ def lib():
         L.fp8_delayed_scale_update.argtypes = [P, I32, P, P, C.c_int, C.c_int, I32, F, I32, P, P, P]
         L.fp8_weight_only_gemm.restype = C.c_int
         L.fp8_weight_only_gemm.argtypes = [P, C.c_int, I64, P, C.c_int, I64, Gran, P, I64, I64, I64, P,
-                                           C.c_int, P, C.c_int, I64, P]
+                                           C.c_int, P, C.c_int, I64, U32, P]
+        L.fp8_pack_weights16.restype = C.c_int
+        L.fp8_pack_weights16.argtypes = [P, I64, I64, I64, P, P]
         L.fp8_scaled_gemm_fp8out.restype = C.c_int
         L.fp8_scaled_gemm_fp8out.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                              I64, P, C.c_int, C.c_int, P, P, P, I64, P, P, U32, P]
@@ -189,9 +192,45 @@ def fp8_amax_history_update(history, head, amax_new, fmt, eps, pow2_round_up, sc
                                          _ptr(inv_scale_next), _stream(stream)))
 
 
+class PackedWeights:
+    """A fragment-ordered weight image (fp8_pack_weights16): the uint8 device
+    tensor `data` and the logical shape [N x K] of the codes it holds."""
+
+    def __init__(self, data, N, K):
+        self.data, self.N, self.K = data, int(N), int(K)
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+
+def packed16_bytes(N, K):
+    return (N + 15) // 16 * 16 * K
+
+
+def fp8_pack_weights16(q, out=None, stream=None):
+    """Fragment-ordered image of row-major codes q [N x K] (K % 128 == 0)."""
+    if q.dtype != torch.uint8:
+        raise ValueError("q must be uint8 codes")
+    N, K, ldq = _mat(q)
+    if out is None:
+        out = torch.empty(packed16_bytes(N, K), dtype=torch.uint8, device=q.device)
+    if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < packed16_bytes(N, K):
+        raise ValueError("out must be contiguous uint8 with packed16_bytes(N, K) bytes")
+    _check("fp8_pack_weights16", lib().fp8_pack_weights16(_ptr(q), N, K, ldq, _ptr(out), _stream(stream)))
+    return PackedWeights(out, N, K)
+
+
+def _weight(b, flags):
+    """(N, K, ld, flags) of a row-major code matrix or a PackedWeights."""
+    if isinstance(b, PackedWeights):
+        return b.N, b.K, b.K, flags | B_PACKED16
+    N, K, ld = _mat(b)
+    return N, K, ld, flags
+
+
 def fp8_scaled_gemm(a, fa, ga, scale_a, b, fb, gb, scale_b, y, bias=None, flags=0, stream=None):
     M, K, lda = _mat(a)
-    N, K2, ldb = _mat(b)
+    N, K2, ldb, flags = _weight(b, flags)
     if K2 != K:
         raise ValueError("A and B disagree on K")
     _, _, ldy = _mat(y)
@@ -280,20 +319,22 @@ def fp8_delayed_scale_update(history, head, amax_new, fmt, fn, margin, eps, pow2
                                           _stream(stream)))
 
 
-def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, stream=None):
-    """y = x (s_w o dec(w))^T + bias: x [M, K] bf16, w [N, K] uint8 codes."""
+def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, flags=0, stream=None):
+    """y = x (s_w o dec(w))^T + bias: x [M, K] bf16, w [N, K] uint8 codes or
+    their PackedWeights image."""
     M, K, ldx = _mat(x)
-    N, K2, ldw = _mat(w)
+    N, K2, ldw, flags = _weight(w, flags)
     if K2 != K:
         raise ValueError("x and w disagree on K")
     _, _, ldy = _mat(y)
     bt = F32 if bias is None else _dtype(bias)
     _check("fp8_weight_only_gemm",
            lib().fp8_weight_only_gemm(_ptr(x), _dtype(x), ldx, _ptr(w), fw, ldw, Gran(*gw), _ptr(scale_w),
-                                      M, N, K, _ptr(bias), bt, _ptr(y), _dtype(y), ldy, _stream(stream)))
+                                      M, N, K, _ptr(bias), bt, _ptr(y), _dtype(y), ldy, flags,
+                                      _stream(stream)))
 
 
-__all__ = ["fp8_quant_error", "fp8_granularity_ledger", "LedgerSpec", "LedgerRow", "fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
+__all__ = ["fp8_pack_weights16", "PackedWeights", "packed16_bytes", "B_PACKED16", "fp8_quant_error", "fp8_granularity_ledger", "LedgerSpec", "LedgerRow", "fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
            "scale_shape"]

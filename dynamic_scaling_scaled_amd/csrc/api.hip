@@ -218,10 +218,12 @@ fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gr
                         uint32_t flags, GemmArgs& g) {
   if (!a || !b || !scale_a || !scale_b) return FP8RT_EINVAL;
   if (!valid_fmt(fa) || !valid_fmt(fb) || (bias && !valid_dtype(bias_t))) return FP8RT_EINVAL;
+  if ((flags & ~(FP8RT_POW2_SCALES | FP8RT_B_PACKED16)) != 0) return FP8RT_EINVAL;
+  const bool packed = (flags & FP8RT_B_PACKED16) != 0;
+  if (packed) ldb = K;  // ignored: the packed image has no leading dimension
   if (M <= 0 || N <= 0 || K <= 0 || lda < K || ldb < K || ldy < N) return FP8RT_EINVAL;
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
   if (ga.rows < 0 || ga.cols < 0 || gb.rows < 0 || gb.cols < 0) return FP8RT_EINVAL;
-  if ((flags & ~FP8RT_POW2_SCALES) != 0) return FP8RT_EINVAL;
   if (K % 16 != 0 || lda % 16 != 0 || ldb % 16 != 0) return FP8RT_EALIGN;
   if (!aligned16(a) || !aligned16(b) || !aligned4(scale_a) || !aligned4(scale_b)) return FP8RT_EALIGN;
   if (bias && !aligned4(bias)) return FP8RT_EALIGN;
@@ -257,6 +259,9 @@ fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gr
     if (b_kblk && g.ecb % 128 != 0) return FP8RT_EUNSUPPORTED;
     if (a_kblk && b_kblk && g.eca != g.ecb) return FP8RT_EUNSUPPORTED;
   }
+  // the packed weight image is read by the decode kernel only
+  g.b_packed = packed;
+  if (packed && !gemm_skinny_eligible(g)) return FP8RT_EUNSUPPORTED;
   return FP8RT_OK;
 }
 
@@ -288,6 +293,7 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
                                     int64_t ldy, float* amax_y, uint64_t* sat_underflow, uint32_t flags,
                                     hipStream_t stream) {
   if (!yq || !scale_y || !valid_fmt(fy)) return FP8RT_EINVAL;
+  if (flags & FP8RT_B_PACKED16) return FP8RT_EUNSUPPORTED;
   GemmArgs g{};
   const fp8rt_status st =
       gemm_setup(a, fa, lda, ga, scale_a, b, fb, ldb, gb, scale_b, M, N, K, bias, bias_t, ldy, flags, g);
@@ -313,15 +319,18 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
 fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, const uint8_t* w, fp8rt_format fw,
                                   int64_t ldw, fp8rt_gran gw, const float* scale_w, int64_t M, int64_t N,
                                   int64_t K, const void* bias, fp8rt_dtype bias_t, void* y, fp8rt_dtype yt,
-                                  int64_t ldy, hipStream_t stream) {
+                                  int64_t ldy, uint32_t flags, hipStream_t stream) {
   if (!x || !w || !scale_w || !y) return FP8RT_EINVAL;
   if (!valid_dtype(xt) || !valid_fmt(fw) || !valid_dtype(yt) || (bias && !valid_dtype(bias_t)))
     return FP8RT_EINVAL;
+  if ((flags & ~FP8RT_B_PACKED16) != 0) return FP8RT_EINVAL;
+  const bool packed = (flags & FP8RT_B_PACKED16) != 0;
+  if (packed) ldw = K;  // ignored: the packed image has no leading dimension
   if (M <= 0 || N <= 0 || K <= 0 || ldx < K || ldw < K || ldy < N || gw.rows < 0 || gw.cols < 0)
     return FP8RT_EINVAL;
   if (M > int64_t(16) * 65535 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
   if (xt != FP8RT_BF16) return FP8RT_EUNSUPPORTED;  // activations stay BF16
-  if (K % 16 != 0 || ldx % 8 != 0 || ldw % 16 != 0) return FP8RT_EALIGN;
+  if (K % 16 != 0 || ldx % 8 != 0 || ldw % 16 != 0 || (packed && K % 128 != 0)) return FP8RT_EALIGN;
   if (!aligned16(x) || !aligned16(w) || !aligned4(scale_w) || (bias && !aligned4(bias))) return FP8RT_EALIGN;
   if ((yt == FP8RT_F32 && !aligned4(y)) || (yt == FP8RT_BF16 && (reinterpret_cast<uintptr_t>(y) & 1u)))
     return FP8RT_EALIGN;
@@ -344,7 +353,16 @@ fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, co
   g.y = y;
   g.yt = yt;
   g.ldy = ldy;
+  g.w_packed = packed;
   return from_hip(launch_gemm_wonly(g, stream));
+}
+
+fp8rt_status fp8_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp,
+                                hipStream_t stream) {
+  if (!q || !qp || N <= 0 || K <= 0 || ldq < K) return FP8RT_EINVAL;
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return FP8RT_EINVAL;
+  if (K % 128 != 0 || ldq % 16 != 0 || !aligned16(q) || !aligned16(qp)) return FP8RT_EALIGN;
+  return from_hip(launch_pack_weights16(q, N, K, ldq, qp, stream));
 }
 
 namespace {

@@ -28,6 +28,11 @@
 //    both operands.
 //  - The 16 partial sums meet in LDS; wave 0 adds them in wave order,
 //    scales, adds the bias, rounds and stores.
+//  - Fragment-ordered W (fp8_pack_weights16): the lane's two 16-byte pieces
+//    of a step sit at the same place of its tile's two KB halves, so each
+//    weight load instruction reads 1 KB contiguous; the MFMA gets the same
+//    bytes as from row-major W and the results are identical.  A packed W has
+//    K a multiple of 128 (no tail step).
 //  - A K tail (K a multiple of 16) is handled in the last step by loading
 //    whole 16-byte pieces from the row start and zeroing them (both operands,
 //    so no code beyond K can contribute a NaN).
@@ -75,16 +80,20 @@ struct Step {
   u32x4 x[4];            // K [32 q + 8 j, +8) of the lane's activation row
 };
 
-template <bool GUARD>
+// Row-major W: wrow[t] is the lane's row, the piece at K offset off.  Packed
+// W: wrow[t] is the lane's slot of its group's first tile; step ko / 128 is
+// 2048 bytes further, half h 1024 (GUARD is never taken: K % 128 == 0).
+template <bool GUARD, bool PACKED>
 __device__ __forceinline__ void load_step(Step& s, const uint8_t* const (&wrow)[kWoTiles], const uint16_t* xrow,
                                           int64_t ko, int q, int64_t K) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t off = ko + 32 * q + 16 * h;
     const bool ok = !GUARD || off < K;
+    const int64_t woff = PACKED ? (ko >> 7) * 2048 + 1024 * h : off;
 #pragma unroll
     for (int t = 0; t < kWoTiles; ++t) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[t] + (ok ? off : 0)));
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[t] + (ok ? woff : 0)));
       s.w[t][h] = ok ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -112,7 +121,7 @@ __device__ __forceinline__ void mma_step(const Step& s, f32x4 (&p)[kWoTiles]) {
   }
 }
 
-template <int F, bool GROUPED, bool BF16OUT>
+template <int F, bool GROUPED, bool BF16OUT, bool PACKED>
 __global__ __launch_bounds__(kWoThreads, 1) void k_gemm_wonly(
     const uint16_t* __restrict__ X, int64_t ldx, const uint8_t* __restrict__ W, int64_t ldw, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sw, int64_t erw, int64_t ecw, int64_t ncw,
@@ -125,7 +134,16 @@ __global__ __launch_bounds__(kWoThreads, 1) void k_gemm_wonly(
   const uint16_t* xrow = X + min(m, M - 1) * ldx;
   const uint8_t* wrow[kWoTiles];
 #pragma unroll
-  for (int t = 0; t < kWoTiles; ++t) wrow[t] = W + min(n0 + 16 * t + r, N - 1) * ldw;
+  for (int t = 0; t < kWoTiles; ++t) {
+    if constexpr (PACKED) {
+      // 16-row group 2 blockIdx.x + t, clamped to the last one (a tile past N
+      // loads valid bytes whose outputs are never stored)
+      const int64_t grp = min(static_cast<int64_t>(blockIdx.x) * kWoTiles + t, (N + 15) / 16 - 1);
+      wrow[t] = W + grp * (K / 128) * 2048 + lane * 16;
+    } else {
+      wrow[t] = W + min(n0 + 16 * t + r, N - 1) * ldw;
+    }
+  }
 
   // K-group scales: element offsets of the scale rows of the lane's output
   // columns n0 + 16 t + 4 q + v (the table has fewer than 2^31 entries)
@@ -169,11 +187,11 @@ __global__ __launch_bounds__(kWoThreads, 1) void k_gemm_wonly(
     const int64_t ko = static_cast<int64_t>(st) * 128;
     Step a, b;
     if (ko + 256 <= K) {
-      load_step<false>(a, wrow, xrow, ko, q, K);
-      load_step<false>(b, wrow, xrow, ko + 128, q, K);
+      load_step<false, PACKED>(a, wrow, xrow, ko, q, K);
+      load_step<false, PACKED>(b, wrow, xrow, ko + 128, q, K);
     } else {
-      load_step<true>(a, wrow, xrow, ko, q, K);
-      load_step<true>(b, wrow, xrow, ko + 128, q, K);
+      load_step<true, PACKED>(a, wrow, xrow, ko, q, K);
+      load_step<true, PACKED>(b, wrow, xrow, ko + 128, q, K);
     }
     run(a, st);
     run(b, st + 1);
@@ -181,8 +199,8 @@ __global__ __launch_bounds__(kWoThreads, 1) void k_gemm_wonly(
   for (; st < s1; ++st) {
     const int64_t ko = static_cast<int64_t>(st) * 128;
     Step a;
-    if (ko + 128 <= K) load_step<false>(a, wrow, xrow, ko, q, K);
-    else load_step<true>(a, wrow, xrow, ko, q, K);
+    if (ko + 128 <= K) load_step<false, PACKED>(a, wrow, xrow, ko, q, K);
+    else load_step<true, PACKED>(a, wrow, xrow, ko, q, K);
     run(a, st);
   }
 
@@ -236,17 +254,23 @@ __global__ __launch_bounds__(kWoThreads, 1) void k_gemm_wonly(
   }
 }
 
-template <int F, bool GROUPED>
-void launch_f(const WonlyArgs& g, hipStream_t st, int vec) {
+template <int F, bool GROUPED, bool PACKED>
+void launch_fp(const WonlyArgs& g, hipStream_t st, int vec) {
   const dim3 grid(static_cast<unsigned>((g.N + kWoCols - 1) / kWoCols), static_cast<unsigned>((g.M + 15) / 16));
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
   const int64_t ncw = (g.K + g.ecw - 1) / g.ecw;
   if (g.yt == FP8RT_BF16)
-    hipLaunchKernelGGL((k_gemm_wonly<F, GROUPED, true>), grid, dim3(kWoThreads), 0, st, g.x, g.ldx, g.w, g.ldw,
-                       g.M, g.N, g.K, g.sw, g.erw, g.ecw, ncw, g.bias, bb, g.y, g.ldy, vec);
+    hipLaunchKernelGGL((k_gemm_wonly<F, GROUPED, true, PACKED>), grid, dim3(kWoThreads), 0, st, g.x, g.ldx, g.w,
+                       g.ldw, g.M, g.N, g.K, g.sw, g.erw, g.ecw, ncw, g.bias, bb, g.y, g.ldy, vec);
   else
-    hipLaunchKernelGGL((k_gemm_wonly<F, GROUPED, false>), grid, dim3(kWoThreads), 0, st, g.x, g.ldx, g.w, g.ldw,
-                       g.M, g.N, g.K, g.sw, g.erw, g.ecw, ncw, g.bias, bb, g.y, g.ldy, vec);
+    hipLaunchKernelGGL((k_gemm_wonly<F, GROUPED, false, PACKED>), grid, dim3(kWoThreads), 0, st, g.x, g.ldx, g.w,
+                       g.ldw, g.M, g.N, g.K, g.sw, g.erw, g.ecw, ncw, g.bias, bb, g.y, g.ldy, vec);
+}
+
+template <int F, bool GROUPED>
+void launch_f(const WonlyArgs& g, hipStream_t st, int vec) {
+  if (g.w_packed) launch_fp<F, GROUPED, true>(g, st, vec);
+  else launch_fp<F, GROUPED, false>(g, st, vec);
 }
 
 }  // namespace

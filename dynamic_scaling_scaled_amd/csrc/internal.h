@@ -98,6 +98,7 @@ struct GemmArgs {
   int yt;
   int64_t ldy;
   bool pow2_mx;  // 1x32 power-of-two scales through the scaled MFMA
+  bool b_packed = false;  // b is fragment-ordered (launch_pack_weights16)
   // FP8 output (fp8_scaled_gemm_fp8out) when yq_fmt >= 0: y then holds codes
   // of y_fp32 * r_y, r_y = ry[0] or fl32(1 / sy[0]); per-block partials of
   // max |y| and the saturation / underflow counts go to part.
@@ -146,6 +147,7 @@ struct WonlyArgs {
   void* y = nullptr;
   int yt = 0;
   int64_t ldy = 0;
+  bool w_packed = false;  // w is fragment-ordered (launch_pack_weights16)
 };
 hipError_t launch_gemm_wonly(const WonlyArgs& g, hipStream_t stream);
 
@@ -169,5 +171,9 @@ struct QuantErrorArgs {
 size_t quant_error_partials_bytes(int64_t N);
 hipError_t launch_quant_error(const QuantErrorArgs& g, void* partials, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream);
+// Fragment-ordered copy of row-major codes q [N x K] (ldq; K % 128 == 0) into
+// qp: 2 KB per (16-row group, 128-byte K step), groups zero-padded past N.
+hipError_t launch_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp,
+                                 hipStream_t stream);
 
 }  // namespace fp8rt

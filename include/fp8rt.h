@@ -83,8 +83,9 @@ typedef enum fp8rt_mode {
     FP8RT_GIVEN = 1    /* static or delayed: s (and optionally r) supplied */
 } fp8rt_mode;
 
-/* fp8_scaled_gemm flags */
+/* GEMM flags (fp8_scaled_gemm, fp8_scaled_gemm_fp8out, fp8_weight_only_gemm) */
 #define FP8RT_POW2_SCALES 1u /* every scale is a power of two (enables 1x32 scaled MFMA) */
+#define FP8RT_B_PACKED16 2u  /* the weight operand is fragment-ordered (fp8_pack_weights16) */
 
 /* Per-group amax a_g = max |x| over each group [P2 "How a scale fits a tensor
  * into E4M3" (a_max = max|X|), "Per-channel and block scaling" (a_g)].
@@ -201,7 +202,11 @@ fp8rt_status fp8_delayed_scale_update(float* history, int32_t len, int32_t* head
  * block {gr,g}} with g a multiple of 128 and equal for A and B when both are
  * K-blocked; or {1,32} on both with FP8RT_POW2_SCALES (hardware-scaled MFMA).
  * Accumulation is FP32 on the matrix cores; K-blocked scales are applied once
- * per 128-deep K step.  Alignment: K, lda, ldb multiples of 16; M, N any. */
+ * per 128-deep K step.  Alignment: K, lda, ldb multiples of 16; M, N any.
+ * FP8RT_B_PACKED16: b is the fp8_pack_weights16 image of the [N x K] codes
+ * (ldb ignored); decode shapes only (M <= 16, K a multiple of 128, tensor or
+ * row scales on both sides), else FP8RT_EUNSUPPORTED.  The result is
+ * bit-identical to the row-major call. */
 fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
                              const float* scale_a, const uint8_t* b, fp8rt_format fb,
                              int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
@@ -225,7 +230,8 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
  * power-of-two scales) runs it, a ragged last wave of tiles split along K
  * with the requantization in the reduction kernel; other shapes run on the
  * general kernel.  Limit: ceil(M/128) ceil(N/128) <= 8192 (one per-block
- * statistics partial per output tile), else FP8RT_EUNSUPPORTED. */
+ * statistics partial per output tile), else FP8RT_EUNSUPPORTED.
+ * FP8RT_B_PACKED16 is not accepted here (FP8RT_EUNSUPPORTED). */
 fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
                                     const float* scale_a, const uint8_t* b, fp8rt_format fb, int64_t ldb,
                                     fp8rt_gran gb, const float* scale_b, int64_t M, int64_t N, int64_t K,
@@ -251,12 +257,36 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
  * FP32.  Built for decode shapes (W streamed once per 16 activation rows;
  * larger M re-reads W per 16 rows).  Limits: M <= 16 * 65535.
  * Alignment: K a multiple of 16, ldx a multiple of 8, ldw of 16; x and w
- * 16-byte aligned, scales and fp32 bias / y 4-byte aligned. */
+ * 16-byte aligned, scales and fp32 bias / y 4-byte aligned.
+ * flags: 0 or FP8RT_B_PACKED16 (w is the fp8_pack_weights16 image of the
+ * codes, ldw ignored, K a multiple of 128 else FP8RT_EALIGN; bit-identical to
+ * the row-major call); other bits FP8RT_EINVAL. */
 fp8rt_status fp8_weight_only_gemm(const void* x, fp8rt_dtype xt, int64_t ldx, const uint8_t* w,
                                   fp8rt_format fw, int64_t ldw, fp8rt_gran gw, const float* scale_w,
                                   int64_t M, int64_t N, int64_t K, const void* bias,
                                   fp8rt_dtype bias_t, void* y, fp8rt_dtype yt, int64_t ldy,
-                                  hipStream_t stream);
+                                  uint32_t flags, hipStream_t stream);
+
+/* Fragment-ordered weight image for the decode GEMMs [the layout is this
+ * library's, not the sources': "FP8 formats and scaling for LLM inference",
+ * section "Weight scale and activation scale lifetimes" -- a weight is
+ * quantized and laid out once, offline, and reused by every call].  For a
+ * decode GEMM (M <= 16) the work is streaming the weight; in row-major order
+ * each load instruction of the matrix-core fragment touches 16 rows 64 bytes
+ * apart, in this order 1 KB contiguous.
+ *   q  : [N x K] codes (ldq bytes), K a multiple of 128
+ *   qp : fp8_packed16_bytes(N, K) bytes (caller-owned, not overlapping q):
+ *        for 16-row group G, 128-byte step s, half h in {0,1}, lane l in
+ *        [0,64), byte b in [0,16):
+ *          qp[((G * K/128 + s) * 2 + h) * 1024 + 16 l + b]
+ *            = q[16 G + l % 16][128 s + 32 (l / 16) + 16 h + b],
+ *        0 for rows >= N.
+ * One pass, codes copied unchanged.  Errors: null pointers, N or K <= 0,
+ * ldq < K, N or K > 2^31: FP8RT_EINVAL; K or ldq not a multiple of 128 / 16,
+ * pointers not 16-byte aligned: FP8RT_EALIGN. */
+static inline int64_t fp8_packed16_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * 16 * K; }
+fp8rt_status fp8_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp,
+                                hipStream_t stream);
 
 /* Quantization error of a weight, for the granularity ledger ["Quantization
  * W8A16" (datawhalechina llm-algo-leetcode): the granularity comparison

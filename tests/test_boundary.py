@@ -133,6 +133,12 @@ def test_gemm_validation(rt):
     assert g(rt, K=256, lda=256, ldb=256, ga=(1, 64), gb=(0, 0)) == rt.EUNSUPPORTED       # not a multiple of 128
     assert g(rt, K=256, lda=256, ldb=256, ga=(1, 32), gb=(1, 32)) == rt.EUNSUPPORTED      # 1x32 needs POW2 flag
     assert g(rt, K=256, lda=256, ldb=256, ga=(2, 128), gb=(0, 0)) == rt.EUNSUPPORTED      # A blocks span rows
+    # the packed weight image: decode shapes only
+    assert g(rt, flags=6) == rt.EINVAL
+    assert g(rt, flags=rt.B_PACKED16) == rt.EUNSUPPORTED                                  # M = 64 > 16
+    assert g(rt, flags=rt.B_PACKED16, M=16, K=144, lda=144, ldb=144) == rt.EUNSUPPORTED  # K % 128
+    assert g(rt, flags=rt.B_PACKED16, M=8, K=256, lda=256, ga=(1, 128)) == rt.EUNSUPPORTED  # K-group scales
+    assert g(rt, flags=rt.B_PACKED16, M=8, lda=64) == rt.EINVAL                           # lda < K still checked
 
 
 def qtr(rt, **kw):
@@ -176,6 +182,7 @@ def test_gemm_fp8out_validation(rt):
     assert call(K=48, lda=48, ldb=48) == rt.EALIGN or call(K=40, lda=48, ldb=48) == rt.EALIGN
     assert call(sy=FAKE + 2) == rt.EALIGN
     assert call(M=128 * 8193, N=128, ldy=128) == rt.EUNSUPPORTED
+    assert call(flags=rt.B_PACKED16) == rt.EUNSUPPORTED
 
 
 def test_weight_only_gemm_validation(rt):
@@ -184,10 +191,11 @@ def test_weight_only_gemm_validation(rt):
 
     def call(**kw):
         a = dict(x=FAKE, xt=rt.BF16, ldx=256, w=FAKE, fw=rt.E4M3, ldw=256, gw=(1, 0), sw=FAKE, M=16, N=64,
-                 K=256, bias=None, bt=rt.F32, y=FAKE, yt=rt.BF16, ldy=64)
+                 K=256, bias=None, bt=rt.F32, y=FAKE, yt=rt.BF16, ldy=64, flags=0)
         a.update(kw)
         return L.fp8_weight_only_gemm(a["x"], a["xt"], a["ldx"], a["w"], a["fw"], a["ldw"], G(*a["gw"]), a["sw"],
-                                      a["M"], a["N"], a["K"], a["bias"], a["bt"], a["y"], a["yt"], a["ldy"], None)
+                                      a["M"], a["N"], a["K"], a["bias"], a["bt"], a["y"], a["yt"], a["ldy"],
+                                      a["flags"], None)
     assert call(x=None) == rt.EINVAL
     assert call(w=None) == rt.EINVAL
     assert call(sw=None) == rt.EINVAL
@@ -207,6 +215,29 @@ def test_weight_only_gemm_validation(rt):
     assert call(sw=FAKE + 2) == rt.EALIGN
     assert call(gw=(1, 64)) == rt.EUNSUPPORTED   # K groups are whole 128-deep steps
     assert call(gw=(1, 192)) == rt.EUNSUPPORTED
+    assert call(flags=1) == rt.EINVAL                                       # POW2 means nothing here
+    assert call(flags=rt.B_PACKED16, K=144, ldx=144, ldw=144) == rt.EALIGN  # packed: K % 128
+    assert call(flags=rt.B_PACKED16, K=144, ldx=144, ldw=0) == rt.EALIGN    # ldw ignored, K still checked
+
+
+def test_pack_weights16_validation(rt):
+    L = rt.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, N=64, K=256, ldq=256, qp=FAKE)
+        a.update(kw)
+        return L.fp8_pack_weights16(a["q"], a["N"], a["K"], a["ldq"], a["qp"], None)
+    assert call(q=None) == rt.EINVAL
+    assert call(qp=None) == rt.EINVAL
+    assert call(N=0) == rt.EINVAL
+    assert call(K=0) == rt.EINVAL
+    assert call(ldq=128) == rt.EINVAL
+    assert call(N=2 ** 31 + 1) == rt.EINVAL
+    assert call(K=144, ldq=144) == rt.EALIGN
+    assert call(ldq=264) == rt.EALIGN
+    assert call(q=FAKE + 8) == rt.EALIGN
+    assert call(qp=FAKE + 8) == rt.EALIGN
+    assert rt.packed16_bytes(17, 256) == 32 * 256 and rt.packed16_bytes(16, 128) == 2048
 
 
 def test_delayed_scale_update_validation(rt):
