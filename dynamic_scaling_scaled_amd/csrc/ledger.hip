@@ -14,19 +14,29 @@
 //
 // Readings: the restored weight is the dequantization fl32(s dec(q)); the
 // output error is the quantization's, not a GEMM's rounding: y_ref = x W^T
-// and d = y_q - y_ref = x (W_hat - W)^T with FP32 products summed over
-// 8-element runs and combined in binary64; cosine = <y_ref, y_q> /
-// max(|y_ref| |y_q|, 1e-8).
+// and d = y_q - y_ref = x (W_hat - W)^T, with FP32 accumulation of exact
+// products; cosine = <y_ref, y_q> / max(|y_ref| |y_q|, 1e-8).
 //
-// Design for MI355X: a wave takes 4 weight rows (grid-stride), lane l taking
-// 8 consecutive elements of every 512-wide K chunk, so W, its codes and each
-// activation row are read with 16-, 8- and 16-byte loads, and one activation
-// load serves the 4 rows (the activations are re-read from L2 once per 4
-// weight rows).  The weight sums are binary64 (e is exact there); each output
-// dot product keeps one FP32 partial per lane (8 activation rows per pass),
-// reduced across the wave in a fixed butterfly.  Per-block partials go to a
-// finisher that adds them in a fixed order: the result does not depend on
-// scheduling.
+// Design for MI355X: the weight is streamed once and the 2 M N K products
+// run on the matrix cores, not the vector ALU.
+//  - One workgroup of 8 waves owns 16 weight rows (grid-stride over such
+//    tiles); wave w takes the w-th eighth of the 128-deep K steps.  Lane
+//    (r, q) = (lane % 16, lane / 16) takes, in run j of a step, row r's K
+//    range [32 j + 8 q, +8) on both operands (the matrix core pairs the same
+//    K positions of both): per load instruction the four lanes of a row read
+//    one contiguous piece (64 bytes of bf16 W, 32 bytes of codes, 64 bytes of
+//    the activation row).
+//  - Each lane forms e = fl32(s dec(q)) - w for its 32 elements.  The weight
+//    sums are binary64 (e exact there).  For the products, e is split
+//    exactly into three bf16 parts (truncate to the top 8 significant bits,
+//    subtract, again): e = e_hi + e_mid + e_lo, so every bf16 x bf16 product
+//    on v_mfma_f32_16x16x32_bf16 is exact and only the FP32 accumulation
+//    rounds.  x W^T uses W's bf16 bits directly (an fp32 W is split the
+//    same way).
+//  - The 8 waves' 16 x 16 partial dot products meet in LDS, summed in wave
+//    order; wave 0 squares and accumulates them in binary64.  Per-block
+//    partials go to a finisher that adds them in a fixed order: the result
+//    does not depend on scheduling.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -41,22 +51,17 @@ namespace fp8rt {
 
 namespace {
 
-constexpr int kLgWaves = 4;
+constexpr int kLgWaves = 8;
 constexpr int kLgThreads = kLgWaves * 64;
-constexpr int kLgM = 8;        // activation rows per pass
-constexpr int kLgR = 4;        // weight rows per wave
 constexpr int kLgMaxBlocks = 4096;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // {sum e^2, sum w^2, max |e|, sum d^2, sum y_ref^2, sum y_q^2, sum y_ref y_q, any NaN e}
 struct LedgerPartial {
   double v[8];
 };
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -70,128 +75,200 @@ __device__ __forceinline__ double wave_max_f64(double v) {
   return v;
 }
 
+// Exact split of a binary32 value into three bf16 bit patterns whose sum is
+// the value: each part keeps the top 8 significant bits of what is left.  A
+// non-finite value goes whole into the first part (NaN stays NaN, +-Inf stays
+// +-Inf).
+__device__ __forceinline__ void split3(float v, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+  float r = v - __uint_as_float(hb);
+  r = (__uint_as_float(hb) == v) ? 0.0f : r;  // exact already, or +-Inf
+  const uint32_t mb = __float_as_uint(r) & 0xFFFF0000u;
+  const float lo = r - __uint_as_float(mb);
+  h = hb >> 16;
+  m = mb >> 16;
+  l = __float_as_uint(lo) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
+
+// 8 weights of one run as floats: bf16 from one 16-byte vector, fp32 from two.
+template <typename WT>
+struct WRun;
+template <>
+struct WRun<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = v[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+template <>
+struct WRun<float> {
+  u32x4 v[2];
+  __device__ __forceinline__ void load(const float* p) {
+    v[0] = *reinterpret_cast<const u32x4*>(p);
+    v[1] = *reinterpret_cast<const u32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { v[0] = v[1] = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ float get(int i) const { return __uint_as_float(v[i >> 2][i & 3]); }
+};
+
 template <typename WT, int F>
-__global__ __launch_bounds__(kLgThreads) void k_quant_error(const WT* __restrict__ W, int64_t ldw,
-                                                            const uint8_t* __restrict__ Q, int64_t ldq, int64_t N,
-                                                            int64_t K, const float* __restrict__ S, int64_t er,
-                                                            int64_t ec, int64_t nc, const uint16_t* __restrict__ X,
-                                                            int64_t M, int64_t ldx,
-                                                            LedgerPartial* __restrict__ part) {
-  __shared__ double red[kLgWaves][8];
+__global__ __launch_bounds__(kLgThreads, 2) void k_quant_error(const WT* __restrict__ W, int64_t ldw,
+                                                               const uint8_t* __restrict__ Q, int64_t ldq, int64_t N,
+                                                               int64_t K, const float* __restrict__ S, int64_t er,
+                                                               int64_t ec, int64_t nc, const uint16_t* __restrict__ X,
+                                                               int64_t M, int64_t ldx,
+                                                               LedgerPartial* __restrict__ part) {
+  __shared__ f32x4 red[kLgWaves][2][64];
+  __shared__ double wred[kLgWaves][8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kLgWaves;
-  double se = 0.0, sw = 0.0, emax = 0.0, sd = 0.0, syr = 0.0, syq = 0.0, syrq = 0.0;
-  uint32_t nan = 0;
-  const int64_t nchunks = (K + 511) / 512;
-  const int npass = X ? static_cast<int>((M + kLgM - 1) / kLgM) : 1;
-  // kLgR weight rows per wave: each activation octet loaded serves all of them
-  for (int64_t n0 = (static_cast<int64_t>(blockIdx.x) * kLgWaves + wave) * kLgR; n0 < N; n0 += nwaves * kLgR) {
-    const WT* wrow[kLgR];
-    const uint8_t* qrow[kLgR];
-    const float* srow[kLgR];
-    bool live[kLgR];
+  const int r = lane & 15, lq = lane >> 4;
+  const int64_t tiles = (N + 15) / 16;
+  const int nk = static_cast<int>((K + 127) / 128);
+  const int s0 = (nk * wave) / kLgWaves, s1 = (nk * (wave + 1)) / kLgWaves;
+  const int64_t mtiles = X ? (M + 15) / 16 : 1;
+  double se2[2] = {0.0, 0.0}, sw2[2] = {0.0, 0.0}, emax2[2] = {0.0, 0.0};
+  double sd = 0.0, syr = 0.0, syq = 0.0, syrq = 0.0;
+
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t n = tile * 16 + r;
+    const bool live = n < N;
+    const int64_t nr = live ? n : N - 1;  // clamped: loads stay in bounds, operands zeroed
+    const WT* wrow = W + nr * ldw;
+    const uint8_t* qrow = Q + nr * ldq;
+    const float* srow = S + (nr / er) * nc;
+    const float s_row = srow[0];  // the only scale of the row when nc == 1
+    for (int64_t mt = 0; mt < mtiles; ++mt) {
+      const bool first = mt == 0;
+      const int64_t m = mt * 16 + r;
+      const bool mlive = X != nullptr && m < M;
+      const uint16_t* xrow = X ? X + (mlive ? m : M - 1) * ldx : nullptr;
+      f32x4 ae = f32x4{0.f, 0.f, 0.f, 0.f}, aw = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = s0; st < s1; ++st) {
 #pragma unroll
-    for (int i = 0; i < kLgR; ++i) {
-      live[i] = n0 + i < N;
-      const int64_t n = live[i] ? n0 + i : N - 1;  // clamped: loads stay in bounds, results unused
-      wrow[i] = W + n * ldw;
-      qrow[i] = Q + n * ldq;
-      srow[i] = S + (n / er) * nc;
-    }
-    for (int p = 0; p < npass; ++p) {
-      float ad[kLgR][kLgM], ay[kLgR][kLgM];
-#pragma unroll
-      for (int i = 0; i < kLgR; ++i)
-#pragma unroll
-        for (int mm = 0; mm < kLgM; ++mm) ad[i][mm] = ay[i][mm] = 0.0f;
-      for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t k0 = c * 512 + 8 * lane;
-        if (k0 >= K) continue;  // K is a multiple of 8: a started octet is whole
-        float e[kLgR][8], wv[kLgR][8];
-#pragma unroll
-        for (int i = 0; i < kLgR; ++i) {
-          Octet<WT> wo;
-          wo.load(wrow[i] + k0);
-          const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow[i] + k0);
-          const float sv = srow[i][k0 / ec];
+        for (int j = 0; j < 4; ++j) {
+          // run j: K [128 st + 32 j + 8 lq, +8); K % 16 == 0, so a run is
+          // wholly inside or wholly past K
+          const int64_t k = static_cast<int64_t>(st) * 128 + 32 * j + 8 * lq;
+          const bool ok = k < K;
+          const int64_t kk = ok ? k : 0;
+          WRun<WT> wr;
+          wr.load(wrow + kk);
+          const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow + kk);
+          u32x4 xv = u32x4{0u, 0u, 0u, 0u};
+          if (X) xv = *reinterpret_cast<const u32x4*>(xrow + kk);
+          const float sv =
+              nc == 1 ? s_row : srow[static_cast<int>(static_cast<uint32_t>(kk) / static_cast<uint32_t>(ec))];
           float dq[8];
           decode4<F>(qv[0], dq);
           decode4<F>(qv[1], dq + 4);
+          const bool use = ok && live;
+          uint32_t eh[8], em[8], el[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float wh = sv * dq[j];  // the dequantization fl32(s dec(q))
-            wv[i][j] = wo.get(j);
-            e[i][j] = wh - wv[i][j];
-            if (p == 0 && live[i]) {
-              const double ed = static_cast<double>(wh) - static_cast<double>(wv[i][j]);  // exact
-              se += ed * ed;
-              sw += static_cast<double>(wv[i][j]) * static_cast<double>(wv[i][j]);
-              nan |= (ed != ed) ? 1u : 0u;
-              emax = fmax(emax, fabs(ed));
+          for (int i = 0; i < 8; ++i) {
+            const float wv = wr.get(i);
+            const float wh = sv * dq[i];  // the dequantization fl32(s dec(q))
+            if (first && use) {  // two independent chains per sum (even / odd i)
+              const double ed = static_cast<double>(wh) - static_cast<double>(wv);  // exact
+              se2[i & 1] += ed * ed;
+              sw2[i & 1] += static_cast<double>(wv) * static_cast<double>(wv);
+              emax2[i & 1] = fmax(emax2[i & 1], fabs(ed));
             }
+            split3(wh - wv, eh[i], em[i], el[i]);
           }
-        }
-        if (X) {
+          if (X) {
+            if (!(mlive && ok)) xv = u32x4{0u, 0u, 0u, 0u};
+            if (!use) {
 #pragma unroll
-          for (int mm = 0; mm < kLgM; ++mm) {
-            const int64_t m = static_cast<int64_t>(p) * kLgM + mm;
-            if (m >= M) break;
-            Octet<uint16_t> xo;
-            xo.load(X + m * ldx + k0);
+              for (int i = 0; i < 8; ++i) eh[i] = em[i] = el[i] = 0u;
+            }
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, xv);
+            const u32x4 ph = u32x4{pack2(eh[0], eh[1]), pack2(eh[2], eh[3]), pack2(eh[4], eh[5]), pack2(eh[6], eh[7])};
+            const u32x4 pm = u32x4{pack2(em[0], em[1]), pack2(em[2], em[3]), pack2(em[4], em[5]), pack2(em[6], em[7])};
+            const u32x4 pl = u32x4{pack2(el[0], el[1]), pack2(el[2], el[3]), pack2(el[4], el[5]), pack2(el[6], el[7])};
+            ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph), xb, ae, 0, 0, 0);
+            ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pm), xb, ae, 0, 0, 0);
+            ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl), xb, ae, 0, 0, 0);
+            if constexpr (sizeof(WT) == 2) {
+              const u32x4 wb = use ? wr.v : u32x4{0u, 0u, 0u, 0u};
+              aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb), xb, aw, 0, 0, 0);
+            } else {
+              uint32_t wh8[8], wm8[8], wl8[8];
 #pragma unroll
-            for (int i = 0; i < kLgR; ++i) {
-              float pd = 0.0f, py = 0.0f;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                pd += xo.get(j) * e[i][j];
-                py += xo.get(j) * wv[i][j];
+              for (int i = 0; i < 8; ++i) {
+                split3(wr.get(i), wh8[i], wm8[i], wl8[i]);
+                if (!use) wh8[i] = wm8[i] = wl8[i] = 0u;
               }
-              ad[i][mm] += pd;
-              ay[i][mm] += py;
+              const u32x4 qh = u32x4{pack2(wh8[0], wh8[1]), pack2(wh8[2], wh8[3]), pack2(wh8[4], wh8[5]),
+                                     pack2(wh8[6], wh8[7])};
+              const u32x4 qm = u32x4{pack2(wm8[0], wm8[1]), pack2(wm8[2], wm8[3]), pack2(wm8[4], wm8[5]),
+                                     pack2(wm8[6], wm8[7])};
+              const u32x4 ql = u32x4{pack2(wl8[0], wl8[1]), pack2(wl8[2], wl8[3]), pack2(wl8[4], wl8[5]),
+                                     pack2(wl8[6], wl8[7])};
+              aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qh), xb, aw, 0, 0, 0);
+              aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qm), xb, aw, 0, 0, 0);
+              aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ql), xb, aw, 0, 0, 0);
             }
           }
         }
       }
       if (X) {
-#pragma unroll
-        for (int i = 0; i < kLgR; ++i)
-#pragma unroll
-          for (int mm = 0; mm < kLgM; ++mm) {
-            const int64_t m = static_cast<int64_t>(p) * kLgM + mm;
-            if (m >= M) break;
-            const double dd = static_cast<double>(wave_sum_f32(ad[i][mm]));
-            const double yr = static_cast<double>(wave_sum_f32(ay[i][mm]));
-            if (lane == 0 && live[i]) {
-              const double yq = yr + dd;
-              sd += dd * dd;
-              syr += yr * yr;
-              syq += yq * yq;
-              syrq += yr * yq;
-            }
+        // the 8 waves' partial dot products, added in wave order by wave 0
+        red[wave][0][lane] = ae;
+        red[wave][1][lane] = aw;
+        __syncthreads();
+        if (wave == 0) {
+          f32x4 de = red[0][0][lane], dy = red[0][1][lane];
+#pragma unroll 1
+          for (int w = 1; w < kLgWaves; ++w) {
+            de += red[w][0][lane];
+            dy += red[w][1][lane];
           }
+          // this lane holds weight rows 16 tile + 4 lq + v of activation row m;
+          // padding entries are left out (0 x Inf would be NaN there)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (!(mlive && tile * 16 + 4 * lq + v < N)) continue;
+            const double dd = static_cast<double>(de[v]);
+            const double yr = static_cast<double>(dy[v]);
+            const double yq = yr + dd;
+            sd += dd * dd;
+            syr += yr * yr;
+            syq += yq * yq;
+            syrq += yr * yq;
+          }
+        }
+        __syncthreads();
       }
     }
   }
-  // lane partials -> wave -> block (fixed orders)
-  se = wave_sum_f64(se);
-  sw = wave_sum_f64(sw);
-  emax = wave_max_f64(emax);
-  nan = wave_max_u32(nan);
+  // lane partials -> wave -> block (fixed orders); a NaN e makes sum e^2 NaN
+  const double se = wave_sum_f64(se2[0] + se2[1]);
+  const double sw = wave_sum_f64(sw2[0] + sw2[1]);
+  const double emax = wave_max_f64(fmax(emax2[0], emax2[1]));
+  sd = wave_sum_f64(sd);
+  syr = wave_sum_f64(syr);
+  syq = wave_sum_f64(syq);
+  syrq = wave_sum_f64(syrq);
   if (lane == 0) {
-    red[wave][0] = se;
-    red[wave][1] = sw;
-    red[wave][2] = emax;
-    red[wave][3] = sd;
-    red[wave][4] = syr;
-    red[wave][5] = syq;
-    red[wave][6] = syrq;
-    red[wave][7] = nan ? 1.0 : 0.0;
+    wred[wave][0] = se;
+    wred[wave][1] = sw;
+    wred[wave][2] = emax;
+    wred[wave][3] = sd;
+    wred[wave][4] = syr;
+    wred[wave][5] = syq;
+    wred[wave][6] = syrq;
+    wred[wave][7] = (se != se) ? 1.0 : 0.0;
   }
   __syncthreads();
   if (threadIdx.x < 8) {
     const int j = threadIdx.x;
-    double a = red[0][j];
-    for (int w = 1; w < kLgWaves; ++w) a = (j == 2 || j == 7) ? fmax(a, red[w][j]) : a + red[w][j];
+    double a = wred[0][j];
+    for (int w = 1; w < kLgWaves; ++w) a = (j == 2 || j == 7) ? fmax(a, wred[w][j]) : a + wred[w][j];
     part[blockIdx.x].v[j] = a;
   }
 }
@@ -223,13 +300,12 @@ __global__ __launch_bounds__(256) void k_ledger_finish(const LedgerPartial* __re
 }  // namespace
 
 size_t quant_error_partials_bytes(int64_t N) {
-  const int64_t nb = std::min<int64_t>((N + kLgWaves * kLgR - 1) / (kLgWaves * kLgR), kLgMaxBlocks);
+  const int64_t nb = std::min<int64_t>((N + 15) / 16, kLgMaxBlocks);
   return static_cast<size_t>(nb) * sizeof(LedgerPartial);
 }
 
 hipError_t launch_quant_error(const QuantErrorArgs& g, void* partials, hipStream_t st) {
-  const int nb = static_cast<int>(
-      std::min<int64_t>((g.N + kLgWaves * kLgR - 1) / (kLgWaves * kLgR), kLgMaxBlocks));
+  const int nb = static_cast<int>(std::min<int64_t>((g.N + 15) / 16, kLgMaxBlocks));
   LedgerPartial* part = static_cast<LedgerPartial*>(partials);
   const int64_t nc = (g.K + g.ec - 1) / g.ec;
 #define FP8RT_QE(WT, F)                                                                                      \

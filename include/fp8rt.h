@@ -299,8 +299,10 @@ fp8rt_status fp8_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t 
  *   stats : device double[7], OVERWRITTEN:
  *     {sum e^2, sum w^2, max |e|, sum d^2, sum y_ref^2, sum y_q^2, sum y_ref y_q}
  *     with w_hat = fl32(s dec(q)) (the dequantization), e = w_hat - w (exact),
- *     y_ref = x W^T, y_q = x W_hat^T, d = y_q - y_ref (FP32 products over
- *     8-element runs, combined in binary64; 3..6 are 0 when x is NULL).
+ *     y_ref = x W^T, y_q = x W_hat^T, d = y_q - y_ref (each dot product an
+ *     FP32 accumulation of exact products: e split exactly into three bf16
+ *     parts on the matrix cores; squares and sums in binary64; 3..6 are 0
+ *     when x is NULL).
  *     NaN propagates (max |e| is NaN when any e is).
  * K a multiple of 16; w and x 16-byte aligned, q and stats 8-byte aligned.
  * Scratch: the per-stream GEMM scratch buffer holds per-block partials. */

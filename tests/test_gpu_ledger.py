@@ -4,11 +4,14 @@ granularity ledger (fp8_granularity_ledger) with the CPU oracle.
 The weight sums (sum e^2, sum w^2) are binary64 sums of N K nonnegative
 terms, added in different orders on the two sides: each within (n - 1) 2^-53
 of the exact sum, so they agree within 2 N K 2^-53 relative; max |e| is
-bit-exact.  The output sums
-use FP32 dot products (8-element runs, a per-lane chain over the K chunks, a
-64-lane butterfly), so each d and y_ref is within
-gamma * sum_k |x e| (resp. |x w|) of the exact value, gamma = (chunks + 16)
-2^-24; the test propagates those bounds to each sum of squares.  Codes and
+bit-exact.  The output sums use FP32 dot products of exact products (the
+binary32 error split exactly into three bf16 parts, bf16 activations, on the
+matrix cores), so each d and y_ref is within gamma * sum_k |x e| (resp.
+|x w|) of the exact value, plus 2^-24 |x e| per term for rounding e to
+binary32; gamma (dot_gamma) follows the kernel's summation: a product passes
+through at most 32 additions inside one matrix-core instruction, the chain of
+its wave's instructions and the 8 wave partials, each addition losing at most
+one ulp.  The test propagates those bounds to each sum of squares.  Codes and
 scales come from the oracle's quantization; the ledger's counters and scale
 counts must equal the oracle's exactly."""
 import numpy as np
@@ -46,6 +49,17 @@ def wdouble(w):
     return bf16_to_f64(w) if w.dtype == np.uint16 else w.astype(np.float64)
 
 
+def dot_gamma(K):
+    """Relative bound of one kernel dot product: 128-deep K steps, 8 waves
+    each taking a contiguous share, 4 eight-element runs per step and at most
+    3 instructions per run (the three parts of the split), so a chain of at
+    most 12 ceil(steps / 8) instructions per wave; at most 32 additions inside
+    one instruction; 8 wave partials added in order; one ulp (2^-23) each."""
+    steps = -(-K // 128)
+    chain = 12 * -(-steps // 8)
+    return (32 + chain + 8) * 2.0 ** -23
+
+
 def bounds(orc, w, q, s, fmt, gran, x):
     """Per-sum tolerances for stats[3..6] from the FP32 summation bound."""
     K = w.shape[1]
@@ -53,7 +67,7 @@ def bounds(orc, w, q, s, fmt, gran, x):
     wd = wdouble(w)
     e = wh - wd
     xd = np.abs(bf16_to_f64(x))
-    gamma = ((K + 511) // 512 + 16) * 2.0 ** -24 * 1.01
+    gamma = dot_gamma(K) * 1.01
     # the FP32 error e32 = fl32(w_hat - w) adds at most 2^-24 |e| per term
     Bd = (gamma + 2.0 ** -24) * (xd @ np.abs(e).T)
     By = gamma * (xd @ np.abs(wd).T)
@@ -80,11 +94,13 @@ def run_quant_error(rt, w, q, s, fmt, gran, x):
 
 
 CASES = [  # (N, K, M, fmt, gran, dtype)
-    (200, 1040, 5, 0, (1, 0), "bf16"),      # K tail inside the third 512 chunk, ragged rows per block
+    (200, 1040, 5, 0, (1, 0), "bf16"),      # K tail inside the ninth step, a ragged last 16-row tile
     (64, 512, 0, 1, (0, 0), "f32"),         # no inputs: weight sums only
-    (128, 2048, 20, 0, (1, 128), "bf16"),   # two activation passes (16 + 4 rows)
+    (128, 2048, 20, 0, (1, 128), "bf16"),   # two activation tiles (16 + 4 rows)
     (256, 1024, 8, 0, (128, 128), "f32"),   # 2-D blocks
     (96, 768, 3, 0, (1, 32), "bf16"),       # 1x32 groups
+    (40, 384, 40, 1, (1, 0), "f32"),        # three activation tiles, fp32 weight split too, 3 K steps for 8 waves
+    (70000, 128, 2, 0, (1, 0), "bf16"),     # 4375 row tiles: more than the 4096 blocks of the grid
 ]
 
 
@@ -102,6 +118,7 @@ def test_quant_error_matches_oracle(rt, orc, case):
         assert not got[3:].any()
     else:
         tol = bounds(orc, w, q, s, fmt, gran, x) + 1e-12 * np.abs(ref[3:])
+        print("error / bound", np.abs(got[3:] - ref[3:]) / tol)
         assert np.all(np.abs(got[3:] - ref[3:]) <= tol), (got[3:] - ref[3:], tol)
 
 
@@ -112,6 +129,21 @@ def test_quant_error_nan(rt, orc):
     w[7, 9] = np.nan
     got = run_quant_error(rt, w, q, s, 0, (1, 0), x)
     assert np.isnan(got[0]) and np.isnan(got[2]) and np.isnan(got[3])
+
+
+@pytest.mark.parametrize("inf", [np.inf, -np.inf])
+def test_quant_error_inf_weight(rt, orc, inf):
+    """An infinite weight under finite codes: e = -+Inf; the sums become Inf
+    or NaN exactly where the oracle's do."""
+    w, x = make(6, 48, 256, 3, "f32")
+    q, s, _, _, _ = orc.quantize(w, 0, (1, 0))
+    w = w.copy()
+    w[7, 9] = inf
+    got = run_quant_error(rt, w, q, s, 0, (1, 0), x)
+    ref = orc.quant_error(w, q, 0, s, (1, 0), x)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.array_equal(np.isinf(got), np.isinf(ref)), (got, ref)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[~fin & ~np.isnan(ref)], ref[~fin & ~np.isnan(ref)])
 
 
 SPECS = [((0, 0), 0), ((1, 0), 0), ((1, 128), 0), ((128, 128), 0), ((1, 32), 1)]
