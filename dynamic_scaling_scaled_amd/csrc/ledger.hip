@@ -19,21 +19,24 @@
 //
 // Design for MI355X: the weight is streamed once and the 2 M N K products
 // run on the matrix cores, not the vector ALU.
-//  - One workgroup of 8 waves owns 16 weight rows (grid-stride over such
-//    tiles); wave w takes the w-th eighth of the 128-deep K steps.  Lane
-//    (r, q) = (lane % 16, lane / 16) takes, in run j of a step, row r's K
-//    range [32 j + 8 q, +8) on both operands (the matrix core pairs the same
-//    K positions of both): per load instruction the four lanes of a row read
-//    one contiguous piece (64 bytes of bf16 W, 32 bytes of codes, 64 bytes of
-//    the activation row).
-//  - Each lane forms e = fl32(s dec(q)) - w for its 32 elements.  The weight
-//    sums are binary64 (e exact there).  For the products, e is split
-//    exactly into three bf16 parts (truncate to the top 8 significant bits,
-//    subtract, again): e = e_hi + e_mid + e_lo, so every bf16 x bf16 product
-//    on v_mfma_f32_16x16x32_bf16 is exact and only the FP32 accumulation
-//    rounds.  x W^T uses W's bf16 bits directly (an fp32 W is split the
-//    same way).
-//  - The 8 waves' 16 x 16 partial dot products meet in LDS, summed in wave
+//  - One workgroup of 4 waves owns 16 weight rows (grid-stride over such
+//    tiles); wave w takes the w-th quarter of the 128-deep K steps.
+//  - Per step a wave reads its 16 x 128 slice row-contiguously: lane l takes
+//    8 elements of row 4 i + l / 16 at K offset 8 (l % 16), so each load
+//    instruction covers whole 128-byte lines of 4 rows (W, 16 bytes a lane)
+//    or 128 contiguous code bytes of each row (8 bytes a lane).  In that
+//    layout it forms e = fl32(s dec(q)) - w and the binary64 weight sums (e
+//    exact there).
+//  - For the products, e (binary32) and W's bits are staged in the wave's own
+//    LDS slice and read back in the matrix-core layout: lane (r, q) =
+//    (lane % 16, lane / 16) takes row r's K [32 j + 8 q, +8) in run j, the
+//    same K positions as its activation row r (read from L2 in that layout).
+//    e is split exactly into three bf16 parts (truncate to the top 8
+//    significant bits, subtract, again): e = e_hi + e_mid + e_lo, so every
+//    bf16 x bf16 product on v_mfma_f32_16x16x32_bf16 is exact and only the
+//    FP32 accumulation rounds.  x W^T uses W's bf16 bits directly (an fp32 W
+//    is split the same way).
+//  - The 4 waves' 16 x 16 partial dot products meet in LDS, summed in wave
 //    order; wave 0 squares and accumulates them in binary64.  Per-block
 //    partials go to a finisher that adds them in a fixed order: the result
 //    does not depend on scheduling.
@@ -51,8 +54,10 @@ namespace fp8rt {
 
 namespace {
 
-constexpr int kLgWaves = 8;
-constexpr int kLgThreads = kLgWaves * 64;
+// waves per 16-row tile: 4 with inputs (each stages a step in LDS), 8 for
+// the weight sums alone (more loads in flight per CU)
+template <bool HAS_X>
+constexpr int lg_waves() { return HAS_X ? 4 : 8; }
 constexpr int kLgMaxBlocks = 4096;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -116,77 +121,160 @@ struct WRun<float> {
   __device__ __forceinline__ float get(int i) const { return __uint_as_float(v[i >> 2][i & 3]); }
 };
 
-template <typename WT, int F>
-__global__ __launch_bounds__(kLgThreads, 2) void k_quant_error(const WT* __restrict__ W, int64_t ldw,
-                                                               const uint8_t* __restrict__ Q, int64_t ldq, int64_t N,
-                                                               int64_t K, const float* __restrict__ S, int64_t er,
-                                                               int64_t ec, int64_t nc, const uint16_t* __restrict__ X,
-                                                               int64_t M, int64_t ldx,
-                                                               LedgerPartial* __restrict__ part) {
+// The loads of one 128-deep step of a lane: 8 weights, 8 codes and a scale
+// of 4 rows (row-contiguous layout), 8 activations of 4 runs (matrix-core
+// layout).
+template <typename WT>
+struct LgStep {
+  WRun<WT> wr[4];
+  u32x2 qv[4];
+  float sv[4];
+};
+
+template <typename WT, int F, bool HAS_X>
+__global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT* __restrict__ W, int64_t ldw,
+                                                            const uint8_t* __restrict__ Q, int64_t ldq, int64_t N,
+                                                            int64_t K, const float* __restrict__ S, int64_t er,
+                                                            int64_t ec, int64_t nc, const uint16_t* __restrict__ X,
+                                                            int64_t M, int64_t ldx,
+                                                            LedgerPartial* __restrict__ part) {
+  // staged e (binary32) and W bits of one step per wave; rows padded so that
+  // the 16 rows of a matrix-core read start 4 banks apart
+  constexpr int kEd = 132;                               // floats per row of e
+  constexpr int kWd = sizeof(WT) == 2 ? 68 : 132;        // dwords per row of W
+  constexpr int kLgWaves = lg_waves<HAS_X>();
+  constexpr int kSl = HAS_X ? kLgWaves : 1;
+  __shared__ float lde[kSl][16][kEd];
+  __shared__ uint32_t ldw_[kSl][16][kWd];
   __shared__ f32x4 red[kLgWaves][2][64];
   __shared__ double wred[kLgWaves][8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, lq = lane >> 4;
+  const int kap = 8 * r;  // row-contiguous layout: K offset of this lane's 8 elements
   const int64_t tiles = (N + 15) / 16;
   const int nk = static_cast<int>((K + 127) / 128);
   const int s0 = (nk * wave) / kLgWaves, s1 = (nk * (wave + 1)) / kLgWaves;
-  const int64_t mtiles = X ? (M + 15) / 16 : 1;
+  const int64_t mtiles = HAS_X ? (M + 15) / 16 : 1;
   double se2[2] = {0.0, 0.0}, sw2[2] = {0.0, 0.0}, emax2[2] = {0.0, 0.0};
   double sd = 0.0, syr = 0.0, syq = 0.0, syrq = 0.0;
 
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t n = tile * 16 + r;
-    const bool live = n < N;
-    const int64_t nr = live ? n : N - 1;  // clamped: loads stay in bounds, operands zeroed
-    const WT* wrow = W + nr * ldw;
-    const uint8_t* qrow = Q + nr * ldq;
-    const float* srow = S + (nr / er) * nc;
-    const float s_row = srow[0];  // the only scale of the row when nc == 1
+    // the 4 rows this lane reads row-contiguously: 4 i + lq
+    const WT* wrow[4];
+    const uint8_t* qrow[4];
+    const float* srow[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = tile * 16 + 4 * i + lq;
+      live[i] = n < N;
+      const int64_t nr = live[i] ? n : N - 1;  // clamped: loads stay in bounds, values zeroed
+      wrow[i] = W + nr * ldw;
+      qrow[i] = Q + nr * ldq;
+      srow[i] = S + (nr / er) * nc;
+    }
     for (int64_t mt = 0; mt < mtiles; ++mt) {
       const bool first = mt == 0;
       const int64_t m = mt * 16 + r;
-      const bool mlive = X != nullptr && m < M;
-      const uint16_t* xrow = X ? X + (mlive ? m : M - 1) * ldx : nullptr;
+      const bool mlive = HAS_X && m < M;
+      const uint16_t* xrow = HAS_X ? X + (mlive ? m : M - 1) * ldx : nullptr;
       f32x4 ae = f32x4{0.f, 0.f, 0.f, 0.f}, aw = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int st = s0; st < s1; ++st) {
+      // K % 16 == 0, so 8 elements are wholly inside or wholly past K (then
+      // they read offset 0 and are zeroed)
+      auto load_x = [&](u32x4 (&xv)[4], int st) {
+        const int64_t kb = static_cast<int64_t>(st) * 128;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // run j: K [128 st + 32 j + 8 lq, +8); K % 16 == 0, so a run is
-          // wholly inside or wholly past K
-          const int64_t k = static_cast<int64_t>(st) * 128 + 32 * j + 8 * lq;
-          const bool ok = k < K;
-          const int64_t kk = ok ? k : 0;
-          WRun<WT> wr;
-          wr.load(wrow + kk);
-          const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow + kk);
-          u32x4 xv = u32x4{0u, 0u, 0u, 0u};
-          if (X) xv = *reinterpret_cast<const u32x4*>(xrow + kk);
-          const float sv =
-              nc == 1 ? s_row : srow[static_cast<int>(static_cast<uint32_t>(kk) / static_cast<uint32_t>(ec))];
-          float dq[8];
-          decode4<F>(qv[0], dq);
-          decode4<F>(qv[1], dq + 4);
-          const bool use = ok && live;
-          uint32_t eh[8], em[8], el[8];
+          const int64_t k = kb + 32 * j + 8 * lq;
+          xv[j] = *reinterpret_cast<const u32x4*>(xrow + (k < K ? k : 0));
+        }
+      };
+      auto load_step = [&](LgStep<WT>& L, int st) {
+        const int64_t kb = static_cast<int64_t>(st) * 128;
+        const int64_t kk = kb + kap < K ? kb + kap : 0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float wv = wr.get(i);
-            const float wh = sv * dq[i];  // the dequantization fl32(s dec(q))
-            if (first && use) {  // two independent chains per sum (even / odd i)
+        for (int i = 0; i < 4; ++i) {
+          L.wr[i].load(wrow[i] + kk);
+          L.qv[i] = *reinterpret_cast<const u32x2*>(qrow[i] + kk);
+        }
+        // kk < K and ec = K for whole-row scales: the group index is 0 there
+        // (computed without a branch, which would split the loads' block)
+        const int sg = static_cast<int>(static_cast<uint32_t>(kk) / static_cast<uint32_t>(ec));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.sv[i] = srow[i][sg];
+      };
+      // weights and codes kDepth steps ahead (2 for the weight sums alone; 1
+      // with inputs, whose registers allow no more), activations (from L2)
+      // one: later steps' loads are in flight during this one's arithmetic
+      // (past the last step the last one is reloaded, unused)
+      constexpr int kDepth = HAS_X ? 1 : 2;
+      LgStep<WT> buf[kDepth + 1];
+      u32x4 xcur[4], xnxt[4];
+      if (s0 < s1) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) load_step(buf[d], min(s0 + d, s1 - 1));
+        if constexpr (HAS_X) load_x(xcur, s0);
+      }
+      for (int st = s0; st < s1; ++st) {
+        load_step(buf[kDepth], min(st + kDepth, s1 - 1));
+        if constexpr (HAS_X) load_x(xnxt, min(st + 1, s1 - 1));
+        const LgStep<WT>& cur = buf[0];
+        const int64_t kb = static_cast<int64_t>(st) * 128;
+        const bool kok = kb + kap < K;
+        bool xok[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xok[j] = mlive && kb + 32 * j + 8 * lq < K;
+        const WRun<WT>(&wr)[4] = cur.wr;
+        const u32x2(&qv)[4] = cur.qv;
+        const float(&sv)[4] = cur.sv;
+        const u32x4(&xv)[4] = xcur;
+        // e and the weight sums, row-contiguous; stage e and W for the products
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool use = kok && live[i];
+          float dq[8], ev[8];
+          decode4<F>(qv[i][0], dq);
+          decode4<F>(qv[i][1], dq + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float wv = wr[i].get(e);
+            const float wh = sv[i] * dq[e];  // the dequantization fl32(s dec(q))
+            if (first && use) {  // two independent chains per sum (even / odd e)
               const double ed = static_cast<double>(wh) - static_cast<double>(wv);  // exact
-              se2[i & 1] += ed * ed;
-              sw2[i & 1] += static_cast<double>(wv) * static_cast<double>(wv);
-              emax2[i & 1] = fmax(emax2[i & 1], fabs(ed));
+              se2[e & 1] += ed * ed;
+              sw2[e & 1] += static_cast<double>(wv) * static_cast<double>(wv);
+              emax2[e & 1] = fmax(emax2[e & 1], fabs(ed));
             }
-            split3(wh - wv, eh[i], em[i], el[i]);
+            ev[e] = use ? wh - wv : 0.0f;
           }
-          if (X) {
-            if (!(mlive && ok)) xv = u32x4{0u, 0u, 0u, 0u};
-            if (!use) {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) eh[i] = em[i] = el[i] = 0u;
+          if constexpr (HAS_X) {
+            const int row = 4 * i + lq;
+            *reinterpret_cast<f32x4*>(&lde[wave][row][kap]) = f32x4{ev[0], ev[1], ev[2], ev[3]};
+            *reinterpret_cast<f32x4*>(&lde[wave][row][kap + 4]) = f32x4{ev[4], ev[5], ev[6], ev[7]};
+            if constexpr (sizeof(WT) == 2) {
+              *reinterpret_cast<u32x4*>(&ldw_[wave][row][kap / 2]) = use ? wr[i].v : u32x4{0u, 0u, 0u, 0u};
+            } else {
+              *reinterpret_cast<u32x4*>(&ldw_[wave][row][kap]) = use ? wr[i].v[0] : u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(&ldw_[wave][row][kap + 4]) = use ? wr[i].v[1] : u32x4{0u, 0u, 0u, 0u};
             }
-            const bf16x8 xb = __builtin_bit_cast(bf16x8, xv);
+          }
+        }
+        if constexpr (HAS_X) {
+          // the wave reads back what its own lanes wrote: LDS operations of a
+          // wave complete in order; the fence keeps the compiler's order too
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kc = 32 * j + 8 * lq;
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(&lde[wave][r][kc]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(&lde[wave][r][kc + 4]);
+            uint32_t eh[8], em[8], el[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              split3(e0[e], eh[e], em[e], el[e]);
+              split3(e1[e], eh[e + 4], em[e + 4], el[e + 4]);
+            }
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, xok[j] ? xv[j] : u32x4{0u, 0u, 0u, 0u});
             const u32x4 ph = u32x4{pack2(eh[0], eh[1]), pack2(eh[2], eh[3]), pack2(eh[4], eh[5]), pack2(eh[6], eh[7])};
             const u32x4 pm = u32x4{pack2(em[0], em[1]), pack2(em[2], em[3]), pack2(em[4], em[5]), pack2(em[6], em[7])};
             const u32x4 pl = u32x4{pack2(el[0], el[1]), pack2(el[2], el[3]), pack2(el[4], el[5]), pack2(el[6], el[7])};
@@ -194,14 +282,16 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_quant_error(const WT* __restr
             ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pm), xb, ae, 0, 0, 0);
             ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl), xb, ae, 0, 0, 0);
             if constexpr (sizeof(WT) == 2) {
-              const u32x4 wb = use ? wr.v : u32x4{0u, 0u, 0u, 0u};
+              const u32x4 wb = *reinterpret_cast<const u32x4*>(&ldw_[wave][r][kc / 2]);
               aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb), xb, aw, 0, 0, 0);
             } else {
+              const u32x4 w0 = *reinterpret_cast<const u32x4*>(&ldw_[wave][r][kc]);
+              const u32x4 w1 = *reinterpret_cast<const u32x4*>(&ldw_[wave][r][kc + 4]);
               uint32_t wh8[8], wm8[8], wl8[8];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                split3(wr.get(i), wh8[i], wm8[i], wl8[i]);
-                if (!use) wh8[i] = wm8[i] = wl8[i] = 0u;
+              for (int e = 0; e < 4; ++e) {
+                split3(__uint_as_float(w0[e]), wh8[e], wm8[e], wl8[e]);
+                split3(__uint_as_float(w1[e]), wh8[e + 4], wm8[e + 4], wl8[e + 4]);
               }
               const u32x4 qh = u32x4{pack2(wh8[0], wh8[1]), pack2(wh8[2], wh8[3]), pack2(wh8[4], wh8[5]),
                                      pack2(wh8[6], wh8[7])};
@@ -214,10 +304,18 @@ __global__ __launch_bounds__(kLgThreads, 2) void k_quant_error(const WT* __restr
               aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ql), xb, aw, 0, 0, 0);
             }
           }
+          // the next step's stores come after these reads (same wave, in order)
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) buf[d] = buf[d + 1];
+        if constexpr (HAS_X) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xcur[j] = xnxt[j];
         }
       }
-      if (X) {
-        // the 8 waves' partial dot products, added in wave order by wave 0
+      if constexpr (HAS_X) {
+        // the 4 waves' partial dot products, added in wave order by wave 0
         red[wave][0][lane] = ae;
         red[wave][1][lane] = aw;
         __syncthreads();
@@ -308,9 +406,17 @@ hipError_t launch_quant_error(const QuantErrorArgs& g, void* partials, hipStream
   const int nb = static_cast<int>(std::min<int64_t>((g.N + 15) / 16, kLgMaxBlocks));
   LedgerPartial* part = static_cast<LedgerPartial*>(partials);
   const int64_t nc = (g.K + g.ec - 1) / g.ec;
-#define FP8RT_QE(WT, F)                                                                                      \
-  hipLaunchKernelGGL((k_quant_error<WT, F>), dim3(nb), dim3(kLgThreads), 0, st, static_cast<const WT*>(g.w), \
-                     g.ldw, g.q, g.ldq, g.N, g.K, g.scale, g.er, g.ec, nc, g.x, g.M, g.ldx, part)
+#define FP8RT_QE(WT, F)                                                                                           \
+  do {                                                                                                            \
+    if (g.x)                                                                                                      \
+      hipLaunchKernelGGL((k_quant_error<WT, F, true>), dim3(nb), dim3(lg_waves<true>() * 64), 0, st,                        \
+                         static_cast<const WT*>(g.w), g.ldw, g.q, g.ldq, g.N, g.K, g.scale, g.er, g.ec, nc, g.x, \
+                         g.M, g.ldx, part);                                                                       \
+    else                                                                                                          \
+      hipLaunchKernelGGL((k_quant_error<WT, F, false>), dim3(nb), dim3(lg_waves<false>() * 64), 0, st,                       \
+                         static_cast<const WT*>(g.w), g.ldw, g.q, g.ldq, g.N, g.K, g.scale, g.er, g.ec, nc, g.x, \
+                         g.M, g.ldx, part);                                                                       \
+  } while (0)
   if (g.wt == FP8RT_BF16) {
     if (g.f == FP8RT_E4M3) FP8RT_QE(uint16_t, kE4M3);
     else FP8RT_QE(uint16_t, kE5M2);

@@ -10,7 +10,7 @@ matrix cores), so each d and y_ref is within gamma * sum_k |x e| (resp.
 |x w|) of the exact value, plus 2^-24 |x e| per term for rounding e to
 binary32; gamma (dot_gamma) follows the kernel's summation: a product passes
 through at most 32 additions inside one matrix-core instruction, the chain of
-its wave's instructions and the 8 wave partials, each addition losing at most
+its wave's instructions and the 4 wave partials, each addition losing at most
 one ulp.  The test propagates those bounds to each sum of squares.  Codes and
 scales come from the oracle's quantization; the ledger's counters and scale
 counts must equal the oracle's exactly."""
@@ -50,14 +50,14 @@ def wdouble(w):
 
 
 def dot_gamma(K):
-    """Relative bound of one kernel dot product: 128-deep K steps, 8 waves
+    """Relative bound of one kernel dot product: 128-deep K steps, 4 waves
     each taking a contiguous share, 4 eight-element runs per step and at most
     3 instructions per run (the three parts of the split), so a chain of at
-    most 12 ceil(steps / 8) instructions per wave; at most 32 additions inside
-    one instruction; 8 wave partials added in order; one ulp (2^-23) each."""
+    most 12 ceil(steps / 4) instructions per wave; at most 32 additions inside
+    one instruction; 4 wave partials added in order; one ulp (2^-23) each."""
     steps = -(-K // 128)
-    chain = 12 * -(-steps // 8)
-    return (32 + chain + 8) * 2.0 ** -23
+    chain = 12 * -(-steps // 4)
+    return (32 + chain + 4) * 2.0 ** -23
 
 
 def bounds(orc, w, q, s, fmt, gran, x):
@@ -99,7 +99,7 @@ CASES = [  # (N, K, M, fmt, gran, dtype)
     (128, 2048, 20, 0, (1, 128), "bf16"),   # two activation tiles (16 + 4 rows)
     (256, 1024, 8, 0, (128, 128), "f32"),   # 2-D blocks
     (96, 768, 3, 0, (1, 32), "bf16"),       # 1x32 groups
-    (40, 384, 40, 1, (1, 0), "f32"),        # three activation tiles, fp32 weight split too, 3 K steps for 8 waves
+    (40, 384, 40, 1, (1, 0), "f32"),        # three activation tiles, fp32 weight split too, 3 K steps for 4 waves
     (70000, 128, 2, 0, (1, 0), "bf16"),     # 4375 row tiles: more than the 4096 blocks of the grid
 ]
 
