@@ -360,7 +360,25 @@ def extra_components(torch, rt, wl):
     e = hbm_entry(time_op(torch, wop, scrub=scrub), wo_bytes, "k_gemm_wonly (packed W)")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_weight_only_gemm_bf16_bias_packed_w"] = e
-    del P
+    # one decode step (per-token quantize of A, then the GEMM on the weight
+    # image: two launches), eager and as a replayed HIP graph, on a stream of
+    # its own that holds the library's workspace before capture
+    gs = torch.cuda.Stream()
+    dstep = lambda: (qa(), gmp())
+    with torch.cuda.stream(gs):
+        dstep()
+    gs.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        dstep()
+    step_bytes = M * K * 3 + M * 4 + g_bytes
+    with torch.cuda.stream(gs):
+        comp["decode_step_packed_eager"] = hbm_entry(time_op(torch, dstep, scrub=scrub), step_bytes,
+                                                     "k_rowgroups + k_gemm_skinny (packed B)")
+        comp["decode_step_packed_hip_graph"] = hbm_entry(time_op(torch, graph.replay, scrub=scrub), step_bytes,
+                                                         "the same two kernels, one graph replay")
+    gs.synchronize()
+    del P, graph
     # granularity ledger: error statistics of the per-channel weight codes
     # against the bf16 weight, with the 16 activation rows
     stats = torch.empty(7, dtype=torch.float64, device=dev)
