@@ -19,8 +19,9 @@
 //
 // Design for MI355X: the weight is streamed once and the 2 M N K products
 // run on the matrix cores, not the vector ALU.
-//  - One workgroup of 4 waves owns 16 weight rows (grid-stride over such
-//    tiles); wave w takes the w-th quarter of the 128-deep K steps.
+//  - One workgroup owns 16 weight rows (grid-stride over such tiles): 4
+//    waves with inputs, 8 for the weight sums alone; wave w takes the w-th
+//    share of the 128-deep K steps.
 //  - Per step a wave reads its 16 x 128 slice row-contiguously: lane l takes
 //    8 elements of row 4 i + l / 16 at K offset 8 (l % 16), so each load
 //    instruction covers whole 128-byte lines of 4 rows (W, 16 bytes a lane)
