@@ -17,26 +17,27 @@
 // and d = y_q - y_ref = x (W_hat - W)^T, with FP32 accumulation of exact
 // products; cosine = <y_ref, y_q> / max(|y_ref| |y_q|, 1e-8).
 //
-// Design for MI355X: the weight is streamed once and the 2 M N K products
-// run on the matrix cores, not the vector ALU.
-//  - One workgroup owns 16 weight rows (grid-stride over such tiles): 4
-//    waves with inputs, 8 for the weight sums alone; wave w takes the w-th
-//    share of the 128-deep K steps.
-//  - Per step a wave reads its 16 x 128 slice row-contiguously: lane l takes
-//    8 elements of row 4 i + l / 16 at K offset 8 (l % 16), so each load
-//    instruction covers whole 128-byte lines of 4 rows (W, 16 bytes a lane)
-//    or 128 contiguous code bytes of each row (8 bytes a lane).  In that
-//    layout it forms e = fl32(s dec(q)) - w and the binary64 weight sums (e
-//    exact there).
-//  - For the products, e (binary32) and W's bits are staged in the wave's own
-//    LDS slice and read back in the matrix-core layout: lane (r, q) =
-//    (lane % 16, lane / 16) takes row r's K [32 j + 8 q, +8) in run j, the
-//    same K positions as its activation row r (read from L2 in that layout).
-//    e is split exactly into three bf16 parts (truncate to the top 8
-//    significant bits, subtract, again): e = e_hi + e_mid + e_lo, so every
-//    bf16 x bf16 product on v_mfma_f32_16x16x32_bf16 is exact and only the
-//    FP32 accumulation rounds.  x W^T uses W's bf16 bits directly (an fp32 W
-//    is split the same way).
+// Design for MI355X: the weight and its codes are streamed once, with
+// nontemporal loads, and the 2 M N K products run on the matrix cores, not
+// the vector ALU.
+//  - One workgroup of 4 waves owns 16 weight rows (grid-stride over such
+//    tiles) and walks K in 512-deep super-steps.  In a super-step wave w
+//    reads rows 4 w .. 4 w + 3 row-contiguously: lane l takes 8 elements at K
+//    offset 8 l, so each load instruction covers 1 KB of one row (bf16 W) or
+//    512 code bytes (whole DRAM bursts of one row; reading 256 bytes from
+//    each of 4 rows per instruction left the L1 stalled on its outstanding
+//    misses at 2.2 TB/s).  In that layout it forms e = fl32(s dec(q)) - w and
+//    the binary64 weight sums (e exact there).
+//  - For the products, e (binary32) and W's bits are staged in LDS for the
+//    block; after a barrier wave w takes the super-step's w-th 128-deep step
+//    in the matrix-core layout: lane (r, q) = (lane % 16, lane / 16) takes
+//    row r's K [32 j + 8 q, +8) in run j, the same K positions as its
+//    activation row r (read from L2 in that layout).  e is split exactly into
+//    three bf16 parts (truncate to the top 8 significant bits, subtract,
+//    again): e = e_hi + e_mid + e_lo, so every bf16 x bf16 product on
+//    v_mfma_f32_16x16x32_bf16 is exact and only the FP32 accumulation
+//    rounds.  x W^T uses W's bf16 bits directly (an fp32 W is split the same
+//    way).
 //  - The 4 waves' 16 x 16 partial dot products meet in LDS, summed in wave
 //    order; wave 0 squares and accumulates them in binary64.  Per-block
 //    partials go to a finisher that adds them in a fixed order: the result
@@ -55,10 +56,8 @@ namespace fp8rt {
 
 namespace {
 
-// waves per 16-row tile: 4 with inputs (each stages a step in LDS), 8 for
-// the weight sums alone (more loads in flight per CU)
-template <bool HAS_X>
-constexpr int lg_waves() { return HAS_X ? 4 : 8; }
+constexpr int kLgWaves = 4;  // waves per 16-row tile
+constexpr int kLgThreads = kLgWaves * 64;
 constexpr int kLgMaxBlocks = 4096;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -104,7 +103,9 @@ struct WRun;
 template <>
 struct WRun<uint16_t> {
   u32x4 v;
-  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ float get(int i) const {
     const uint32_t w = v[i >> 1];
@@ -115,16 +116,16 @@ template <>
 struct WRun<float> {
   u32x4 v[2];
   __device__ __forceinline__ void load(const float* p) {
-    v[0] = *reinterpret_cast<const u32x4*>(p);
-    v[1] = *reinterpret_cast<const u32x4*>(p + 4);
+    v[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
   }
   __device__ __forceinline__ void zero() { v[0] = v[1] = u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ float get(int i) const { return __uint_as_float(v[i >> 2][i & 3]); }
 };
 
-// The loads of one 128-deep step of a lane: 8 weights, 8 codes and a scale
-// of 4 rows (row-contiguous layout), 8 activations of 4 runs (matrix-core
-// layout).
+// The loads of one 512-deep super-step of a lane: 8 weights, 8 codes and a
+// scale of each of its wave's 4 rows; lane l takes K offset 8 l, so one load
+// instruction reads 1 KB (bf16 W) or 512 bytes (codes) of one row.
 template <typename WT>
 struct LgStep {
   WRun<WT> wr[4];
@@ -133,41 +134,40 @@ struct LgStep {
 };
 
 template <typename WT, int F, bool HAS_X>
-__global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(kLgThreads) void k_quant_error(const WT* __restrict__ W, int64_t ldw,
                                                             const uint8_t* __restrict__ Q, int64_t ldq, int64_t N,
                                                             int64_t K, const float* __restrict__ S, int64_t er,
                                                             int64_t ec, int64_t nc, const uint16_t* __restrict__ X,
                                                             int64_t M, int64_t ldx,
                                                             LedgerPartial* __restrict__ part) {
-  // staged e (binary32) and W bits of one step per wave; rows padded so that
-  // the 16 rows of a matrix-core read start 4 banks apart
-  constexpr int kEd = 132;                               // floats per row of e
-  constexpr int kWd = sizeof(WT) == 2 ? 68 : 132;        // dwords per row of W
-  constexpr int kLgWaves = lg_waves<HAS_X>();
-  constexpr int kSl = HAS_X ? kLgWaves : 1;
-  __shared__ float lde[kSl][16][kEd];
-  __shared__ uint32_t ldw_[kSl][16][kWd];
+  constexpr int kSs = 512;  // K per super-step
+  // staged e (binary32) and W bits of a super-step, shared by the block; rows
+  // padded so that the 16 rows of a matrix-core read start 4 banks apart
+  constexpr int kEd = kSs + 4;                                // floats per row of e
+  constexpr int kWd = sizeof(WT) == 2 ? kSs / 2 + 4 : kSs + 4;  // dwords per row of W
+  constexpr int kRows = HAS_X ? 16 : 1;
+  __shared__ __attribute__((aligned(16))) float lde[kRows][kEd];
+  __shared__ __attribute__((aligned(16))) uint32_t ldw_[kRows][kWd];
   __shared__ f32x4 red[kLgWaves][2][64];
   __shared__ double wred[kLgWaves][8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, lq = lane >> 4;
-  const int kap = 8 * r;  // row-contiguous layout: K offset of this lane's 8 elements
+  const int kl = 8 * lane;  // load layout: K offset of this lane's 8 elements in a super-step
   const int64_t tiles = (N + 15) / 16;
-  const int nk = static_cast<int>((K + 127) / 128);
-  const int s0 = (nk * wave) / kLgWaves, s1 = (nk * (wave + 1)) / kLgWaves;
+  const int nss = static_cast<int>((K + kSs - 1) / kSs);
   const int64_t mtiles = HAS_X ? (M + 15) / 16 : 1;
   double se2[2] = {0.0, 0.0}, sw2[2] = {0.0, 0.0}, emax2[2] = {0.0, 0.0};
   double sd = 0.0, syr = 0.0, syq = 0.0, syrq = 0.0;
 
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    // the 4 rows this lane reads row-contiguously: 4 i + lq
+    // the 4 rows this wave loads: 4 wave + i
     const WT* wrow[4];
     const uint8_t* qrow[4];
     const float* srow[4];
     bool live[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t n = tile * 16 + 4 * i + lq;
+      const int64_t n = tile * 16 + 4 * wave + i;
       live[i] = n < N;
       const int64_t nr = live[i] ? n : N - 1;  // clamped: loads stay in bounds, values zeroed
       wrow[i] = W + nr * ldw;
@@ -182,21 +182,13 @@ __global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT
       f32x4 ae = f32x4{0.f, 0.f, 0.f, 0.f}, aw = f32x4{0.f, 0.f, 0.f, 0.f};
       // K % 16 == 0, so 8 elements are wholly inside or wholly past K (then
       // they read offset 0 and are zeroed)
-      auto load_x = [&](u32x4 (&xv)[4], int st) {
-        const int64_t kb = static_cast<int64_t>(st) * 128;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t k = kb + 32 * j + 8 * lq;
-          xv[j] = *reinterpret_cast<const u32x4*>(xrow + (k < K ? k : 0));
-        }
-      };
-      auto load_step = [&](LgStep<WT>& L, int st) {
-        const int64_t kb = static_cast<int64_t>(st) * 128;
-        const int64_t kk = kb + kap < K ? kb + kap : 0;
+      auto load_step = [&](LgStep<WT>& L, int ss) {
+        const int64_t kb = static_cast<int64_t>(ss) * kSs;
+        const int64_t kk = kb + kl < K ? kb + kl : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           L.wr[i].load(wrow[i] + kk);
-          L.qv[i] = *reinterpret_cast<const u32x2*>(qrow[i] + kk);
+          L.qv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(qrow[i] + kk));
         }
         // kk < K and ec = K for whole-row scales: the group index is 0 there
         // (computed without a branch, which would split the loads' block)
@@ -204,42 +196,42 @@ __global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT
 #pragma unroll
         for (int i = 0; i < 4; ++i) L.sv[i] = srow[i][sg];
       };
-      // weights and codes kDepth steps ahead (2 for the weight sums alone; 1
-      // with inputs, whose registers allow no more), activations (from L2)
-      // one: later steps' loads are in flight during this one's arithmetic
-      // (past the last step the last one is reloaded, unused)
+      // this wave's matrix-core step of a super-step: K [128 wave, +128),
+      // run j at 32 j + 8 lq
+      auto load_x = [&](u32x4 (&xv)[4], int ss) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t k = static_cast<int64_t>(ss) * kSs + 128 * wave + 32 * j + 8 * lq;
+          xv[j] = *reinterpret_cast<const u32x4*>(xrow + (k < K ? k : 0));
+        }
+      };
+      // weights and codes kDepth super-steps ahead (2 for the weight sums
+      // alone; 1 with inputs, whose registers allow no more), activations
+      // (from L2) one (past the last super-step the last one is reloaded,
+      // unused)
       constexpr int kDepth = HAS_X ? 1 : 2;
       LgStep<WT> buf[kDepth + 1];
       u32x4 xcur[4], xnxt[4];
-      if (s0 < s1) {
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) load_step(buf[d], min(s0 + d, s1 - 1));
-        if constexpr (HAS_X) load_x(xcur, s0);
-      }
-      for (int st = s0; st < s1; ++st) {
-        load_step(buf[kDepth], min(st + kDepth, s1 - 1));
-        if constexpr (HAS_X) load_x(xnxt, min(st + 1, s1 - 1));
+      for (int d = 0; d < kDepth; ++d) load_step(buf[d], min(d, nss - 1));
+      if constexpr (HAS_X) load_x(xcur, 0);
+      for (int ss = 0; ss < nss; ++ss) {
+        load_step(buf[kDepth], min(ss + kDepth, nss - 1));
+        if constexpr (HAS_X) load_x(xnxt, min(ss + 1, nss - 1));
         const LgStep<WT>& cur = buf[0];
-        const int64_t kb = static_cast<int64_t>(st) * 128;
-        const bool kok = kb + kap < K;
-        bool xok[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xok[j] = mlive && kb + 32 * j + 8 * lq < K;
-        const WRun<WT>(&wr)[4] = cur.wr;
-        const u32x2(&qv)[4] = cur.qv;
-        const float(&sv)[4] = cur.sv;
-        const u32x4(&xv)[4] = xcur;
-        // e and the weight sums, row-contiguous; stage e and W for the products
+        const int64_t kb = static_cast<int64_t>(ss) * kSs;
+        const bool kok = kb + kl < K;
+        // e and the weight sums in the load layout; stage e and W for the products
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool use = kok && live[i];
           float dq[8], ev[8];
-          decode4<F>(qv[i][0], dq);
-          decode4<F>(qv[i][1], dq + 4);
+          decode4<F>(cur.qv[i][0], dq);
+          decode4<F>(cur.qv[i][1], dq + 4);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float wv = wr[i].get(e);
-            const float wh = sv[i] * dq[e];  // the dequantization fl32(s dec(q))
+            const float wv = cur.wr[i].get(e);
+            const float wh = cur.sv[i] * dq[e];  // the dequantization fl32(s dec(q))
             if (first && use) {  // two independent chains per sum (even / odd e)
               const double ed = static_cast<double>(wh) - static_cast<double>(wv);  // exact
               se2[e & 1] += ed * ed;
@@ -249,33 +241,32 @@ __global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT
             ev[e] = use ? wh - wv : 0.0f;
           }
           if constexpr (HAS_X) {
-            const int row = 4 * i + lq;
-            *reinterpret_cast<f32x4*>(&lde[wave][row][kap]) = f32x4{ev[0], ev[1], ev[2], ev[3]};
-            *reinterpret_cast<f32x4*>(&lde[wave][row][kap + 4]) = f32x4{ev[4], ev[5], ev[6], ev[7]};
+            const int row = 4 * wave + i;
+            *reinterpret_cast<f32x4*>(&lde[row][kl]) = f32x4{ev[0], ev[1], ev[2], ev[3]};
+            *reinterpret_cast<f32x4*>(&lde[row][kl + 4]) = f32x4{ev[4], ev[5], ev[6], ev[7]};
             if constexpr (sizeof(WT) == 2) {
-              *reinterpret_cast<u32x4*>(&ldw_[wave][row][kap / 2]) = use ? wr[i].v : u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(&ldw_[row][kl / 2]) = use ? cur.wr[i].v : u32x4{0u, 0u, 0u, 0u};
             } else {
-              *reinterpret_cast<u32x4*>(&ldw_[wave][row][kap]) = use ? wr[i].v[0] : u32x4{0u, 0u, 0u, 0u};
-              *reinterpret_cast<u32x4*>(&ldw_[wave][row][kap + 4]) = use ? wr[i].v[1] : u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(&ldw_[row][kl]) = use ? cur.wr[i].v[0] : u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(&ldw_[row][kl + 4]) = use ? cur.wr[i].v[1] : u32x4{0u, 0u, 0u, 0u};
             }
           }
         }
         if constexpr (HAS_X) {
-          // the wave reads back what its own lanes wrote: LDS operations of a
-          // wave complete in order; the fence keeps the compiler's order too
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __syncthreads();  // the block's 16 rows of the super-step are staged
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int kc = 32 * j + 8 * lq;
-            const f32x4 e0 = *reinterpret_cast<const f32x4*>(&lde[wave][r][kc]);
-            const f32x4 e1 = *reinterpret_cast<const f32x4*>(&lde[wave][r][kc + 4]);
+            const int kc = 128 * wave + 32 * j + 8 * lq;
+            const bool xok = mlive && kb + kc < K;
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(&lde[r][kc]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(&lde[r][kc + 4]);
             uint32_t eh[8], em[8], el[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               split3(e0[e], eh[e], em[e], el[e]);
               split3(e1[e], eh[e + 4], em[e + 4], el[e + 4]);
             }
-            const bf16x8 xb = __builtin_bit_cast(bf16x8, xok[j] ? xv[j] : u32x4{0u, 0u, 0u, 0u});
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, xok ? xcur[j] : u32x4{0u, 0u, 0u, 0u});
             const u32x4 ph = u32x4{pack2(eh[0], eh[1]), pack2(eh[2], eh[3]), pack2(eh[4], eh[5]), pack2(eh[6], eh[7])};
             const u32x4 pm = u32x4{pack2(em[0], em[1]), pack2(em[2], em[3]), pack2(em[4], em[5]), pack2(em[6], em[7])};
             const u32x4 pl = u32x4{pack2(el[0], el[1]), pack2(el[2], el[3]), pack2(el[4], el[5]), pack2(el[6], el[7])};
@@ -283,11 +274,11 @@ __global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT
             ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pm), xb, ae, 0, 0, 0);
             ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl), xb, ae, 0, 0, 0);
             if constexpr (sizeof(WT) == 2) {
-              const u32x4 wb = *reinterpret_cast<const u32x4*>(&ldw_[wave][r][kc / 2]);
+              const u32x4 wb = *reinterpret_cast<const u32x4*>(&ldw_[r][kc / 2]);
               aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb), xb, aw, 0, 0, 0);
             } else {
-              const u32x4 w0 = *reinterpret_cast<const u32x4*>(&ldw_[wave][r][kc]);
-              const u32x4 w1 = *reinterpret_cast<const u32x4*>(&ldw_[wave][r][kc + 4]);
+              const u32x4 w0 = *reinterpret_cast<const u32x4*>(&ldw_[r][kc]);
+              const u32x4 w1 = *reinterpret_cast<const u32x4*>(&ldw_[r][kc + 4]);
               uint32_t wh8[8], wm8[8], wl8[8];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -305,8 +296,7 @@ __global__ __launch_bounds__(lg_waves<HAS_X>() * 64) void k_quant_error(const WT
               aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ql), xb, aw, 0, 0, 0);
             }
           }
-          // the next step's stores come after these reads (same wave, in order)
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __syncthreads();  // every read done before the next super-step's stores
         }
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) buf[d] = buf[d + 1];
@@ -410,11 +400,11 @@ hipError_t launch_quant_error(const QuantErrorArgs& g, void* partials, hipStream
 #define FP8RT_QE(WT, F)                                                                                           \
   do {                                                                                                            \
     if (g.x)                                                                                                      \
-      hipLaunchKernelGGL((k_quant_error<WT, F, true>), dim3(nb), dim3(lg_waves<true>() * 64), 0, st,                        \
+      hipLaunchKernelGGL((k_quant_error<WT, F, true>), dim3(nb), dim3(kLgThreads), 0, st,                        \
                          static_cast<const WT*>(g.w), g.ldw, g.q, g.ldq, g.N, g.K, g.scale, g.er, g.ec, nc, g.x, \
                          g.M, g.ldx, part);                                                                       \
     else                                                                                                          \
-      hipLaunchKernelGGL((k_quant_error<WT, F, false>), dim3(nb), dim3(lg_waves<false>() * 64), 0, st,                       \
+      hipLaunchKernelGGL((k_quant_error<WT, F, false>), dim3(nb), dim3(kLgThreads), 0, st,                       \
                          static_cast<const WT*>(g.w), g.ldw, g.q, g.ldq, g.N, g.K, g.scale, g.er, g.ec, nc, g.x, \
                          g.M, g.ldx, part);                                                                       \
   } while (0)
