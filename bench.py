@@ -307,6 +307,45 @@ def mfma_entry(us, flops, nbytes):
     return e
 
 
+def recipe_staleness(torch, rt, wl):
+    """The delayed-scaling workload's 32-step sequence (spike included) at
+    256 x 8192, quantized to E5M2 under each recipe: current scaling, and
+    delayed scaling from the 16-entry history with the window maximum or the
+    latest amax, with margins.  Per recipe: saturated and underflowed
+    elements over the sequence, steps with any saturation, and the relative
+    error energy sum_t sum e^2 / sum_t sum g^2 of the restored tensors."""
+    dev = "cuda"
+    c = wl.C4Delayed(M=256)
+    gs = [torch.from_numpy(c.make_g(t).view(np.int16)).view(torch.bfloat16).to(dev) for t in range(c.steps)]
+    _, spikes = c.sigmas()
+    M, K = c.M, c.K
+    recipes = [("current", None, 0), ("window_max", rt.HIST_MAX, 0), ("latest", rt.HIST_LATEST, 0),
+               ("window_max_margin1", rt.HIST_MAX, 1), ("window_max_margin2", rt.HIST_MAX, 2)]
+    out = {"workload": "delayed E5M2, %d steps of %dx%d bf16, spike x100 at step(s) %s, history %d"
+                       % (c.steps, M, K, [int(x) for x in spikes], c.history)}
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s, r, am = (torch.empty((1, 1), dtype=torch.float32, device=dev) for _ in range(3))
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    st = torch.empty(7, dtype=torch.float64, device=dev)
+    for name, fn, margin in recipes:
+        hist = torch.zeros(c.history, dtype=torch.float32, device=dev)
+        head = torch.zeros(1, dtype=torch.int32, device=dev)
+        sat = und = sat_steps = 0
+        se = sg = 0.0
+        for t, g in enumerate(gs):
+            mode = rt.DYNAMIC if (fn is None or t == 0) else rt.GIVEN  # step 0: cold start
+            rt.fp8_quantize(g, (0, 0), rt.E5M2, mode, 1e-12, False, s, r, q, am, cnt)
+            rt.fp8_quant_error(g, q, rt.E5M2, (0, 0), s, st)
+            if fn is not None:
+                rt.fp8_delayed_scale_update(hist, head, am, rt.E5M2, fn, margin, 1e-12, False, s, r)
+            cn, sv = cnt.tolist(), st.tolist()
+            sat, und, sat_steps = sat + cn[0], und + cn[1], sat_steps + (cn[0] > 0)
+            se, sg = se + sv[0], sg + sv[1]
+        out[name] = {"saturated": sat, "underflowed": und, "steps_with_saturation": sat_steps,
+                     "relative_error_energy": se / sg}
+    return out
+
+
 def extra_components(torch, rt, wl):
     """Quantize and GEMM kernels of the other workload shapes, each timed alone
     (3 untimed calls, then median and 95th percentile of 20, caches scrubbed
@@ -488,6 +527,7 @@ def main():
     out = bench_prefill(args, torch, rt, wl)
     if not args.no_extra:
         out["components"].update(extra_components(torch, rt, wl))
+        out["delayed_recipe_staleness"] = recipe_staleness(torch, rt, wl)
         fr = [v["frac_hbm"] for k, v in out["components"].items()
               if isinstance(v, dict) and "frac_hbm" in v and "quantize" in k and "decode_quantize_a" not in k]
         out["components"]["quantize_min_frac_hbm_large"] = min(fr)
