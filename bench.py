@@ -428,6 +428,16 @@ def extra_components(torch, rt, wl):
     e = hbm_entry(time_op(torch, le, scrub=scrub), N * K * 3 + N * 4 + M * K * 2, "k_quant_error + k_ledger_finish")
     e["TFLOP_s"] = 4.0 * M * N * K / (e["us"] * 1e-6) / 1e12  # x.e and x.w per (m, n, k)
     comp["ledger_quant_error_w_per_channel_x16"] = e
+    # the ledger itself at this weight: scale metadata against error per granularity
+    specs = [((0, 0), 0), ((1, 0), 0), ((1, 128), 0), ((128, 128), 0), ((1, 32), 1)]
+    rows = rt.fp8_granularity_ledger(W, rt.E4M3, specs, x=A)
+    ledger = {}
+    for r in rows:
+        key = "%dx%d%s" % (r["gran"][0], r["gran"][1], "_pow2" if r["pow2_round_up"] else "")
+        ledger[key] = {k: r[k] for k in ("qparam_count", "qparam_bytes", "total_state_bytes", "weight_mse",
+                                         "weight_max_abs_err", "output_mse", "output_cosine", "saturated",
+                                         "underflowed")}
+    comp["granularity_ledger_decode_w_e4m3"] = ledger
     del A, W, bias, Aq, Wq, y, yw, d, stats
 
     # delayed-scaling backward GEMM, one step: G 8192x8192 E5M2 with the scale of
