@@ -21,6 +21,15 @@ import numpy as np
 BASE_SEED = 42
 
 
+def case_seed(*parts) -> int:
+    """A seed that depends only on the text of ``parts`` (CRC-32 of their repr):
+    the same in every process, unlike ``hash`` of tuples holding ``str`` or
+    ``None``, which Python salts per process."""
+    import zlib
+
+    return zlib.crc32(repr(parts).encode()) & 0x7FFFFFFF
+
+
 def rng(config: int, tensor_id: int) -> np.random.Generator:
     return np.random.Generator(np.random.Philox(key=BASE_SEED + 1000 * config + tensor_id))
 
