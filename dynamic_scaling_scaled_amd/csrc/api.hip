@@ -251,7 +251,9 @@ fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gr
   // Scale granularities the kernels implement.
   const bool a_kblk = g.eca < K, b_kblk = g.ecb < K;
   if (a_kblk && g.era != 1) return FP8RT_EUNSUPPORTED;  // A: tensor, row or {1, g}
-  if (g.eca == 32 && g.ecb == 32 && g.era == 1 && g.erb == 1) {
+  // 1x32 blocks only when both operands are split along K into 32-wide blocks
+  // (at K = 32 a {1, 32} group is the whole row: per-row scales)
+  if (a_kblk && b_kblk && g.eca == 32 && g.ecb == 32 && g.era == 1 && g.erb == 1) {
     if (!(flags & FP8RT_POW2_SCALES)) return FP8RT_EUNSUPPORTED;
     g.pow2_mx = true;
   } else {

@@ -12,19 +12,31 @@
  * Conventions shared by every entry point
  *  - Every array pointer is a caller-owned DEVICE pointer (HBM of the current
  *    HIP device).  The library owns two kinds of device memory, both per
- *    (device, stream) pair and kept until the process ends:
- *      * a workspace of 256 KB that the quantize entry points use for
- *        per-block partial results; it is allocated and zeroed (with a device
- *        synchronization) on the first such call on that pair;
- *      * a GEMM scratch buffer for repacked block scales, used by
- *        fp8_scaled_gemm with 1x32 power-of-two scales ((ceil(M/32) +
- *        ceil(N/32)) * K/128 * 256 bytes) and with 1x128 A groups on large
- *        shapes (ceil(M/256) * 256 * K/128 * 4 bytes).  It grows on demand;
- *        before a smaller buffer is freed the stream is synchronized.
- *    Calls on one stream are ordered and share them; calls on different
- *    streams never do.  Work is enqueued on `stream` and the call returns
- *    without synchronizing (apart from the allocations above); results are
- *    valid once the stream reaches that point.
+ *    (device, stream) pair, allocated (hipMalloc) on first use and kept, at
+ *    the same address, until the process ends; nothing is zeroed and no call
+ *    synchronizes the device or the stream:
+ *      * a workspace of 256 KB for the per-block partial results of the
+ *        quantize kernels and of the FP8-output GEMM;
+ *      * a scratch buffer for the GEMM's repacked 1x32 exponents ((ceil(M/32)
+ *        + ceil(N/32)) * K/128 * 256 bytes) and transposed 1x128 A scales
+ *        (ceil(M/256) * 256 * K/128 * 4 bytes), the FP32 parts of a last wave
+ *        split along K (up to 4 parts x 256 KB per split 256 x 256 tile), the
+ *        cast-transpose's per-group arrays and the ledger's partials.  When a
+ *        call needs more, a larger buffer (at least twice the old) is
+ *        allocated and the old one is KEPT, never freed: every address handed
+ *        to a kernel stays valid for the process's life.
+ *    Calls on one stream are ordered and share that stream's memory; calls on
+ *    different streams never share it.  Work is enqueued on `stream` and the
+ *    call returns without synchronizing; results are valid once the stream
+ *    reaches that point.
+ *  - HIP graph capture: a call that needs no new allocation only enqueues
+ *    kernels and can be captured.  Warm each entry point up eagerly on the
+ *    capture stream with the largest shapes the graph will use (a first call
+ *    or a growth allocates with hipMalloc, which capture may reject: the call
+ *    then returns FP8RT_EHIP and enqueues nothing).  A captured graph holds
+ *    the capture stream's workspace and scratch addresses: replay it on that
+ *    stream, or at least never while other calls on that stream run, since
+ *    they would share the same memory.
  *  - Matrices are row-major with a leading dimension in ELEMENTS (ldx >= cols).
  *  - Arguments are validated on the host before anything is launched; on an
  *    error nothing is written and nothing is enqueued.

@@ -163,3 +163,15 @@ def test_gemm_split_last_wave(rt, orc, fa, grans, out):
     ok, st = check_gemm(y[m, n], yref, S, out == "bf16", orc, t_hw=thw, bias=bias_f)
     print("split", fa, grans, out, st)
     assert ok, st
+
+
+def test_k32_per_row_scales_are_not_mx_blocks(rt, orc):
+    """At K = 32 a {1, 32} group is the whole row: per-token x per-channel
+    scales, accepted without the power-of-two flag and computed as per-row."""
+    M, N, K = 40, 72, 32
+    a, sa, b, sb = operands(orc, 21, M, N, K, 0, 0, (1, 0), (1, 0), False)
+    y = run_gemm(rt, a, 0, (1, 32), sa, b, 0, (1, 32), sb, "f32")
+    yref, S = orc.gemm_full(a, 0, sa, (1, 0), b, 0, sb, (1, 0))
+    thw = orc.dot_truncation_bound_full(a, 0, sa, (1, 0), b, 0, sb, (1, 0))
+    ok, st = check_gemm(y, yref, S, False, orc, t_hw=thw)
+    assert ok, st
