@@ -28,7 +28,8 @@ POW2_SCALES = 1
 B_PACKED16 = 2
 FMAX = {E4M3: 448.0, E5M2: 57344.0}
 
-OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, ESCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Fp8rtError(RuntimeError):
@@ -84,6 +85,8 @@ def lib():
         L.fp8_scaled_gemm.restype = C.c_int
         L.fp8_scaled_gemm.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                       I64, P, C.c_int, P, C.c_int, I64, U32, P]
+        L.fp8_scaled_gemm_noalloc.restype = C.c_int
+        L.fp8_scaled_gemm_noalloc.argtypes = L.fp8_scaled_gemm.argtypes
         L.fp8_quant_error.restype = C.c_int
         L.fp8_quant_error.argtypes = [P, C.c_int, I64, I64, I64, P, C.c_int, I64, Gran, P, P, I64, I64, P, P]
         L.fp8_granularity_ledger.restype = C.c_int
@@ -239,6 +242,20 @@ def fp8_scaled_gemm(a, fa, ga, scale_a, b, fb, gb, scale_b, y, bias=None, flags=
            lib().fp8_scaled_gemm(_ptr(a), fa, lda, Gran(*ga), _ptr(scale_a), _ptr(b), fb, ldb,
                                  Gran(*gb), _ptr(scale_b), M, N, K, _ptr(bias), bias_t, _ptr(y),
                                  _dtype(y), ldy, flags, _stream(stream)))
+
+
+def fp8_scaled_gemm_noalloc(a, fa, ga, scale_a, b, fb, gb, scale_b, y, bias=None, flags=0, stream=None):
+    """fp8_scaled_gemm on the library's fixed device scratch: allocates nothing."""
+    M, K, lda = _mat(a)
+    N, K2, ldb, flags = _weight(b, flags)
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    _, _, ldy = _mat(y)
+    bias_t = _dtype(bias) if bias is not None else F32
+    _check("fp8_scaled_gemm_noalloc",
+           lib().fp8_scaled_gemm_noalloc(_ptr(a), fa, lda, Gran(*ga), _ptr(scale_a), _ptr(b), fb, ldb,
+                                         Gran(*gb), _ptr(scale_b), M, N, K, _ptr(bias), bias_t, _ptr(y),
+                                         _dtype(y), ldy, flags, _stream(stream)))
 
 
 def raw_call(name: str, *args) -> int:

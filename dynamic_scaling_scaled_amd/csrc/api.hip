@@ -49,6 +49,7 @@ const char* fp8rt_status_string(fp8rt_status s) {
     case FP8RT_EALIGN: return "misaligned size, leading dimension or pointer (16 required)";
     case FP8RT_EUNSUPPORTED: return "unsupported format or scale-granularity combination";
     case FP8RT_EHIP: return "HIP launch error";
+    case FP8RT_ESCRATCH: return "the call needs more scratch than the allocation-free entry point's fixed 16 MiB";
   }
   return "unknown status";
 }
@@ -284,6 +285,29 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
     return FP8RT_EALIGN;
   g.y = y;
   g.yt = yt;
+  return from_hip(launch_gemm(g, stream));
+}
+
+fp8rt_status fp8_scaled_gemm_noalloc(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                                     const float* scale_a, const uint8_t* b, fp8rt_format fb,
+                                     int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
+                                     int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
+                                     void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
+                                     hipStream_t stream) {
+  if (!y || !valid_dtype(yt)) return FP8RT_EINVAL;
+  GemmArgs g{};
+  const fp8rt_status st =
+      gemm_setup(a, fa, lda, ga, scale_a, b, fb, ldb, gb, scale_b, M, N, K, bias, bias_t, ldy, flags, g);
+  if (st != FP8RT_OK) return st;
+  if ((yt == FP8RT_F32 && !aligned4(y)) || (yt == FP8RT_BF16 && (reinterpret_cast<uintptr_t>(y) & 1u)))
+    return FP8RT_EALIGN;
+  g.y = y;
+  g.yt = yt;
+  if (gemm_required_scratch(g) > kNoAllocScratchBytes) return FP8RT_ESCRATCH;
+  void* p = nullptr;
+  if (noalloc_scratch(&p) != hipSuccess) return FP8RT_EHIP;
+  g.fixed_scratch = p;
+  g.fixed_scratch_bytes = kNoAllocScratchBytes;
   return from_hip(launch_gemm(g, stream));
 }
 

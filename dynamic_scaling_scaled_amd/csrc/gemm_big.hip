@@ -597,6 +597,12 @@ bool gemm_big_eligible(const GemmArgs& g) {
          g.N >= 128 && g.lda < (int64_t(1) << 23) && g.ldb < (int64_t(1) << 23);
 }
 
+size_t gemm_big_required_scratch(const GemmArgs& g) {
+  if (!g.pow2_mx) return 0;
+  const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
+  return static_cast<size_t>((ga + gb) * ns * 64) * 4;  // E8M0 exponent dwords
+}
+
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
   const int tiles_m = static_cast<int>((g.M + TM - 1) / TM);
   const int tiles_n = static_cast<int>((g.N + TN - 1) / TN);
@@ -618,11 +624,14 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
     // FP8 output: one statistics slot per whole tile and per reduce block
     const bool slots_ok = okind < kOutE4M3 || (T - rem) + rem * kRedBlocks <= kMaxBlocks;
     if (!g.pow2_mx && slots_ok && T > cus && rem > 0 && 2 * rem <= cus) {
+      const size_t part_bytes = static_cast<size_t>(rem) * TM * TN * sizeof(float);  // per K part
       int sp = std::min(cus / rem, 4);
+      if (g.fixed_scratch)  // a fixed buffer: as many parts as fit
+        sp = static_cast<int>(std::min<size_t>(sp, g.fixed_scratch_bytes / part_bytes));
       while (sp > 1 && ns % (2 * sp) != 0) --sp;  // every part an even number of stages
       if (sp > 1) {
         void* p = nullptr;
-        hipError_t e = get_scratch(st, static_cast<size_t>(rem) * sp * TM * TN * sizeof(float), &p);
+        hipError_t e = gemm_scratch(g, st, part_bytes * sp, &p);
         if (e != hipSuccess) return e;
         part = static_cast<float*>(p);
         split = sp;
@@ -637,7 +646,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
   if (g.pow2_mx) {
     const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
     void* p = nullptr;
-    hipError_t e = get_scratch(st, static_cast<size_t>((ga + gb) * ns * 64) * 4, &p);
+    hipError_t e = gemm_scratch(g, st, gemm_big_required_scratch(g), &p);
     if (e != hipSuccess) return e;
     xpa = static_cast<uint32_t*>(p);
     xpb = xpa + ga * ns * 64;

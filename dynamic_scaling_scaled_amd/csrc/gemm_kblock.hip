@@ -317,6 +317,12 @@ bool gemm_kblock_eligible(const GemmArgs& g) {
   return true;
 }
 
+size_t gemm_kblock_required_scratch(const GemmArgs& g) {
+  if (!(g.eca < g.K)) return 0;
+  const int64_t Mp = (g.M + TM - 1) / TM * static_cast<int64_t>(TM);
+  return static_cast<size_t>(Mp * (g.K / TKS)) * sizeof(float);  // A's group scales, transposed
+}
+
 hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = static_cast<int>((g.M + TM - 1) / TM);
   const int tiles_n = static_cast<int>((g.N + TN - 1) / TN);
@@ -328,7 +334,7 @@ hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t st) {
   const int64_t Mp = tiles_m * static_cast<int64_t>(TM);  // rows padded to whole tiles
   if (a_kb) {
     void* p = nullptr;
-    hipError_t e = get_scratch(st, static_cast<size_t>(Mp * ns) * sizeof(float), &p);
+    hipError_t e = gemm_scratch(g, st, gemm_kblock_required_scratch(g), &p);
     if (e != hipSuccess) return e;
     sat = static_cast<float*>(p);
     hipLaunchKernelGGL(k_transpose_scales,

@@ -260,6 +260,21 @@ static hipError_t launch_generic(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t gemm_scratch(const GemmArgs& g, hipStream_t st, size_t bytes, void** ptr) {
+  if (!g.fixed_scratch) return get_scratch(st, bytes, ptr);
+  if (bytes > g.fixed_scratch_bytes) return hipErrorInvalidValue;  // checked by the caller first
+  *ptr = g.fixed_scratch;
+  return hipSuccess;
+}
+
+size_t gemm_required_scratch(const GemmArgs& g) {
+  // the same order of choice as launch_gemm (BF16 / FP32 output)
+  if (gemm_skinny_eligible(g)) return 0;
+  if (gemm_big_eligible(g)) return gemm_big_required_scratch(g);
+  if (gemm_kblock_eligible(g)) return gemm_kblock_required_scratch(g);
+  return 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.yq_fmt >= 0) {
     // FP8 output: the large kernel or the general one, then the partials of

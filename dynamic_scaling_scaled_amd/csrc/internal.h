@@ -108,7 +108,28 @@ struct GemmArgs {
   float* amax_y = nullptr;
   unsigned long long* counts_y = nullptr;
   BlockPartial* part = nullptr;
+  // When set, the GEMM's scratch comes from this fixed buffer instead of the
+  // stream's growable one (the allocation-free entry point): scale repacks
+  // must fit (gemm_required_scratch), a split last wave takes fewer K parts,
+  // or none, to fit.
+  void* fixed_scratch = nullptr;
+  size_t fixed_scratch_bytes = 0;
 };
+
+// Scratch for a GEMM call: the fixed buffer when g has one (an error if it is
+// smaller than `bytes`), else the stream's buffer (get_scratch).
+hipError_t gemm_scratch(const GemmArgs& g, hipStream_t stream, size_t bytes, void** ptr);
+// Bytes of scratch the kernel that launch_gemm picks for g cannot do without
+// (the repacked 1x32 exponents, the transposed 1x128 A scales); the FP32
+// parts of a split last wave are optional and not counted.
+size_t gemm_required_scratch(const GemmArgs& g);
+size_t gemm_big_required_scratch(const GemmArgs& g);
+size_t gemm_kblock_required_scratch(const GemmArgs& g);
+
+// The allocation-free GEMM's scratch: a fixed device array of the library
+// (noalloc.hip) of kNoAllocScratchBytes; its address on the current device.
+constexpr size_t kNoAllocScratchBytes = FP8RT_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 // Output kinds of the GEMM kernels' epilogues.
 constexpr int kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2, kOutE5M2 = 3;

@@ -70,7 +70,9 @@ typedef enum fp8rt_status {
                                of 16, or a base pointer not 16-byte aligned ([P2 "Hardware
                                support ..." notes dims divisible by 16 for FP8 linears) */
     FP8RT_EUNSUPPORTED = 3, /* GEMM format pair / scale-granularity combination not built */
-    FP8RT_EHIP = 4          /* a HIP launch error */
+    FP8RT_EHIP = 4,         /* a HIP launch error */
+    FP8RT_ESCRATCH = 5      /* fp8_scaled_gemm_noalloc: the shape needs more scratch than its
+                               fixed buffer (FP8RT_NOALLOC_SCRATCH_BYTES) */
 } fp8rt_status;
 
 /* [P2 "How the 8 bits are allocated"]: E4M3 max finite 448, E5M2 max finite
@@ -225,6 +227,36 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
                              int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
                              void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
                              hipStream_t stream);
+
+/* fp8_scaled_gemm for callers that cannot allocate device memory: code
+ * under HIP graph capture that has not warmed the library up on its stream,
+ * tight serving loops, and harnesses that forbid hipMalloc.  Arguments,
+ * results, validation and statuses are those of fp8_scaled_gemm, with one
+ * difference in where the scratch comes from: this entry point never calls
+ * hipMalloc / hipFree or any allocating routine.  Its scratch is a fixed
+ * device array of the library, FP8RT_NOALLOC_SCRATCH_BYTES (16 MiB) on each
+ * GPU, reserved when the library's code is loaded onto that GPU and kept
+ * until the process ends; its address is looked up on the first call on each
+ * device.
+ *  - A call whose kernel needs more scratch than that (repacked 1x32
+ *    exponents: (ceil(M/32) + ceil(N/32)) * K/128 * 256 bytes; transposed
+ *    1x128 A scales on large shapes: ceil(M/256) * 256 * K/128 * 4 bytes)
+ *    returns FP8RT_ESCRATCH before anything is enqueued.
+ *  - A ragged last wave of tiles is split along K into as many parts as fit
+ *    (256 KB per part and 256 x 256 tile), or not at all; the result can then
+ *    differ from fp8_scaled_gemm's in FP32 summation order only, within the
+ *    same tolerance.
+ *  - Every call on a GPU shares that GPU's one array (whatever the stream),
+ *    and the array keeps the last call's contents (nothing in it needs to
+ *    start at zero): calls that overlap in time on one GPU race and give
+ *    undefined results.  Order them on one stream, or synchronize. */
+#define FP8RT_NOALLOC_SCRATCH_BYTES (16u << 20)
+fp8rt_status fp8_scaled_gemm_noalloc(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
+                                     const float* scale_a, const uint8_t* b, fp8rt_format fb,
+                                     int64_t ldb, fp8rt_gran gb, const float* scale_b, int64_t M,
+                                     int64_t N, int64_t K, const void* bias, fp8rt_dtype bias_t,
+                                     void* y, fp8rt_dtype yt, int64_t ldy, uint32_t flags,
+                                     hipStream_t stream);
 
 /* Scaled GEMM with an FP8 output [P2 "The full precision contract of one FP8
  * GEMM": the contract names the output scale / requantization when the next

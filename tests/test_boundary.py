@@ -105,17 +105,19 @@ def test_amax_scale_dequant_history_validation(rt):
     assert L.fp8_amax_history_update(FAKE + 2, 16, FAKE, FAKE, 0, 1e-12, 0, FAKE, None, None) == rt.EALIGN
 
 
-def g(rt, **kw):
+def g(rt, fn="fp8_scaled_gemm", **kw):
     a = dict(a=FAKE, fa=rt.E4M3, lda=128, ga=(0, 0), sa=FAKE, b=FAKE, fb=rt.E4M3, ldb=128, gb=(0, 0),
              sb=FAKE, M=64, N=64, K=128, bias=None, bt=0, y=FAKE, yt=rt.BF16, ldy=64, flags=0)
     a.update(kw)
-    return rt.lib().fp8_scaled_gemm(a["a"], a["fa"], a["lda"], rt.Gran(*a["ga"]), a["sa"], a["b"],
+    return getattr(rt.lib(), fn)(a["a"], a["fa"], a["lda"], rt.Gran(*a["ga"]), a["sa"], a["b"],
                                     a["fb"], a["ldb"], rt.Gran(*a["gb"]), a["sb"], a["M"], a["N"],
                                     a["K"], a["bias"], a["bt"], a["y"], a["yt"], a["ldy"],
                                     a["flags"], None)
 
 
-def test_gemm_validation(rt):
+@pytest.mark.parametrize("fn", ["fp8_scaled_gemm", "fp8_scaled_gemm_noalloc"])
+def test_gemm_validation(rt, fn):
+    g = lambda rt, **kw: globals()["g"](rt, fn, **kw)
     assert g(rt, a=None) == rt.EINVAL
     assert g(rt, sb=None) == rt.EINVAL
     assert g(rt, y=None) == rt.EINVAL
@@ -298,3 +300,16 @@ def test_quant_error_and_ledger_validation(rt):
     assert led(eps=float("nan")) == rt.EINVAL
     assert led(K=40, ldw=40) == rt.EALIGN
     assert C.sizeof(rt.LedgerRow) == 96 and C.sizeof(rt.LedgerSpec) == 12
+
+
+def test_gemm_noalloc_refuses_shapes_beyond_its_scratch(rt):
+    """The allocation-free GEMM checks its fixed scratch (16 MiB) on the host:
+    1x32 exponent tables of (ceil(M/32) + ceil(N/32)) * K/128 * 256 bytes fit
+    at M = N = 16384, K = 8192 (exactly 16 MiB) and not at N = 16416."""
+    big = dict(M=16384, K=8192, lda=8192, ldb=8192, ga=(1, 32), gb=(1, 32), flags=rt.POW2_SCALES)
+    assert g(rt, "fp8_scaled_gemm_noalloc", N=16416, ldy=16416, **big) == rt.ESCRATCH
+    # 128 x 128 B blocks with 1x128 A groups on a large shape: ceil(M/256)*256 * K/128 * 4 bytes
+    assert g(rt, "fp8_scaled_gemm_noalloc", M=65536 * 2, N=256, K=65536 // 2, lda=32768, ldb=32768,
+             ldy=256, ga=(1, 128), gb=(128, 128)) == rt.ESCRATCH
+    assert rt.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert b"16 MiB" in rt.lib().fp8rt_status_string(rt.ESCRATCH)
