@@ -89,49 +89,265 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
 
+def host_cpu():
+    """CPU model and the logical CPUs this process may run on (capped at 16,
+    the host share of one GPU on a shared node)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return model, avail, max(1, min(16, avail))
+
+
+def pick(n, k, seed):
+    return np.sort(np.random.default_rng(seed).choice(n, size=min(k, n), replace=False))
+
+
+def gather(torch, t, rows, cols=None):
+    """Host copy of t[rows][:, cols] (or whole rows)."""
+    r = torch.as_tensor(rows, device=t.device, dtype=torch.long)
+    v = t.index_select(0, r)
+    if cols is not None:
+        v = v.index_select(1, torch.as_tensor(cols, device=t.device, dtype=torch.long))
+    v = v.cpu()
+    if v.dtype == torch.bfloat16:
+        return v.view(torch.int16).numpy().view(np.uint16)
+    return v.numpy()
+
+
+def oracle_prefill_sample(oracle, x_bits, w_bits, M, N, K, budget_s, threads, plan=None):
+    """One sample of the prefill step on the oracle, on `threads` host threads
+    (the oracle's C calls run without the GIL, each on its own row range or
+    point batch): the full amax of X, the cast of a sample of X rows under the
+    resulting scale, and GEMM dot products between those rows and a sample of
+    W rows.  With plan=None the sample grows until budget_s seconds (a quarter
+    for the cast, the rest for the GEMM); otherwise the same amounts as plan.
+    Returns (seconds for amax, rows cast, cast seconds, dot products, GEMM
+    seconds, the amounts as a plan)."""
+    import concurrent.futures as cf
+
+    g = np.random.default_rng(7)
+    w_rows = np.sort(g.choice(N, size=256, replace=False))
+    s_w, _ = oracle.compute_scale(oracle.amax(w_bits), oracle.E4M3)  # untimed setup
+    wq, _, _, _, _ = oracle.quantize(np.ascontiguousarray(w_bits[w_rows]), oracle.E4M3, (0, 0),
+                                     mode=oracle.GIVEN, scale=s_w)
+    ex = cf.ThreadPoolExecutor(threads)
+    bounds = np.linspace(0, M, threads + 1).astype(int)
+    t0 = time.perf_counter()
+    parts = list(ex.map(lambda i: oracle.amax(x_bits[bounds[i]:bounds[i + 1]]), range(threads)))
+    a_x = np.max(np.array(parts, np.float32))
+    s_x, r_x = oracle.compute_scale(np.array([[a_x]], np.float32), oracle.E4M3)
+    t_amax = time.perf_counter() - t0
+    chunk = 64
+
+    def cast(r0):
+        return oracle.quantize(np.ascontiguousarray(x_bits[r0:r0 + chunk]), oracle.E4M3, (0, 0),
+                               mode=oracle.GIVEN, scale=s_x, inv_scale=r_x)[0]
+
+    rows_done, tq, xq = 0, 0.0, []
+    while (rows_done < plan[0] if plan else tq < budget_s * 0.25) and rows_done + chunk * threads <= M:
+        t0 = time.perf_counter()
+        xq += list(ex.map(cast, range(rows_done, rows_done + chunk * threads, chunk)))
+        tq += time.perf_counter() - t0
+        rows_done += chunk * threads
+    xq = np.concatenate(xq)
+    npts, tg, batch = 0, 0.0, 256
+
+    def dots(seed):
+        gi = np.random.default_rng(seed)
+        m, n = gi.integers(0, xq.shape[0], batch), gi.integers(0, wq.shape[0], batch)
+        oracle.gemm_points(xq, oracle.E4M3, s_x, (0, 0), wq, oracle.E4M3, s_w, (0, 0), m, n)
+
+    while npts < plan[1] if plan else tg < budget_s * 0.75:
+        t0 = time.perf_counter()
+        list(ex.map(dots, range(npts, npts + batch * threads, batch)))
+        tg += time.perf_counter() - t0
+        npts += batch * threads
+    ex.shutdown()
+    return t_amax, rows_done, tq, npts, tg, (rows_done, npts)
+
+
 def cpu_baseline_prefill(x_bits, w_bits, M, N, K, budget_s):
-    """The oracle as it stands, single-threaded, on a bounded sample of the
-    same workload, extrapolated to one full step (TFLOP/s of the step).  All
-    oracle inputs come from the seeded generators and the oracle itself."""
+    """The oracle as it stands (never tuned for speed) on a bounded sample of
+    the prefill step, extrapolated to one full step (TFLOP/s of the step):
+    first on one thread with about budget_s seconds of work, then the same
+    sample on all the host threads this process may use.  All oracle inputs
+    come from the seeded generators and the oracle itself."""
     import oracle
 
     oracle.build(force=False)
-    # untimed setup: static weight scale and the codes of a sample of W rows
-    g = np.random.default_rng(7)
-    w_rows = np.sort(g.choice(N, size=256, replace=False))
-    s_w, _ = oracle.compute_scale(oracle.amax(w_bits), oracle.E4M3)
-    wq, _, _, _, _ = oracle.quantize(np.ascontiguousarray(w_bits[w_rows]), oracle.E4M3, (0, 0),
-                                     mode=oracle.GIVEN, scale=s_w)
-    # timed: full amax of X, then the cast of a sample of rows
-    t0 = time.perf_counter()
-    oracle.amax(x_bits)
-    t_amax = time.perf_counter() - t0
-    rows_done, tq, chunk = 0, 0.0, 64
-    while tq < budget_s * 0.25 and rows_done + chunk <= M:
-        t0 = time.perf_counter()
-        xq, s_x, _, _, _ = oracle.quantize(np.ascontiguousarray(x_bits[rows_done:rows_done + chunk]),
-                                           oracle.E4M3, (0, 0))
-        tq += time.perf_counter() - t0
-        rows_done += chunk
-    quant_full_s = t_amax + tq * (M / rows_done)
-    npts, tg = 0, 0.0
-    while tg < budget_s * 0.75:
-        m = g.integers(0, xq.shape[0], 256)
-        n = g.integers(0, wq.shape[0], 256)
-        t0 = time.perf_counter()
-        oracle.gemm_points(xq, oracle.E4M3, s_x, (0, 0), wq, oracle.E4M3, s_w, (0, 0), m, n)
-        tg += time.perf_counter() - t0
-        npts += 256
-    gemm_full_s = tg / npts * M * N
-    step_s = quant_full_s + gemm_full_s
-    return {"value": 2.0 * M * N * K / step_s / 1e12, "unit": "TFLOP/s", "cores": 1,
-            "kind": "oracle",
-            "sample": ("oracle amax of all of X (%.2f s), cast of %d of %d X rows (%.2f s) and %d "
-                       "GEMM dot products of K=%d (%.2f s), extrapolated to one full step: %.1f s"
-                       % (t_amax, rows_done, M, tq, npts, K, tg, step_s))}
+    model, avail, threads = host_cpu()
+    res = {}
+    plan = None
+    for nt in (1, threads):
+        t_amax, rows, tq, npts, tg, plan = oracle_prefill_sample(oracle, x_bits, w_bits, M, N, K, budget_s,
+                                                                 nt, plan)
+        step_s = t_amax + tq * (M / rows) + tg / npts * M * N
+        res[nt] = {"value": 2.0 * M * N * K / step_s / 1e12, "unit": "TFLOP/s", "cores": nt,
+                   "kind": "oracle",
+                   "sample": ("oracle on %d thread(s): amax of all of X (%.2f s), cast of %d of %d X rows "
+                              "(%.2f s), %d GEMM dot products of K=%d (%.2f s); extrapolated to one full "
+                              "step: %.1f s" % (nt, t_amax, rows, M, tq, npts, K, tg, step_s))}
+    out = dict(res[threads])
+    out["cpu_model"] = model
+    out["logical_cpus_available"] = avail
+    out["single_thread"] = res[1]
+    return out
 
 
-def bench_prefill(args, torch, rt, wl):
+def _pool_map(threads, fn, items):
+    import concurrent.futures as cf
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, items))
+
+
+def _row_chunks(rows, threads):
+    b = np.linspace(0, rows, threads * 4 + 1).astype(int)
+    return [(b[i], b[i + 1]) for i in range(len(b) - 1) if b[i + 1] > b[i]]
+
+
+def oracle_tensor_scale(oracle, x, fmt, threads):
+    """Per-tensor amax (exact: max of row-range maxima) and (s, r) of x."""
+    parts = _pool_map(threads, lambda r: oracle.amax(x[r[0]:r[1]]), _row_chunks(x.shape[0], threads))
+    a = np.max(np.array(parts, np.float32)).reshape(1, 1)
+    s, r = oracle.compute_scale(a, fmt)
+    return a, s, r
+
+
+def oracle_given_counts(oracle, x, fmt, s, r, threads):
+    """Saturation / underflow counts of the GIVEN-mode cast of all of x (row
+    ranges on threads; the counts add up exactly)."""
+    parts = _pool_map(threads, lambda rr: oracle.quantize(np.ascontiguousarray(x[rr[0]:rr[1]]), fmt, (0, 0),
+                                                          mode=oracle.GIVEN, scale=s, inv_scale=r)[4],
+                      _row_chunks(x.shape[0], threads))
+    return np.sum(np.array(parts, np.uint64), axis=0)
+
+
+def _same(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    if a.shape != b.shape:
+        return False
+    if a.dtype == np.float32 or b.dtype == np.float32:
+        a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+        na, nb = np.isnan(a), np.isnan(b)
+        return bool(np.array_equal(na, nb) and np.array_equal(a[~na].view(np.uint32), b[~nb].view(np.uint32)))
+    return bool(np.array_equal(a, b))
+
+
+def _gemm_stats(oracle, y_gpu, aq, fa, sa, ga, bq, fb, sb, gb, out_bf16, bias=None):
+    """The parity tests' per-element GEMM rule on every (row of aq, row of bq)
+    pair: stats of |y - y_ref| against 1e-5 S and 1e-5 S + T_hw."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import check_gemm
+
+    Ma, Nb = aq.shape[0], bq.shape[0]
+    m, n = np.repeat(np.arange(Ma), Nb), np.tile(np.arange(Nb), Ma)
+    yref, S = oracle.gemm_points(aq, fa, sa, ga, bq, fb, sb, gb, m, n, bias=bias)
+    thw = oracle.dot_truncation_bound(aq, fa, sa, ga, bq, fb, sb, gb, m, n)
+    bias_f = None if bias is None else oracle.bf16_bits_to_f32(bias)[n]
+    ok, st = check_gemm(np.asarray(y_gpu).reshape(-1), yref, S, out_bf16, oracle, bias=bias_f, t_hw=thw)
+    st["within_tolerance"] = ok
+    return st
+
+
+def parity_leg(oracle, keep, threads):
+    """The oracle on the inputs of every workload the benchmark ran, compared
+    with what the GPU produced at full size: per-tensor amax and scales over
+    the whole tensors, codes of sampled rows, saturation / underflow counts
+    over whole tensors, every step of the delayed chain, and the GEMM on all
+    pairs of sampled rows under the parity tests' rule.  Bit-exact items are
+    reported as true / false; GEMM items as the largest |y - y_ref| / S and
+    the count above 1e-5 S."""
+    E4, E5 = oracle.E4M3, oracle.E5M2
+    out = {}
+    if "tiny" in keep:
+        k = keep["tiny"]
+        xq, sx, rx, ax, cx = oracle.quantize(k["x"], E4, (0, 0))
+        wq, sw, _, _, _ = oracle.quantize(k["w"], E4, (1, 0))
+        M = k["y"].shape[0]
+        exact = (_same(xq, k["xq"]) and _same(sx, k["s_x"]) and _same(rx, k["r_x"]) and _same(ax, k["am_x"])
+                 and _same(cx.astype(np.int64), k["cnt_x"]) and _same(wq, k["wq"]) and _same(sw, k["s_w"]))
+        out["tiny"] = {"codes_scales_counts_bit_exact": exact,
+                       "gemm_f32_all_outputs": _gemm_stats(oracle, k["y"], xq[:M], E4, sx, (0, 0), wq, E4, sw,
+                                                           (1, 0), False)}
+    if "decode" in keep:
+        k = keep["decode"]
+        aq, sa, ra, _, _ = oracle.quantize(k["a_bits"], E4, (1, 0))
+        wq, sw, rw, _, _ = oracle.quantize(k["w_rows"], E4, (1, 0))
+        exact = (_same(aq, k["aq"]) and _same(sa, k["s_a"]) and _same(ra, k["r_a"]) and _same(wq, k["wq"])
+                 and _same(sw, k["s_w"]) and _same(rw, k["r_w"]))
+        out["decode"] = {"codes_scales_bit_exact": exact, "sample": "all 16 A rows x 256 W rows",
+                         "gemm_bf16_bias": _gemm_stats(oracle, k["y"], aq, E4, sa, (1, 0), wq, E4, sw, (1, 0), True,
+                                                       bias=k["bias"][k["rows_b"]])}
+    if "prefill" in keep:
+        k = keep["prefill"]
+        ax, sx, rx = oracle_tensor_scale(oracle, k["x_bits"], E4, threads)
+        cx = oracle_given_counts(oracle, k["x_bits"], E4, sx, rx, threads)
+        aw, sw, rw = oracle_tensor_scale(oracle, k["w_bits"], E4, threads)
+        cw = oracle_given_counts(oracle, k["w_bits"], E4, sw, rw, threads)
+        xq = oracle.quantize(np.ascontiguousarray(k["x_bits"][k["rows_a"]]), E4, (0, 0), mode=oracle.GIVEN,
+                             scale=sx, inv_scale=rx)[0]
+        wq = oracle.quantize(np.ascontiguousarray(k["w_bits"][k["rows_b"]]), E4, (0, 0), mode=oracle.GIVEN,
+                             scale=sw, inv_scale=rw)[0]
+        exact = (_same(ax, k["am_x"]) and _same(sx, k["s_x"]) and _same(rx, k["r_x"])
+                 and _same(cx.astype(np.int64), k["cnt_x"]) and _same(xq, k["xq"]) and _same(aw, k["am_w"])
+                 and _same(sw, k["s_w"]) and _same(rw, k["r_w"]) and _same(cw.astype(np.int64), k["cnt_w"])
+                 and _same(wq, k["wq"]))
+        out["prefill"] = {"amax_scales_counts_bit_exact_whole_tensors_codes_sampled_rows": exact,
+                          "sample": "64 X rows x 64 W rows",
+                          "gemm_bf16": _gemm_stats(oracle, k["y"], xq, E4, sx, (0, 0), wq, E4, sw, (0, 0), True)}
+    if "delayed" in keep:
+        k = keep["delayed"]
+        st = k["steps"]
+        hist = np.zeros(16, np.float32)
+        head, s_o, r_o = 0, None, None
+        bad = []
+        for t, g in enumerate(k["chain_g"]):
+            a_t, s0, r0 = oracle_tensor_scale(oracle, g, E5, threads)
+            if t == 0:
+                s_o, r_o = s0[0, 0], r0[0, 0]
+            s_arr, r_arr = np.array([[s_o]], np.float32), np.array([[r_o]], np.float32)
+            cn = oracle_given_counts(oracle, g, E5, s_arr, r_arr, threads)
+            if not (_same(np.float32(st["amax"][t]), a_t[0, 0]) and _same(np.float32(st["scale_used"][t]), s_o)
+                    and [st["saturated"][t], st["underflowed"][t]] == cn.astype(np.int64).tolist()):
+                bad.append(t)
+            if t == len(k["chain_g"]) - 1:
+                gq = oracle.quantize(np.ascontiguousarray(g[k["rows_a"]]), E5, (0, 0), mode=oracle.GIVEN,
+                                     scale=s_arr, inv_scale=r_arr)[0]
+            head, s_o, r_o = oracle.history_update(hist, head, float(a_t[0, 0]), E5)
+        aw, sw, rw = oracle_tensor_scale(oracle, k["w_bits"], E4, threads)
+        wq = oracle.quantize(np.ascontiguousarray(k["w_bits"][k["rows_b"]]), E4, (0, 0), mode=oracle.GIVEN,
+                             scale=sw, inv_scale=rw)[0]
+        out["delayed"] = {"steps_checked": len(k["chain_g"]), "steps_not_bit_exact": bad,
+                          "last_step_codes_and_w_bit_exact": _same(gq, k["gq"]) and _same(wq, k["wq"])
+                          and _same(sw, k["s_w"]) and _same(rw, k["r_w"]),
+                          "sample": "amax, scale used and counts of every step over all of G_t; GEMM of the "
+                                    "last step on 64 G rows x 64 W rows",
+                          "gemm_f32_last_step": _gemm_stats(oracle, k["y"], gq, E5, np.float32(k["s_g"]).reshape(1, 1),
+                                                            (0, 0), wq, E4, sw, (0, 0), False)}
+    for name, ga, gb, pow2 in (("block", (1, 128), (128, 128), False), ("block_mx", (1, 32), (1, 32), True)):
+        if name not in keep:
+            continue
+        k = keep[name]
+        aq, sa, _, _, _ = oracle.quantize(k["a_rows"], E4, ga, pow2=pow2)
+        wq, sw, _, _, _ = oracle.quantize(k["w_rows"], E4, gb, pow2=pow2)
+        exact = _same(aq, k["aq"]) and _same(sa, k["s_a"]) and _same(wq, k["wq"]) and _same(sw, k["s_w"])
+        out[name] = {"codes_scales_bit_exact": exact,
+                     "sample": "64 A rows x %d W rows" % k["w_rows"].shape[0],
+                     "gemm_bf16": _gemm_stats(oracle, k["y"], aq, E4, sa, ga, wq, E4, sw, gb, True)}
+    return out
+
+
+def bench_prefill(args, torch, rt, wl, keep):
     M, N, K = 4096, 29568, 8192
     w = wl.C3Prefill()
     t0 = time.time()
@@ -256,8 +472,52 @@ def bench_prefill(args, torch, rt, wl):
         },
         "wall_s_timed": wall,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_prefill(x_bits, w_bits, M, N, K, args.cpu_seconds)
+    # what the parity leg compares with the oracle: 64 rows of X and 64 rows of W
+    ra, rb = pick(M, 64, 31), pick(N, 64, 32)
+    keep["prefill"] = {"x_bits": x_bits, "w_bits": w_bits, "rows_a": ra, "rows_b": rb,
+                       "xq": gather(torch, xq, ra), "wq": gather(torch, Wq, rb), "y": gather(torch, y, ra, rb),
+                       "s_x": s_x.cpu().numpy(), "r_x": r_x.cpu().numpy(), "am_x": am_x.cpu().numpy(),
+                       "cnt_x": cnt.cpu().numpy(), "s_w": s_w.cpu().numpy(), "r_w": r_w.cpu().numpy(),
+                       "am_w": am_w.cpu().numpy(), "cnt_w": cnt_w.cpu().numpy()}
+    del x, W, Wq, xq, y, yq
+    torch.cuda.empty_cache()
+    return out
+
+
+def tiny_latency(torch, rt, wl, keep):
+    """The tiny per-tensor workload end to end: dynamic E4M3 quantize of X
+    (256 x 1024 fp32, with counters) and the GEMM X[0:64] W^T (K = 1024, fp32
+    out, W per-channel codes from setup).  Launch-latency bound: absolute
+    microseconds, warm (back to back) and with the caches scrubbed."""
+    dev = "cuda"
+    c = wl.C1Tiny()
+    d = c.make()
+    X = torch.from_numpy(d["x"]).to(dev)
+    Wt = torch.from_numpy(d["w"]).to(dev)
+    xq = torch.empty(X.shape, dtype=torch.uint8, device=dev)
+    wq = torch.empty(Wt.shape, dtype=torch.uint8, device=dev)
+    sx, rx, ax = (torch.empty((1, 1), device=dev) for _ in range(3))
+    sw = torch.empty((c.N, 1), device=dev)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    y = torch.empty((c.M_gemm, c.N), device=dev)
+    rt.fp8_quantize(Wt, (1, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sw, None, wq)
+    q = lambda: rt.fp8_quantize(X, (0, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sx, rx, xq, ax, cnt)
+    gm = lambda: rt.fp8_scaled_gemm(xq[:c.M_gemm], rt.E4M3, (0, 0), sx, wq, rt.E4M3, (1, 0), sw, y)
+    step = lambda: (q(), gm())
+    junk = torch.empty(2**26, dtype=torch.float32, device=dev)
+    scrub = lambda: junk.fill_(1.0)
+    out = {"workload": "X 256x1024 fp32 (4 entries +-400) per-tensor dynamic E4M3 -> GEMM 64x256x1024 "
+                       "(W per-channel E4M3) -> fp32",
+           "step_us_warm": float(time_op(torch, step, reps=200, warmup=10)),
+           "step_us_scrubbed": float(time_op(torch, step, reps=50, warmup=3, scrub=scrub)),
+           "quantize_us_warm": float(time_op(torch, q, reps=200, warmup=10)),
+           "gemm_us_warm": float(time_op(torch, gm, reps=200, warmup=10)),
+           "kernels": "k_tensor_amax + k_tensor_cast + k_finish; k_gemm (general kernel)"}
+    step()
+    torch.cuda.synchronize()
+    keep["tiny"] = {"x": d["x"], "w": d["w"], "xq": xq.cpu().numpy(), "wq": wq.cpu().numpy(),
+                    "s_x": sx.cpu().numpy(), "r_x": rx.cpu().numpy(), "am_x": ax.cpu().numpy(),
+                    "cnt_x": cnt.cpu().numpy(), "s_w": sw.cpu().numpy(), "y": y.cpu().numpy()}
     return out
 
 
@@ -346,10 +606,13 @@ def recipe_staleness(torch, rt, wl):
     return out
 
 
-def extra_components(torch, rt, wl):
+def extra_components(torch, rt, wl, keep):
     """Quantize and GEMM kernels of the other workload shapes, each timed alone
     (3 untimed calls, then median and 95th percentile of 20, caches scrubbed
-    between repeats by a 1 GiB fill)."""
+    between repeats by a 1 GiB fill); the delayed workload runs its 32-step
+    chain.  keep: None, or a dict that receives what the parity leg checks."""
+    check = keep is not None
+    keep = keep if check else {}
     dev = "cuda"
     junk = torch.empty(2**28, dtype=torch.float32, device=dev)
     scrub = lambda: junk.fill_(1.0)
@@ -438,34 +701,93 @@ def extra_components(torch, rt, wl):
                                          "weight_max_abs_err", "output_mse", "output_cosine", "saturated",
                                          "underflowed")}
     comp["granularity_ledger_decode_w_e4m3"] = ledger
+    gm()
+    torch.cuda.synchronize()
+    rb = pick(N, 256, 21)
+    keep["decode"] = {"a_bits": d["a"], "w_rows": d["w"][rb], "bias": d["bias"], "rows_b": rb,
+                      "aq": Aq.cpu().numpy(), "wq": gather(torch, Wq, rb), "s_a": sa.cpu().numpy(),
+                      "r_a": ra.cpu().numpy(), "s_w": gather(torch, sw, rb), "r_w": gather(torch, rw, rb),
+                      "y": gather(torch, y, np.arange(M), rb)}
     del A, W, bias, Aq, Wq, y, yw, d, stats
 
-    # delayed-scaling backward GEMM, one step: G 8192x8192 E5M2 with the scale of
-    # the history window, W 8192x8192 E4M3 per tensor, fp32 out
+    # delayed-scaling backward GEMM: the full 32-step chain at 8192 x 8192.  Step 0
+    # uses current scaling (cold start), later steps the scale of the 16-entry
+    # amax history; every step pushes its observed amax.  Per step: the E5M2
+    # quantize of G_t (with observed amax and counters), the history update and
+    # the GEMM G_t(E5M2) W^T(E4M3, per tensor) -> fp32, each event-timed after a
+    # cache scrub.
     c4 = wl.C4Delayed()
     M, N, K = c4.M, c4.N, c4.K
-    G = from_bits(c4.make_g(1))
-    W = from_bits(c4.make_w())
+    sig, spikes = c4.sigmas()
+    w4 = c4.make_w()
+    W = from_bits(w4)
+    G = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     Gq, Wq = u8(M, K), u8(N, K)
     hist = torch.zeros(c4.history, dtype=torch.float32, device=dev)
     head = torch.zeros(1, dtype=torch.int32, device=dev)
     sg, rg, am, sw, rw = f32(1, 1), f32(1, 1), f32(1, 1), f32(1, 1), f32(1, 1)
     cnt = torch.zeros(2, dtype=torch.int64, device=dev)
-    rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.DYNAMIC, 1e-12, False, sg, rg, Gq, am, cnt)
-    rt.fp8_amax_history_update(hist, head, am, rt.E5M2, 1e-12, False, sg, rg)
     rt.fp8_quantize(W, (0, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sw, rw, Wq)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    qg = lambda: rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.GIVEN, 1e-12, False, sg, rg, Gq, am, cnt)
-    hu = lambda: rt.fp8_amax_history_update(hist, head, am, rt.E5M2, 1e-12, False, sg, rg)
-    gm = lambda: rt.fp8_scaled_gemm(Gq, rt.E5M2, (0, 0), sg, Wq, rt.E4M3, (0, 0), sw, y)
-    comp["delayed_quantize_g_given_e5m2"] = hbm_entry(time_op(torch, qg, scrub=scrub), M * K * 3 + 4,
+    steps = {"sigma": [], "amax": [], "scale_used": [], "saturated": [], "underflowed": [],
+             "quantize_us": [], "history_update_us": [], "gemm_us": []}
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        return e0, e1
+
+    chain_g = [] if check else None
+    for t in range(c4.steps):
+        g_bits = c4.make_g(t)
+        if chain_g is not None:
+            chain_g.append(g_bits)           # kept for the oracle's check of every step
+        G.copy_(torch.from_numpy(g_bits.view(np.int16)).view(torch.bfloat16))
+        if t == 0:
+            q = lambda: rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.DYNAMIC, 1e-12, False, sg, rg, Gq, am, cnt)
+        else:
+            q = lambda: rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.GIVEN, 1e-12, False, sg, rg, Gq, am, cnt)
+        scrub()
+        eq = timed(q)
+        s_used = sg.clone()
+        scrub()
+        eg = timed(lambda: rt.fp8_scaled_gemm(Gq, rt.E5M2, (0, 0), sg, Wq, rt.E4M3, (0, 0), sw, y))
+        eh = timed(lambda: rt.fp8_amax_history_update(hist, head, am, rt.E5M2, 1e-12, False, sg, rg))
+        torch.cuda.synchronize()
+        cn = cnt.tolist()
+        steps["sigma"].append(float(sig[t]))
+        steps["amax"].append(float(am.item()))
+        steps["scale_used"].append(float(s_used.item()))
+        steps["saturated"].append(int(cn[0]))
+        steps["underflowed"].append(int(cn[1]))
+        steps["quantize_us"].append(eq[0].elapsed_time(eq[1]) * 1e3)
+        steps["gemm_us"].append(eg[0].elapsed_time(eg[1]) * 1e3)
+        steps["history_update_us"].append(eh[0].elapsed_time(eh[1]) * 1e3)
+        if t == c4.steps - 1 and check:
+            ra, rb = pick(M, 64, 41), pick(N, 64, 42)
+            keep["delayed"] = {"w_bits": w4, "rows_a": ra, "rows_b": rb, "gq": gather(torch, Gq, ra),
+                               "wq": gather(torch, Wq, rb), "s_g": s_used.cpu().numpy(),
+                               "s_w": sw.cpu().numpy(), "r_w": rw.cpu().numpy(), "y": gather(torch, y, ra, rb),
+                               "steps": steps, "chain_g": chain_g}
+    later = slice(1, None)  # GIVEN steps
+    qus = Timing(float(np.median(steps["quantize_us"][later])), float(np.percentile(steps["quantize_us"][later], 95)))
+    gus = Timing(float(np.median(steps["gemm_us"])), float(np.percentile(steps["gemm_us"], 95)))
+    comp["delayed_quantize_g_given_e5m2"] = hbm_entry(qus, M * K * 3 + 4,
                                                        "k_tensor_cast (given, amax + counts) + k_finish")
-    comp["delayed_history_update_us"] = float(time_op(torch, hu))
-    comp["delayed_gemm_e5m2_e4m3_f32"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
-                                                    M * K + N * K + M * N * 4 + 8)
-    # cast-transpose of the same G (the backward reads it in both orientations):
-    # codes row-major and K-major in one pass, per-tensor GIVEN (+ amax, counters),
-    # and per-column DYNAMIC (column amax pass, scales, then the pass)
+    comp["delayed_history_update_us"] = float(np.median(steps["history_update_us"]))
+    comp["delayed_gemm_e5m2_e4m3_f32"] = mfma_entry(gus, 2.0 * M * N * K, M * K + N * K + M * N * 4 + 8)
+    comp["delayed_chain_32_steps"] = {
+        "workload": "G_t bf16 8192x8192 = N(0,1) sigma_t, sigma_t = exp(z_t), x100 spike at step(s) %s; "
+                    "E5M2, 16-entry amax history (step 0 current scaling); W 8192x8192 per-tensor E4M3; "
+                    "fp32 out" % [int(v) for v in spikes],
+        "per_step": steps,
+        "saturated_total": int(sum(steps["saturated"])), "underflowed_total": int(sum(steps["underflowed"])),
+        "steps_with_saturation": int(sum(v > 0 for v in steps["saturated"]))}
+    # cast-transpose of the last step's G (the backward reads it in both
+    # orientations): codes row-major and K-major in one pass, per-tensor GIVEN
+    # (+ amax, counters), and per-column DYNAMIC (column amax pass, scales, then the pass)
     Gt = u8(K, M)
     ct = lambda: rt.fp8_quantize_transpose(G, (0, 0), rt.E5M2, rt.GIVEN, 1e-12, False, sg, rg, Gq, Gt, am, cnt)
     comp["cast_transpose_g_e5m2_given"] = hbm_entry(time_op(torch, ct, scrub=scrub), M * K * 4 + 4,
@@ -495,6 +817,13 @@ def extra_components(torch, rt, wl):
                                                  N * K * 3 + sw.numel() * 4, "k_blocktile")
     comp["block_gemm_bf16"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
                                          M * K + N * K + M * N * 2 + (sa.numel() + sw.numel()) * 4)
+    a5, w5 = c5.make_a(), c5.make_w()  # host copies for the parity leg (same seeds)
+    ra = pick(M, 64, 51)
+    blocks = pick(N // 128, 2, 52)
+    rb = np.concatenate([b * 128 + np.arange(128) for b in blocks])
+    keep["block"] = {"a_rows": a5[ra], "w_rows": w5[rb], "rows_a": ra, "rows_b": rb, "blocks": blocks,
+                     "aq": gather(torch, Aq, ra), "wq": gather(torch, Wq, rb), "s_a": gather(torch, sa, ra),
+                     "s_w": gather(torch, sw, blocks), "y": gather(torch, y, ra, rb)}
     sa32, sw32 = f32(M, K // 32), f32(N, K // 32)
     qa = lambda: rt.fp8_quantize(A, (1, 32), rt.E4M3, rt.DYNAMIC, 1e-12, True, sa32, None, Aq)
     qw = lambda: rt.fp8_quantize(W, (1, 32), rt.E4M3, rt.DYNAMIC, 1e-12, True, sw32, None, Wq)
@@ -505,6 +834,11 @@ def extra_components(torch, rt, wl):
                                                       M * K * 3 + sa32.numel() * 4, "k_rowgroups")
     comp["block_mx_gemm_bf16"] = mfma_entry(time_op(torch, gm, scrub=scrub), 2.0 * M * N * K,
                                             M * K + N * K + M * N * 2 + (sa32.numel() + sw32.numel()) * 4)
+    ra, rb = pick(M, 64, 53), pick(N, 64, 54)
+    keep["block_mx"] = {"a_rows": a5[ra], "w_rows": w5[rb], "rows_a": ra, "rows_b": rb,
+                        "aq": gather(torch, Aq, ra), "wq": gather(torch, Wq, rb), "s_a": gather(torch, sa32, ra),
+                        "s_w": gather(torch, sw32, rb), "y": gather(torch, y, ra, rb)}
+    del a5, w5
     del A, W, Aq, Wq, y, junk
     torch.cuda.empty_cache()
     return comp
@@ -534,13 +868,28 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "repeats": 3}), flush=True)
         return
-    out = bench_prefill(args, torch, rt, wl)
+    keep = {}
+    out = bench_prefill(args, torch, rt, wl, keep)
+    print("prefill step timed", file=sys.stderr, flush=True)
+    out["components"]["tiny_latency"] = tiny_latency(torch, rt, wl, keep)
     if not args.no_extra:
-        out["components"].update(extra_components(torch, rt, wl))
+        out["components"].update(extra_components(torch, rt, wl, None if args.no_cpu_baseline else keep))
+        print("other workloads timed", file=sys.stderr, flush=True)
         out["delayed_recipe_staleness"] = recipe_staleness(torch, rt, wl)
         fr = [v["frac_hbm"] for k, v in out["components"].items()
               if isinstance(v, dict) and "frac_hbm" in v and "quantize" in k and "decode_quantize_a" not in k]
         out["components"]["quantize_min_frac_hbm_large"] = min(fr)
+    if not args.no_cpu_baseline:
+        # the CPU-baseline leg: the oracle timed on a sample of the prefill
+        # step, then run on every workload's inputs to check the GPU's results
+        p = keep["prefill"]
+        out["cpu_baseline"] = cpu_baseline_prefill(p["x_bits"], p["w_bits"], 4096, 29568, 8192, args.cpu_seconds)
+        print("cpu baseline timed", file=sys.stderr, flush=True)
+        import oracle
+
+        t0 = time.perf_counter()
+        out["parity_full_size"] = parity_leg(oracle, keep, host_cpu()[2])
+        out["parity_full_size"]["oracle_seconds"] = time.perf_counter() - t0
     print(json.dumps(out), flush=True)
 
 

@@ -5,7 +5,10 @@ arithmetic (no amax, scale, cast or GEMM).  Both the CPU oracle and the HIP
 library are fed from it.  Arrays are numpy: float32, or bfloat16 carried as
 ``uint16`` bit patterns (rounded to nearest even from float32 by torch's CPU
 cast).  The random source is numpy's Philox4x32-10 counter-based generator,
-keyed by ``42 + 1000 * config + tensor_id``.
+keyed by ``42 + 1000 * config + tensor_id``; a draw of more than 2^22
+elements is made of 2^22-element chunks, chunk i from that generator's
+stream jumped i + 1 times (drawn on several threads, the same values
+whatever their number).
 
 The five workloads stand in for the LLM linear layers the pages discuss (a
 decode-time linear, a 72B-class MLP up-projection at prefill, a backward GEMM
@@ -14,7 +17,9 @@ layer); the pages measured real models, which are not used here.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 
 import numpy as np
 
@@ -42,18 +47,54 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+CHUNK = 1 << 22  # elements per independent stream of a large draw
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _chunked(g: np.random.Generator, shape, fill) -> np.ndarray:
+    """A float32 array of `shape` filled chunk by chunk: chunk i (CHUNK elements,
+    the last one shorter) comes from its own stream, g's bit generator jumped
+    i + 1 times, so the values depend on the seed and CHUNK only, not on the
+    number of threads.  Arrays of at most CHUNK elements are one draw from g."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    if n <= CHUNK:
+        fill(g, out)
+        return out.reshape(shape)
+    bg = g.bit_generator
+    starts = range(0, n, CHUNK)
+
+    def one(i):
+        fill(np.random.Generator(bg.jumped(i + 1)), out[i * CHUNK:(i + 1) * CHUNK])
+
+    with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(starts))))
+    return out.reshape(shape)
+
+
 def normal(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
-    x = g.standard_normal(shape, dtype=np.float32)
+    x = _chunked(g, shape, lambda gi, o: gi.standard_normal(o.shape, dtype=np.float32, out=o))
     if std != 1.0:
         x *= np.float32(std)
     return x
 
 
 def student_t3(g: np.random.Generator, shape) -> np.ndarray:
-    """Student-t with 3 degrees of freedom: Z / sqrt(chi2_3 / 3)."""
-    z = g.standard_normal(shape, dtype=np.float32)
-    chi = g.chisquare(3, size=shape).astype(np.float32)
-    return z / np.sqrt(chi / np.float32(3.0))
+    """Student-t with 3 degrees of freedom: Z / sqrt(chi2_3 / 3), Z and the
+    chi-square drawn in the same chunk stream."""
+    def fill(gi, o):
+        z = gi.standard_normal(o.shape, dtype=np.float32)
+        chi = gi.chisquare(3, size=o.shape).astype(np.float32)
+        o[:] = z / np.sqrt(chi / np.float32(3.0))
+
+    return _chunked(g, shape, fill)
 
 
 # --------------------------------------------------------------------------
