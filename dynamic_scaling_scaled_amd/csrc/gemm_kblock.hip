@@ -169,12 +169,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
     }
   };
   // One stage from LDS: B fragments first, A one row tile ahead; each tile's
-  // partial is a single MFMA from zero, promoted at once.
-  auto stage_mma = [&](const uint8_t* la, const uint8_t* lb, const float* ssa, int st) {
-    float f[MI];
+  // partial is a single MFMA from zero.  The promotion of row tile i's
+  // partials (acc += f p) is issued among the MFMAs of row tile i + 1, so
+  // the FMAs never wait on an MFMA that has just started; the last row
+  // tile's partials are promoted among the next stage's first MFMAs.
+  f32x4 pend[NJ];   // partials of the previous row tile, not yet promoted
+  float fpend = 0.0f;
+  auto stage_mma = [&](const uint8_t* la, const uint8_t* lb, const float* ssa, int st, bool first) {
     const float fb = BKB ? sSb[(wn * WTN) / 128][st] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) f[i] = (AKB ? ssa[wm * WTM + i * 16 + fr] : 1.0f) * fb;
     i32x8 bfr[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bfr[j] = frag(lb, wn * WTN + j * 16 + fr, fq);
@@ -183,14 +185,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
     for (int i = 0; i < MI; ++i) {
       const i32x8 cur = afr;
       if (i + 1 < MI) afr = frag(la, wm * WTM + (i + 1) * 16 + fr, fq);
+      f32x4 p[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const f32x4 p =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], cur, f32x4{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
+        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], cur, f32x4{0.f, 0.f, 0.f, 0.f}, FB, FA,
+                                                               0, 0, 0, 0);
+        // promote the previous row tile (of this stage, or the last of the previous one)
+        const int ip = i == 0 ? MI - 1 : i - 1;
+        if (i > 0 || !first) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(f[i], p[e], acc[i][j][e]);
+          for (int e = 0; e < 4; ++e) acc[ip][j][e] = fmaf(fpend, pend[j][e], acc[ip][j][e]);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pend[j] = p[j];
+      fpend = (AKB ? ssa[wm * WTM + i * 16 + fr] : 1.0f) * fb;
+      __builtin_amdgcn_sched_barrier(0);  // keep each row tile's MFMAs with the previous tile's FMAs
     }
+  };
+  auto drain = [&]() {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[MI - 1][j][e] = fmaf(fpend, pend[j][e], acc[MI - 1][j][e]);
   };
 
   sa_dma(0, sSa0);
@@ -200,20 +217,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
   // Stage st (in arrays X): issue the loads of stage st+1 into the other
   // arrays (free: the previous stage ended with a barrier), multiply and
   // promote stage st, wait for everything issued.
-#define FP8RT_KSTAGE(LA, LB, LS, DA, DB, DS, ST)                               \
+#define FP8RT_KSTAGE(LA, LB, LS, DA, DB, DS, ST, FIRST)                        \
   {                                                                           \
     const int kn = min(ST + 1, ns - 1);                                       \
     sa_dma(kn, DS);                                                           \
     dma_tile<kDmaA>(a_base + kn * TKS, voa, DA, wave);                        \
     dma_tile<kDmaB>(b_base + kn * TKS, vob, DB, wave);                        \
-    stage_mma(LA, LB, LS, ST);                                                \
+    stage_mma(LA, LB, LS, ST, FIRST);                                         \
     step_barrier<0>();                                                        \
   }
-  for (int st = 0; st < ns; st += 2) {
-    FP8RT_KSTAGE(sA0, sB0, sSa0, sA1, sB1, sSa1, st)
-    FP8RT_KSTAGE(sA1, sB1, sSa1, sA0, sB0, sSa0, st + 1)
+  FP8RT_KSTAGE(sA0, sB0, sSa0, sA1, sB1, sSa1, 0, true)
+  FP8RT_KSTAGE(sA1, sB1, sSa1, sA0, sB0, sSa0, 1, false)
+  for (int st = 2; st < ns; st += 2) {
+    FP8RT_KSTAGE(sA0, sB0, sSa0, sA1, sB1, sSa1, st, false)
+    FP8RT_KSTAGE(sA1, sB1, sSa1, sA0, sB0, sSa0, st + 1, false)
   }
 #undef FP8RT_KSTAGE
+  drain();
 
   // ---- epilogue: lane l holds output row 16 i + (l % 16) and columns
   // 16 j + 4 (l / 16) + (0..3) of the wave tile.
