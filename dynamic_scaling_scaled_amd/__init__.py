@@ -20,6 +20,10 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp8rt.so")
+# FP8RT_LIB names another build of this library to load instead (the
+# host-sanitized build of the CPU checks); there is no fallback either way.
+if os.environ.get("FP8RT_LIB"):
+    LIB_PATH = os.environ["FP8RT_LIB"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1

@@ -65,5 +65,52 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build for CPU checks
+# of the library's host code (argument validation and dispatch), loaded with
+# clang's ASan runtime preloaded.  Device code is built without
+# instrumentation; this library is never used on a GPU.
+ASAN_BUILD = os.path.join(ROOT, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_BUILD, "libfp8rt_asan.so")
+HOST_SANITIZE = ["-fno-gpu-sanitize", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """clang's shared ASan runtime (the one hipcc's host compiler links against)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+
+        hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        path = hits[-1] if hits else ""
+    return path
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    os.makedirs(ASAN_BUILD, exist_ok=True)
+
+    def comp(src):
+        obj = os.path.join(ASAN_BUILD, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *HIPCC_FLAGS, *HOST_SANITIZE, *FILE_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE,
+               "-I", CSRC, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
+        return obj
+
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", *HOST_SANITIZE, "-o",
+           ASAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
+    if verbose:
+        print("built", ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -62,7 +62,17 @@
 extern "C" {
 #endif
 
-typedef enum fp8rt_status {
+/* The enumerations below are plain C enums (int-sized).  Compiled as C++
+ * they get a fixed underlying type of int, so a value that is not one of the
+ * enumerators (which the entry points reject with FP8RT_EINVAL) is still a
+ * valid object of the type on both sides of the ABI. */
+#ifdef __cplusplus
+#define FP8RT_ENUM(name) enum name : int
+#else
+#define FP8RT_ENUM(name) enum name
+#endif
+
+typedef FP8RT_ENUM(fp8rt_status) {
     FP8RT_OK = 0,
     FP8RT_EINVAL = 1,       /* null required pointer, dims <= 0, ld < cols, bad eps /
                                history length / head, granularity not allowed for the op */
@@ -78,9 +88,9 @@ typedef enum fp8rt_status {
 /* [P2 "How the 8 bits are allocated"]: E4M3 max finite 448, E5M2 max finite
  * 57344; [P5 "numeric properties"]: bias 7 and 15.  E4M3 is the OCP "fn"
  * variant (no Inf, NaN = 0x7F/0xFF); E5M2 has IEEE-style Inf/NaN. */
-typedef enum fp8rt_format { FP8RT_E4M3 = 0, FP8RT_E5M2 = 1 } fp8rt_format;
+typedef FP8RT_ENUM(fp8rt_format) { FP8RT_E4M3 = 0, FP8RT_E5M2 = 1 } fp8rt_format;
 
-typedef enum fp8rt_dtype { FP8RT_F32 = 0, FP8RT_BF16 = 1 } fp8rt_dtype;
+typedef FP8RT_ENUM(fp8rt_dtype) { FP8RT_F32 = 0, FP8RT_BF16 = 1 } fp8rt_dtype;
 
 /* Group extent of one scale [P2 "Per-channel and block scaling"]:
  *   per-tensor {0,0} | per-row / per-token / per-output-channel {1,0} |
@@ -92,7 +102,7 @@ typedef struct fp8rt_gran {
 
 /* Where the scale comes from [P2 "Current scaling", "Delayed scaling",
  * "Weight scale and activation scale lifetimes"]. */
-typedef enum fp8rt_mode {
+typedef FP8RT_ENUM(fp8rt_mode) {
     FP8RT_DYNAMIC = 0, /* current scaling: amax of this tensor -> s, r */
     FP8RT_GIVEN = 1    /* static or delayed: s (and optionally r) supplied */
 } fp8rt_mode;
@@ -183,7 +193,7 @@ fp8rt_status fp8_amax_history_update(float* history, int32_t len, int32_t* head,
                                      float* inv_scale_next, hipStream_t stream);
 
 /* History function of a delayed-scaling recipe. */
-typedef enum fp8rt_history_fn {
+typedef FP8RT_ENUM(fp8rt_history_fn) {
   FP8RT_HIST_MAX = 0,    /* window maximum over the history ring */
   FP8RT_HIST_LATEST = 1  /* the newest amax alone */
 } fp8rt_history_fn;

@@ -20,6 +20,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "fp8_oracle.c"), os.path.join(_HERE, "fp8_dot_bound.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A build with AddressSanitizer and UndefinedBehaviorSanitizer, loaded instead
+# when FP8RT_ORACLE_SANITIZED=1 (the process must preload gcc's libasan).
+_ASAN_PATH = os.path.join(_HERE, "liboracle_asan.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
@@ -37,15 +41,29 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized() -> str:
+    """Compile the same sources with ASan + UBSan (every UB report fatal)."""
+    tmp = _ASAN_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-std=c99", "-O1", "-Wall", "-fPIC", "-shared", *SANITIZE_FLAGS,
+                           "-o", tmp, *_SRCS, "-lm"])
+    os.replace(tmp, _ASAN_PATH)
+    return _ASAN_PATH
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = _LIB_PATH
+        if os.environ.get("FP8RT_ORACLE_SANITIZED") == "1":
+            path = _ASAN_PATH
+            if not os.path.exists(path):
+                raise ImportError("liboracle_asan.so is not built (oracle.build_sanitized())")
+        elif not os.path.exists(_LIB_PATH):
             build()
-        L = C.CDLL(_LIB_PATH)
+        L = C.CDLL(path)
         P, I64, I, F, D = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_double
         L.orc_fmax.restype = D
         L.orc_fmax.argtypes = [I]
