@@ -14,7 +14,7 @@ if ROOT not in sys.path:
 # after these; test_zz_* files stay last.
 _ORDER = ["test_oracle_", "test_boundary", "test_bench_cli", "test_gpu_quant.py", "test_gpu_quant_large",
           "test_gpu_gemm.py", "test_gpu_dot_model", "test_gpu_workloads.py", "test_gpu_graph",
-          "test_gpu_workspace", "test_gpu_recipe", "test_gpu_gemm_fp8out", "test_gpu_transpose",
+          "test_gpu_workspace", "test_gpu_determinism", "test_gpu_recipe", "test_gpu_gemm_fp8out", "test_gpu_transpose",
           "test_gpu_wonly", "test_gpu_packed", "test_gpu_ledger", "test_gpu_workloads_next"]
 
 
