@@ -1,5 +1,5 @@
 // gemm_skinny.hip -- scaled FP8 GEMM for a few rows of A (decode-shaped
-// layers, M <= 16): streaming B at HBM speed is the whole job.
+// layers, M <= 64): streaming B at HBM speed is the whole job.
 //
 // Method: "FP8 formats and scaling for LLM inference", section "The full
 // precision contract of one FP8 GEMM" (Y ~ s_x s_w X8 W8, FP32 accumulation,
@@ -7,7 +7,7 @@
 // (per-token and per-output-channel scales):
 //   Y[m,n] = s_a(m) s_b(n) sum_k dec(A[m,k]) dec(B[n,k]) + bias[n].
 //
-// Design for MI355X: with M <= 16 the arithmetic intensity is at most 2M
+// Design for MI355X: with M <= 64 the arithmetic intensity is at most 2M
 // FLOP per byte of B, far below the MFMA ridge, so the kernel is built
 // around keeping enough of B in flight: many small waves instead of deep
 // per-wave prefetch.
@@ -18,8 +18,9 @@
 //    VGPRs per lane) keep 32 waves' loads in flight, which hides the HBM
 //    latency.
 //  - v_mfma_f32_16x16x128 with B as the first operand: the 16 x 16 result
-//    holds 16 rows of B (output columns) by 16 rows of A; each lane ends with
-//    4 consecutive output columns of one output row.  Lane quarter g loads
+//    holds 16 rows of B (output columns) by 16 rows of A (one MFMA per 16-row
+//    tile of A, up to 4); each lane ends with 4 consecutive output columns of
+//    one output row per tile.  Lane quarter g loads
 //    bytes [32 g, 32 g + 32) of every 128-byte K step of both operands, the
 //    same K permutation on both sides, which the per-row scales (applied
 //    after the sum) do not see.
@@ -48,7 +49,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSkWaves = 16;
 constexpr int kSkThreads = kSkWaves * 64;
-constexpr int kSkMaxM = 16;
+constexpr int kSkMaxM = 64;  // up to 4 MFMA row tiles of A
 
 template <int FA, int FB, int MT, bool BF16OUT, bool PACKED>
 __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
@@ -173,10 +174,17 @@ void launch_mt(const GemmArgs& g, hipStream_t st, int vec) {
                        g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
 }
 
+template <int FA, int FB, bool PACKED>
+void launch_rows(const GemmArgs& g, hipStream_t st, int vec) {
+  if (g.M <= 16) launch_mt<FA, FB, 1, PACKED>(g, st, vec);
+  else if (g.M <= 32) launch_mt<FA, FB, 2, PACKED>(g, st, vec);
+  else launch_mt<FA, FB, 4, PACKED>(g, st, vec);
+}
+
 template <int FA, int FB>
 void launch_fmt(const GemmArgs& g, hipStream_t st, int vec) {
-  if (g.b_packed) launch_mt<FA, FB, 1, true>(g, st, vec);
-  else launch_mt<FA, FB, 1, false>(g, st, vec);
+  if (g.b_packed) launch_rows<FA, FB, true>(g, st, vec);
+  else launch_rows<FA, FB, false>(g, st, vec);
 }
 
 // Fragment-ordered copy of row-major codes: 16-byte piece c of qp is tile

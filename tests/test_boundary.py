@@ -137,7 +137,7 @@ def test_gemm_validation(rt, fn):
     assert g(rt, K=256, lda=256, ldb=256, ga=(2, 128), gb=(0, 0)) == rt.EUNSUPPORTED      # A blocks span rows
     # the packed weight image: decode shapes only
     assert g(rt, flags=6) == rt.EINVAL
-    assert g(rt, flags=rt.B_PACKED16) == rt.EUNSUPPORTED                                  # M = 64 > 16
+    assert g(rt, flags=rt.B_PACKED16, M=80, ldy=64) == rt.EUNSUPPORTED                    # M = 80 > 64
     assert g(rt, flags=rt.B_PACKED16, M=16, K=144, lda=144, ldb=144) == rt.EUNSUPPORTED  # K % 128
     assert g(rt, flags=rt.B_PACKED16, M=8, K=256, lda=256, ga=(1, 128)) == rt.EUNSUPPORTED  # K-group scales
     assert g(rt, flags=rt.B_PACKED16, M=8, lda=64) == rt.EINVAL                           # lda < K still checked
