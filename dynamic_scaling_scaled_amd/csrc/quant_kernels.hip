@@ -599,6 +599,34 @@ __global__ __launch_bounds__(kBlock) void k_col_amax_finish(const uint32_t* __re
   amax[c] = __uint_as_float(m);
 }
 
+// The per-column DYNAMIC finish in one launch: each column's amax from the
+// nchunk row-chunk partials part[k][c] (wave w of a block reads chunks w,
+// w + 4, ... of 64 consecutive columns: coalesced), the waves' maxima
+// combined in LDS, then s and r of the column as k_compute_scale derives them;
+// amax_out (nullable) receives the amax.
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_col_amax_scale(const uint32_t* __restrict__ part, int64_t nchunk,
+                                                           int64_t cols, float eps, int pow2, float* amax_out,
+                                                           float* s_out, float* r_out) {
+  __shared__ uint32_t sh[kWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const int64_t cc = min(c, cols - 1);
+  uint32_t m = 0;
+  for (int64_t k = w; k < nchunk; k += kWaves) m = max(m, part[k * cols + cc]);
+  sh[w][lane] = m;
+  __syncthreads();
+  if (w != 0 || c >= cols) return;
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = max(m, sh[i][lane]);
+  const float a = __uint_as_float(m);
+  float s, r;
+  scale_from_amax(a, Fmt<F>::kMax, eps, pow2 != 0, s, r);
+  if (amax_out) amax_out[c] = a;
+  s_out[c] = s;
+  if (r_out) r_out[c] = r;
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 
@@ -787,12 +815,22 @@ hipError_t quant_transpose_typed(const QuantArgs& a, uint8_t* qt, int64_t ldqt, 
   float* amax = a.amax_out ? a.amax_out : static_cast<float*>(scr);
   float* rbuf = static_cast<float*>(scr) + G;
   uint32_t* cpart = reinterpret_cast<uint32_t*>(static_cast<float*>(scr) + 2 * G);
+  const float* r = a.inv_scale;
+  bool scaled = false;  // s and r already derived (per-column DYNAMIC)
   if (need_amax) {
     if (gk == 2) {
       hipLaunchKernelGGL(k_col_amax<T>, dim3(static_cast<unsigned>(colblocks), static_cast<unsigned>(nchunk)),
                          dim3(kBlock), 0, st, static_cast<const T*>(a.x), a.rows, a.cols, a.ldx, rpc, cpart);
-      hipLaunchKernelGGL(k_col_amax_finish, dim3(static_cast<unsigned>(ceil_div(a.cols, kBlock))), dim3(kBlock),
-                         0, st, cpart, nchunk, a.cols, amax);
+      if (dynamic) {  // the column amax, s and r in one launch
+        float* rw = a.inv_scale ? a.inv_scale : rbuf;
+        hipLaunchKernelGGL(k_col_amax_scale<F>, dim3(static_cast<unsigned>(ceil_div(a.cols, 64))), dim3(kBlock),
+                           0, st, cpart, nchunk, a.cols, a.eps, a.pow2, a.amax_out, a.scale, rw);
+        r = rw;
+        scaled = true;
+      } else {
+        hipLaunchKernelGGL(k_col_amax_finish, dim3(static_cast<unsigned>(ceil_div(a.cols, kBlock))),
+                           dim3(kBlock), 0, st, cpart, nchunk, a.cols, amax);
+      }
     } else {
       QuantArgs b = a;
       b.amax_only = true;
@@ -802,8 +840,7 @@ hipError_t quant_transpose_typed(const QuantArgs& a, uint8_t* qt, int64_t ldqt, 
       if (e != hipSuccess) return e;
     }
   }
-  const float* r = a.inv_scale;
-  if (dynamic) {
+  if (dynamic && !scaled) {
     float* rw = a.inv_scale ? a.inv_scale : rbuf;
     e = launch_compute_scale(amax, G, a.fmt, a.eps, a.pow2 != 0, a.scale, rw, st);
     if (e != hipSuccess) return e;
