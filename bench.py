@@ -487,6 +487,9 @@ def bench_prefill(args, torch, rt, wl, keep):
     qx["frac_of_copy_rate"] = qx["moved_GB_s"] / qx["copy_same_bytes_GB_s"]
     qx["note"] = ("two passes by construction (X is read for amax, then again for the cast): 2 reads + 1 write; "
                   "the copy moves the same bytes with torch's device copy")
+    # HBM bytes per call from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    # (null once the kernels' source has changed since it was taken)
+    qx["traffic"] = traffic_from_profile("quantize_x_prefill_traffic.json")
     del junk, src, dst
     # what the parity leg compares with the oracle: 64 rows of X and 64 rows of W
     ra, rb = pick(M, 64, 31), pick(N, 64, 32)
