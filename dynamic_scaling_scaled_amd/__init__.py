@@ -30,6 +30,8 @@ F32, BF16 = 0, 1
 DYNAMIC, GIVEN = 0, 1
 POW2_SCALES = 1
 B_PACKED16 = 2
+EXACT_PRODUCTS = 4
+EXACT_AUTO_BYTES = 1 << 20
 FMAX = {E4M3: 448.0, E5M2: 57344.0}
 
 OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, ESCRATCH = 0, 1, 2, 3, 4, 5
@@ -357,5 +359,5 @@ def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, flags=0, stream=No
 
 __all__ = ["fp8_pack_weights16", "PackedWeights", "packed16_bytes", "B_PACKED16", "fp8_quant_error", "fp8_granularity_ledger", "LedgerSpec", "LedgerRow", "fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
-           "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "FMAX", "ngroups",
+           "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "EXACT_PRODUCTS", "EXACT_AUTO_BYTES", "FMAX", "ngroups",
            "scale_shape"]

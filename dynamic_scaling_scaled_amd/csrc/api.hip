@@ -219,7 +219,7 @@ fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gr
                         uint32_t flags, GemmArgs& g) {
   if (!a || !b || !scale_a || !scale_b) return FP8RT_EINVAL;
   if (!valid_fmt(fa) || !valid_fmt(fb) || (bias && !valid_dtype(bias_t))) return FP8RT_EINVAL;
-  if ((flags & ~(FP8RT_POW2_SCALES | FP8RT_B_PACKED16)) != 0) return FP8RT_EINVAL;
+  if ((flags & ~(FP8RT_POW2_SCALES | FP8RT_B_PACKED16 | FP8RT_EXACT_PRODUCTS)) != 0) return FP8RT_EINVAL;
   const bool packed = (flags & FP8RT_B_PACKED16) != 0;
   if (packed) ldb = K;  // ignored: the packed image has no leading dimension
   if (M <= 0 || N <= 0 || K <= 0 || lda < K || ldb < K || ldy < N) return FP8RT_EINVAL;
@@ -264,7 +264,12 @@ fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gr
   }
   // the packed weight image is read by the decode kernel only
   g.b_packed = packed;
-  if (packed && !gemm_skinny_eligible(g)) return FP8RT_EUNSUPPORTED;
+  const bool decode = gemm_skinny_eligible(g);
+  if (packed && !decode) return FP8RT_EUNSUPPORTED;
+  // exact products: asked for, or free where the decode kernel is latency bound
+  const bool exact = (flags & FP8RT_EXACT_PRODUCTS) != 0;
+  if (exact && !decode) return FP8RT_EUNSUPPORTED;
+  g.exact_products = decode && (exact || N * K <= int64_t(FP8RT_EXACT_AUTO_BYTES));
   return FP8RT_OK;
 }
 
@@ -319,7 +324,7 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
                                     int64_t ldy, float* amax_y, uint64_t* sat_underflow, uint32_t flags,
                                     hipStream_t stream) {
   if (!yq || !scale_y || !valid_fmt(fy)) return FP8RT_EINVAL;
-  if (flags & FP8RT_B_PACKED16) return FP8RT_EUNSUPPORTED;
+  if (flags & (FP8RT_B_PACKED16 | FP8RT_EXACT_PRODUCTS)) return FP8RT_EUNSUPPORTED;
   GemmArgs g{};
   const fp8rt_status st =
       gemm_setup(a, fa, lda, ga, scale_a, b, fb, ldb, gb, scale_b, M, N, K, bias, bias_t, ldy, flags, g);

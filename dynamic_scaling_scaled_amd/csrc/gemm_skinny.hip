@@ -26,6 +26,15 @@
 //    after the sum) do not see.
 //  - The 16 partial sums meet in LDS; wave 0 applies the scales and the bias,
 //    rounds and stores 8- or 16-byte pieces.
+//  - Exact products (a template flag): each 128-deep step becomes four
+//    v_mfma_f32_16x16x32_bf16, instruction j taking bytes [8 j, 8 j + 8) of
+//    every lane's 32 on both operands, widened exactly to bf16 in registers
+//    (v_cvt_scalef32_pk_bf16_fp8 / _bf8 with scale 1: two codes each).  The
+//    bf16 matrix cores multiply exactly, so only the FP32 accumulation
+//    rounds, where the FP8 ones align each 8-deep run's products to the
+//    largest and drop the bits below 2^-13 of it.  Four times the matrix-core
+//    instructions and one VALU op per two codes: free where the launch is
+//    latency bound.
 //  - Fragment-ordered B (fp8_pack_weights16): each 16-row x 128-byte step of
 //    B is one 2 KB tile whose first KB holds every lane's first 16 bytes in
 //    lane order and whose second KB their last 16 bytes, so each load
@@ -45,14 +54,43 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Exact products: every E4M3 / E5M2 value is a bf16 value, and the bf16
+// matrix cores multiply bf16 exactly into FP32.  One conversion turns two
+// codes of a dword half into two bf16 (element order kept; the conversion's
+// scale operand is 1.0, so nothing is rounded); 8 codes -> 8 bf16.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <int F, bool HI>
+__device__ __forceinline__ uint32_t widen2(int w) {
+  bf16x2 h;
+  if constexpr (F == kE4M3) {
+    h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  } else {
+    h = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
+  }
+  return __builtin_bit_cast(uint32_t, h);
+}
+template <int F>
+__device__ __forceinline__ bf16x8 widen8(int w0, int w1) {
+  return __builtin_bit_cast(bf16x8, u32x4{widen2<F, false>(w0), widen2<F, true>(w0), widen2<F, false>(w1),
+                                          widen2<F, true>(w1)});
+}
 
 constexpr int kSkWaves = 16;
 constexpr int kSkThreads = kSkWaves * 64;
 constexpr int kSkMaxM = 64;  // up to 4 MFMA row tiles of A
 
-template <int FA, int FB, int MT, bool BF16OUT, bool PACKED>
-__global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
+// Waves per SIMD the register budget is sized for: 8 (two workgroups per CU,
+// 64 VGPRs) for one or two row tiles of A, or one with exact products; 4 (one
+// workgroup, 128 VGPRs) for four row tiles, whose A fragments alone fill 64
+// VGPRs, and for two with exact products (their widened operands).
+constexpr int sk_waves_per_simd(int mt, bool exact) { return (mt >= 4 || (exact && mt >= 2)) ? 4 : 8; }
+
+template <int FA, int FB, int MT, bool BF16OUT, bool PACKED, bool EXACT>
+__global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_gemm_skinny(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, int64_t era, const float* __restrict__ sb,
     int64_t erb, const void* __restrict__ bias, int bias_bf16, void* __restrict__ Y, int64_t ldy,
@@ -61,6 +99,7 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t mb = static_cast<int64_t>(blockIdx.y) * (16 * MT);  // first row of A
   // row-major: row n0 + r, bytes 32 g of each step; packed: the lane's
   // 16-byte slots of its group's 2 KB tiles
   const uint8_t* brow = PACKED ? B + static_cast<int64_t>(blockIdx.x) * (K / 128) * 2048 + lane * 16
@@ -68,7 +107,7 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
   const int64_t bstep = PACKED ? 2048 : 128, bhalf = PACKED ? 1024 : 16;
   const uint8_t* arow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) arow[t] = A + min<int64_t>(16 * t + r, M - 1) * lda + 32 * g;
+  for (int t = 0; t < MT; ++t) arow[t] = A + min<int64_t>(mb + 16 * t + r, M - 1) * lda + 32 * g;
 
   // this wave's K steps: [s0, s1)
   const int nk = static_cast<int>(K / 128);
@@ -78,16 +117,36 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Two steps per iteration (loads of both first, then both MFMAs): twice
   // the bytes in flight per wave.  An odd last step loads step s1 - 1 again
-  // (a cache hit) and multiplies zeros in its place.
+  // (a cache hit) and must add nothing: the FP8 variant skips its MFMAs (a
+  // wave-uniform branch); the exact one, whose widening the compiler then
+  // schedules worse, multiplies +0 codes on both sides instead (never a
+  // stand-in zero against a real code: 0 x Inf would be NaN).
   auto mma = [&](const u32x4& b0, const u32x4& b1, const u32x4 (&a0)[MT], const u32x4 (&a1)[MT], bool on) {
     i32x8 bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bf[e] = on ? bf[e] : 0;
+      for (int e = 0; e < 8; ++e) bf[e] = on ? bf[e] : 0;
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const i32x8 af = i32x8{(int)a0[t][0], (int)a0[t][1], (int)a0[t][2], (int)a0[t][3],
-                             (int)a1[t][0], (int)a1[t][1], (int)a1[t][2], (int)a1[t][3]};
-      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[t], FB, FA, 0, 0, 0, 0);
+      i32x8 af = i32x8{(int)a0[t][0], (int)a0[t][1], (int)a0[t][2], (int)a0[t][3],
+                       (int)a1[t][0], (int)a1[t][1], (int)a1[t][2], (int)a1[t][3]};
+      if constexpr (EXACT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) af[e] = on ? af[e] : 0;
+      }
+      if constexpr (EXACT) {
+        // the step's 128 K as 4 bf16 MFMAs of 32: instruction j takes codes
+        // [8 j, +8) of every lane's 32 on both operands (the same K set in
+        // the same order, a permutation of the step that the per-row scales
+        // do not see); products exact, FP32 accumulation
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8<FB>(bf[2 * j], bf[2 * j + 1]),
+                                                           widen8<FA>(af[2 * j], af[2 * j + 1]), acc[t], 0, 0, 0);
+      } else {
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[t], FB, FA, 0, 0, 0, 0);
+      }
     }
   };
   for (int st = s0; st < s1; st += 2) {
@@ -107,7 +166,11 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
       d1[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko2 + 16);
     }
     mma(b0, b1, a0, a1, true);
-    mma(c0, c1, d0, d1, st + 1 < s1);
+    if constexpr (EXACT) {
+      mma(c0, c1, d0, d1, st + 1 < s1);
+    } else {
+      if (st + 1 < s1) mma(c0, c1, d0, d1, true);
+    }
   }
 
   // The partial sums meet in LDS; wave 0 finishes.
@@ -122,7 +185,7 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
 #pragma unroll 1
     for (int w = 0; w < kSkWaves - 1; ++w) acc[t] += red[w][t][lane];
 
-  // lane: output row m = 16 t + r, columns n0 + 4 g + (0..3)
+  // lane: output row m = mb + 16 t + r, columns n0 + 4 g + (0..3)
   const int64_t nb = n0 + 4 * g;
   float sbv[4], bv[4];
 #pragma unroll
@@ -136,7 +199,7 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int64_t m = 16 * t + r;
+    const int64_t m = mb + 16 * t + r;
     if (m >= M) continue;
     const float sav = sa[era == 1 ? m : 0];
     float v[4];
@@ -162,22 +225,41 @@ __global__ __launch_bounds__(kSkThreads, 8) void k_gemm_skinny(
   }
 }
 
-template <int FA, int FB, int MT, bool PACKED>
-void launch_mt(const GemmArgs& g, hipStream_t st, int vec) {
-  const dim3 grid(static_cast<unsigned>((g.N + 15) / 16));
+template <int FA, int FB, int MT, bool PACKED, bool EXACT>
+void launch_mt_e(const GemmArgs& g, hipStream_t st, int vec) {
+  const dim3 grid(static_cast<unsigned>((g.N + 15) / 16), static_cast<unsigned>((g.M + 16 * MT - 1) / (16 * MT)));
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
   if (g.yt == FP8RT_BF16)
-    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, true, PACKED>), grid, dim3(kSkThreads), 0, st, g.a, g.lda, g.b,
-                       g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, true, PACKED, EXACT>), grid, dim3(kSkThreads), 0, st, g.a, g.lda,
+                       g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, false, PACKED>), grid, dim3(kSkThreads), 0, st, g.a, g.lda, g.b,
-                       g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, false, PACKED, EXACT>), grid, dim3(kSkThreads), 0, st, g.a,
+                       g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+}
+
+template <int FA, int FB, int MT, bool PACKED>
+void launch_mt(const GemmArgs& g, hipStream_t st, int vec) {
+  if (g.exact_products) launch_mt_e<FA, FB, MT, PACKED, true>(g, st, vec);
+  else launch_mt_e<FA, FB, MT, PACKED, false>(g, st, vec);
+}
+
+// Row tiles of A per workgroup.  All of M in one workgroup reads B once,
+// which is what counts when the 16-row groups of B alone give every CU a
+// workgroup; with fewer groups of B each 16-row tile of A gets a workgroup of
+// its own (B re-read per tile, mostly from L2): up to four times the CUs and
+// a quarter of the matrix-core work per SIMD (64 x 2048 x 2048: 18.1 -> 14.2
+// us per call; 64 x 4096 x 4096, 256 groups: 21.2 with one workgroup per
+// group, 23.2 split).
+int skinny_row_tiles(const GemmArgs& g) {
+  if ((g.N + 15) / 16 < static_cast<int64_t>(device_cus())) return 1;
+  return g.M <= 16 ? 1 : g.M <= 32 ? 2 : 4;
 }
 
 template <int FA, int FB, bool PACKED>
 void launch_rows(const GemmArgs& g, hipStream_t st, int vec) {
-  if (g.M <= 16) launch_mt<FA, FB, 1, PACKED>(g, st, vec);
-  else if (g.M <= 32) launch_mt<FA, FB, 2, PACKED>(g, st, vec);
+  const int mt = skinny_row_tiles(g);
+  if (mt == 1) launch_mt<FA, FB, 1, PACKED>(g, st, vec);
+  else if (mt == 2) launch_mt<FA, FB, 2, PACKED>(g, st, vec);
   else launch_mt<FA, FB, 4, PACKED>(g, st, vec);
 }
 

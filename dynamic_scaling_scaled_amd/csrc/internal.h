@@ -99,6 +99,7 @@ struct GemmArgs {
   int64_t ldy;
   bool pow2_mx;  // 1x32 power-of-two scales through the scaled MFMA
   bool b_packed = false;  // b is fragment-ordered (launch_pack_weights16)
+  bool exact_products = false;  // decode kernel: codes widened to bf16, bf16 MFMA
   // FP8 output (fp8_scaled_gemm_fp8out) when yq_fmt >= 0: y then holds codes
   // of y_fp32 * r_y, r_y = ry[0] or fl32(1 / sy[0]); per-block partials of
   // max |y| and the saturation / underflow counts go to part.

@@ -124,7 +124,8 @@ def test_gemm_validation(rt, fn):
     assert g(rt, M=0) == rt.EINVAL
     assert g(rt, lda=64) == rt.EINVAL
     assert g(rt, ldy=32) == rt.EINVAL
-    assert g(rt, flags=4) == rt.EINVAL
+    assert g(rt, flags=8) == rt.EINVAL
+    assert g(rt, flags=15) == rt.EINVAL
     assert g(rt, fa=9) == rt.EINVAL
     assert g(rt, K=120, lda=128, ldb=128) == rt.EALIGN
     assert g(rt, lda=136) == rt.EALIGN
@@ -136,11 +137,18 @@ def test_gemm_validation(rt, fn):
     assert g(rt, K=256, lda=256, ldb=256, ga=(1, 32), gb=(1, 32)) == rt.EUNSUPPORTED      # 1x32 needs POW2 flag
     assert g(rt, K=256, lda=256, ldb=256, ga=(2, 128), gb=(0, 0)) == rt.EUNSUPPORTED      # A blocks span rows
     # the packed weight image: decode shapes only
-    assert g(rt, flags=6) == rt.EINVAL
+    assert g(rt, flags=10) == rt.EINVAL
     assert g(rt, flags=rt.B_PACKED16, M=80, ldy=64) == rt.EUNSUPPORTED                    # M = 80 > 64
     assert g(rt, flags=rt.B_PACKED16, M=16, K=144, lda=144, ldb=144) == rt.EUNSUPPORTED  # K % 128
     assert g(rt, flags=rt.B_PACKED16, M=8, K=256, lda=256, ga=(1, 128)) == rt.EUNSUPPORTED  # K-group scales
     assert g(rt, flags=rt.B_PACKED16, M=8, lda=64) == rt.EINVAL                           # lda < K still checked
+    # exact products: decode shapes only, row-major or packed
+    X = rt.EXACT_PRODUCTS
+    assert g(rt, flags=X, M=80, ldy=64) == rt.EUNSUPPORTED                                # M = 80 > 64
+    assert g(rt, flags=X, M=16, K=144, lda=144, ldb=144) == rt.EUNSUPPORTED              # K % 128
+    assert g(rt, flags=X, M=8, K=256, lda=256, ldb=256, gb=(128, 128)) == rt.EUNSUPPORTED  # block scales
+    assert g(rt, flags=X | rt.B_PACKED16, M=65, ldy=64) == rt.EUNSUPPORTED
+    assert g(rt, flags=X | rt.POW2_SCALES, K=256, lda=256, ldb=256, ga=(1, 32), gb=(1, 32)) == rt.EUNSUPPORTED
 
 
 def qtr(rt, **kw):
@@ -185,6 +193,7 @@ def test_gemm_fp8out_validation(rt):
     assert call(sy=FAKE + 2) == rt.EALIGN
     assert call(M=128 * 8193, N=128, ldy=128) == rt.EUNSUPPORTED
     assert call(flags=rt.B_PACKED16) == rt.EUNSUPPORTED
+    assert call(flags=rt.EXACT_PRODUCTS) == rt.EUNSUPPORTED  # FP8 matrix cores only
 
 
 def test_weight_only_gemm_validation(rt):
@@ -218,6 +227,7 @@ def test_weight_only_gemm_validation(rt):
     assert call(gw=(1, 64)) == rt.EUNSUPPORTED   # K groups are whole 128-deep steps
     assert call(gw=(1, 192)) == rt.EUNSUPPORTED
     assert call(flags=1) == rt.EINVAL                                       # POW2 means nothing here
+    assert call(flags=4) == rt.EINVAL                                       # products are exact already
     assert call(flags=rt.B_PACKED16, K=144, ldx=144, ldw=144) == rt.EALIGN  # packed: K % 128
     assert call(flags=rt.B_PACKED16, K=144, ldx=144, ldw=0) == rt.EALIGN    # ldw ignored, K still checked
 

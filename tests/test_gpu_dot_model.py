@@ -17,7 +17,14 @@ exact sum (the property the GEMM tolerance relies on).
 One case per kernel route: the general kernel (small M; and K-blocked
 scales), the large kernel (per-tensor, per-row; 1x32 power-of-two scales on
 the scaled MFMA; a split last wave), the K-blocked large kernel, and the
-decode kernel on row-major and fragment-ordered weights."""
+decode kernel on row-major and fragment-ordered weights (with a weight
+above the size that selects exact products by itself; outputs compared on a
+column sample).
+
+The decode kernel's exact-product variant (chosen by itself for weights of
+at most 1 MiB of codes, or by FP8RT_EXACT_PRODUCTS) must instead return the
+exact sum bit for bit on the same operands, where the truncation model
+differs from it in most outputs."""
 import numpy as np
 import pytest
 import torch
@@ -69,12 +76,6 @@ def to_codes(orc, vals, fmt):
     return codes[inv].reshape(vals.shape)
 
 
-def magnitude_sum(a, fa, sa, ga, b, sb, gb):
-    """sum_k |s_a s_b a_k b_k| per output, from the model's exact sums of |codes|."""
-    _, exa = dm.emulate_full(a & 0x7F, fa, np.abs(sa), ga, b & 0x7F, E4M3, np.abs(sb), gb)
-    return exa
-
-
 def scales_for(g, rows, K, gran, pow2_values):
     er = rows if gran[0] <= 0 else gran[0]
     ec = K if gran[1] <= 0 or gran[1] >= K else gran[1]
@@ -90,8 +91,17 @@ ROUTES = [
     ("big-row", 384, 256, 512, (1, 0), (1, 0), 0, [1.0, 2.0], False),
     ("big-mx32", 256, 256, 512, (1, 32), (1, 32), 1, [1.0, 2.0], False),
     ("kblock", 256, 256, 512, (1, 128), (128, 128), 0, [1.0, 2.0], False),
-    ("decode", 16, 256, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
-    ("decode-packed", 16, 256, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], True),
+    ("decode", 16, 4224, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
+    ("decode-packed", 48, 4224, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], True),
+]
+
+POW2, EXACT = 1, 4  # FP8RT_POW2_SCALES, FP8RT_EXACT_PRODUCTS
+EXACT_ROUTES = [
+    ("decode-auto", 16, 256, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
+    ("decode-auto-m64", 64, 256, 1024, (0, 0), (1, 0), 0, [2.0], False),
+    ("decode-auto-packed", 40, 512, 2048, (1, 0), (0, 0), 0, [1.0, 2.0], True),
+    ("decode-flag", 16, 4224, 1024, (1, 0), (1, 0), EXACT, [1.0, 2.0], False),
+    ("decode-flag-packed", 32, 4224, 1024, (1, 0), (1, 0), EXACT, [1.0, 2.0], True),
 ]
 
 
@@ -101,10 +111,31 @@ def run(rt, a, fa, ga, sa, b, gb, sb, flags, packed):
     bd = dev(b)
     if packed:
         bd = rt.fp8_pack_weights16(bd)
-    rt.fp8_scaled_gemm(dev(a), fa, ga, dev(sa), bd, E4M3, gb, dev(sb), y,
-                       flags=rt.POW2_SCALES if flags else 0)
+    rt.fp8_scaled_gemm(dev(a), fa, ga, dev(sa), bd, E4M3, gb, dev(sb), y, flags=flags)
     torch.cuda.synchronize()
     return host(y)
+
+
+def sample_cols(N):
+    """All columns up to 512; else the first 256, the last 80 (the ragged
+    end of the grid) and 64 in between."""
+    if N <= 512:
+        return np.arange(N)
+    g = np.random.default_rng(N)
+    return np.unique(np.concatenate([np.arange(256), np.arange(N - 80, N), g.integers(256, N - 80, 64)]))
+
+
+def model_on(orc, a, fa, sa, ga, b, sb, gb, cols):
+    """(truncation model, exact sum, T_hw, sum of magnitudes) on every row x
+    the given columns."""
+    M = a.shape[0]
+    m = np.repeat(np.arange(M), len(cols))
+    n = np.tile(cols, M)
+    shape = (M, len(cols))
+    emu, exa = dm.emulate_points(a, fa, sa, ga, b, E4M3, sb, gb, m, n)
+    _, mag = dm.emulate_points(a & 0x7F, fa, np.abs(sa), ga, b & 0x7F, E4M3, np.abs(sb), gb, m, n)
+    thw = orc.dot_truncation_bound(a, fa, sa, ga, b, E4M3, sb, gb, m, n)
+    return emu.reshape(shape), exa.reshape(shape), thw.reshape(shape), mag.reshape(shape)
 
 
 @pytest.mark.parametrize("fa", [E4M3, E5M2])
@@ -115,8 +146,9 @@ def test_kernel_matches_truncation_model(rt, orc, route, fa):
     a, b = structured(orc, seed, M, N, K, fa, signed=False)
     g = np.random.default_rng(seed + 1)
     sa, sb = scales_for(g, M, K, ga, svals), scales_for(g, N, K, gb, [1.0])
-    y = run(rt, a, fa, ga, sa, b, gb, sb, flags, packed)
-    emu, exa = dm.emulate_full(a, fa, sa, ga, b, E4M3, sb, gb)
+    cols = sample_cols(N)
+    y = run(rt, a, fa, ga, sa, b, gb, sb, flags, packed)[:, cols]
+    emu, exa, _, _ = model_on(orc, a, fa, sa, ga, b, sb, gb, cols)
     # all partial sums are multiples of 2^-6 below 2^18: exact in FP32
     assert np.all(exa < 2.0 ** 18)
     same = y.astype(np.float64) == emu
@@ -134,14 +166,38 @@ def test_kernel_signed_matches_model(rt, orc, route, fa):
     a, b = structured(orc, seed, M, N, K, fa, signed=True)
     g = np.random.default_rng(seed + 1)
     sa, sb = scales_for(g, M, K, ga, svals), scales_for(g, N, K, gb, [1.0])
-    y = run(rt, a, fa, ga, sa, b, gb, sb, flags, packed).astype(np.float64)
-    emu, exa = dm.emulate_full(a, fa, sa, ga, b, E4M3, sb, gb)
-    assert np.all(magnitude_sum(a, fa, sa, ga, b, sb, gb) < 2.0 ** 18)
-    thw = orc.dot_truncation_bound_full(a, fa, sa, ga, b, E4M3, sb, gb)
+    cols = sample_cols(N)
+    y = run(rt, a, fa, ga, sa, b, gb, sb, flags, packed)[:, cols].astype(np.float64)
+    emu, exa, thw, mag = model_on(orc, a, fa, sa, ga, b, sb, gb, cols)
+    assert np.all(mag < 2.0 ** 18)
     print(name, fa, "signed: equal to the toward-zero model %d of %d, max |y - exact| / T_hw = %.3f" % (
         int((y == emu).sum()), y.size, float((np.abs(y - exa) / np.maximum(thw, 1e-300)).max())))
     assert np.all(np.abs(y - exa) <= thw)
     assert np.array_equal(y, emu)
+
+
+@pytest.mark.parametrize("signed", [False, True], ids=["positive", "signed"])
+@pytest.mark.parametrize("fa", [E4M3, E5M2])
+@pytest.mark.parametrize("route", EXACT_ROUTES, ids=[r[0] for r in EXACT_ROUTES])
+def test_exact_products_give_the_exact_sum(rt, orc, route, fa, signed):
+    """Every partial sum of these operands is a multiple of 2^-6 below 2^18,
+    exact in FP32 in any order: with exact products the output is the exact
+    sum, where the FP8 matrix cores' truncation shows in most outputs."""
+    name, M, N, K, ga, gb, flags, svals, packed = route
+    seed = case_seed("dotmodel-exact", name, fa, signed)
+    a, b = structured(orc, seed, M, N, K, fa, signed=signed)
+    g = np.random.default_rng(seed + 1)
+    sa, sb = scales_for(g, M, K, ga, svals), scales_for(g, N, K, gb, [1.0])
+    assert (flags & EXACT) or N * K <= rt.EXACT_AUTO_BYTES
+    cols = sample_cols(N)
+    y = run(rt, a, fa, ga, sa, b, gb, sb, flags, packed)[:, cols].astype(np.float64)
+    emu, exa, _, mag = model_on(orc, a, fa, sa, ga, b, sb, gb, cols)
+    assert np.all(mag < 2.0 ** 18)
+    same = y == exa
+    print(name, fa, signed, "equal to the exact sum %d of %d; the truncation model differs from it in %d" % (
+        int(same.sum()), same.size, int((emu != exa).sum())))
+    assert same.all(), (np.argwhere(~same)[:5], y[~same][:5], exa[~same][:5])
+    assert (emu != exa).mean() > 0.3
 
 
 def test_split_last_wave_matches_model(rt, orc):
@@ -160,3 +216,33 @@ def test_split_last_wave_matches_model(rt, orc):
     same = y[m, n].astype(np.float64) == emu
     print("split: equal to the model %d of %d" % (int(same.sum()), same.size))
     assert same.all()
+
+
+@pytest.mark.parametrize("flags", [0, EXACT], ids=["auto", "flag"])
+@pytest.mark.parametrize("fa", [E4M3, E5M2])
+def test_exact_products_reproduce_every_code(rt, orc, fa, flags):
+    """One-hot operands, so each output is one product: y[m, n] = dec(A[m, n])
+    * dec(B[n, n]) with B's diagonal cycling through 2^-3 .. 2^3 (every finite
+    code of A's format, subnormals and signed zeros included, at every K
+    position mod 16), then y[m, n] = dec(B[n, m]) against A = identity (every
+    finite E4M3 code of B).  Exact in FP32, so equal bit for bit up to the
+    sign of zero."""
+    M, N, K = 16, 256, 256
+    ta, tb = orc.decode_table(fa), orc.decode_table(E4M3)
+    fin_a = np.flatnonzero(np.isfinite(ta)).astype(np.uint8)
+    fin_b = np.flatnonzero(np.isfinite(tb)).astype(np.uint8)
+    one = np.ones((1, 1), np.float32)
+    pow2 = to_codes(orc, 2.0 ** (np.arange(N) % 7 - 3), E4M3)
+    kk = np.arange(K)
+    a = fin_a[(16 * np.arange(M)[:, None] + kk[None, :]) % len(fin_a)]
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), np.arange(N)] = pow2
+    y = run(rt, a, fa, (0, 0), one, b, (0, 0), one, flags, False).astype(np.float64)
+    want = ta[a[:, :N]] * tb[pow2][None, :]
+    assert np.array_equal(y, want), np.argwhere(y != want)[:5]
+    a = np.zeros((M, K), np.uint8)
+    a[np.arange(M), np.arange(M)] = to_codes(orc, np.ones(M), fa)
+    b = fin_b[(np.arange(N)[:, None] + kk[None, :]) % len(fin_b)]
+    y = run(rt, a, fa, (0, 0), one, b, (0, 0), one, flags, False).astype(np.float64)
+    want = tb[b[:, :M]].T
+    assert np.array_equal(y, want), np.argwhere(y != want)[:5]
