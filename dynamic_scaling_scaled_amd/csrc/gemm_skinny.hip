@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
   if (wave != 0) return;
 #pragma unroll
   for (int t = 0; t < MT; ++t)
-#pragma unroll 1
+#pragma unroll 5  // 15 partials: three batches of 5 reads in flight
     for (int w = 0; w < kSkWaves - 1; ++w) acc[t] += red[w][t][lane];
 
   // lane: output row m = mb + 16 t + r, columns n0 + 4 g + (0..3)

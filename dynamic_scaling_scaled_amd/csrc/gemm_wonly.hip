@@ -9,8 +9,8 @@
 //
 // Design for MI355X:
 //  - Every E4M3 and E5M2 value is exactly a bf16 value, so the codes are
-//    widened to bf16 in registers (v_cvt_pk_f32_fp8 / _bf8, then the high
-//    halves packed by one byte permute) and multiplied on
+//    widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8 / _bf8 with
+//    scale 1, two codes per instruction) and multiplied on
 //    v_mfma_f32_16x16x32_bf16, whose bf16 x bf16 products are exact in FP32.
 //    The weight scale is applied in FP32: once in the epilogue for tensor /
 //    channel scales, or to each 128-deep step's partial sum for K-group
@@ -48,24 +48,24 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWoWaves = 16;
 constexpr int kWoThreads = kWoWaves * 64;
 constexpr int kWoTiles = 2;            // 16-column tiles per workgroup
 constexpr int kWoCols = 16 * kWoTiles;
 
-// Two FP8 codes of a dword half -> two floats (exact), then the high halves
-// of both packed into one dword of two bf16 (element order kept).
+// Two FP8 codes of a dword half -> two bf16 in one dword (element order
+// kept), by one conversion whose scale operand is 1.0: exact.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int F, bool HI>
 __device__ __forceinline__ uint32_t widen2(uint32_t w) {
-  f32x2 f;
+  bf16x2 h;
   if constexpr (F == kE4M3) {
-    f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+    h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI);
   } else {
-    f = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), HI);
+    h = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(static_cast<int>(w), 1.0f, HI);
   }
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // 8 codes (2 dwords, K order) -> 8 bf16 in K order.
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kWoThreads, 1) void k_gemm_wonly(
   if (wave != 0) return;
 #pragma unroll
   for (int t = 0; t < kWoTiles; ++t)
-#pragma unroll 1
+#pragma unroll 5  // 15 partials: three batches of 5 reads in flight
     for (int w = 0; w < kWoWaves - 1; ++w) acc[t] += red[w][t][lane];
   if (m >= M) return;
 
