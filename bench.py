@@ -790,10 +790,13 @@ def extra_components(torch, rt, wl, keep):
                                "wq": gather(torch, Wq, rb), "s_g": s_used.cpu().numpy(),
                                "s_w": sw.cpu().numpy(), "r_w": rw.cpu().numpy(), "y": gather(torch, y, ra, rb),
                                "steps": steps, "chain_g": chain_g}
-    later = slice(1, None)  # GIVEN steps
-    qus = Timing(float(np.median(steps["quantize_us"][later])), float(np.percentile(steps["quantize_us"][later], 95)))
     gus = Timing(float(np.median(steps["gemm_us"])), float(np.percentile(steps["gemm_us"], 95)))
-    comp["delayed_quantize_g_given_e5m2"] = hbm_entry(qus, M * K * 3 + 4,
+    # the GIVEN-mode quantize of the last step's G with the history's next
+    # scale, timed like every other component (the chain's per-step times
+    # follow each step's host-side draw of G_t, half a second with the GPU
+    # idle, so they also hold the clock's ramp back up)
+    qg = lambda: rt.fp8_quantize(G, (0, 0), rt.E5M2, rt.GIVEN, 1e-12, False, sg, rg, Gq, am, cnt)
+    comp["delayed_quantize_g_given_e5m2"] = hbm_entry(time_op(torch, qg, scrub=scrub), M * K * 3 + 4,
                                                        "k_tensor_cast (given, amax + counts) + k_finish")
     comp["delayed_history_update_us"] = float(np.median(steps["history_update_us"]))
     comp["delayed_gemm_e5m2_e4m3_f32"] = mfma_entry(gus, 2.0 * M * N * K, M * K + N * K + M * N * 4 + 8)
@@ -802,6 +805,7 @@ def extra_components(torch, rt, wl, keep):
                     "E5M2, 16-entry amax history (step 0 current scaling); W 8192x8192 per-tensor E4M3; "
                     "fp32 out" % [int(v) for v in spikes],
         "per_step": steps,
+        "per_step_timing": "event-timed after a cache scrub, right after the host draws G_t (GPU idle meanwhile)",
         "saturated_total": int(sum(steps["saturated"])), "underflowed_total": int(sum(steps["underflowed"])),
         "steps_with_saturation": int(sum(v > 0 for v in steps["saturated"]))}
     # cast-transpose of the last step's G (the backward reads it in both
