@@ -13,18 +13,22 @@
 //  - Two LDS stages of 128 K bytes (64 KB each).  A stage row is 128 bytes,
 //    a whole cache line, so every vector-memory request moves a full line
 //    (64-byte half rows doubled the L1->L2 request count and stalled the
-//    address path).  Operands move HBM -> LDS with global_load_lds_dwordx4
-//    (no VGPR staging): one instruction fills 8 rows; each lane picks the
-//    global chunk that belongs at its LDS slot, an XOR swizzle of the 8
-//    chunks of a row by (row / 2) that makes the ds_read_b128 fragment reads
-//    conflict-free on the 64-bank LDS.
+//    address path).  Operands move HBM -> LDS with buffer_load_dwordx4 ...
+//    lds (no VGPR staging; a uniform buffer descriptor per operand tile, the
+//    lane's row / chunk offset in a VGPR and the stage's K offset in an SGPR,
+//    so no per-load address arithmetic): one instruction fills 8 rows; each
+//    lane picks the global chunk that belongs at its LDS slot, an XOR swizzle
+//    of the 8 chunks of a row by (row / 2) that makes the ds_read_b128
+//    fragment reads conflict-free on the 64-bank LDS.
 //  - Software pipeline over sub-steps, with two fragment register sets P/Q:
 //    even sub-step 2j multiplies P (stage j, K bytes 0-63) while it reads
-//    stage j, K bytes 64-127 into Q, then waits for stage j+1 and joins one
-//    s_barrier (stage j is then free); odd sub-step 2j+1 multiplies Q while
-//    it refills stage j's arrays with stage j+2 and reads stage j+1 into P.
-//    One barrier per 128-deep stage; scheduling groups interleave the LDS
-//    reads and the loads between the MFMAs.
+//    stage j, K bytes 64-127 into Q, then joins a barrier (every wave has
+//    read stage j: its arrays are free); odd sub-step 2j+1 refills them with
+//    stage j+2 during its first 8 MFMAs on Q, waits for stage j+1 (issued
+//    one odd sub-step earlier, so 2.5 sub-steps in flight) and joins a
+//    second barrier, then reads stage j+1 into P during its last 8 MFMAs.
+//    Scheduling groups interleave the LDS reads and the loads between the
+//    MFMAs.
 //  - Tile order: blocks are dealt round-robin to the 8 XCDs; each XCD gets a
 //    contiguous range of a grouped (GROUP_M M-tiles x all N-tiles) order, so
 //    the 32 CUs of an XCD share A and B slices in their own L2.
@@ -67,15 +71,6 @@ constexpr int GROUP_M = 4;
 // Byte offset of 16-byte chunk c (0..7) of stage row r (128-byte rows).
 __device__ __forceinline__ int swz(int r, int c) { return r * TKS + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int NDMA>
-__device__ __forceinline__ void dma_tile(const uint8_t* base, const uint32_t (&voff)[NDMA], uint8_t* lds,
-                                         int wave) {
-#pragma unroll
-  for (int j = 0; j < NDMA; ++j)
-    __builtin_amdgcn_global_load_lds((gbl_void*)(base + voff[j]), (lds_void*)(lds + (wave * NDMA + j) * 1024),
-                                     16, 0, 0);
-}
-
 // 32x32x64 operand of sub-step h: lane l holds row (l % 32); the matrix
 // core reads the lane's first 16 bytes as K [16 g, 16 g + 16) and the last 16
 // as K [32 + 16 g, 48 + 16 g) of the sub-step, g = l / 32, so the lane loads
@@ -108,6 +103,38 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[MI][NJ],
                                           const uint32_t (&xb)[NJ]) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (MX)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, OPSEL,
+                                                                    xb[j], OPSEL, xa[i]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    }
+}
+
+template <int NDMA>
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, int soff, const uint32_t (&voff)[NDMA], uint8_t* lds,
+                                        int wave) {
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * NDMA + j) * 1024), 16,
+                                             static_cast<int>(voff[j]), soff, 0, 0);
+}
+
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Half of a sub-step's MFMAs: row tiles 2 H and 2 H + 1.
+template <int FA, int FB, bool MX, int OPSEL, int H>
+__device__ __forceinline__ void mfma_step_half(const Frags& f, f32x16 (&acc)[MI][NJ], const uint32_t (&xa)[MI],
+                                               const uint32_t (&xb)[NJ]) {
+#pragma unroll
+  for (int i = 2 * H; i < 2 * H + 2; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if constexpr (MX)
@@ -321,8 +348,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
   }
-  const uint8_t* a_base = A + m0 * lda + static_cast<int64_t>(s0) * TKS;
-  const uint8_t* b_base = B + n0 * ldb + static_cast<int64_t>(s0) * TKS;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(A + m0 * lda + static_cast<int64_t>(s0) * TKS), 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(B + n0 * ldb + static_cast<int64_t>(s0) * TKS), 0, -1, 0x00020000);
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -371,18 +400,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
   };
   sc_dma(0, sX0);
   sc_dma(1, sX1);
-  dma_tile<kDmaA>(a_base, voa, sA0, wave);
-  dma_tile<kDmaB>(b_base, vob, sB0, wave);
-  dma_tile<kDmaA>(a_base + TKS, voa, sA1, wave);
-  dma_tile<kDmaB>(b_base + TKS, vob, sB1, wave);
+  dma_buf<kDmaA>(ra, 0, voa, sA0, wave);
+  dma_buf<kDmaB>(rb, 0, vob, sB0, wave);
+  dma_buf<kDmaA>(ra, TKS, voa, sA1, wave);
+  dma_buf<kDmaB>(rb, TKS, vob, sB1, wave);
   step_barrier<kDmaStage>();  // stage 0 (and the scales, issued first) landed
   Frags fp, fq;
   read_frags(fp, sA0, sB0, wm, wn, fr, c_lo);
   sc_read(sX0, xa0, xb0);
   // Sub-step 2j: MFMAs on P (stage j, first half), read stage j second half
-  // into Q; then wait for stage j+1 and join the barrier (stage j is free).
-  // Sub-step 2j+1: MFMAs on Q, refill stage j's arrays with stage j+2, read
-  // stage j+1 first half into P.
+  // into Q; then the barrier after which stage j's arrays are free (stage
+  // j+1's loads stay in flight).  Sub-step 2j+1: refill stage j's arrays with
+  // stage j+2 during the first half of the MFMAs on Q, wait for stage j+1
+  // and join the barrier, then read its first half into P during the second.
+  constexpr int kVmStage = kDmaStage + (MX ? 1 : 0);  // vector-memory ops per stage and wave
 #define FP8RT_EVEN(LA, LB, XA, XB)                                            \
   {                                                                           \
     read_frags(fq, LA, LB, wm, wn, fr, c_hi);                                 \
@@ -396,29 +427,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
     }                                                                         \
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                        \
-    step_barrier<0>();                                                        \
+    step_barrier<kVmStage>();                                                 \
   }
 #define FP8RT_ODD(DA, DB, DX, KS, LA, LB, LX, XA, XB, NXA, NXB)              \
   {                                                                           \
-    sc_read(LX, NXA, NXB);                                                    \
     const int kn = min(KS, ns - 1);                                           \
-    dma_tile<kDmaA>(a_base + kn * TKS, voa, DA, wave);                        \
-    dma_tile<kDmaB>(b_base + kn * TKS, vob, DB, wave);                        \
+    dma_buf<kDmaA>(ra, kn * TKS, voa, DA, wave);                              \
+    dma_buf<kDmaB>(rb, kn * TKS, vob, DB, wave);                              \
     sc_dma(KS, DX);                                                           \
-    read_frags(fp, LA, LB, wm, wn, fr, c_lo);                                 \
-    mfma_step<FA, FB, MX, 2>(fq, acc, XA, XB);                                \
-    for (int s = 0; s < 4; ++s) {                                             \
+    mfma_step_half<FA, FB, MX, 2, 0>(fq, acc, XA, XB);                        \
+    for (int s = 0; s < 8; ++s) {                                             \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
     }                                                                         \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                        \
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                        \
+    step_barrier<kVmStage>();                                                 \
+    sc_read(LX, NXA, NXB);                                                    \
+    read_frags(fp, LA, LB, wm, wn, fr, c_lo);                                 \
+    mfma_step_half<FA, FB, MX, 2, 1>(fq, acc, XA, XB);                        \
+    for (int s = 0; s < 8; ++s) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
+    }                                                                         \
     __builtin_amdgcn_sched_barrier(0);                                        \
   }
   for (int j = 0; j < ns; j += 2) {
