@@ -19,8 +19,9 @@
 //    MFMA results in VGPRs (-amdgpu-mfma-vgpr-form) so the FMA reads them
 //    directly; the result is the transposed tile, so a lane's 4 elements of
 //    a tile share one output row and one factor.
-//  - Operands move HBM -> LDS with global_load_lds_dwordx4 into two 64 KB
-//    stages with 128-byte rows (full cache lines, XOR-swizzled by row / 2);
+//  - Operands move HBM -> LDS with buffer_load_dwordx4 ... lds (a uniform
+//    descriptor per operand tile, the stage's K offset in an SGPR) into two
+//    64 KB stages with 128-byte rows (full cache lines, XOR-swizzled by row / 2);
 //    the loads of stage g+1 fly while stage g multiplies; B's fragments are
 //    read at the stage start, A's one row tile ahead.  One s_barrier per stage.
 //  - A's group scales are transposed once per call (k_transpose_scales) so a
@@ -62,12 +63,19 @@ constexpr int kMaxStages = 2048;  // K / 128 limit (B block scales of a tile liv
 __device__ __forceinline__ int swz(int r, int c) { return r * TKS + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <int NDMA>
-__device__ __forceinline__ void dma_tile(const uint8_t* base, const uint32_t (&voff)[NDMA], uint8_t* lds,
-                                         int wave) {
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, int soff, const uint32_t (&voff)[NDMA], uint8_t* lds,
+                                        int wave) {
 #pragma unroll
   for (int j = 0; j < NDMA; ++j)
-    __builtin_amdgcn_global_load_lds((gbl_void*)(base + voff[j]), (lds_void*)(lds + (wave * NDMA + j) * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * NDMA + j) * 1024), 16,
+                                             static_cast<int>(voff[j]), soff, 0, 0);
+}
+
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // 16x16x128 operand: lane l holds row l % 16; the matrix core reads its
@@ -140,8 +148,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
   }
-  const uint8_t* a_base = A + m0 * lda;
-  const uint8_t* b_base = B + n0 * ldb;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(A + m0 * lda), 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(B + n0 * ldb), 0, -1, 0x00020000);
 
   f32x4 acc[MI][NJ];
 #pragma unroll
@@ -211,8 +219,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
   };
 
   sa_dma(0, sSa0);
-  dma_tile<kDmaA>(a_base, voa, sA0, wave);
-  dma_tile<kDmaB>(b_base, vob, sB0, wave);
+  dma_buf<kDmaA>(ra, 0, voa, sA0, wave);
+  dma_buf<kDmaB>(rb, 0, vob, sB0, wave);
   step_barrier<0>();  // stage 0, its scales and the B scale table landed
   // Stage st (in arrays X): issue the loads of stage st+1 into the other
   // arrays (free: the previous stage ended with a barrier), multiply and
@@ -221,8 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
   {                                                                           \
     const int kn = min(ST + 1, ns - 1);                                       \
     sa_dma(kn, DS);                                                           \
-    dma_tile<kDmaA>(a_base + kn * TKS, voa, DA, wave);                        \
-    dma_tile<kDmaB>(b_base + kn * TKS, vob, DB, wave);                        \
+    dma_buf<kDmaA>(ra, kn * TKS, voa, DA, wave);                              \
+    dma_buf<kDmaB>(rb, kn * TKS, vob, DB, wave);                              \
     stage_mma(LA, LB, LS, ST, FIRST);                                         \
     step_barrier<0>();                                                        \
   }
