@@ -175,3 +175,74 @@ def test_k32_per_row_scales_are_not_mx_blocks(rt, orc):
     thw = orc.dot_truncation_bound_full(a, 0, sa, (1, 0), b, 0, sb, (1, 0))
     ok, st = check_gemm(y, yref, S, False, orc, t_hw=thw)
     assert ok, st
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+@pytest.mark.parametrize("N", [256, 1152], ids=["exact-products", "fp8-cores"])
+def test_decode_gemm_special_codes(rt, orc, N, packed):
+    """E5M2 activation codes holding +Inf, -Inf and NaN in the decode kernel,
+    with K = 1024: eight 128-deep steps over 16 waves, so every wave that has
+    a step also passes its odd-count tail, which must add nothing (no 0 x Inf).
+    Non-finite outputs (Inf of either sign, NaN from Inf - Inf, 0 x Inf or a
+    NaN code) must sit exactly where the binary64 reference has them, the rest
+    within the acceptance rule.  N = 256 runs the exact-product variant
+    (automatic for small weights), N = 1152 the FP8 matrix cores."""
+    M, K = 16, 1024
+    a, sa, b, sb = operands(orc, case_seed("special", N), M, N, K, 1, 0, (1, 0), (1, 0), False)
+    a = a.copy()
+    a[0, 7 * 128 + 5] = 0x7C                  # +Inf in the last step
+    a[1, 3 * 128 + 70] = 0xFC                 # -Inf
+    a[2, 1000] = 0x7E                         # NaN
+    a[3, 10], a[3, 900] = 0x7C, 0xFC          # +Inf and -Inf in one row
+    a[4, 1023] = 0x7C                         # +Inf at the last K
+    b = b.copy()
+    b[7, :] = 0                               # a zero weight row: 0 x Inf
+    bd = dev(b)
+    if packed:
+        bd = rt.fp8_pack_weights16(bd)
+    y = torch.full((M, N), 12345.0, dtype=torch.float32, device="cuda")
+    rt.fp8_scaled_gemm(dev(a), 1, (1, 0), dev(sa), bd, 0, (1, 0), dev(sb), y)
+    torch.cuda.synchronize()
+    y = host(y)
+    yref, S = orc.gemm_full(a, 1, sa, (1, 0), b, 0, sb, (1, 0))
+    fin = np.isfinite(yref)
+    assert np.array_equal(np.isnan(y), np.isnan(yref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(yref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(yref))
+    assert (~fin).sum() >= 4 * N - 8
+    t_hw = None if N * K <= rt.EXACT_AUTO_BYTES else orc.dot_truncation_bound_full(a, 1, sa, (1, 0), b, 0, sb, (1, 0))
+    rows = fin.all(axis=1)
+    ok, st = check_gemm(y[rows], yref[rows], S[rows], False, orc, t_hw=None if t_hw is None else t_hw[rows])
+    assert ok, st
+
+
+SPECIAL_ROUTES = [  # name, M, N, K, ga, gb
+    ("general-ragged-k", 96, 160, 528, (1, 0), (1, 0)),
+    ("large", 256, 384, 512, (1, 0), (1, 0)),
+    ("kblock", 256, 256, 512, (1, 128), (128, 128)),
+]
+
+
+@pytest.mark.parametrize("route", SPECIAL_ROUTES, ids=[r[0] for r in SPECIAL_ROUTES])
+def test_gemm_special_codes_other_kernels(rt, orc, route):
+    """The same special E5M2 codes through the general kernel (a ragged last
+    K step, padded on both operands), the large kernel and the K-blocked
+    kernel: non-finite outputs exactly where the reference has them."""
+    name, M, N, K, ga, gb = route
+    a, sa, b, sb = operands(orc, case_seed("special-other", name), M, N, K, 1, 0, ga, gb, False)
+    a = a.copy()
+    a[0, K - 1] = 0x7C
+    a[1, K // 2] = 0xFC
+    a[2, 3] = 0x7E
+    a[3, 10], a[3, K - 20] = 0x7C, 0xFC
+    b = b.copy()
+    b[7, :] = 0
+    y = run_gemm(rt, a, 1, ga, sa, b, 0, gb, sb, "f32")
+    yref, S = orc.gemm_full(a, 1, sa, ga, b, 0, sb, gb)
+    assert np.array_equal(np.isnan(y), np.isnan(yref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(yref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(yref))
+    rows = np.isfinite(yref).all(axis=1)
+    t_hw = orc.dot_truncation_bound_full(a, 1, sa, ga, b, 0, sb, gb)
+    ok, st = check_gemm(y[rows], yref[rows], S[rows], False, orc, t_hw=t_hw[rows])
+    assert ok, st
