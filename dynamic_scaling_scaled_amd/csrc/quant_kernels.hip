@@ -754,7 +754,10 @@ hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;
   const int64_t nCg = ceil_div(a.cols, a.ec);
   const int64_t ng = ceil_div(a.rows, a.er) * nCg;
-  const int grid = static_cast<int>(std::min<int64_t>({ng, int64_t(8) * device_cus(), int64_t(kMaxBlocks)}));
+  // up to 32 workgroups per CU: one group each where possible (8 per CU left
+  // each workgroup several groups in sequence: 8192 x 8192 per-row 41.1 us,
+  // 37.3 at 32)
+  const int grid = static_cast<int>(std::min<int64_t>({ng, int64_t(32) * device_cus(), int64_t(kMaxBlocks)}));
   DevWorkspace* ws = nullptr;
   hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
