@@ -653,9 +653,9 @@ def extra_components(torch, rt, wl, keep):
     gm = lambda: rt.fp8_scaled_gemm(Aq, rt.E4M3, (1, 0), sa, Wq, rt.E4M3, (1, 0), sw, y, bias=bias)
     qa(); qw()
     comp["decode_quantize_a_per_token"] = hbm_entry(time_op(torch, qa, scrub=scrub), M * K * 3 + M * 4,
-                                                     "k_rowgroups")
+                                                     "k_blocktile")
     comp["decode_quantize_w_per_channel"] = hbm_entry(time_op(torch, qw, scrub=scrub), N * K * 3 + N * 4,
-                                                       "k_rowgroups")
+                                                       "k_blocktile")
     g_bytes = M * K + N * K + M * N * 2 + (M + N) * 4 + N * 2
     e = hbm_entry(time_op(torch, gm, scrub=scrub), g_bytes, "k_gemm_skinny")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
@@ -683,6 +683,20 @@ def extra_components(torch, rt, wl, keep):
     e = hbm_entry(time_op(torch, wop, scrub=scrub), wo_bytes, "k_gemm_wonly (packed W)")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_weight_only_gemm_bf16_bias_packed_w"] = e
+    # block-scaled decode: 1x128 token groups on A, 128x128 blocks on W (the
+    # same bf16 operands), on the weight image
+    Aqb, Wqb = u8(M, K), u8(N, K)
+    sab, swb = f32(M, K // 128), f32(N // 128, K // 128)
+    rt.fp8_quantize(A, (1, 128), rt.E4M3, rt.DYNAMIC, 1e-12, False, sab, None, Aqb)
+    rt.fp8_quantize(W, (128, 128), rt.E4M3, rt.DYNAMIC, 1e-12, False, swb, None, Wqb)
+    Pb = rt.fp8_pack_weights16(Wqb)
+    gmb = lambda: rt.fp8_scaled_gemm(Aqb, rt.E4M3, (1, 128), sab, Pb, rt.E4M3, (128, 128), swb, y, bias=bias)
+    gmb()
+    gb_bytes = M * K + N * K + M * N * 2 + (M * K // 128 + N * K // 16384) * 4 + N * 2
+    e = hbm_entry(time_op(torch, gmb, scrub=scrub), gb_bytes, "k_gemm_skinny (packed B, per-step scales)")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_gemm_block_scaled_bf16_bias_packed_w"] = e
+    del Aqb, Wqb, Pb
     # one decode step (per-token quantize of A, then the GEMM on the weight
     # image: two launches), eager and as a replayed HIP graph, on a stream of
     # its own that holds the library's workspace before capture

@@ -4,8 +4,9 @@
 // Method: "FP8 formats and scaling for LLM inference", section "The full
 // precision contract of one FP8 GEMM" (Y ~ s_x s_w X8 W8, FP32 accumulation,
 // BF16/FP32 output, bias) and section "Per-channel and block scaling"
-// (per-token and per-output-channel scales):
-//   Y[m,n] = s_a(m) s_b(n) sum_k dec(A[m,k]) dec(B[n,k]) + bias[n].
+// (per-token and per-output-channel scales, and scales per block):
+//   Y[m,n] = sum_g s_a(m,g) s_b(n,g) sum_{k in g} dec(A[m,k]) dec(B[n,k]) + bias[n]
+// with g over the 128-deep K steps (one group of each operand per step).
 //
 // Design for MI355X: with M <= 64 the arithmetic intensity is at most 2M
 // FLOP per byte of B, far below the MFMA ridge, so the kernel is built
@@ -26,6 +27,12 @@
 //    after the sum) do not see.
 //  - The 16 partial sums meet in LDS; wave 0 applies the scales and the bias,
 //    rounds and stores 8- or 16-byte pieces.
+//  - Scales that change along K (1 x g token groups, g_r x g weight blocks,
+//    g a multiple of 128): each step's MFMAs start from zero and the partial
+//    is added to the accumulator times s_a(m, step) s_b(n, step) (one FMA
+//    per element; the step's scales are cached loads), so the epilogue only
+//    adds the bias.  The stream of B is the same, so such decode GEMMs cost
+//    what per-channel ones do.
 //  - Exact products (a template flag): each 128-deep step becomes four
 //    v_mfma_f32_16x16x32_bf16, instruction j taking bytes [8 j, 8 j + 8) of
 //    every lane's 32 on both operands, widened exactly to bf16 in registers
@@ -87,13 +94,20 @@ constexpr int kSkMaxM = 64;  // up to 4 MFMA row tiles of A
 // 64 VGPRs) for one or two row tiles of A, or one with exact products; 4 (one
 // workgroup, 128 VGPRs) for four row tiles, whose A fragments alone fill 64
 // VGPRs, and for two with exact products (their widened operands).
-constexpr int sk_waves_per_simd(int mt, bool exact) { return (mt >= 4 || (exact && mt >= 2)) ? 4 : 8; }
+constexpr int sk_waves_per_simd(int mt, bool exact, bool kb) {
+  return (mt >= 4 || (mt >= 2 && (exact || kb)) || (exact && kb)) ? 4 : 8;
+}
 
-template <int FA, int FB, int MT, bool BF16OUT, bool PACKED, bool EXACT>
-__global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_gemm_skinny(
+// KB: scales that change along K (1 x g groups on A, g_r x g blocks on B,
+// g a multiple of 128) or whose row groups are neither one row nor all rows.
+// Each 128-deep step's partial sum then comes out of MFMAs started from zero
+// and is added to the accumulator times s_a(m, step) s_b(n, step), the
+// scales of the groups that hold the step; the epilogue adds only the bias.
+template <int FA, int FB, int MT, bool BF16OUT, bool PACKED, bool EXACT, bool KB>
+__global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void k_gemm_skinny(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
-    int64_t N, int64_t K, const float* __restrict__ sa, int64_t era, const float* __restrict__ sb,
-    int64_t erb, const void* __restrict__ bias, int bias_bf16, void* __restrict__ Y, int64_t ldy,
+    int64_t N, int64_t K, const float* __restrict__ sa, int64_t era, int64_t eca, const float* __restrict__ sb,
+    int64_t erb, int64_t ecb, const void* __restrict__ bias, int bias_bf16, void* __restrict__ Y, int64_t ldy,
     int vec_store) {
   __shared__ f32x4 red[kSkWaves - 1][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -115,20 +129,44 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // KB: offsets of the scale rows of the lane's output row (per row tile)
+  // and of its 4 output columns n0 + 4 g + e
+  int64_t aoff[KB ? MT : 1], boff[KB ? 4 : 1];
+  int spa = 1, spb = 1;  // 128-deep steps per scale group along K
+  if constexpr (KB) {
+    const int64_t nga = (K + eca - 1) / eca, ngb = (K + ecb - 1) / ecb;
+    spa = static_cast<int>(min(eca, K) / 128);
+    spb = static_cast<int>(min(ecb, K) / 128);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) aoff[t] = (min<int64_t>(mb + 16 * t + r, M - 1) / era) * nga;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) boff[e] = (min<int64_t>(n0 + 4 * g + e, N - 1) / erb) * ngb;
+  }
   // Two steps per iteration (loads of both first, then both MFMAs): twice
   // the bytes in flight per wave.  An odd last step loads step s1 - 1 again
   // (a cache hit) and must add nothing: the FP8 variant skips its MFMAs (a
   // wave-uniform branch); the exact one, whose widening the compiler then
   // schedules worse, multiplies +0 codes on both sides instead (never a
   // stand-in zero against a real code: 0 x Inf would be NaN).
-  auto mma = [&](const u32x4& b0, const u32x4& b1, const u32x4 (&a0)[MT], const u32x4 (&a1)[MT], bool on) {
+  auto mma = [&](const u32x4& b0, const u32x4& b1, const u32x4 (&a0)[MT], const u32x4 (&a1)[MT], bool on,
+                 int step) {
     i32x8 bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    // the step's scale factors (KB); a skipped tail step adds exactly zero
+    float fb[4] = {1.f, 1.f, 1.f, 1.f};
+    int ka = 0;
+    if constexpr (KB) {
+      ka = step / spa;
+      const int kb = step / spb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fb[e] = sb[boff[e] + kb];
+    }
     if constexpr (EXACT) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) bf[e] = on ? bf[e] : 0;
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
+      f32x4 c = KB ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[t];
       i32x8 af = i32x8{(int)a0[t][0], (int)a0[t][1], (int)a0[t][2], (int)a0[t][3],
                        (int)a1[t][0], (int)a1[t][1], (int)a1[t][2], (int)a1[t][3]};
       if constexpr (EXACT) {
@@ -142,10 +180,17 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
         // do not see); products exact, FP32 accumulation
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8<FB>(bf[2 * j], bf[2 * j + 1]),
-                                                           widen8<FA>(af[2 * j], af[2 * j + 1]), acc[t], 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8<FB>(bf[2 * j], bf[2 * j + 1]),
+                                                      widen8<FA>(af[2 * j], af[2 * j + 1]), c, 0, 0, 0);
       } else {
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[t], FB, FA, 0, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, c, FB, FA, 0, 0, 0, 0);
+      }
+      if constexpr (KB) {
+        const float fa = sa[aoff[t] + ka];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(on ? fa * fb[e] : 0.0f, c[e], acc[t][e]);
+      } else {
+        acc[t] = c;
       }
     }
   };
@@ -165,11 +210,11 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
       d0[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko2);
       d1[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko2 + 16);
     }
-    mma(b0, b1, a0, a1, true);
+    mma(b0, b1, a0, a1, true, st);
     if constexpr (EXACT) {
-      mma(c0, c1, d0, d1, st + 1 < s1);
+      mma(c0, c1, d0, d1, st + 1 < s1, st2);
     } else {
-      if (st + 1 < s1) mma(c0, c1, d0, d1, true);
+      if (st + 1 < s1) mma(c0, c1, d0, d1, true, st2);
     }
   }
 
@@ -191,7 +236,7 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t n = min(nb + e, N - 1);
-    sbv[e] = sb[erb == 1 ? n : 0];
+    sbv[e] = KB ? 1.0f : sb[erb == 1 ? n : 0];
     bv[e] = 0.0f;
     if (bias)
       bv[e] = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[n]) << 16)
@@ -201,7 +246,7 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
   for (int t = 0; t < MT; ++t) {
     const int64_t m = mb + 16 * t + r;
     if (m >= M) continue;
-    const float sav = sa[era == 1 ? m : 0];
+    const float sav = KB ? 1.0f : sa[era == 1 ? m : 0];
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = acc[t][e] * (sav * sbv[e]) + bv[e];
@@ -225,16 +270,32 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT)) void k_ge
   }
 }
 
-template <int FA, int FB, int MT, bool PACKED, bool EXACT>
-void launch_mt_e(const GemmArgs& g, hipStream_t st, int vec) {
+// Scales the epilogue applies: per tensor or per row on both sides, whole K.
+bool skinny_epilogue_scales(const GemmArgs& g) {
+  return (g.era == 1 || g.era >= g.M) && (g.erb == 1 || g.erb >= g.N) && g.eca >= g.K && g.ecb >= g.K;
+}
+
+template <int FA, int FB, int MT, bool PACKED, bool EXACT, bool KB>
+void launch_mt_k(const GemmArgs& g, hipStream_t st, int vec) {
   const dim3 grid(static_cast<unsigned>((g.N + 15) / 16), static_cast<unsigned>((g.M + 16 * MT - 1) / (16 * MT)));
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
   if (g.yt == FP8RT_BF16)
-    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, true, PACKED, EXACT>), grid, dim3(kSkThreads), 0, st, g.a, g.lda,
-                       g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, true, PACKED, EXACT, KB>), grid, dim3(kSkThreads), 0, st, g.a,
+                       g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.eca, g.sb, g.erb, g.ecb, g.bias, bb, g.y,
+                       g.ldy, vec);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, false, PACKED, EXACT>), grid, dim3(kSkThreads), 0, st, g.a,
-                       g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec);
+    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, false, PACKED, EXACT, KB>), grid, dim3(kSkThreads), 0, st, g.a,
+                       g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.eca, g.sb, g.erb, g.ecb, g.bias, bb, g.y,
+                       g.ldy, vec);
+}
+
+template <int FA, int FB, int MT, bool PACKED, bool EXACT>
+void launch_mt_e(const GemmArgs& g, hipStream_t st, int vec) {
+  if (skinny_epilogue_scales(g)) {
+    launch_mt_k<FA, FB, MT, PACKED, EXACT, false>(g, st, vec);
+  } else {
+    if constexpr (!(MT == 4 && EXACT)) launch_mt_k<FA, FB, MT, PACKED, EXACT, true>(g, st, vec);  // see skinny_row_tiles
+  }
 }
 
 template <int FA, int FB, int MT, bool PACKED>
@@ -252,7 +313,9 @@ void launch_mt(const GemmArgs& g, hipStream_t st, int vec) {
 // group, 23.2 split).
 int skinny_row_tiles(const GemmArgs& g) {
   if ((g.N + 15) / 16 < static_cast<int64_t>(device_cus())) return 1;
-  return g.M <= 16 ? 1 : g.M <= 32 ? 2 : 4;
+  const int mt = g.M <= 16 ? 1 : g.M <= 32 ? 2 : 4;
+  // four tiles with exact products and per-step scales exceed 128 VGPRs
+  return (mt == 4 && g.exact_products && !skinny_epilogue_scales(g)) ? 2 : mt;
 }
 
 template <int FA, int FB, bool PACKED>
@@ -291,9 +354,9 @@ __global__ __launch_bounds__(256) void k_pack_weights16(const uint8_t* __restric
 }  // namespace
 
 bool gemm_skinny_eligible(const GemmArgs& g) {
-  // per-tensor or per-row scales (selected, not divided); whole 128-deep K steps
-  const bool rows_ok = (g.era == 1 || g.era >= g.M) && (g.erb == 1 || g.erb >= g.N);
-  return rows_ok && !g.pow2_mx && g.eca >= g.K && g.ecb >= g.K && g.M <= kSkMaxM && g.K % 128 == 0;
+  // whole 128-deep K steps, each inside one scale group of either operand
+  const bool k_ok = (g.eca >= g.K || g.eca % 128 == 0) && (g.ecb >= g.K || g.ecb % 128 == 0);
+  return k_ok && !g.pow2_mx && g.M <= kSkMaxM && g.K % 128 == 0;
 }
 
 hipError_t launch_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp,

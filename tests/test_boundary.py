@@ -140,13 +140,13 @@ def test_gemm_validation(rt, fn):
     assert g(rt, flags=10) == rt.EINVAL
     assert g(rt, flags=rt.B_PACKED16, M=80, ldy=64) == rt.EUNSUPPORTED                    # M = 80 > 64
     assert g(rt, flags=rt.B_PACKED16, M=16, K=144, lda=144, ldb=144) == rt.EUNSUPPORTED  # K % 128
-    assert g(rt, flags=rt.B_PACKED16, M=8, K=256, lda=256, ga=(1, 128)) == rt.EUNSUPPORTED  # K-group scales
+    assert g(rt, flags=rt.B_PACKED16 | rt.POW2_SCALES, K=256, lda=256, ldb=256, ga=(1, 32),
+             gb=(1, 32)) == rt.EUNSUPPORTED                                               # 1x32 scales
     assert g(rt, flags=rt.B_PACKED16, M=8, lda=64) == rt.EINVAL                           # lda < K still checked
     # exact products: decode shapes only, row-major or packed
     X = rt.EXACT_PRODUCTS
     assert g(rt, flags=X, M=80, ldy=64) == rt.EUNSUPPORTED                                # M = 80 > 64
     assert g(rt, flags=X, M=16, K=144, lda=144, ldb=144) == rt.EUNSUPPORTED              # K % 128
-    assert g(rt, flags=X, M=8, K=256, lda=256, ldb=256, gb=(128, 128)) == rt.EUNSUPPORTED  # block scales
     assert g(rt, flags=X | rt.B_PACKED16, M=65, ldy=64) == rt.EUNSUPPORTED
     assert g(rt, flags=X | rt.POW2_SCALES, K=256, lda=256, ldb=256, ga=(1, 32), gb=(1, 32)) == rt.EUNSUPPORTED
 

@@ -17,7 +17,8 @@ exact sum (the property the GEMM tolerance relies on).
 One case per kernel route: the general kernel (small M; and K-blocked
 scales), the large kernel (per-tensor, per-row; 1x32 power-of-two scales on
 the scaled MFMA; a split last wave), the K-blocked large kernel, and the
-decode kernel on row-major and fragment-ordered weights (with a weight
+decode kernel on row-major and fragment-ordered weights, with per-row and
+with 1x128 / 128x128 scales (with a weight
 above the size that selects exact products by itself; outputs compared on a
 column sample).
 
@@ -86,13 +87,15 @@ def scales_for(g, rows, K, gran, pow2_values):
 # name, M, N, K, ga, gb, flags, A-scale values, packed B
 ROUTES = [
     ("general", 96, 160, 512, (0, 0), (0, 0), 0, [1.0], False),
-    ("general-kblock", 64, 256, 512, (1, 128), (128, 128), 0, [1.0, 2.0], False),
+    ("general-kblock", 96, 256, 512, (1, 128), (128, 128), 0, [1.0, 2.0], False),
     ("big-tensor", 256, 384, 512, (0, 0), (0, 0), 0, [1.0], False),
     ("big-row", 384, 256, 512, (1, 0), (1, 0), 0, [1.0, 2.0], False),
     ("big-mx32", 256, 256, 512, (1, 32), (1, 32), 1, [1.0, 2.0], False),
     ("kblock", 256, 256, 512, (1, 128), (128, 128), 0, [1.0, 2.0], False),
     ("decode", 16, 4224, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
     ("decode-packed", 48, 4224, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], True),
+    ("decode-kblock", 16, 4224, 1024, (1, 128), (128, 128), 0, [1.0, 2.0], False),
+    ("decode-kblock-packed", 40, 4224, 1024, (1, 128), (128, 128), 0, [1.0, 2.0], True),
 ]
 
 POW2, EXACT = 1, 4  # FP8RT_POW2_SCALES, FP8RT_EXACT_PRODUCTS
@@ -102,6 +105,8 @@ EXACT_ROUTES = [
     ("decode-auto-packed", 40, 512, 2048, (1, 0), (0, 0), 0, [1.0, 2.0], True),
     ("decode-flag", 16, 4224, 1024, (1, 0), (1, 0), EXACT, [1.0, 2.0], False),
     ("decode-flag-packed", 32, 4224, 1024, (1, 0), (1, 0), EXACT, [1.0, 2.0], True),
+    ("decode-auto-kblock", 16, 256, 1024, (1, 128), (128, 128), 0, [1.0, 2.0], False),
+    ("decode-flag-kblock-packed", 64, 4224, 1024, (1, 128), (128, 128), EXACT, [1.0, 2.0], True),
 ]
 
 

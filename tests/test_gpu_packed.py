@@ -185,3 +185,36 @@ def test_decode_workload_packed(rt, orc):
     h = [host(t) for t in y]
     assert np.array_equal(h[0], h[1]), "decode GEMM: packed and row-major differ"
     assert np.array_equal(h[2], h[3]), "weight-only decode: packed and row-major differ"
+
+
+@pytest.mark.parametrize("grans", [((1, 128), (128, 128)), ((1, 0), (128, 128)), ((1, 128), (1, 0))],
+                         ids=["tokgroup-block", "token-block", "tokgroup-channel"])
+def test_decode_workload_block_scaled(rt, orc, grans):
+    """The decode workload's operands under 1x128 token-group and 128x128
+    weight-block scales (each 128-deep step's partial promoted by its two
+    scales in the decode kernel): the weight image bit-identical to the
+    row-major call on the whole output, and every row of 640 sampled output
+    columns within the acceptance rule of the binary64 reference."""
+    ga, gb = grans
+    c = wl.C2Decode()
+    d = c.make()
+    M, N, K = c.M, c.N, c.K
+    aq, sa, _, _, _ = orc.quantize(d["a"], orc.E4M3, ga)
+    wq, sw, _, _, _ = orc.quantize(d["w"], orc.E4M3, gb)
+    Aq, Wq, SA, SW, Bias = dev(aq), dev(wq), dev(sa), dev(sw), dev(d["bias"])
+    P = pack(rt, Wq)
+    y = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    rt.fp8_scaled_gemm(Aq, rt.E4M3, ga, SA, Wq, rt.E4M3, gb, SW, y[0], bias=Bias)
+    rt.fp8_scaled_gemm(Aq, rt.E4M3, ga, SA, P, rt.E4M3, gb, SW, y[1], bias=Bias)
+    torch.cuda.synchronize()
+    h = [host(t) for t in y]
+    assert np.array_equal(h[0], h[1]), "block-scaled decode GEMM: packed and row-major differ"
+    g = np.random.default_rng(case_seed("decode-block", ga, gb))
+    cols = np.unique(np.concatenate([np.arange(128), np.arange(N - 128, N), g.integers(0, N, 384)]))
+    m = np.repeat(np.arange(M), len(cols))
+    n = np.tile(cols, M)
+    yref, S = orc.gemm_points(aq, orc.E4M3, sa, ga, wq, orc.E4M3, sw, gb, m, n, bias=d["bias"])
+    thw = orc.dot_truncation_bound(aq, orc.E4M3, sa, ga, wq, orc.E4M3, sw, gb, m, n)
+    ok, st = check_gemm(h[0][m, n], yref, S, True, orc, bias=orc.bf16_bits_to_f32(d["bias"])[n], t_hw=thw)
+    print(grans, st)
+    assert ok, st
