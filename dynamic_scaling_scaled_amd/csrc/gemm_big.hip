@@ -623,7 +623,9 @@ bool gemm_big_eligible(const GemmArgs& g) {
   const bool rows_ok = (g.era == 1 || g.era >= g.M) && (g.erb == 1 || g.erb >= g.N);
   const bool scales_ok = g.pow2_mx ? (g.era == 1 && g.erb == 1 && g.eca == 32 && g.ecb == 32)
                                    : (g.eca >= g.K && g.ecb >= g.K);
-  return rows_ok && scales_ok && g.K % (2 * TKS) == 0 && g.M >= 128 &&
+  // M from 65 (below, the decode kernel): a few hundred rows make a grid of
+  // fewer tiles than CUs, which the launch splits along K
+  return rows_ok && scales_ok && g.K % (2 * TKS) == 0 && g.M >= 65 &&
          g.N >= 128 && g.lda < (int64_t(1) << 23) && g.ldb < (int64_t(1) << 23);
 }
 
@@ -645,17 +647,20 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
   // plus a last wave at most half full (the 4096 x 29568 up-projection: 7
   // waves + 64 tiles), each last-wave tile is split along K into up to 4
   // units so the last wave fills the CUs; k_split_reduce adds the parts.
+  // A grid of at most half the CUs in all (a few hundred rows of A) is one
+  // such wave: every tile is split, into up to 8 parts.
   int t_main = T, split = 1, ns_part = 0;
   float* part = nullptr;
   {
     const int cus = device_cus();
-    const int rem = T % cus;
+    const bool small = 2 * T <= cus;
+    const int rem = small ? T : T % cus;
     const int64_t ns = g.K / TKS;
     // FP8 output: one statistics slot per whole tile and per reduce block
     const bool slots_ok = okind < kOutE4M3 || (T - rem) + rem * kRedBlocks <= kMaxBlocks;
-    if (!g.pow2_mx && slots_ok && T > cus && rem > 0 && 2 * rem <= cus) {
+    if (!g.pow2_mx && slots_ok && (small || (T > cus && rem > 0 && 2 * rem <= cus))) {
       const size_t part_bytes = static_cast<size_t>(rem) * TM * TN * sizeof(float);  // per K part
-      int sp = std::min(cus / rem, 4);
+      int sp = std::min(cus / rem, small ? 8 : 4);
       if (g.fixed_scratch)  // a fixed buffer: as many parts as fit
         sp = static_cast<int>(std::min<size_t>(sp, g.fixed_scratch_bytes / part_bytes));
       while (sp > 1 && ns % (2 * sp) != 0) --sp;  // every part an even number of stages

@@ -74,7 +74,8 @@ GEMMS = [  # M, N, K, ga, gb, flags, out
     (1024, 2048, 2048, (1, 0), (1, 0), 0, torch.float32),       # large kernel, per-row scales
     (1024, 1024, 2048, (1, 128), (128, 128), 0, torch.bfloat16),  # K-blocked kernel
     (512, 768, 1024, (1, 32), (1, 32), 1, torch.bfloat16),      # 1x32 power-of-two scales
-    (96, 1000, 1024, (0, 0), (1, 0), 0, torch.float32),         # general kernel
+    (96, 1000, 1040, (0, 0), (1, 0), 0, torch.float32),         # general kernel (K not a multiple of 256)
+    (96, 1000, 1024, (0, 0), (1, 0), 0, torch.float32),         # large kernel, every tile split along K
     (16, 8192, 4096, (1, 0), (1, 0), 0, torch.bfloat16),        # decode kernel
 ]
 

@@ -16,7 +16,8 @@ exact sum (the property the GEMM tolerance relies on).
 
 One case per kernel route: the general kernel (small M; and K-blocked
 scales), the large kernel (per-tensor, per-row; 1x32 power-of-two scales on
-the scaled MFMA; a split last wave), the K-blocked large kernel, and the
+the scaled MFMA; a split last wave; a grid so small that every tile is
+split along K), the K-blocked large kernel, and the
 decode kernel on row-major and fragment-ordered weights, with per-row and
 with 1x128 / 128x128 scales (with a weight
 above the size that selects exact products by itself; outputs compared on a
@@ -86,7 +87,8 @@ def scales_for(g, rows, K, gran, pow2_values):
 
 # name, M, N, K, ga, gb, flags, A-scale values, packed B
 ROUTES = [
-    ("general", 96, 160, 512, (0, 0), (0, 0), 0, [1.0], False),
+    ("general", 96, 120, 512, (0, 0), (0, 0), 0, [1.0], False),
+    ("big-split-all", 96, 384, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
     ("general-kblock", 96, 256, 512, (1, 128), (128, 128), 0, [1.0, 2.0], False),
     ("big-tensor", 256, 384, 512, (0, 0), (0, 0), 0, [1.0], False),
     ("big-row", 384, 256, 512, (1, 0), (1, 0), 0, [1.0, 2.0], False),
