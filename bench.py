@@ -660,6 +660,17 @@ def extra_components(torch, rt, wl, keep):
     e = hbm_entry(time_op(torch, gm, scrub=scrub), g_bytes, "k_gemm_skinny")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_gemm_bf16_bias"] = e
+    # the same layer with an E4M3 output (GIVEN output scale, amax of y and counters)
+    yq8 = u8(M, N)
+    sy8 = torch.full((1, 1), 0.01, dtype=torch.float32, device=dev)
+    amy, cnty = f32(1), torch.zeros(2, dtype=torch.int64, device=dev)
+    g8 = lambda: rt.fp8_scaled_gemm_fp8out(Aq, rt.E4M3, (1, 0), sa, Wq, rt.E4M3, (1, 0), sw, yq8, rt.E4M3, sy8,
+                                           None, amy, cnty, bias=bias)
+    g8()
+    e = hbm_entry(time_op(torch, g8, scrub=scrub), M * K + N * K + M * N + (M + N) * 4 + N * 2,
+                  "k_gemm_skinny (E4M3 output) + k_finish")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_gemm_fp8_out_e4m3"] = e
     # weight-only FP8: the same per-channel E4M3 weight codes, bf16 activations
     yw = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     wo = lambda: rt.fp8_weight_only_gemm(A, Wq, rt.E4M3, (1, 0), sw, yw, bias=bias)

@@ -338,6 +338,7 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
   if (get_workspace(stream, &ws) != hipSuccess) return FP8RT_EHIP;
   g.y = yq;
   g.yt = FP8RT_F32;  // unused with yq_fmt set
+  g.exact_products = false;  // the FP8 matrix cores form the products here
   g.yq_fmt = fy;
   g.sy = scale_y;
   g.ry = inv_scale_y;

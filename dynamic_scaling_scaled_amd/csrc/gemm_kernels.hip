@@ -277,11 +277,15 @@ size_t gemm_required_scratch(const GemmArgs& g) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.yq_fmt >= 0) {
-    // FP8 output: the large kernel or the general one, then the partials of
-    // max |y| and the counters (one per tile, or per split-K reduce block).
+    // FP8 output: the decode kernel, the large kernel or the general one,
+    // then the partials of max |y| and the counters (one per workgroup or
+    // tile, or per split-K reduce block).
     int nb = 0;
     hipError_t e;
-    if (gemm_big_eligible(g)) {
+    if (gemm_skinny_eligible(g) && !g.b_packed && !g.exact_products && skinny_blocks(g) <= kMaxBlocks) {
+      e = launch_gemm_skinny(g, st);
+      nb = static_cast<int>(skinny_blocks(g));
+    } else if (gemm_big_eligible(g)) {
       e = launch_gemm_big(g, st, &nb);
     } else {
       e = launch_generic(g, st);

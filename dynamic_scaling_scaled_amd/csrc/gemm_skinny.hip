@@ -103,12 +103,15 @@ constexpr int sk_waves_per_simd(int mt, bool exact, bool kb) {
 // Each 128-deep step's partial sum then comes out of MFMAs started from zero
 // and is added to the accumulator times s_a(m, step) s_b(n, step), the
 // scales of the groups that hold the step; the epilogue adds only the bias.
-template <int FA, int FB, int MT, bool BF16OUT, bool PACKED, bool EXACT, bool KB>
+// OUT: kOutF32 / kOutBF16, or FP8 codes (kOutE4M3 / kOutE5M2) of y * r_y,
+// r_y = ry[0] or fl32(1 / sy[0]), with the workgroup's max |y| and
+// saturation / underflow counts in ypart[workgroup] (combined by k_finish).
+template <int FA, int FB, int MT, int OUT, bool PACKED, bool EXACT, bool KB>
 __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void k_gemm_skinny(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, int64_t era, int64_t eca, const float* __restrict__ sb,
     int64_t erb, int64_t ecb, const void* __restrict__ bias, int bias_bf16, void* __restrict__ Y, int64_t ldy,
-    int vec_store) {
+    int vec_store, const float* __restrict__ sy, const float* __restrict__ ry, BlockPartial* __restrict__ ypart) {
   __shared__ f32x4 red[kSkWaves - 1][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -242,6 +245,9 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
       bv[e] = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[n]) << 16)
                         : static_cast<const float*>(bias)[n];
   }
+  float rq = 1.0f;
+  uint32_t ymax = 0, sat_l = 0, under_l = 0;  // FP8 output: this lane's statistics
+  if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int64_t m = mb + 16 * t + r;
@@ -250,7 +256,28 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = acc[t][e] * (sav * sbv[e]) + bv[e];
-    if constexpr (BF16OUT) {
+    if constexpr (OUT >= kOutE4M3) {
+      // the GIVEN-mode cast of the quantize kernels on y * r_y; statistics of
+      // stored elements only (columns past N are clamped repeats)
+      constexpr int F = OUT == kOutE4M3 ? kE4M3 : kE5M2;
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = v[e] * rq;
+        const uint32_t ab = nb + e < N ? (__float_as_uint(v[e]) & kAbsMask) : 0u;  // 0: not counted
+        ymax = max(ymax, ab);
+        sat_l += (ab != 0u && fabsf(f[e]) > Fmt<F>::kMax) ? 1u : 0u;
+        under_l += (ab != 0u && fabsf(f[e]) <= Fmt<F>::kZeroEdge) ? 1u : 0u;
+      }
+      uint32_t w = cvt4<F>(f[0], f[1], f[2], f[3]);
+      if (__builtin_isunordered(f[0], f[1]) || __builtin_isunordered(f[2], f[3])) w = cvt4_nan<F>(f[0], f[1], f[2], f[3]);
+      uint8_t* dst = static_cast<uint8_t*>(Y) + m * ldy + nb;
+      if (vec_store && nb + 4 <= N) {
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+        for (int e = 0; e < 4 && nb + e < N; ++e) dst[e] = static_cast<uint8_t>(w >> (8 * e));
+      }
+    } else if constexpr (OUT == kOutBF16) {
       uint16_t* dst = static_cast<uint16_t*>(Y) + m * ldy + nb;
       const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
       if (vec_store && nb + 4 <= N) {
@@ -268,6 +295,14 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
       }
     }
   }
+  if constexpr (OUT >= kOutE4M3) {
+    ymax = wave_max_u32(ymax);
+    const uint32_t s_w = static_cast<uint32_t>(wave_sum_u64(sat_l));
+    const uint32_t u_w = static_cast<uint32_t>(wave_sum_u64(under_l));
+    if (lane == 0)
+      *reinterpret_cast<u32x4*>(&ypart[static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x]) =
+          u32x4{ymax, s_w, u_w, 0u};
+  }
 }
 
 // Scales the epilogue applies: per tensor or per row on both sides, whole K.
@@ -279,14 +314,22 @@ template <int FA, int FB, int MT, bool PACKED, bool EXACT, bool KB>
 void launch_mt_k(const GemmArgs& g, hipStream_t st, int vec) {
   const dim3 grid(static_cast<unsigned>((g.N + 15) / 16), static_cast<unsigned>((g.M + 16 * MT - 1) / (16 * MT)));
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
-  if (g.yt == FP8RT_BF16)
-    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, true, PACKED, EXACT, KB>), grid, dim3(kSkThreads), 0, st, g.a,
-                       g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.eca, g.sb, g.erb, g.ecb, g.bias, bb, g.y,
-                       g.ldy, vec);
-  else
-    hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, false, PACKED, EXACT, KB>), grid, dim3(kSkThreads), 0, st, g.a,
-                       g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.eca, g.sb, g.erb, g.ecb, g.bias, bb, g.y,
-                       g.ldy, vec);
+#define FP8RT_SK(OUT)                                                                                            \
+  hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, OUT, PACKED, EXACT, KB>), grid, dim3(kSkThreads), 0, st, g.a,   \
+                     g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.eca, g.sb, g.erb, g.ecb, g.bias, bb, g.y, \
+                     g.ldy, vec, g.sy, g.ry, g.part)
+  switch (gemm_out_kind(g)) {
+    case kOutBF16: FP8RT_SK(kOutBF16); break;
+    case kOutF32: FP8RT_SK(kOutF32); break;
+    default:
+      // FP8 output: FP8 matrix cores and a row-major B only
+      if constexpr (!PACKED && !EXACT) {
+        if (gemm_out_kind(g) == kOutE4M3) FP8RT_SK(kOutE4M3);
+        else FP8RT_SK(kOutE5M2);
+      }
+      break;
+  }
+#undef FP8RT_SK
 }
 
 template <int FA, int FB, int MT, bool PACKED, bool EXACT>
@@ -367,8 +410,14 @@ hipError_t launch_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t
   return hipGetLastError();
 }
 
+int64_t skinny_blocks(const GemmArgs& g) {
+  const int mt = skinny_row_tiles(g);
+  return (g.N + 15) / 16 * ((g.M + 16 * mt - 1) / (16 * mt));
+}
+
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t st) {
-  const int esz = g.yt == FP8RT_BF16 ? 2 : 4;
+  const int kind = gemm_out_kind(g);
+  const int esz = kind == kOutF32 ? 4 : kind == kOutBF16 ? 2 : 1;
   const int vec = ((g.ldy * esz) % (4 * esz) == 0) && ((reinterpret_cast<uintptr_t>(g.y) & (4 * esz - 1)) == 0);
   if (g.fa == FP8RT_E4M3) launch_fmt<0, 0>(g, st, vec);
   else launch_fmt<1, 0>(g, st, vec);

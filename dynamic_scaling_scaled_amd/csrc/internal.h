@@ -151,6 +151,9 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream, int* nparts = 
 bool gemm_kblock_eligible(const GemmArgs& g);
 hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t stream);
 bool gemm_skinny_eligible(const GemmArgs& g);
+// Workgroups of the decode kernel's grid for g (one statistics partial each
+// with an FP8 output).
+int64_t skinny_blocks(const GemmArgs& g);
 
 // Weight-only FP8 GEMM (gemm_wonly.hip): bf16 activations x [M x K] (ldx in
 // elements), FP8 weights w [N x K] (ldw bytes) with fp32 scales

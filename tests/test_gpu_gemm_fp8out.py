@@ -6,7 +6,9 @@ y_ref - T and y_ref + T (both cast by the oracle's GIVEN-mode quantize with
 the same output scale; the bounds rounded outward to binary32).  amax_y must
 be within T of max |y_ref|, and each counter between the number of elements
 certain to be counted and the number that may be.  Shapes exercise the
-general kernel, the large kernel and its 1x32 (MX) path."""
+general kernel, the decode kernel (one to four row tiles, per-step block
+scales, a ragged last column group), the large kernel and its 1x32 (MX)
+path."""
 import numpy as np
 import pytest
 import torch
@@ -41,7 +43,10 @@ def order(c):
 CASES = [  # (shape, ga, gb, pow2)
     ((200, 300, 320), (0, 0), (0, 0), False),    # general kernel, ragged
     ((520, 776, 1024), (0, 0), (1, 0), False),   # large kernel, per-channel B
-    ((16, 512, 1024), (1, 0), (1, 0), False),    # decode shape (general kernel)
+    ((16, 512, 1024), (1, 0), (1, 0), False),    # decode kernel
+    ((40, 1003, 1024), (0, 0), (1, 0), False),   # decode kernel, two row tiles, ragged N
+    ((64, 4160, 512), (1, 0), (1, 0), False),    # decode kernel, four row tiles in one workgroup
+    ((16, 640, 1024), (1, 128), (128, 128), False),  # decode kernel, per-step block scales
     ((264, 400, 512), (1, 128), (128, 128), False),  # K-blocked scales (general kernel)
     ((520, 776, 1024), (1, 32), (1, 32), True),  # 1x32 power-of-two scales (large kernel)
 ]
