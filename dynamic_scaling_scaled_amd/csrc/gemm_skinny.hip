@@ -417,6 +417,8 @@ int64_t skinny_blocks(const GemmArgs& g) {
 
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t st) {
   const int kind = gemm_out_kind(g);
+  // FP8 codes out: built for the FP8 matrix cores on a row-major B only
+  if (kind >= kOutE4M3 && (g.b_packed || g.exact_products)) return hipErrorInvalidValue;
   const int esz = kind == kOutF32 ? 4 : kind == kOutBF16 ? 2 : 1;
   const int vec = ((g.ldy * esz) % (4 * esz) == 0) && ((reinterpret_cast<uintptr_t>(g.y) & (4 * esz - 1)) == 0);
   if (g.fa == FP8RT_E4M3) launch_fmt<0, 0>(g, st, vec);
