@@ -16,17 +16,20 @@
 //    sixteenth of the 128-deep K steps and runs a plain load -> MFMA loop
 //    (global loads straight into the MFMA operand layout, no LDS staging: B
 //    is read exactly once, nontemporally).  Two workgroups per CU (64
-//    VGPRs per lane) keep 32 waves' loads in flight, which hides the HBM
-//    latency.
+//    VGPRs per lane, where the variant fits) keep 32 waves' loads in flight,
+//    which hides the HBM latency.
 //  - v_mfma_f32_16x16x128 with B as the first operand: the 16 x 16 result
 //    holds 16 rows of B (output columns) by 16 rows of A (one MFMA per 16-row
-//    tile of A, up to 4); each lane ends with 4 consecutive output columns of
-//    one output row per tile.  Lane quarter g loads
+//    tile of A, up to 4 per workgroup; with fewer 16-row groups of B than
+//    CUs each tile of A gets a workgroup of its own); each lane ends with 4
+//    consecutive output columns of one output row per tile.  Lane quarter g loads
 //    bytes [32 g, 32 g + 32) of every 128-byte K step of both operands, the
 //    same K permutation on both sides, which the per-row scales (applied
 //    after the sum) do not see.
 //  - The 16 partial sums meet in LDS; wave 0 applies the scales and the bias,
-//    rounds and stores 8- or 16-byte pieces.
+//    rounds and stores 8- or 16-byte pieces, or (FP8 output) casts y * r_y as
+//    the quantize kernels do and writes the workgroup's max |y| and
+//    saturation / underflow counts for the finisher.
 //  - Scales that change along K (1 x g token groups, g_r x g weight blocks,
 //    g a multiple of 128): each step's MFMAs start from zero and the partial
 //    is added to the accumulator times s_a(m, step) s_b(n, step) (one FMA
