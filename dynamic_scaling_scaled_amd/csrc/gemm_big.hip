@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
     const float* p = part + static_cast<int64_t>(k) * split * (TM * TN) + r * TN + c;
     f32x4 acc = *reinterpret_cast<const f32x4*>(p);
     for (int q = 1; q < split; ++q) acc += *reinterpret_cast<const f32x4*>(p + static_cast<int64_t>(q) * (TM * TN));
-    const float sav = sa[era == 1 ? row : 0];
+    const float sav = sa ? sa[era == 1 ? row : 0] : 1.0f;  // null: applied inside the MFMA (1x32 scales)
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
       if (bias)
         bv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[cc]) << 16)
                        : static_cast<const float*>(bias)[cc];
-      v[e] = acc[e] * (sav * sb[erb == 1 ? cc : 0]) + bv;
+      v[e] = acc[e] * (sav * (sb ? sb[erb == 1 ? cc : 0] : 1.0f)) + bv;
     }
     if constexpr (OUT == kOutBF16) {
       const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
@@ -632,7 +632,7 @@ bool gemm_big_eligible(const GemmArgs& g) {
 size_t gemm_big_required_scratch(const GemmArgs& g) {
   if (!g.pow2_mx) return 0;
   const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
-  return static_cast<size_t>((ga + gb) * ns * 64) * 4;  // E8M0 exponent dwords
+  return (static_cast<size_t>((ga + gb) * ns * 64) * 4 + 255) & ~size_t(255);  // E8M0 exponent dwords
 }
 
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
@@ -649,8 +649,11 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
   // units so the last wave fills the CUs; k_split_reduce adds the parts.
   // A grid of at most half the CUs in all (a few hundred rows of A) is one
   // such wave: every tile is split, into up to 8 parts.
+  // One scratch region holds both: the repacked 1x32 exponents (MX) first,
+  // then the FP32 K-parts of split tiles (256-byte aligned).
+  const size_t mx_bytes = (gemm_big_required_scratch(g) + 255) & ~size_t(255);
   int t_main = T, split = 1, ns_part = 0;
-  float* part = nullptr;
+  size_t part_total = 0;
   {
     const int cus = device_cus();
     const bool small = 2 * T <= cus;
@@ -658,32 +661,35 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
     const int64_t ns = g.K / TKS;
     // FP8 output: one statistics slot per whole tile and per reduce block
     const bool slots_ok = okind < kOutE4M3 || (T - rem) + rem * kRedBlocks <= kMaxBlocks;
-    if (!g.pow2_mx && slots_ok && (small || (T > cus && rem > 0 && 2 * rem <= cus))) {
+    if (slots_ok && (small || (T > cus && rem > 0 && 2 * rem <= cus))) {
       const size_t part_bytes = static_cast<size_t>(rem) * TM * TN * sizeof(float);  // per K part
       int sp = std::min(cus / rem, small ? 8 : 4);
-      if (g.fixed_scratch)  // a fixed buffer: as many parts as fit
-        sp = static_cast<int>(std::min<size_t>(sp, g.fixed_scratch_bytes / part_bytes));
+      if (g.fixed_scratch)  // a fixed buffer: as many parts as fit beside the exponents
+        sp = static_cast<int>(std::min<size_t>(
+            sp, g.fixed_scratch_bytes > mx_bytes ? (g.fixed_scratch_bytes - mx_bytes) / part_bytes : 0));
       while (sp > 1 && ns % (2 * sp) != 0) --sp;  // every part an even number of stages
       if (sp > 1) {
-        void* p = nullptr;
-        hipError_t e = gemm_scratch(g, st, part_bytes * sp, &p);
-        if (e != hipSuccess) return e;
-        part = static_cast<float*>(p);
         split = sp;
         t_main = T - rem;
         ns_part = static_cast<int>(ns / sp);
+        part_total = part_bytes * sp;
       }
     }
   }
+  uint8_t* scratch = nullptr;
+  if (mx_bytes + part_total > 0) {
+    void* p = nullptr;
+    hipError_t e = gemm_scratch(g, st, mx_bytes + part_total, &p);
+    if (e != hipSuccess) return e;
+    scratch = static_cast<uint8_t*>(p);
+  }
+  float* part = split > 1 ? reinterpret_cast<float*>(scratch + mx_bytes) : nullptr;
   const dim3 grid(static_cast<unsigned>(t_main + (T - t_main) * split));
   uint32_t* xpa = nullptr;
   uint32_t* xpb = nullptr;
   if (g.pow2_mx) {
     const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
-    void* p = nullptr;
-    hipError_t e = gemm_scratch(g, st, gemm_big_required_scratch(g), &p);
-    if (e != hipSuccess) return e;
-    xpa = static_cast<uint32_t*>(p);
+    xpa = reinterpret_cast<uint32_t*>(scratch);
     xpb = xpa + ga * ns * 64;
     hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((ga * ns * 64 + 255) / 256)), dim3(256), 0, st,
                        g.sa, g.M, g.K / 32, ga, ns, xpa);
@@ -712,7 +718,8 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
     const dim3 rgrid(kRedBlocks, static_cast<unsigned>(T - t_main));
 #define FP8RT_RED(OUT)                                                                                          \
   hipLaunchKernelGGL(k_split_reduce<OUT>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M, \
-                     g.N, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, vec, g.sy, g.ry, g.part)
+                     g.N, g.pow2_mx ? nullptr : g.sa, g.era, g.pow2_mx ? nullptr : g.sb, g.erb, g.bias, bb, g.y,   \
+                     g.ldy, vec, g.sy, g.ry, g.part)
     switch (okind) {
       case kOutBF16: FP8RT_RED(kOutBF16); break;
       case kOutE4M3: FP8RT_RED(kOutE4M3); break;

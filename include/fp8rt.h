@@ -264,10 +264,11 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
  *    exponents: (ceil(M/32) + ceil(N/32)) * K/128 * 256 bytes; transposed
  *    1x128 A scales on large shapes: ceil(M/256) * 256 * K/128 * 4 bytes)
  *    returns FP8RT_ESCRATCH before anything is enqueued.
- *  - A ragged last wave of tiles is split along K into as many parts as fit
- *    (256 KB per part and 256 x 256 tile), or not at all; the result can then
- *    differ from fp8_scaled_gemm's in FP32 summation order only, within the
- *    same tolerance.
+ *  - A ragged last wave of tiles, or a grid of tiles that fills at most half
+ *    the CUs, is split along K into as many parts as fit beside the repacked
+ *    exponents (256 KB per part and 256 x 256 tile), or not at all; the
+ *    result can then differ from fp8_scaled_gemm's in FP32 summation order
+ *    only, within the same tolerance.
  *  - Every call on a GPU shares that GPU's one array (whatever the stream),
  *    and the array keeps the last call's contents (nothing in it needs to
  *    start at zero): calls that overlap in time on one GPU race and give
