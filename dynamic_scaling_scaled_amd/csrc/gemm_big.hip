@@ -715,20 +715,31 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
 #undef FP8RT_BIG_OUT
 #undef FP8RT_BIG
   if (split > 1) {
-    const dim3 rgrid(kRedBlocks, static_cast<unsigned>(T - t_main));
-#define FP8RT_RED(OUT)                                                                                          \
-  hipLaunchKernelGGL(k_split_reduce<OUT>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M, \
-                     g.N, g.pow2_mx ? nullptr : g.sa, g.era, g.pow2_mx ? nullptr : g.sb, g.erb, g.bias, bb, g.y,   \
-                     g.ldy, vec, g.sy, g.ry, g.part)
-    switch (okind) {
-      case kOutBF16: FP8RT_RED(kOutBF16); break;
-      case kOutE4M3: FP8RT_RED(kOutE4M3); break;
-      case kOutE5M2: FP8RT_RED(kOutE5M2); break;
-      default: FP8RT_RED(kOutF32); break;
-    }
-#undef FP8RT_RED
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_split_reduce(g, st, part, t_main, split, tiles_m, tiles_n, g.pow2_mx ? nullptr : g.sa,
+                            g.pow2_mx ? nullptr : g.sb, vec);
+    if (e != hipSuccess) return e;
   }
   if (nparts) *nparts = split > 1 ? t_main + (T - t_main) * kRedBlocks : T;
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const GemmArgs& g, hipStream_t st, const float* part, int t_main, int split,
+                               int tiles_m, int tiles_n, const float* sa, const float* sb, int vec) {
+  const int T = tiles_m * tiles_n;
+  const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
+  const dim3 rgrid(kRedBlocks, static_cast<unsigned>(T - t_main));
+#define FP8RT_RED(OUT)                                                                                          \
+  hipLaunchKernelGGL(k_split_reduce<OUT>, rgrid, dim3(256), 0, st, part, t_main, split, tiles_m, tiles_n, g.M, \
+                     g.N, sa, g.era, sb, g.erb, g.bias, bb, g.y, g.ldy, vec, g.sy, g.ry, g.part)
+  switch (gemm_out_kind(g)) {
+    case kOutBF16: FP8RT_RED(kOutBF16); break;
+    case kOutE4M3: FP8RT_RED(kOutE4M3); break;
+    case kOutE5M2: FP8RT_RED(kOutE5M2); break;
+    default: FP8RT_RED(kOutF32); break;
+  }
+#undef FP8RT_RED
   return hipGetLastError();
 }
 

@@ -100,6 +100,66 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Epilogue of one wave: lane l holds output row 16 i + (l % 16) and columns
+// 16 j + 4 (l / 16) + (0..3) of its 128 x 64 tile; values are scaled (row
+// factor sav, column vectors scol / sbias from LDS), staged in the wave's
+// quarter of an LDS stage (16-byte chunks XOR-swizzled by row) and stored
+// as 16-byte row chunks of ESZ-byte elements (2: bf16, 4: fp32); rows and
+// columns at or past (M, N) are skipped.
+template <int ESZ>
+__device__ __forceinline__ void kb_store(const f32x4 (&acc)[MI][NJ], uint8_t* stage, const float* scol,
+                                         const float* sbias, const float (&sav)[MI], int64_t wrow0, int64_t wcol0,
+                                         int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
+                                         int wn, int fr, int fq, int lane) {
+  constexpr int RB = WTN * ESZ;                 // staged row bytes: 128 or 256
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8 or 16
+  constexpr int ROWS = (kStageA / 4) / RB;      // rows per pass: 64 or 32
+  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass: 4 or 2
+  constexpr int EPC = 16 / ESZ;
+#pragma unroll
+  for (int pass = 0; pass < MI / IPP; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < IPP; ++ii) {
+      const int i = pass * IPP + ii;
+      const int lrow = ii * 16 + fr;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = j * 16 + 4 * fq;
+        const f32x4 scv = *reinterpret_cast<const f32x4*>(&scol[wn * WTN + c]);
+        const f32x4 biv = *reinterpret_cast<const f32x4*>(&sbias[wn * WTN + c]);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sav[i] * scv[r]) + biv[r];
+        const int byte = c * ESZ;
+        const int chunk = (byte >> 4) ^ (lrow & (CPR - 1));
+        uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
+        if constexpr (ESZ == 2) {
+          *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+    __syncthreads();
+    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
+      const int lrow = ch / CPR, cc = ch % CPR;
+      const int64_t row = wrow0 + pass * ROWS + lrow;
+      const int64_t col = wcol0 + cc * EPC;
+      if (row >= M || col >= N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & (CPR - 1))) << 4));
+      char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
+      if (vec_store && col + EPC <= N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const char* src = reinterpret_cast<const char*>(&v);
+        for (int e = 0; e < EPC && col + e < N; ++e)
+          for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // sat: A's group scales transposed to [K / 128][M] (null: A scale constant
 // along K, taken from sa in the epilogue).  sbk: B's block scales
 // [ceil(N / erb)][K / 128] (null: constant along K, from sb in the epilogue).
@@ -108,7 +168,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sat, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sbk, const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias,
-    int bias_bf16, void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store, int64_t Mp) {
+    int bias_bf16, void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store, int64_t Mp,
+    int t_main, int split, int ns_part, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) float sSa0[TM];   // A row scales of the stage in sA0
   __shared__ __attribute__((aligned(16))) float sSa1[TM];
@@ -117,11 +178,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
 
-  const int T = tiles_m * tiles_n;
+  // Blocks below t_main take whole tiles of the grouped order, dealt to the
+  // XCDs in contiguous ranges; the rest are split-K units: unit u runs the
+  // stages [(u % split) ns_part, +ns_part) of tile t_main + u / split and
+  // writes its promoted FP32 sums to part[u] (launch_split_reduce finishes).
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int q = T >> 3, rem = T & 7;
-  const int logical = xcd * q + min(xcd, rem) + loc;
+  const bool unit = bid >= t_main;
+  int logical, s0 = 0;
+  if (!unit) {
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int q = t_main >> 3, rem = t_main & 7;
+    logical = xcd * q + min(xcd, rem) + loc;
+  } else {
+    const int u = bid - t_main;
+    logical = t_main + u / split;
+    s0 = (u % split) * ns_part;
+  }
   const int group = GROUP_M * tiles_n;
   const int gidx = logical / group;
   const int first_m = gidx * GROUP_M;
@@ -158,6 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ns = static_cast<int>(K / TKS);  // even
+  const int nsl = unit ? ns_part : ns;        // stages this block runs (even), from s0
   const int64_t wrow0 = m0 + wm * WTM;
   const int fr = lane & 15, fq = lane >> 4;
   // B block scales of this tile's block row for every stage, once, in LDS.
@@ -218,25 +291,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
       for (int e = 0; e < 4; ++e) acc[MI - 1][j][e] = fmaf(fpend, pend[j][e], acc[MI - 1][j][e]);
   };
 
-  sa_dma(0, sSa0);
-  dma_buf<kDmaA>(ra, 0, voa, sA0, wave);
-  dma_buf<kDmaB>(rb, 0, vob, sB0, wave);
-  step_barrier<0>();  // stage 0, its scales and the B scale table landed
+  sa_dma(s0, sSa0);
+  dma_buf<kDmaA>(ra, s0 * TKS, voa, sA0, wave);
+  dma_buf<kDmaB>(rb, s0 * TKS, vob, sB0, wave);
+  step_barrier<0>();  // stage s0, its scales and the B scale table landed
   // Stage st (in arrays X): issue the loads of stage st+1 into the other
   // arrays (free: the previous stage ended with a barrier), multiply and
   // promote stage st, wait for everything issued.
 #define FP8RT_KSTAGE(LA, LB, LS, DA, DB, DS, ST, FIRST)                        \
   {                                                                           \
-    const int kn = min(ST + 1, ns - 1);                                       \
+    const int kn = s0 + min(ST + 1, nsl - 1);                                 \
     sa_dma(kn, DS);                                                           \
     dma_buf<kDmaA>(ra, kn * TKS, voa, DA, wave);                              \
     dma_buf<kDmaB>(rb, kn * TKS, vob, DB, wave);                              \
-    stage_mma(LA, LB, LS, ST, FIRST);                                         \
+    stage_mma(LA, LB, LS, s0 + ST, FIRST);                                    \
     step_barrier<0>();                                                        \
   }
   FP8RT_KSTAGE(sA0, sB0, sSa0, sA1, sB1, sSa1, 0, true)
   FP8RT_KSTAGE(sA1, sB1, sSa1, sA0, sB0, sSa0, 1, false)
-  for (int st = 2; st < ns; st += 2) {
+  for (int st = 2; st < nsl; st += 2) {
     FP8RT_KSTAGE(sA0, sB0, sSa0, sA1, sB1, sSa1, st, false)
     FP8RT_KSTAGE(sA1, sB1, sSa1, sA0, sB0, sSa0, st + 1, false)
   }
@@ -248,66 +321,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_kblock(
   __shared__ __attribute__((aligned(16))) float sCol[2][TN];
   if (t < TN) {
     const int64_t col = min(n0 + t, N - 1);
-    sCol[0][t] = BKB ? 1.0f : sb[erb == 1 ? col : 0];
+    sCol[0][t] = (BKB || unit) ? 1.0f : sb[erb == 1 ? col : 0];
     float bvv = 0.0f;
-    if (bias)
+    if (bias && !unit)
       bvv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
                       : static_cast<const float*>(bias)[col];
     sCol[1][t] = bvv;
   }
   __syncthreads();
   uint8_t* stage = (wave < 4 ? sA0 : sA1) + (wave & 3) * (kStageA / 4);
-  const int64_t wcol0 = n0 + wn * WTN;
   float sav[MI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) sav[i] = AKB ? 1.0f : sa[era == 1 ? min(wrow0 + i * 16 + fr, M - 1) : 0];
-  constexpr int ESZ = BF16OUT ? 2 : 4;
-  constexpr int RB = WTN * ESZ;                 // staged row bytes: 128 or 256
-  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8 or 16
-  constexpr int ROWS = (kStageA / 4) / RB;      // rows per pass: 64 or 32
-  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass: 4 or 2
-  constexpr int EPC = 16 / ESZ;
-#pragma unroll
-  for (int pass = 0; pass < MI / IPP; ++pass) {
-#pragma unroll
-    for (int ii = 0; ii < IPP; ++ii) {
-      const int i = pass * IPP + ii;
-      const int lrow = ii * 16 + fr;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int c = j * 16 + 4 * fq;
-        const f32x4 scv = *reinterpret_cast<const f32x4*>(&sCol[0][wn * WTN + c]);
-        const f32x4 biv = *reinterpret_cast<const f32x4*>(&sCol[1][wn * WTN + c]);
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sav[i] * scv[r]) + biv[r];
-        const int byte = c * ESZ;
-        const int chunk = (byte >> 4) ^ (lrow & (CPR - 1));
-        uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
-        if constexpr (BF16OUT) {
-          *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-        }
-      }
-    }
-    __syncthreads();
-    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
-      const int lrow = ch / CPR, cc = ch % CPR;
-      const int64_t row = wrow0 + pass * ROWS + lrow;
-      const int64_t col = wcol0 + cc * EPC;
-      if (row >= M || col >= N) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & (CPR - 1))) << 4));
-      char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
-      if (vec_store && col + EPC <= N) {
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
-        const char* src = reinterpret_cast<const char*>(&v);
-        for (int e = 0; e < EPC && col + e < N; ++e)
-          for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < MI; ++i)
+    sav[i] = (AKB || unit) ? 1.0f : sa[era == 1 ? min(wrow0 + i * 16 + fr, M - 1) : 0];
+  if (unit) {
+    // raw sums of the unit's stages, the whole 256 x 256 tile, FP32
+    kb_store<4>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN,
+                part + static_cast<int64_t>(bid - t_main) * (TM * TN), TN, 1, wn, fr, fq, lane);
+  } else {
+    kb_store<BF16OUT ? 2 : 4>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, n0 + wn * WTN, M, N, Y, ldy,
+                              vec_store, wn, fr, fq, lane);
   }
 }
 
@@ -334,7 +367,7 @@ __global__ __launch_bounds__(256) void k_transpose_scales(const float* __restric
 }  // namespace
 
 bool gemm_kblock_eligible(const GemmArgs& g) {
-  if (g.pow2_mx || g.K % (2 * TKS) != 0 || g.K / TKS > kMaxStages || g.M < 128 || g.N < 128) return false;
+  if (g.pow2_mx || g.K % (2 * TKS) != 0 || g.K / TKS > kMaxStages || g.M < 65 || g.N < 128) return false;
   if (g.lda >= (int64_t(1) << 23) || g.ldb >= (int64_t(1) << 23)) return false;
   const bool a_kb = g.eca < g.K, b_kb = g.ecb < g.K;
   if (!a_kb && !b_kb) return false;
@@ -348,7 +381,7 @@ bool gemm_kblock_eligible(const GemmArgs& g) {
 size_t gemm_kblock_required_scratch(const GemmArgs& g) {
   if (!(g.eca < g.K)) return 0;
   const int64_t Mp = (g.M + TM - 1) / TM * static_cast<int64_t>(TM);
-  return static_cast<size_t>(Mp * (g.K / TKS)) * sizeof(float);  // A's group scales, transposed
+  return (static_cast<size_t>(Mp * (g.K / TKS)) * sizeof(float) + 255) & ~size_t(255);  // A's scales, transposed
 }
 
 hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t st) {
@@ -358,24 +391,55 @@ hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t st) {
   const int vec = ((g.ldy * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(g.y) & 15u) == 0);
   const bool a_kb = g.eca < g.K, b_kb = g.ecb < g.K;
   const int64_t ns = g.K / TKS;
-  float* sat = nullptr;
   const int64_t Mp = tiles_m * static_cast<int64_t>(TM);  // rows padded to whole tiles
-  if (a_kb) {
+  const int T = tiles_m * tiles_n;
+  // Split along K, as in the per-tensor kernel: a grid filling at most half
+  // the CUs splits every tile (up to 8 parts), a ragged last wave at most
+  // half full its tiles (up to 4); each part an even number of stages.  The
+  // scratch holds A's transposed scales, then the parts (256 KB per part
+  // and tile).
+  const size_t sat_bytes = gemm_kblock_required_scratch(g);
+  int t_main = T, split = 1, ns_part = 0;
+  size_t part_total = 0;
+  {
+    const int cus = device_cus();
+    const bool small = 2 * T <= cus;
+    const int rem = small ? T : T % cus;
+    if (small || (T > cus && rem > 0 && 2 * rem <= cus)) {
+      const size_t part_bytes = static_cast<size_t>(rem) * TM * TN * sizeof(float);
+      int sp = std::min(cus / rem, small ? 8 : 4);
+      if (g.fixed_scratch)
+        sp = static_cast<int>(std::min<size_t>(
+            sp, g.fixed_scratch_bytes > sat_bytes ? (g.fixed_scratch_bytes - sat_bytes) / part_bytes : 0));
+      while (sp > 1 && ns % (2 * sp) != 0) --sp;
+      if (sp > 1) {
+        split = sp;
+        t_main = T - rem;
+        ns_part = static_cast<int>(ns / sp);
+        part_total = part_bytes * sp;
+      }
+    }
+  }
+  uint8_t* scratch = nullptr;
+  if (sat_bytes + part_total > 0) {
     void* p = nullptr;
-    hipError_t e = gemm_scratch(g, st, gemm_kblock_required_scratch(g), &p);
+    hipError_t e = gemm_scratch(g, st, sat_bytes + part_total, &p);
     if (e != hipSuccess) return e;
-    sat = static_cast<float*>(p);
+    scratch = static_cast<uint8_t*>(p);
+  }
+  float* sat = a_kb ? reinterpret_cast<float*>(scratch) : nullptr;
+  float* part = split > 1 ? reinterpret_cast<float*>(scratch + sat_bytes) : nullptr;
+  if (a_kb)
     hipLaunchKernelGGL(k_transpose_scales,
                        dim3(static_cast<unsigned>((g.M + 31) / 32), static_cast<unsigned>((ns + 31) / 32)),
                        dim3(256), 0, st, g.sa, g.M, ns, Mp, sat);
-  }
   const float* sbk = b_kb ? g.sb : nullptr;
-  const dim3 grid(tiles_m * tiles_n);
+  const dim3 grid(static_cast<unsigned>(t_main + (T - t_main) * split));
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
 #define FP8RT_KB(FA, FB, OUT, AK, BK)                                                                         \
   hipLaunchKernelGGL((k_gemm_kblock<FA, FB, OUT, AK, BK>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
                      g.M, g.N, g.K, sat, g.sa, g.era, sbk, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n,  \
-                     vec, Mp)
+                     vec, Mp, t_main, split, ns_part, part)
 #define FP8RT_KB_OUT(FA, FB, AK, BK)                    \
   if (g.yt == FP8RT_BF16) FP8RT_KB(FA, FB, true, AK, BK); \
   else FP8RT_KB(FA, FB, false, AK, BK);
@@ -391,6 +455,13 @@ hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t st) {
 #undef FP8RT_KB_KIND
 #undef FP8RT_KB_OUT
 #undef FP8RT_KB
+  if (split > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // scales constant along K were left to the epilogue: the reduction applies them
+    return launch_split_reduce(g, st, part, t_main, split, tiles_m, tiles_n, a_kb ? nullptr : g.sa,
+                               b_kb ? nullptr : g.sb, vec);
+  }
   return hipGetLastError();
 }
 

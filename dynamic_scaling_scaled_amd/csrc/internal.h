@@ -150,6 +150,12 @@ bool gemm_big_eligible(const GemmArgs& g);
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t stream, int* nparts = nullptr);
 bool gemm_kblock_eligible(const GemmArgs& g);
 hipError_t launch_gemm_kblock(const GemmArgs& g, hipStream_t stream);
+// Adds the FP32 K-parts of the split 256 x 256 tiles t_main, t_main + 1, ...
+// (part[k split + p], tile order of the large kernels), then applies
+// s_a(row) s_b(col) (a null table: already applied), the bias and g's output
+// type.
+hipError_t launch_split_reduce(const GemmArgs& g, hipStream_t st, const float* part, int t_main, int split,
+                               int tiles_m, int tiles_n, const float* sa, const float* sb, int vec);
 bool gemm_skinny_eligible(const GemmArgs& g);
 // Workgroups of the decode kernel's grid for g (one statistics partial each
 // with an FP8 output).

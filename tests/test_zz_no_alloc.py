@@ -50,10 +50,11 @@ def both(rt, a, sa, ga, b, sb, gb, flags, out=torch.bfloat16):
 
 
 @pytest.mark.parametrize("case", [
-    # 4096 x 4096: one whole wave of tiles, no split; 256 x 384: two tiles,
-    # each split in 2 K parts on both paths (the parts fit the fixed array)
+    # 4096 x 4096: one whole wave of tiles, no split; the smaller shapes:
+    # one or two tiles, each split in 2 K parts on both paths (the parts
+    # fit the fixed array)
     ("mx32", [(4096, 4096, 512), (256, 384, 512)], (1, 32), (1, 32), True),
-    ("kblock", [(768, 1024, 2048), (256, 256, 512)], (1, 128), (128, 128), False),
+    ("kblock", [(4096, 4096, 512), (256, 256, 512)], (1, 128), (128, 128), False),
 ], ids=lambda c: c[0])
 def test_noalloc_bit_identical(rt, orc, case):
     name, shapes, ga, gb, pow2 = case
