@@ -268,8 +268,8 @@ fp8rt_status gemm_setup(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gr
   if (packed && !decode) return FP8RT_EUNSUPPORTED;
   // exact products: asked for, or free where the decode kernel is latency bound
   const bool exact = (flags & FP8RT_EXACT_PRODUCTS) != 0;
-  if (exact && !decode) return FP8RT_EUNSUPPORTED;
-  g.exact_products = decode && (exact || N * K <= int64_t(FP8RT_EXACT_AUTO_BYTES));
+  if (exact && (!decode || g.pow2_mx)) return FP8RT_EUNSUPPORTED;
+  g.exact_products = decode && !g.pow2_mx && (exact || N * K <= int64_t(FP8RT_EXACT_AUTO_BYTES));
   return FP8RT_OK;
 }
 

@@ -96,38 +96,51 @@ constexpr int kSkMaxM = 64;  // up to 4 MFMA row tiles of A
 // Waves per SIMD the register budget is sized for: 8 (two workgroups per CU,
 // 64 VGPRs) for one or two row tiles of A, or one with exact products; 4 (one
 // workgroup, 128 VGPRs) for four row tiles, whose A fragments alone fill 64
-// VGPRs, and for two with exact products (their widened operands).
-constexpr int sk_waves_per_simd(int mt, bool exact, bool kb) {
-  return (mt >= 4 || (mt >= 2 && (exact || kb)) || (exact && kb)) ? 4 : 8;
+// VGPRs, and for two with exact products (their widened operands) or with
+// scales read per step (sm 1 or 2).
+constexpr int sk_waves_per_simd(int mt, bool exact, int sm) {
+  return (mt >= 4 || (mt >= 2 && (exact || sm != 0)) || (exact && sm == 1)) ? 4 : 8;
 }
 
-// KB: scales that change along K (1 x g groups on A, g_r x g blocks on B,
-// g a multiple of 128) or whose row groups are neither one row nor all rows.
-// Each 128-deep step's partial sum then comes out of MFMAs started from zero
-// and is added to the accumulator times s_a(m, step) s_b(n, step), the
-// scales of the groups that hold the step; the epilogue adds only the bias.
+// SM, where the scales apply: 0 in the epilogue (per tensor or per row, whole
+// K); 1 per 128-deep step (1 x g groups on A, g_r x g blocks on B, g a
+// multiple of 128, or row groups that are neither one row nor all rows):
+// the step's partial comes out of MFMAs started from zero and is added to
+// the accumulator times s_a(m, step) s_b(n, step); 2 inside the MFMA (1 x 32
+// power-of-two scales passed as E8M0 exponents, one per lane: its row and
+// its 32-deep K block).  With 1 or 2 the epilogue adds only the bias.
 // OUT: kOutF32 / kOutBF16, or FP8 codes (kOutE4M3 / kOutE5M2) of y * r_y,
 // r_y = ry[0] or fl32(1 / sy[0]), with the workgroup's max |y| and
 // saturation / underflow counts in ypart[workgroup] (combined by k_finish).
-template <int FA, int FB, int MT, int OUT, bool PACKED, bool EXACT, bool KB>
-__global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void k_gemm_skinny(
+template <int FA, int FB, int MT, int OUT, bool PACKED, bool EXACT, int SM>
+__global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, SM)) void k_gemm_skinny(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, int64_t era, int64_t eca, const float* __restrict__ sb,
     int64_t erb, int64_t ecb, const void* __restrict__ bias, int bias_bf16, void* __restrict__ Y, int64_t ldy,
     int vec_store, const float* __restrict__ sy, const float* __restrict__ ry, BlockPartial* __restrict__ ypart) {
+  constexpr bool KB = SM == 1, MX = SM == 2;
   __shared__ f32x4 red[kSkWaves - 1][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t mb = static_cast<int64_t>(blockIdx.y) * (16 * MT);  // first row of A
-  // row-major: row n0 + r, bytes 32 g of each step; packed: the lane's
-  // 16-byte slots of its group's 2 KB tiles
+  // row-major: row n0 + r, bytes [32 g, +32) of each step, or (MX) bytes
+  // [16 g, +16) and [64 + 16 g, +16): the matrix core's own K order, so its
+  // 32-deep scale blocks are the memory's; packed: the lane's 16-byte slots
+  // of its group's 2 KB tiles
+  constexpr int kLane = MX ? 16 : 32;
   const uint8_t* brow = PACKED ? B + static_cast<int64_t>(blockIdx.x) * (K / 128) * 2048 + lane * 16
-                               : B + min(n0 + r, N - 1) * ldb + 32 * g;
-  const int64_t bstep = PACKED ? 2048 : 128, bhalf = PACKED ? 1024 : 16;
+                               : B + min(n0 + r, N - 1) * ldb + kLane * g;
+  const int64_t bstep = PACKED ? 2048 : 128, bhalf = PACKED ? 1024 : (MX ? 64 : 16);
+  constexpr int ahalf = MX ? 64 : 16;
   const uint8_t* arow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) arow[t] = A + min<int64_t>(mb + 16 * t + r, M - 1) * lda + 32 * g;
+  for (int t = 0; t < MT; ++t) arow[t] = A + min<int64_t>(mb + 16 * t + r, M - 1) * lda + kLane * g;
+  // MX: the lane's scale rows (one float per 32 K)
+  const float* sbx = MX ? sb + min(n0 + r, N - 1) * (K / 32) + g : nullptr;
+  const float* sax[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) sax[t] = MX ? sa + min<int64_t>(mb + 16 * t + r, M - 1) * (K / 32) + g : nullptr;
 
   // this wave's K steps: [s0, s1)
   const int nk = static_cast<int>(K / 128);
@@ -150,10 +163,9 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
   }
   // Two steps per iteration (loads of both first, then both MFMAs): twice
   // the bytes in flight per wave.  An odd last step loads step s1 - 1 again
-  // (a cache hit) and must add nothing: the FP8 variant skips its MFMAs (a
-  // wave-uniform branch); the exact one, whose widening the compiler then
-  // schedules worse, multiplies +0 codes on both sides instead (never a
-  // stand-in zero against a real code: 0 x Inf would be NaN).
+  // (a cache hit), runs its MFMAs and keeps the accumulator as it was (a
+  // select, not a branch: loads used only under a branch are sunk into it,
+  // after the first step's MFMAs, which leaves one step in flight).
   auto mma = [&](const u32x4& b0, const u32x4& b1, const u32x4 (&a0)[MT], const u32x4 (&a1)[MT], bool on,
                  int step) {
     i32x8 bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
@@ -166,19 +178,11 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
 #pragma unroll
       for (int e = 0; e < 4; ++e) fb[e] = sb[boff[e] + kb];
     }
-    if constexpr (EXACT) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bf[e] = on ? bf[e] : 0;
-    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       f32x4 c = KB ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[t];
       i32x8 af = i32x8{(int)a0[t][0], (int)a0[t][1], (int)a0[t][2], (int)a0[t][3],
                        (int)a1[t][0], (int)a1[t][1], (int)a1[t][2], (int)a1[t][3]};
-      if constexpr (EXACT) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) af[e] = on ? af[e] : 0;
-      }
       if constexpr (EXACT) {
         // the step's 128 K as 4 bf16 MFMAs of 32: instruction j takes codes
         // [8 j, +8) of every lane's 32 on both operands (the same K set in
@@ -188,16 +192,21 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
         for (int j = 0; j < 4; ++j)
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8<FB>(bf[2 * j], bf[2 * j + 1]),
                                                       widen8<FA>(af[2 * j], af[2 * j + 1]), c, 0, 0, 0);
+      } else if constexpr (MX) {
+        // E8M0 exponents of the power-of-two scales of the lane's rows and K block
+        const int xb = static_cast<int>((__float_as_uint(sbx[step * 4]) >> 23) & 0xFFu);
+        const int xa = static_cast<int>((__float_as_uint(sax[t][step * 4]) >> 23) & 0xFFu);
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, c, FB, FA, 0, xb, 0, xa);
       } else {
         c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, c, FB, FA, 0, 0, 0, 0);
       }
       if constexpr (KB) {
         const float fa = sa[aoff[t] + ka];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(on ? fa * fb[e] : 0.0f, c[e], acc[t][e]);
-      } else {
-        acc[t] = c;
+        for (int e = 0; e < 4; ++e) c[e] = fmaf(fa * fb[e], c[e], acc[t][e]);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] = on ? c[e] : acc[t][e];
     }
   };
   for (int st = s0; st < s1; st += 2) {
@@ -212,16 +221,12 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       a0[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko);
-      a1[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko + 16);
+      a1[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko + ahalf);
       d0[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko2);
-      d1[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko2 + 16);
+      d1[t] = *reinterpret_cast<const u32x4*>(arow[t] + ko2 + ahalf);
     }
     mma(b0, b1, a0, a1, true, st);
-    if constexpr (EXACT) {
-      mma(c0, c1, d0, d1, st + 1 < s1, st2);
-    } else {
-      if (st + 1 < s1) mma(c0, c1, d0, d1, true, st2);
-    }
+    mma(c0, c1, d0, d1, st + 1 < s1, st2);
   }
 
   // The partial sums meet in LDS; wave 0 finishes.
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t n = min(nb + e, N - 1);
-    sbv[e] = KB ? 1.0f : sb[erb == 1 ? n : 0];
+    sbv[e] = SM != 0 ? 1.0f : sb[erb == 1 ? n : 0];
     bv[e] = 0.0f;
     if (bias)
       bv[e] = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[n]) << 16)
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(kSkThreads, sk_waves_per_simd(MT, EXACT, KB)) void 
   for (int t = 0; t < MT; ++t) {
     const int64_t m = mb + 16 * t + r;
     if (m >= M) continue;
-    const float sav = KB ? 1.0f : sa[era == 1 ? m : 0];
+    const float sav = SM != 0 ? 1.0f : sa[era == 1 ? m : 0];
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = acc[t][e] * (sav * sbv[e]) + bv[e];
@@ -313,20 +318,20 @@ bool skinny_epilogue_scales(const GemmArgs& g) {
   return (g.era == 1 || g.era >= g.M) && (g.erb == 1 || g.erb >= g.N) && g.eca >= g.K && g.ecb >= g.K;
 }
 
-template <int FA, int FB, int MT, bool PACKED, bool EXACT, bool KB>
+template <int FA, int FB, int MT, bool PACKED, bool EXACT, int SM>
 void launch_mt_k(const GemmArgs& g, hipStream_t st, int vec) {
   const dim3 grid(static_cast<unsigned>((g.N + 15) / 16), static_cast<unsigned>((g.M + 16 * MT - 1) / (16 * MT)));
   const int bb = g.bias_t == FP8RT_BF16 ? 1 : 0;
 #define FP8RT_SK(OUT)                                                                                            \
-  hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, OUT, PACKED, EXACT, KB>), grid, dim3(kSkThreads), 0, st, g.a,   \
+  hipLaunchKernelGGL((k_gemm_skinny<FA, FB, MT, OUT, PACKED, EXACT, SM>), grid, dim3(kSkThreads), 0, st, g.a,   \
                      g.lda, g.b, g.ldb, g.M, g.N, g.K, g.sa, g.era, g.eca, g.sb, g.erb, g.ecb, g.bias, bb, g.y, \
                      g.ldy, vec, g.sy, g.ry, g.part)
   switch (gemm_out_kind(g)) {
     case kOutBF16: FP8RT_SK(kOutBF16); break;
     case kOutF32: FP8RT_SK(kOutF32); break;
     default:
-      // FP8 output: FP8 matrix cores and a row-major B only
-      if constexpr (!PACKED && !EXACT) {
+      // FP8 output: FP8 matrix cores, a row-major B and no 1 x 32 scales only
+      if constexpr (!PACKED && !EXACT && SM != 2) {
         if (gemm_out_kind(g) == kOutE4M3) FP8RT_SK(kOutE4M3);
         else FP8RT_SK(kOutE5M2);
       }
@@ -337,10 +342,13 @@ void launch_mt_k(const GemmArgs& g, hipStream_t st, int vec) {
 
 template <int FA, int FB, int MT, bool PACKED, bool EXACT>
 void launch_mt_e(const GemmArgs& g, hipStream_t st, int vec) {
-  if (skinny_epilogue_scales(g)) {
-    launch_mt_k<FA, FB, MT, PACKED, EXACT, false>(g, st, vec);
+  if (g.pow2_mx) {
+    // 1 x 32 scales: FP8 matrix cores on a row-major B (the eligibility test)
+    if constexpr (!PACKED && !EXACT) launch_mt_k<FA, FB, MT, PACKED, EXACT, 2>(g, st, vec);
+  } else if (skinny_epilogue_scales(g)) {
+    launch_mt_k<FA, FB, MT, PACKED, EXACT, 0>(g, st, vec);
   } else {
-    if constexpr (!(MT == 4 && EXACT)) launch_mt_k<FA, FB, MT, PACKED, EXACT, true>(g, st, vec);  // see skinny_row_tiles
+    if constexpr (!(MT == 4 && EXACT)) launch_mt_k<FA, FB, MT, PACKED, EXACT, 1>(g, st, vec);  // see skinny_row_tiles
   }
 }
 
@@ -361,7 +369,7 @@ int skinny_row_tiles(const GemmArgs& g) {
   if ((g.N + 15) / 16 < static_cast<int64_t>(device_cus())) return 1;
   const int mt = g.M <= 16 ? 1 : g.M <= 32 ? 2 : 4;
   // four tiles with exact products and per-step scales exceed 128 VGPRs
-  return (mt == 4 && g.exact_products && !skinny_epilogue_scales(g)) ? 2 : mt;
+  return (mt == 4 && g.exact_products && !g.pow2_mx && !skinny_epilogue_scales(g)) ? 2 : mt;
 }
 
 template <int FA, int FB, bool PACKED>
@@ -400,9 +408,11 @@ __global__ __launch_bounds__(256) void k_pack_weights16(const uint8_t* __restric
 }  // namespace
 
 bool gemm_skinny_eligible(const GemmArgs& g) {
-  // whole 128-deep K steps, each inside one scale group of either operand
-  const bool k_ok = (g.eca >= g.K || g.eca % 128 == 0) && (g.ecb >= g.K || g.ecb % 128 == 0);
-  return k_ok && !g.pow2_mx && g.M <= kSkMaxM && g.K % 128 == 0;
+  // whole 128-deep K steps, each inside one scale group of either operand,
+  // or 1 x 32 scales (inside the MFMA) on a row-major B
+  const bool k_ok = g.pow2_mx ? !g.b_packed
+                              : (g.eca >= g.K || g.eca % 128 == 0) && (g.ecb >= g.K || g.ecb % 128 == 0);
+  return k_ok && g.M <= kSkMaxM && g.K % 128 == 0;
 }
 
 hipError_t launch_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp,

@@ -19,9 +19,9 @@ scales), the large kernel (per-tensor, per-row; 1x32 power-of-two scales on
 the scaled MFMA; a split last wave; a grid so small that every tile is
 split along K), the K-blocked large kernel, and the
 decode kernel on row-major and fragment-ordered weights, with per-row and
-with 1x128 / 128x128 scales (with a weight
-above the size that selects exact products by itself; outputs compared on a
-column sample).
+with 1x128 / 128x128 scales, and on row-major weights with 1x32 power-of-two
+scales on the scaled MFMA (with a weight above the size that selects exact
+products by itself; outputs compared on a column sample).
 
 The decode kernel's exact-product variant (chosen by itself for weights of
 at most 1 MiB of codes, or by FP8RT_EXACT_PRODUCTS) must instead return the
@@ -86,6 +86,7 @@ def scales_for(g, rows, K, gran, pow2_values):
 
 
 # name, M, N, K, ga, gb, flags, A-scale values, packed B
+POW2, EXACT = 1, 4  # FP8RT_POW2_SCALES, FP8RT_EXACT_PRODUCTS
 ROUTES = [
     ("general", 96, 120, 512, (0, 0), (0, 0), 0, [1.0], False),
     ("big-split-all", 96, 384, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
@@ -98,9 +99,10 @@ ROUTES = [
     ("decode-packed", 48, 4224, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], True),
     ("decode-kblock", 16, 4224, 1024, (1, 128), (128, 128), 0, [1.0, 2.0], False),
     ("decode-kblock-packed", 40, 4224, 1024, (1, 128), (128, 128), 0, [1.0, 2.0], True),
+    ("decode-mx32", 16, 4224, 1024, (1, 32), (1, 32), POW2, [1.0, 2.0], False),
+    ("decode-mx32-m64", 64, 4224, 512, (1, 32), (1, 32), POW2, [1.0, 2.0], False),
 ]
 
-POW2, EXACT = 1, 4  # FP8RT_POW2_SCALES, FP8RT_EXACT_PRODUCTS
 EXACT_ROUTES = [
     ("decode-auto", 16, 256, 1024, (1, 0), (1, 0), 0, [1.0, 2.0], False),
     ("decode-auto-m64", 64, 256, 1024, (0, 0), (1, 0), 0, [2.0], False),

@@ -71,10 +71,14 @@ def test_gemm_matches_oracle(rt, orc, shape, fa, grans, out):
     assert ok, st
 
 
-@pytest.mark.parametrize("shape", [(200, 300, 320), (128, 256, 512), (300, 520, 512), (520, 776, 1024)])
+@pytest.mark.parametrize("shape", [(200, 300, 320), (128, 256, 512), (300, 520, 512), (520, 776, 1024),
+                                   (16, 512, 1024), (40, 1003, 1024), (64, 4160, 512)])
 @pytest.mark.parametrize("fa", [0, 1])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_mx32_pow2(rt, orc, shape, fa, out):
+    """1x32 power-of-two scales on both operands: the general kernel, the
+    large kernel (split K parts on the small grids) and the decode kernel
+    (M <= 64: one to four row tiles of A per workgroup, a ragged N)."""
     M, N, K = shape
     ga = gb = (1, 32)
     a, sa, b, sb = operands(orc, 3 + fa, M, N, K, fa, 0, ga, gb, True)
