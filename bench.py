@@ -684,6 +684,12 @@ def extra_components(torch, rt, wl, keep):
     P = rt.fp8_pack_weights16(Wq)
     pk = lambda: rt.fp8_pack_weights16(Wq, out=P.data)
     comp["decode_pack_weights16"] = hbm_entry(time_op(torch, pk, scrub=scrub), 2 * N * K, "k_pack_weights16")
+    # or quantized straight into the image (one pass, no row-major codes)
+    sw2 = f32(N, 1)
+    qwp = lambda: rt.fp8_quantize_packed16(W, (1, 0), rt.E4M3, rt.DYNAMIC, 1e-12, False, sw2, None, out=P.data)
+    qwp()
+    comp["decode_quantize_w_per_channel_into_image"] = hbm_entry(time_op(torch, qwp, scrub=scrub),
+                                                                  N * K * 3 + N * 4, "k_image_rows")
     gmp = lambda: rt.fp8_scaled_gemm(Aq, rt.E4M3, (1, 0), sa, P, rt.E4M3, (1, 0), sw, y, bias=bias)
     gmp()
     e = hbm_entry(time_op(torch, gmp, scrub=scrub), g_bytes, "k_gemm_skinny (packed B)")

@@ -105,6 +105,9 @@ def lib():
                                            C.c_int, P, C.c_int, I64, U32, P]
         L.fp8_pack_weights16.restype = C.c_int
         L.fp8_pack_weights16.argtypes = [P, I64, I64, I64, P, P]
+        L.fp8_quantize_packed16.restype = C.c_int
+        L.fp8_quantize_packed16.argtypes = [P, C.c_int, I64, I64, I64, Gran, C.c_int, C.c_int, F, I32, P, P,
+                                            P, P, P, P]
         L.fp8_scaled_gemm_fp8out.restype = C.c_int
         L.fp8_scaled_gemm_fp8out.argtypes = [P, C.c_int, I64, Gran, P, P, C.c_int, I64, Gran, P, I64, I64,
                                              I64, P, C.c_int, C.c_int, P, P, P, I64, P, P, U32, P]
@@ -227,6 +230,22 @@ def fp8_pack_weights16(q, out=None, stream=None):
         raise ValueError("out must be contiguous uint8 with packed16_bytes(N, K) bytes")
     _check("fp8_pack_weights16", lib().fp8_pack_weights16(_ptr(q), N, K, ldq, _ptr(out), _stream(stream)))
     return PackedWeights(out, N, K)
+
+
+def fp8_quantize_packed16(x, gran, fmt, mode, eps, pow2_round_up, scale, inv_scale, out=None, amax_out=None,
+                          sat_underflow=None, stream=None):
+    """fp8_quantize of x [N x K] with the codes written straight into the
+    fragment-ordered weight image (K % 128 == 0); returns PackedWeights."""
+    rows, cols, ld = _mat(x)
+    if out is None:
+        out = torch.empty(packed16_bytes(rows, cols), dtype=torch.uint8, device=x.device)
+    if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < packed16_bytes(rows, cols):
+        raise ValueError("out must be contiguous uint8 with packed16_bytes(N, K) bytes")
+    _check("fp8_quantize_packed16",
+           lib().fp8_quantize_packed16(_ptr(x), _dtype(x), rows, cols, ld, Gran(*gran), fmt, mode, eps,
+                                       int(pow2_round_up), _ptr(scale), _ptr(inv_scale), _ptr(out),
+                                       _ptr(amax_out), _ptr(sat_underflow), _stream(stream)))
+    return PackedWeights(out, rows, cols)
 
 
 def _weight(b, flags):
@@ -357,7 +376,7 @@ def fp8_weight_only_gemm(x, w, fw, gw, scale_w, y, bias=None, flags=0, stream=No
                                       _stream(stream)))
 
 
-__all__ = ["fp8_pack_weights16", "PackedWeights", "packed16_bytes", "B_PACKED16", "fp8_quant_error", "fp8_granularity_ledger", "LedgerSpec", "LedgerRow", "fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
+__all__ = ["fp8_pack_weights16", "fp8_quantize_packed16", "PackedWeights", "packed16_bytes", "B_PACKED16", "fp8_quant_error", "fp8_granularity_ledger", "LedgerSpec", "LedgerRow", "fp8_delayed_scale_update", "HIST_MAX", "HIST_LATEST", "fp8_weight_only_gemm", "fp8_scaled_gemm_fp8out", "fp8_amax", "fp8_compute_scale", "fp8_quantize", "fp8_quantize_transpose", "fp8_dequantize",
            "fp8_amax_history_update", "fp8_scaled_gemm", "lib", "raw_call", "Gran", "Fp8rtError",
            "E4M3", "E5M2", "F32", "BF16", "DYNAMIC", "GIVEN", "POW2_SCALES", "EXACT_PRODUCTS", "EXACT_AUTO_BYTES", "FMAX", "ngroups",
            "scale_shape"]

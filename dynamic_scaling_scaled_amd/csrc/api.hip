@@ -38,6 +38,45 @@ fp8rt_status check_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld,
   return FP8RT_OK;
 }
 
+// fp8_quantize and fp8_quantize_packed16: q row-major with pitch ldq
+// (img == 0), or the weight image of a matrix of cols = 128 img columns.
+fp8rt_status quantize_to(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                         fp8rt_gran g, fp8rt_format f, fp8rt_mode mode, float eps, int32_t pow2_round_up,
+                         float* scale, float* inv_scale, uint8_t* q, int64_t ldq, int64_t img,
+                         float* amax_out, uint64_t* sat_underflow, hipStream_t stream) {
+  if (!valid_dtype(xt) || !valid_fmt(f) || !scale || !q) return FP8RT_EINVAL;
+  if (mode != FP8RT_DYNAMIC && mode != FP8RT_GIVEN) return FP8RT_EINVAL;
+  if (mode == FP8RT_DYNAMIC && !valid_eps(eps)) return FP8RT_EINVAL;
+  fp8rt_status st = check_matrix(x, rows, cols, ldx, g);
+  if (st != FP8RT_OK) return st;
+  if (ldq < cols) return FP8RT_EINVAL;
+  if (ldq % 16 != 0 || !aligned16(q)) return FP8RT_EALIGN;
+  if (!aligned4(scale) || (inv_scale && !aligned4(inv_scale)) || (amax_out && !aligned4(amax_out)) ||
+      (sat_underflow && (reinterpret_cast<uintptr_t>(sat_underflow) & 7u)))
+    return FP8RT_EALIGN;
+  QuantArgs a{};
+  a.x = x;
+  a.xt = xt;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.er = group_extent(rows, g.rows);
+  a.ec = group_extent(cols, g.cols);
+  a.fmt = f;
+  a.mode = mode;
+  a.eps = mode == FP8RT_DYNAMIC ? eps : 1.0f;
+  a.pow2 = pow2_round_up != 0;
+  a.scale = scale;
+  a.inv_scale = inv_scale;
+  a.q = q;
+  a.ldq = ldq;
+  a.img = img;
+  a.amax_out = amax_out;
+  a.counts = reinterpret_cast<unsigned long long*>(sat_underflow);
+  a.amax_only = false;
+  return from_hip(launch_quantize(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,36 +129,20 @@ fp8rt_status fp8_quantize(const void* x, fp8rt_dtype xt, int64_t rows, int64_t c
                           float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
                           uint8_t* q, int64_t ldq, float* amax_out, uint64_t* sat_underflow,
                           hipStream_t stream) {
-  if (!valid_dtype(xt) || !valid_fmt(f) || !scale || !q) return FP8RT_EINVAL;
-  if (mode != FP8RT_DYNAMIC && mode != FP8RT_GIVEN) return FP8RT_EINVAL;
-  if (mode == FP8RT_DYNAMIC && !valid_eps(eps)) return FP8RT_EINVAL;
-  fp8rt_status st = check_matrix(x, rows, cols, ldx, g);
-  if (st != FP8RT_OK) return st;
-  if (ldq < cols) return FP8RT_EINVAL;
-  if (ldq % 16 != 0 || !aligned16(q)) return FP8RT_EALIGN;
-  if (!aligned4(scale) || (inv_scale && !aligned4(inv_scale)) || (amax_out && !aligned4(amax_out)) ||
-      (sat_underflow && (reinterpret_cast<uintptr_t>(sat_underflow) & 7u)))
-    return FP8RT_EALIGN;
-  QuantArgs a{};
-  a.x = x;
-  a.xt = xt;
-  a.rows = rows;
-  a.cols = cols;
-  a.ldx = ldx;
-  a.er = group_extent(rows, g.rows);
-  a.ec = group_extent(cols, g.cols);
-  a.fmt = f;
-  a.mode = mode;
-  a.eps = mode == FP8RT_DYNAMIC ? eps : 1.0f;
-  a.pow2 = pow2_round_up != 0;
-  a.scale = scale;
-  a.inv_scale = inv_scale;
-  a.q = q;
-  a.ldq = ldq;
-  a.amax_out = amax_out;
-  a.counts = reinterpret_cast<unsigned long long*>(sat_underflow);
-  a.amax_only = false;
-  return from_hip(launch_quantize(a, stream));
+  return quantize_to(x, xt, rows, cols, ldx, g, f, mode, eps, pow2_round_up, scale, inv_scale, q, ldq, 0,
+                     amax_out, sat_underflow, stream);
+}
+
+fp8rt_status fp8_quantize_packed16(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,
+                                   int64_t ldx, fp8rt_gran g, fp8rt_format f, fp8rt_mode mode,
+                                   float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
+                                   uint8_t* qp, float* amax_out, uint64_t* sat_underflow,
+                                   hipStream_t stream) {
+  // the limits of fp8_pack_weights16; the rest is fp8_quantize's validation
+  if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return FP8RT_EINVAL;
+  if (cols > 0 && cols % 128 != 0) return FP8RT_EALIGN;
+  return quantize_to(x, xt, rows, cols, ldx, g, f, mode, eps, pow2_round_up, scale, inv_scale, qp, cols,
+                     cols / 128, amax_out, sat_underflow, stream);
 }
 
 fp8rt_status fp8_quantize_transpose(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,

@@ -61,6 +61,7 @@ struct QuantArgs {
   float* inv_scale;
   uint8_t* q;
   int64_t ldq;
+  int64_t img;  // 0: q row-major (ldq); else q is the weight image of cols = 128 img
   float* amax_out;
   unsigned long long* counts;
   bool amax_only;  // fp8_amax: write amax_out only

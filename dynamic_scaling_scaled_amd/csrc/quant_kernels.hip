@@ -135,14 +135,45 @@ __global__ __launch_bounds__(kBlock) void k_tensor_amax(const T* __restrict__ x,
   if (threadIdx.x == 0) part[blockIdx.x].amax_bits = m;
 }
 
+// Byte offset of the 8 codes that start at (row, col), col a multiple of 8:
+// row-major with pitch ldq when img == 0; else in the fragment-ordered
+// weight image of a matrix with 128 img columns, whose 16-row group G,
+// 128-deep step s, half h, lane l and byte b sit at
+// ((G img + s) 2 + h) 1024 + 16 l + b, with l = 16 ((col / 32) % 4) +
+// row % 16, h = (col / 16) % 2 and b = col % 16 (8 codes never straddle
+// two 16-byte slots).
+__device__ __forceinline__ int64_t code_off(int64_t row, int64_t col, int64_t ldq, int64_t img) {
+  if (img == 0) return row * ldq + col;
+  const int64_t l = (((col >> 5) & 3) << 4) | (row & 15);
+  return (((row >> 4) * img + (col >> 7)) * 2 + ((col >> 4) & 1)) * 1024 + (l << 4) + (col & 15);
+}
+
+// The 8 codes c at q + off.  Row-major codes stream out (nontemporal); the
+// image's 128-byte lines each take 16 bytes from 8 rows, so its stores stay
+// in L2 until the other rows' bytes have joined them.
+__device__ __forceinline__ void store_codes(uint8_t* q, int64_t off, u32x2 c, int64_t img) {
+  if (img == 0) __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + off));
+  else *reinterpret_cast<u32x2*>(q + off) = c;
+}
+
+// First work item of this workgroup in a grid-stride loop.  Image mode, on
+// a grid that is a multiple of 8: workgroup b starts at (b % 8) (grid / 8) +
+// b / 8, so the workgroups of each XCD (dealt round-robin) take a contiguous
+// run of items, and the 16 rows of an image group are cast by one XCD at
+// about the same time and meet in its L2.
+__device__ __forceinline__ int64_t first_item(int64_t img) {
+  if (img == 0 || (gridDim.x & 7u) != 0) return blockIdx.x;
+  return static_cast<int64_t>(blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+}
+
 // Pass 2 of DYNAMIC (every block combines the pass-1 partials and derives
 // (s, r) itself; block 0 writes scale / inv_scale / amax_out) or the single
 // pass of GIVEN mode.  Counters and the observed amax go to per-block
 // partials for the finisher.
-template <typename T, int F, bool GIVEN, bool STATS, bool AMAX>
+template <typename T, int F, bool GIVEN, bool STATS, bool AMAX, bool IMG>
 __global__ __launch_bounds__(kBlock) void k_tensor_cast(
     const T* __restrict__ x, int64_t rows, int64_t opr, int64_t ldx, int64_t segs_per_row,
-    uint8_t* __restrict__ q, int64_t ldq, const BlockPartial* __restrict__ part1, int nparts,
+    uint8_t* __restrict__ q, int64_t ldq, int64_t img, const BlockPartial* __restrict__ part1, int nparts,
     float eps, int pow2, const float* __restrict__ s_in, const float* __restrict__ r_in,
     float* s_out, float* r_out, float* amax_out, BlockPartial* __restrict__ part2) {
   constexpr int U = oct_unroll<T>();
@@ -159,7 +190,8 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
     }
   };
   // the first segment's loads fly while the scale is derived from the partials
-  if (blockIdx.x < nseg) load_seg(blockIdx.x);
+  const int64_t sg0 = IMG ? first_item(img) : blockIdx.x;
+  if (sg0 < nseg) load_seg(sg0);
   float r;
   if constexpr (!GIVEN) {
     uint32_t m = 0;
@@ -186,11 +218,11 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
   const bool r_bad = !(fabsf(r) <= FLT_MAX);
   uint32_t mb = 0;
   uint32_t sat_l = 0, under_l = 0;
-  for (int64_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+  for (int64_t sg = sg0; sg < nseg; sg += gridDim.x) {
     const int64_t rr = sg / segs_per_row;
     const int64_t s = sg - rr * segs_per_row;
     uint8_t* qr = q + rr * ldq;
-    if (sg != blockIdx.x) load_seg(sg);
+    if (sg != sg0) load_seg(sg);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (s * U + u) * kBlock + threadIdx.x;
@@ -202,7 +234,8 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
           nan_path |= omb > kInfBits;
         }
         const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_l, under_l);
-        __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qr + o * 8));
+        if constexpr (IMG) store_codes(q, code_off(rr, o * 8, ldq, img), c, img);
+        else __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qr + o * 8));
       }
     }
   }
@@ -264,10 +297,10 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(const BlockPartial* __re
 // lanes reduce their group's maximum with shuffles, one thread per group
 // computes (s, r) into LDS, then every lane casts its octets.
 
-template <typename T, int F, int L, bool GIVEN, bool STATS, bool AMAX_ONLY>
+template <typename T, int F, int L, bool GIVEN, bool STATS, bool AMAX_ONLY, bool IMG>
 __global__ __launch_bounds__(kBlock) void k_rowgroups(
     const T* __restrict__ x, uint32_t rows, uint32_t oct_cols, int64_t ldx, FastDiv div_opr,
-    uint32_t nCg, uint32_t units, uint8_t* __restrict__ q, int64_t ldq, float eps, int pow2,
+    uint32_t nCg, uint32_t units, uint8_t* __restrict__ q, int64_t ldq, int64_t img, float eps, int pow2,
     float* s_io, float* r_io, float* amax_out, DevWorkspace* ws, unsigned long long* counts) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;
   constexpr int GPU = kBlock * U / L;  // groups per unit
@@ -276,7 +309,7 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
   const uint32_t opr = nCg * L;
   const int t = threadIdx.x;
   uint32_t sat_l = 0, under_l = 0;
-  for (uint32_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+  for (uint32_t unit = IMG ? static_cast<uint32_t>(first_item(img)) : blockIdx.x; unit < units; unit += gridDim.x) {
     const uint32_t base = unit * (kBlock * U);
     Octet<T> v[U];
     uint32_t omb[U];
@@ -327,7 +360,8 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
           const float r = sh_r[(u * kBlock + t) / L];
           const bool nan_path = omb[u] > kInfBits || !(fabsf(r) <= FLT_MAX);
           const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_l, under_l);
-          __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + static_cast<int64_t>(row[u]) * ldq + oc[u] * 8));
+          if constexpr (IMG) store_codes(q, code_off(row[u], oc[u] * 8, ldq, img), c, img);
+          else __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + static_cast<int64_t>(row[u]) * ldq + oc[u] * 8));
         }
       }
     }
@@ -342,18 +376,18 @@ __global__ __launch_bounds__(kBlock) void k_rowgroups(
 // registers (<= kBlock * U octets) and is read once; otherwise it is read
 // twice (max, then cast; the second read mostly hits L2).
 
-template <typename T, int F, bool GIVEN, bool STATS, bool AMAX_ONLY, bool REG>
+template <typename T, int F, bool GIVEN, bool STATS, bool AMAX_ONLY, bool REG, bool IMG>
 __global__ __launch_bounds__(kBlock) void k_blocktile(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int64_t er, int64_t ec,
     int64_t nCg, int64_t ngroups, FastDiv div_full, FastDiv div_tail, uint8_t* __restrict__ q,
-    int64_t ldq, float eps, int pow2, float* s_io, float* r_io, float* amax_out,
+    int64_t ldq, int64_t img, float eps, int pow2, float* s_io, float* r_io, float* amax_out,
     DevWorkspace* ws, unsigned long long* counts) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;
   __shared__ uint32_t sh[kWaves];
   __shared__ float sh_r;
   const int t = threadIdx.x;
   uint32_t sat_l = 0, under_l = 0;
-  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+  for (int64_t g = IMG ? first_item(img) : blockIdx.x; g < ngroups; g += gridDim.x) {
     const int64_t gi = g / nCg, gj = g - gi * nCg;
     const int64_t r0 = gi * er, c0 = gj * ec;
     const int64_t nr = min(er, rows - r0);
@@ -412,7 +446,8 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
             const uint32_t rr = dv.div(o), cc = o - rr * oct_row;
             const bool nan_path = r_bad || v[u].absmax_bits() > kInfBits;
             const u32x2 c = cast_octet<T, F, STATS>(v[u], r, nan_path, sat_l, under_l);
-            __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8));
+            if constexpr (IMG) store_codes(q, code_off(r0 + rr, c0 + cc * 8, ldq, img), c, img);
+            else __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8));
           }
         }
       } else {
@@ -421,7 +456,8 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
           v[0].load_nt(xg + static_cast<int64_t>(rr) * ldx + cc * 8);
           const bool nan_path = r_bad || v[0].absmax_bits() > kInfBits;
           const u32x2 c = cast_octet<T, F, STATS>(v[0], r, nan_path, sat_l, under_l);
-          __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8));
+          if constexpr (IMG) store_codes(q, code_off(r0 + rr, c0 + cc * 8, ldq, img), c, img);
+            else __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qg + static_cast<int64_t>(rr) * ldq + cc * 8));
         }
       }
     }
@@ -430,6 +466,167 @@ __global__ __launch_bounds__(kBlock) void k_blocktile(
   if constexpr (STATS) store_block_partial(ws->pass2, 0, sat_l, under_l);
 }
 
+
+// ---------------------------------------------------------------------------
+// Quantize straight into the weight image, with one scale per row or per
+// tensor, for K up to 128 x 16 x NS.  One workgroup of 16 waves per 16-row
+// group; wave w holds the group's steps w, w + 16, ... (NS at most) in
+// registers.  A step (16 rows x 128 values) is read as whole row segments:
+// load u of lane l takes row 4 u + l / 16, values 8 (l % 16) .. +8, so each
+// load instruction reads 4 contiguous row segments.  Per-row scales: row
+// maxima over the 16 lanes of a segment (shuffles) and the 16 waves (LDS),
+// then (s, r) of each row; per tensor: r from the given scale or from the
+// amax pass's partials.  The codes of a step go through the wave's own
+// 16 x 128-byte LDS tile (row pitch 144 bytes, so the 16 rows of a read fall
+// in different banks) and come back in the image's lane order -- lane l:
+// row l % 16, bytes 32 (l / 16) .. +32 -- so each wave stores two contiguous
+// 1 KB runs per step.  Rows past the end load as zeros and leave zero codes,
+// uncounted.
+
+constexpr int kImgWaves = 16;
+constexpr int kImgPitch = 144;
+
+template <typename T, int F, int NS, bool ROW, bool GIVEN, bool STATS, bool AMAX>
+__global__ __launch_bounds__(kImgWaves * 64) void k_image_rows(
+    const T* __restrict__ x, int64_t rows, int64_t steps, int64_t ldx, uint8_t* __restrict__ qp,
+    const BlockPartial* __restrict__ part1, int nparts, float eps, int pow2, float* s_io, float* r_io,
+    float* amax_out, BlockPartial* __restrict__ part2) {
+  __shared__ uint32_t sh_m[kImgWaves][16];
+  __shared__ float sh_r[16];
+  __shared__ unsigned long long sh_s[kImgWaves], sh_u[kImgWaves];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kImgWaves][16 * kImgPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = lane & 15, rq = lane >> 4;  // loads: value octet seg of rows 4 u + rq
+  const int64_t G = blockIdx.x;
+  Octet<T> v[NS][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = G * 16 + 4 * u + rq;
+    const T* xr = x + min(row, rows - 1) * ldx + 8 * seg;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int64_t st = wave + j * kImgWaves;
+      v[j][u].load_nt(xr + min(st, steps - 1) * 128);  // clamped: every load stays in flight
+      v[j][u].keep_if(row < rows && st < steps);
+    }
+  }
+  uint32_t mb = 0;  // this lane's max |x| bits
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mb = max(mb, v[j][u].absmax_bits());
+  float r[4];  // multiplier of each of the lane's 4 rows
+  if constexpr (ROW) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) m = max(m, v[j][u].absmax_bits());
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o)));
+      if (seg == 0) sh_m[wave][4 * u + rq] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      uint32_t am = sh_m[0][threadIdx.x];
+#pragma unroll
+      for (int i = 1; i < kImgWaves; ++i) am = max(am, sh_m[i][threadIdx.x]);
+      const int64_t rr = G * 16 + threadIdx.x;
+      float sv = 1.0f, rv = 1.0f;
+      if (rr < rows) {
+        const float a = __uint_as_float(am);
+        if (amax_out) amax_out[rr] = a;
+        if constexpr (GIVEN) {
+          sv = s_io[rr];
+          rv = r_io ? r_io[rr] : 1.0f / sv;
+        } else {
+          scale_from_amax(a, Fmt<F>::kMax, eps, pow2 != 0, sv, rv);
+          s_io[rr] = sv;
+          if (r_io) r_io[rr] = rv;
+        }
+      }
+      sh_r[threadIdx.x] = rv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = sh_r[4 * u + rq];
+  } else {
+    float rt;
+    if constexpr (GIVEN) {
+      rt = r_io ? r_io[0] : 1.0f / s_io[0];
+    } else {
+      // the tensor's amax from the amax pass's partials
+      uint32_t m = 0;
+      for (int i = threadIdx.x; i < nparts; i += kImgWaves * 64) m = max(m, part1[i].amax_bits);
+      m = wave_max_u32(m);
+      if (lane == 0) sh_m[wave][0] = m;
+      __syncthreads();
+      m = sh_m[0][0];
+#pragma unroll
+      for (int i = 1; i < kImgWaves; ++i) m = max(m, sh_m[i][0]);
+      const float a = __uint_as_float(m);
+      float sv;
+      scale_from_amax(a, Fmt<F>::kMax, eps, pow2 != 0, sv, rt);
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        s_io[0] = sv;
+        if (r_io) r_io[0] = rt;
+        if (amax_out) amax_out[0] = a;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = rt;
+  }
+  uint32_t sat_l = 0, under_l = 0;
+  uint8_t* wt = tile[wave];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int64_t st = wave + j * kImgWaves;
+    if (st < steps) {  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool nan_path = !(fabsf(r[u]) <= FLT_MAX) || v[j][u].absmax_bits() > kInfBits;
+        const u32x2 c = cast_octet<T, F, STATS>(v[j][u], r[u], nan_path, sat_l, under_l);
+        *reinterpret_cast<u32x2*>(wt + (4 * u + rq) * kImgPitch + 8 * seg) = c;
+      }
+      // the wave's own tile: its LDS operations complete in order
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint8_t* src = wt + (lane & 15) * kImgPitch + 32 * (lane >> 4);
+      const u32x4 h0 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 h1 = *reinterpret_cast<const u32x4*>(src + 16);
+      uint8_t* dst = qp + (G * steps + st) * 2048 + lane * 16;
+      __builtin_nontemporal_store(h0, reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(h1, reinterpret_cast<u32x4*>(dst + 1024));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  if constexpr (STATS || (AMAX && !ROW)) {
+    // this workgroup's partial: max |x| bits and the counts
+    const uint32_t mw = wave_max_u32(mb);
+    const unsigned long long sw = wave_sum_u64(sat_l), uw = wave_sum_u64(under_l);
+    __syncthreads();  // sh_m may still be read above
+    if (lane == 0) {
+      sh_m[wave][0] = mw;
+      sh_s[wave] = sw;
+      sh_u[wave] = uw;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+      unsigned long long sa = 0, ua = 0;
+      for (int i = 0; i < kImgWaves; ++i) {
+        m = max(m, sh_m[i][0]);
+        sa += sh_s[i];
+        ua += sh_u[i];
+      }
+      *reinterpret_cast<u32x4*>(&part2[blockIdx.x]) =
+          u32x4{m, static_cast<uint32_t>(sa), static_cast<uint32_t>(ua), 0u};
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Cast-transpose: the cast of the quantize kernels, with every code written
@@ -627,16 +824,30 @@ __global__ __launch_bounds__(kBlock) void k_col_amax_scale(const uint32_t* __res
   if (r_out) r_out[c] = r;
 }
 
+// Zero codes of the weight image for the rows past `rows` in its last
+// 16-row group (rows % 16 != 0): one thread per (step, half, lane) slot of
+// that group, 16 bytes each.
+__global__ __launch_bounds__(256) void k_image_pad_rows(uint8_t* __restrict__ q, int64_t rows, int64_t img) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // (s * 2 + h) * 64 + l
+  if (i >= img * 128 || (i & 15) < (rows & 15)) return;
+  *reinterpret_cast<u32x4*>(q + ((rows >> 4) * img * 2) * 1024 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 
 namespace {
 
+// Image mode: a grid-stride grid rounded down to a multiple of 8 (the
+// kernels' per-XCD order of work items needs it).
+int img_grid(const QuantArgs& a, int grid) { return (a.img != 0 && grid >= 8) ? grid & ~7 : grid; }
+
 template <typename T, int F>
 hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
-  // A contiguous tensor is one long row for per-tensor work.
+  // A contiguous tensor is one long row for per-tensor work (not when the
+  // codes go to the weight image, whose offsets need the true row).
   int64_t rows = a.rows, cols = a.cols;
-  if (a.ldx == a.cols && a.ldq == a.cols) {
+  if (a.img == 0 && a.ldx == a.cols && a.ldq == a.cols) {
     cols = a.rows * a.cols;
     rows = 1;
   }
@@ -649,7 +860,7 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   const bool given = a.mode == FP8RT_GIVEN;
   const bool stats = a.counts != nullptr;
   const bool am = a.amax_out != nullptr;
-  const int grid = static_cast<int>(std::min<int64_t>({nseg, int64_t(8) * cus, int64_t(kMaxBlocks)}));
+  const int grid = img_grid(a, static_cast<int>(std::min<int64_t>({nseg, int64_t(8) * cus, int64_t(kMaxBlocks)})));
   const int grid1 = static_cast<int>(std::min<int64_t>({nseg, int64_t(4) * cus, int64_t(kMaxBlocks)}));
   DevWorkspace* ws = nullptr;
   hipError_t e = get_workspace(st, &ws);
@@ -661,10 +872,13 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass1, grid1, a.amax_out, nullptr);
     return hipGetLastError();
   }
-#define FP8RT_CAST(GV, ST, AM)                                                                        \
-  hipLaunchKernelGGL((k_tensor_cast<T, F, GV, ST, AM>), dim3(grid), dim3(kBlock), 0, st, x, rows, opr, \
-                     a.ldx, spr, a.q, a.ldq, ws->pass1, grid1, a.eps, a.pow2, a.scale, a.inv_scale,   \
+#define FP8RT_CAST_I(GV, ST, AM, IM)                                                                      \
+  hipLaunchKernelGGL((k_tensor_cast<T, F, GV, ST, AM, IM>), dim3(grid), dim3(kBlock), 0, st, x, rows, opr, \
+                     a.ldx, spr, a.q, a.ldq, a.img, ws->pass1, grid1, a.eps, a.pow2, a.scale, a.inv_scale,   \
                      a.scale, a.inv_scale, a.amax_out, ws->pass2)
+#define FP8RT_CAST(GV, ST, AM)                     \
+  if (a.img != 0) FP8RT_CAST_I(GV, ST, AM, true); \
+  else FP8RT_CAST_I(GV, ST, AM, false)
   if (!given) {
     hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid1), dim3(kBlock), 0, st, x, rows, opr, a.ldx, spr,
                        ws->pass1);
@@ -677,18 +891,22 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
     else FP8RT_CAST(true, false, false);
   }
 #undef FP8RT_CAST
+#undef FP8RT_CAST_I
   if (stats || (given && am))
     hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid,
                        given ? a.amax_out : nullptr, a.counts);
   return hipGetLastError();
 }
 
-template <typename T, int F, int L, bool GIVEN, bool STATS, bool AO>
+template <typename T, int F, int L, bool GIVEN, bool STATS, bool AO, bool IMG = false>
 void launch_rowgroups_t(const QuantArgs& a, hipStream_t st, int grid, uint32_t units, FastDiv dv,
                         uint32_t nCg, DevWorkspace* ws) {
-  hipLaunchKernelGGL((k_rowgroups<T, F, L, GIVEN, STATS, AO>), dim3(grid), dim3(kBlock), 0, st,
+  if constexpr (!IMG && !AO) {
+    if (a.img != 0) return launch_rowgroups_t<T, F, L, GIVEN, STATS, AO, true>(a, st, grid, units, dv, nCg, ws);
+  }
+  hipLaunchKernelGGL((k_rowgroups<T, F, L, GIVEN, STATS, AO, IMG>), dim3(grid), dim3(kBlock), 0, st,
                      static_cast<const T*>(a.x), static_cast<uint32_t>(a.rows),
-                     static_cast<uint32_t>(a.cols / 8), a.ldx, dv, nCg, units, a.q, a.ldq, a.eps,
+                     static_cast<uint32_t>(a.cols / 8), a.ldx, dv, nCg, units, a.q, a.ldq, a.img, a.eps,
                      a.pow2, a.scale, a.inv_scale, a.amax_out, ws, a.counts);
 }
 
@@ -709,8 +927,8 @@ hipError_t quant_rowgroups(const QuantArgs& a, int L, hipStream_t st) {
   const int64_t nCg = ceil_div(a.cols, a.ec);
   const int64_t padded = a.rows * nCg * L;
   const uint32_t units = static_cast<uint32_t>(ceil_div(padded, static_cast<int64_t>(kBlock) * U));
-  const int grid = static_cast<int>(std::min<int64_t>({int64_t(units), int64_t(8) * device_cus(),
-                                                       int64_t(kMaxBlocks)}));
+  const int grid = img_grid(a, static_cast<int>(std::min<int64_t>({int64_t(units), int64_t(8) * device_cus(),
+                                                                   int64_t(kMaxBlocks)})));
   DevWorkspace* ws = nullptr;
   hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
@@ -730,12 +948,15 @@ hipError_t quant_rowgroups(const QuantArgs& a, int L, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int F, bool GIVEN, bool STATS, bool AO, bool REG>
+template <typename T, int F, bool GIVEN, bool STATS, bool AO, bool REG, bool IMG = false>
 void launch_blocktile_t(const QuantArgs& a, hipStream_t st, int grid, int64_t nCg, int64_t ng,
                         FastDiv df, FastDiv dt, DevWorkspace* ws) {
-  hipLaunchKernelGGL((k_blocktile<T, F, GIVEN, STATS, AO, REG>), dim3(grid), dim3(kBlock), 0, st,
+  if constexpr (!IMG && !AO) {
+    if (a.img != 0) return launch_blocktile_t<T, F, GIVEN, STATS, AO, REG, true>(a, st, grid, nCg, ng, df, dt, ws);
+  }
+  hipLaunchKernelGGL((k_blocktile<T, F, GIVEN, STATS, AO, REG, IMG>), dim3(grid), dim3(kBlock), 0, st,
                      static_cast<const T*>(a.x), a.rows, a.cols, a.ldx, a.er, a.ec, nCg, ng, df, dt,
-                     a.q, a.ldq, a.eps, a.pow2, a.scale, a.inv_scale, a.amax_out, ws, a.counts);
+                     a.q, a.ldq, a.img, a.eps, a.pow2, a.scale, a.inv_scale, a.amax_out, ws, a.counts);
 }
 
 template <typename T, int F, bool REG>
@@ -757,7 +978,7 @@ hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
   // up to 32 workgroups per CU: one group each where possible (8 per CU left
   // each workgroup several groups in sequence: 8192 x 8192 per-row 41.1 us,
   // 37.3 at 32)
-  const int grid = static_cast<int>(std::min<int64_t>({ng, int64_t(32) * device_cus(), int64_t(kMaxBlocks)}));
+  const int grid = img_grid(a, static_cast<int>(std::min<int64_t>({ng, int64_t(32) * device_cus(), int64_t(kMaxBlocks)})));
   DevWorkspace* ws = nullptr;
   hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
@@ -771,8 +992,105 @@ hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Into the weight image with per-row or per-tensor scales: k_image_rows,
+// when a row's steps fit its registers (NS per wave) and the 16-row groups
+// one grid of partials.
+// (With counters one step less: the per-element counting would spill.)
+template <typename T> constexpr int img_max_ns(bool stats) {
+  return sizeof(T) == 2 ? (stats ? 3 : 4) : (stats ? 1 : 2);
+}
+
+template <typename T>
+bool image_rows_eligible(const QuantArgs& a) {
+  if (a.img == 0 || a.amax_only || a.ec != a.cols) return false;
+  return (a.er == 1 || a.er == a.rows) && a.img <= kImgWaves * img_max_ns<T>(a.counts != nullptr) &&
+         ceil_div(a.rows, 16) <= kMaxBlocks;
+}
+
+template <typename T, int F, int NS, bool ROW, bool GV, bool ST, bool AM>
+void launch_image_t(const QuantArgs& a, hipStream_t st, int grid, int nparts, DevWorkspace* ws) {
+  hipLaunchKernelGGL((k_image_rows<T, F, NS, ROW, GV, ST, AM>), dim3(grid), dim3(kImgWaves * 64), 0, st,
+                     static_cast<const T*>(a.x), a.rows, a.img, a.ldx, a.q, ws->pass1, nparts, a.eps, a.pow2,
+                     a.scale, a.inv_scale, a.amax_out, ws->pass2);
+}
+
+template <typename T, int F, int NS, bool ST>
+void image_dispatch_st(const QuantArgs& a, hipStream_t st, int grid, int nparts, DevWorkspace* ws, bool row) {
+  const bool given = a.mode == FP8RT_GIVEN, am = a.amax_out != nullptr;
+  if (row) {  // a row's observed amax is written directly
+    if (given) launch_image_t<T, F, NS, true, true, ST, false>(a, st, grid, nparts, ws);
+    else launch_image_t<T, F, NS, true, false, ST, false>(a, st, grid, nparts, ws);
+  } else if (!given) {
+    launch_image_t<T, F, NS, false, false, ST, false>(a, st, grid, nparts, ws);
+  } else {
+    if (am) launch_image_t<T, F, NS, false, true, ST, true>(a, st, grid, nparts, ws);
+    else launch_image_t<T, F, NS, false, true, ST, false>(a, st, grid, nparts, ws);
+  }
+}
+
+// false: no variant for these steps (image_rows_eligible rules it out)
+template <typename T, int F, int NS>
+bool image_dispatch(const QuantArgs& a, hipStream_t st, int grid, int nparts, DevWorkspace* ws, bool row) {
+  if constexpr (NS > img_max_ns<T>(false)) {
+    return false;
+  } else {
+    if (a.counts == nullptr) {
+      image_dispatch_st<T, F, NS, false>(a, st, grid, nparts, ws, row);
+      return true;
+    }
+    if constexpr (NS <= img_max_ns<T>(true)) {
+      image_dispatch_st<T, F, NS, true>(a, st, grid, nparts, ws, row);
+      return true;
+    }
+    return false;
+  }
+}
+
+template <typename T, int F>
+hipError_t quant_image_rows(const QuantArgs& a, hipStream_t st) {
+  DevWorkspace* ws = nullptr;
+  hipError_t e = get_workspace(st, &ws);
+  if (e != hipSuccess) return e;
+  const bool row = a.er != a.rows, given = a.mode == FP8RT_GIVEN;
+  const int grid = static_cast<int>(ceil_div(a.rows, 16));
+  int nparts = 0;
+  if (!row && !given) {
+    // the tensor's amax pass (as the row-major per-tensor path runs it)
+    int64_t rows = a.rows, cols = a.cols;
+    if (a.ldx == a.cols) {
+      cols = a.rows * a.cols;
+      rows = 1;
+    }
+    const int64_t opr = cols / 8;
+    const int64_t spr = ceil_div(opr, static_cast<int64_t>(kBlock) * oct_unroll<T>());
+    nparts = static_cast<int>(std::min<int64_t>({rows * spr, int64_t(4) * device_cus(), int64_t(kMaxBlocks)}));
+    hipLaunchKernelGGL(k_tensor_amax<T>, dim3(nparts), dim3(kBlock), 0, st, static_cast<const T*>(a.x), rows, opr,
+                       a.ldx, spr, ws->pass1);
+  }
+  bool ok = false;
+  switch (ceil_div(a.img, int64_t(kImgWaves))) {
+    case 1: ok = image_dispatch<T, F, 1>(a, st, grid, nparts, ws, row); break;
+    case 2: ok = image_dispatch<T, F, 2>(a, st, grid, nparts, ws, row); break;
+    case 3: ok = image_dispatch<T, F, 3>(a, st, grid, nparts, ws, row); break;
+    case 4: ok = image_dispatch<T, F, 4>(a, st, grid, nparts, ws, row); break;
+    default: break;
+  }
+  if (!ok) return hipErrorInvalidValue;
+  if (a.counts || (given && !row && a.amax_out))
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid,
+                       (given && !row) ? a.amax_out : nullptr, a.counts);
+  return hipGetLastError();
+}
+
 template <typename T, int F>
 hipError_t quant_typed(const QuantArgs& a, hipStream_t st) {
+  if (image_rows_eligible<T>(a)) return quant_image_rows<T, F>(a, st);
+  if (a.img != 0 && a.rows % 16 != 0) {
+    // the image's rows past the last one of a short last 16-row group
+    const int64_t n = a.img * 128;
+    hipLaunchKernelGGL(k_image_pad_rows, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, a.q,
+                       a.rows, a.img);
+  }
   if (a.er == a.rows && a.ec == a.cols) return quant_tensor<T, F>(a, st);
   if (a.er == 1) {
     const int64_t L = a.ec / 8;

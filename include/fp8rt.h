@@ -356,6 +356,24 @@ static inline int64_t fp8_packed16_bytes(int64_t N, int64_t K) { return (N + 15)
 fp8rt_status fp8_pack_weights16(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, uint8_t* qp,
                                 hipStream_t stream);
 
+/* fp8_quantize with the codes written straight into the fragment-ordered
+ * weight image [as fp8_pack_weights16: the weight is quantized and laid out
+ * once and reused by every call].  Arguments, scales, amax_out, counters
+ * and statuses are those of fp8_quantize on x [rows x cols] (rows = N,
+ * cols = K), with q replaced by
+ *   qp : fp8_packed16_bytes(rows, cols) bytes, 16-byte aligned, caller-owned,
+ *        not overlapping x or the scale arrays;
+ * on return qp holds exactly what fp8_pack_weights16 makes of the codes
+ * fp8_quantize would write (zeros in the rows past `rows` of a short last
+ * 16-row group), without the row-major codes and the second pass.
+ * Extra conditions: cols a multiple of 128 (else FP8RT_EALIGN), rows and
+ * cols <= 2^31 (else FP8RT_EINVAL).  Every granularity of fp8_quantize. */
+fp8rt_status fp8_quantize_packed16(const void* x, fp8rt_dtype xt, int64_t rows, int64_t cols,
+                                   int64_t ldx, fp8rt_gran g, fp8rt_format f, fp8rt_mode mode,
+                                   float eps, int32_t pow2_round_up, float* scale, float* inv_scale,
+                                   uint8_t* qp, float* amax_out, uint64_t* sat_underflow,
+                                   hipStream_t stream);
+
 /* Quantization error of a weight, for the granularity ledger ["Quantization
  * W8A16" (datawhalechina llm-algo-leetcode): the granularity comparison
  * reports each granularity's restored-weight mean squared error and the layer

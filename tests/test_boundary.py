@@ -252,6 +252,34 @@ def test_pack_weights16_validation(rt):
     assert rt.packed16_bytes(17, 256) == 32 * 256 and rt.packed16_bytes(16, 128) == 2048
 
 
+def test_quantize_packed16_validation(rt):
+    """fp8_quantize's checks, plus K a multiple of 128 and the pack's size limits."""
+    L = rt.lib()
+
+    def call(**kw):
+        a = dict(x=FAKE, xt=rt.BF16, rows=16, cols=256, ldx=256, gran=(1, 0), f=rt.E4M3, mode=rt.DYNAMIC,
+                 eps=1e-12, pow2=0, scale=FAKE, inv=None, qp=FAKE, amax=None, cnt=None)
+        a.update(kw)
+        return L.fp8_quantize_packed16(a["x"], a["xt"], a["rows"], a["cols"], a["ldx"], rt.Gran(*a["gran"]),
+                                       a["f"], a["mode"], a["eps"], a["pow2"], a["scale"], a["inv"], a["qp"],
+                                       a["amax"], a["cnt"], None)
+    assert call(x=None) == rt.EINVAL
+    assert call(qp=None) == rt.EINVAL
+    assert call(scale=None) == rt.EINVAL
+    assert call(rows=0) == rt.EINVAL
+    assert call(cols=0) == rt.EINVAL
+    assert call(rows=2 ** 31 + 1) == rt.EINVAL
+    assert call(ldx=128) == rt.EINVAL
+    assert call(eps=0.0) == rt.EINVAL
+    assert call(mode=5) == rt.EINVAL
+    assert call(cols=64, ldx=64) == rt.EALIGN        # K not a multiple of 128
+    assert call(cols=144, ldx=144) == rt.EALIGN
+    assert call(qp=FAKE + 8) == rt.EALIGN
+    assert call(x=FAKE + 8) == rt.EALIGN
+    assert call(gran=(1, 24)) == rt.EALIGN
+    assert call(cnt=FAKE_ODD) == rt.EALIGN
+
+
 def test_delayed_scale_update_validation(rt):
     L = rt.lib()
 
