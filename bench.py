@@ -695,6 +695,13 @@ def extra_components(torch, rt, wl, keep):
     e = hbm_entry(time_op(torch, gmp, scrub=scrub), g_bytes, "k_gemm_skinny (packed B)")
     e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
     comp["decode_gemm_bf16_bias_packed_w"] = e
+    g8p = lambda: rt.fp8_scaled_gemm_fp8out(Aq, rt.E4M3, (1, 0), sa, P, rt.E4M3, (1, 0), sw, yq8, rt.E4M3, sy8,
+                                            None, amy, cnty, bias=bias)
+    g8p()
+    e = hbm_entry(time_op(torch, g8p, scrub=scrub), M * K + N * K + M * N + (M + N) * 4 + N * 2,
+                  "k_gemm_skinny (packed B, E4M3 output) + k_finish")
+    e["TFLOP_s"] = 2.0 * M * N * K / (e["us"] * 1e-6) / 1e12
+    comp["decode_gemm_fp8_out_e4m3_packed_w"] = e
     wop = lambda: rt.fp8_weight_only_gemm(A, P, rt.E4M3, (1, 0), sw, yw, bias=bias)
     wop()
     e = hbm_entry(time_op(torch, wop, scrub=scrub), wo_bytes, "k_gemm_wonly (packed W)")

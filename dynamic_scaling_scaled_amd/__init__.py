@@ -291,7 +291,7 @@ def raw_call(name: str, *args) -> int:
 def fp8_scaled_gemm_fp8out(a, fa, ga, scale_a, b, fb, gb, scale_b, yq, fy, scale_y, inv_scale_y=None,
                            amax_y=None, sat_underflow=None, bias=None, flags=0, stream=None):
     M, K, lda = _mat(a)
-    N, K2, ldb = _mat(b)
+    N, K2, ldb, flags = _weight(b, flags)
     if K2 != K:
         raise ValueError("A and B disagree on K")
     My, Ny, ldy = _mat(yq)

@@ -347,11 +347,14 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
                                     int64_t ldy, float* amax_y, uint64_t* sat_underflow, uint32_t flags,
                                     hipStream_t stream) {
   if (!yq || !scale_y || !valid_fmt(fy)) return FP8RT_EINVAL;
-  if (flags & (FP8RT_B_PACKED16 | FP8RT_EXACT_PRODUCTS)) return FP8RT_EUNSUPPORTED;
+  if (flags & FP8RT_EXACT_PRODUCTS) return FP8RT_EUNSUPPORTED;
   GemmArgs g{};
   const fp8rt_status st =
       gemm_setup(a, fa, lda, ga, scale_a, b, fb, ldb, gb, scale_b, M, N, K, bias, bias_t, ldy, flags, g);
   if (st != FP8RT_OK) return st;
+  g.exact_products = false;  // the FP8 matrix cores form the products here
+  // the weight image: the decode kernel, one statistics partial per workgroup
+  if (g.b_packed && skinny_blocks(g) > kMaxBlocks) return FP8RT_EUNSUPPORTED;
   if (!aligned4(scale_y) || (inv_scale_y && !aligned4(inv_scale_y)) || (amax_y && !aligned4(amax_y)) ||
       (sat_underflow && (reinterpret_cast<uintptr_t>(sat_underflow) & 7u)))
     return FP8RT_EALIGN;
@@ -361,7 +364,6 @@ fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t l
   if (get_workspace(stream, &ws) != hipSuccess) return FP8RT_EHIP;
   g.y = yq;
   g.yt = FP8RT_F32;  // unused with yq_fmt set
-  g.exact_products = false;  // the FP8 matrix cores form the products here
   g.yq_fmt = fy;
   g.sy = scale_y;
   g.ry = inv_scale_y;

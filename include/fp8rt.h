@@ -293,12 +293,16 @@ fp8rt_status fp8_scaled_gemm_noalloc(const uint8_t* a, fp8rt_format fa, int64_t 
  *   sat_underflow (nullable, [2]): |fl32(y r_y)| > F_max, and y != 0 cast to
  *   a zero code.
  * Operands, granularities and alignment as fp8_scaled_gemm; yq : [M x N]
- * codes (ldy).  The large-shape kernel (per-tensor, per-row and 1x32
- * power-of-two scales) runs it, a ragged last wave of tiles split along K
- * with the requantization in the reduction kernel; other shapes run on the
- * general kernel.  Limit: ceil(M/128) ceil(N/128) <= 8192 (one per-block
- * statistics partial per output tile), else FP8RT_EUNSUPPORTED.
- * FP8RT_B_PACKED16 and FP8RT_EXACT_PRODUCTS are not accepted here
+ * codes (ldy).  Decode shapes (M <= 64, K a multiple of 128, no 1x32
+ * scales) run on the decode kernel, row-major or on the weight image
+ * (FP8RT_B_PACKED16; bit-identical results); the large-shape kernel
+ * (per-tensor, per-row and 1x32 power-of-two scales) runs large shapes, a
+ * ragged last wave of tiles split along K with the requantization in the
+ * reduction kernel; other shapes run on the general kernel.  Limit:
+ * ceil(M/128) ceil(N/128) <= 8192 (one per-block statistics partial per
+ * output tile), and on the weight image ceil(N/16) times the decode
+ * kernel's row-tile workgroups per column group <= 8192, else
+ * FP8RT_EUNSUPPORTED.  FP8RT_EXACT_PRODUCTS is not accepted here
  * (FP8RT_EUNSUPPORTED): the FP8 matrix cores form the products. */
 fp8rt_status fp8_scaled_gemm_fp8out(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8rt_gran ga,
                                     const float* scale_a, const uint8_t* b, fp8rt_format fb, int64_t ldb,

@@ -192,7 +192,8 @@ def test_gemm_fp8out_validation(rt):
     assert call(K=48, lda=48, ldb=48) == rt.EALIGN or call(K=40, lda=48, ldb=48) == rt.EALIGN
     assert call(sy=FAKE + 2) == rt.EALIGN
     assert call(M=128 * 8193, N=128, ldy=128) == rt.EUNSUPPORTED
-    assert call(flags=rt.B_PACKED16) == rt.EUNSUPPORTED
+    assert call(flags=rt.B_PACKED16) == rt.EUNSUPPORTED      # the image needs K a multiple of 128
+    assert call(flags=rt.B_PACKED16, M=16, N=16 * 8193, K=128, lda=128, ldb=128, ldy=16 * 8193) == rt.EUNSUPPORTED
     assert call(flags=rt.EXACT_PRODUCTS) == rt.EUNSUPPORTED  # FP8 matrix cores only
 
 

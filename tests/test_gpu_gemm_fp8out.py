@@ -8,7 +8,8 @@ be within T of max |y_ref|, and each counter between the number of elements
 certain to be counted and the number that may be.  Shapes exercise the
 general kernel, the decode kernel (one to four row tiles, per-step block
 scales, a ragged last column group), the large kernel and its 1x32 (MX)
-path."""
+path; on the fragment-ordered weight image the decode kernel must give the
+row-major call's codes, amax and counters bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -66,6 +67,53 @@ def test_fp8_output_split_last_wave(rt, orc, fy, with_inv):
     both dimensions) run as K-split units; the reduction kernel requantizes
     them and supplies their statistics partials."""
     check_fp8out(rt, orc, ((520, 22000, 512), (1, 0), (1, 0), False), fy, with_inv)
+
+
+IMAGE_CASES = [  # decode shapes: (shape, ga, gb)
+    ((16, 512, 1024), (1, 0), (1, 0)),
+    ((40, 1003, 1024), (0, 0), (1, 0)),        # two row tiles, ragged N (a short last 16-row group)
+    ((64, 4160, 512), (1, 0), (1, 0)),         # four row tiles in one workgroup
+    ((16, 640, 1024), (1, 128), (128, 128)),   # per-step block scales
+    ((16, 8192, 8192), (1, 0), (1, 0)),        # the decode layer's size
+]
+
+
+@pytest.mark.parametrize("case", IMAGE_CASES, ids=[str(c) for c in IMAGE_CASES])
+@pytest.mark.parametrize("fy", [0, 1])
+def test_fp8_output_on_weight_image(rt, case, fy):
+    """FP8 output with B as the fragment-ordered image: the decode kernel reads
+    the same bytes in the same order, so codes, amax and counters equal the
+    row-major call's bit for bit (that call is checked against the oracle
+    above)."""
+    (M, N, K), ga, gb = case
+    g = torch.Generator(device="cuda")
+    g.manual_seed(case_seed("fp8out-image", case, fy))
+    x = torch.randn((M, K), device="cuda", generator=g)
+    w = torch.randn((N, K), device="cuda", generator=g) * 0.02
+    sa = torch.empty(rt.scale_shape((M, K), ga), device="cuda")
+    sb = torch.empty(rt.scale_shape((N, K), gb), device="cuda")
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    b = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    rt.fp8_quantize(x, ga, 0, rt.DYNAMIC, 1e-12, False, sa, None, a)
+    rt.fp8_quantize(w, gb, 0, rt.DYNAMIC, 1e-12, False, sb, None, b)
+    bias = torch.randn(N, device="cuda", generator=g).to(torch.bfloat16)
+    # an output scale that saturates the largest outputs: half of max |y| / F_max
+    am0 = torch.zeros(1, device="cuda")
+    rt.fp8_scaled_gemm_fp8out(a, 0, ga, sa, b, 0, gb, sb, torch.empty((M, N), dtype=torch.uint8, device="cuda"),
+                              fy, torch.ones((1, 1), device="cuda"), None, am0, None, bias=bias)
+    sy = (am0 * 0.5 / (448.0 if fy == 0 else 57344.0)).reshape(1, 1)
+    out = []
+    for B in (b, rt.fp8_pack_weights16(b)):
+        yq = torch.full((M, N), 0xAA, dtype=torch.uint8, device="cuda")
+        amax = torch.full((1,), float("nan"), device="cuda")
+        cnt = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+        rt.fp8_scaled_gemm_fp8out(a, 0, ga, sa, B, 0, gb, sb, yq, fy, sy, None, amax, cnt, bias=bias)
+        out.append((yq, amax, cnt))
+    torch.cuda.synchronize()
+    (q0, a0, c0), (q1, a1, c1) = out
+    assert torch.equal(q0, q1)
+    assert torch.equal(a0.view(torch.int32), a1.view(torch.int32))
+    assert c0.tolist() == c1.tolist() and c0[0].item() > 0
 
 
 def check_fp8out(rt, orc, case, fy, with_inv):
