@@ -282,7 +282,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     // tile, or per split-K reduce block).
     int nb = 0;
     hipError_t e;
-    if (gemm_skinny_eligible(g) && !g.exact_products && !g.pow2_mx && skinny_blocks(g) <= kMaxBlocks) {
+    if (gemm_skinny_eligible(g) && !g.exact_products && skinny_blocks(g) <= kMaxBlocks) {
       e = launch_gemm_skinny(g, st);
       nb = static_cast<int>(skinny_blocks(g));
     } else if (g.b_packed) {

@@ -330,8 +330,8 @@ void launch_mt_k(const GemmArgs& g, hipStream_t st, int vec) {
     case kOutBF16: FP8RT_SK(kOutBF16); break;
     case kOutF32: FP8RT_SK(kOutF32); break;
     default:
-      // FP8 output: FP8 matrix cores and no 1 x 32 scales only
-      if constexpr (!EXACT && SM != 2) {
+      // FP8 output: FP8 matrix cores only
+      if constexpr (!EXACT) {
         if (gemm_out_kind(g) == kOutE4M3) FP8RT_SK(kOutE4M3);
         else FP8RT_SK(kOutE5M2);
       }
@@ -431,7 +431,7 @@ int64_t skinny_blocks(const GemmArgs& g) {
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t st) {
   const int kind = gemm_out_kind(g);
   // FP8 codes out: built for the FP8 matrix cores only
-  if (kind >= kOutE4M3 && (g.exact_products || g.pow2_mx)) return hipErrorInvalidValue;
+  if (kind >= kOutE4M3 && g.exact_products) return hipErrorInvalidValue;
   const int esz = kind == kOutF32 ? 4 : kind == kOutBF16 ? 2 : 1;
   const int vec = ((g.ldy * esz) % (4 * esz) == 0) && ((reinterpret_cast<uintptr_t>(g.y) & (4 * esz - 1)) == 0);
   if (g.fa == FP8RT_E4M3) launch_fmt<0, 0>(g, st, vec);

@@ -293,9 +293,9 @@ fp8rt_status fp8_scaled_gemm_noalloc(const uint8_t* a, fp8rt_format fa, int64_t 
  *   sat_underflow (nullable, [2]): |fl32(y r_y)| > F_max, and y != 0 cast to
  *   a zero code.
  * Operands, granularities and alignment as fp8_scaled_gemm; yq : [M x N]
- * codes (ldy).  Decode shapes (M <= 64, K a multiple of 128, no 1x32
- * scales) run on the decode kernel, row-major or on the weight image
- * (FP8RT_B_PACKED16; bit-identical results); the large-shape kernel
+ * codes (ldy).  Decode shapes (M <= 64, K a multiple of 128) run on the
+ * decode kernel, row-major or on the weight image (FP8RT_B_PACKED16, not
+ * with 1x32 scales; bit-identical results); the large-shape kernel
  * (per-tensor, per-row and 1x32 power-of-two scales) runs large shapes, a
  * ragged last wave of tiles split along K with the requantization in the
  * reduction kernel; other shapes run on the general kernel.  Limit:

@@ -50,6 +50,7 @@ CASES = [  # (shape, ga, gb, pow2)
     ((16, 640, 1024), (1, 128), (128, 128), False),  # decode kernel, per-step block scales
     ((264, 400, 512), (1, 128), (128, 128), False),  # K-blocked scales (general kernel)
     ((520, 776, 1024), (1, 32), (1, 32), True),  # 1x32 power-of-two scales (large kernel)
+    ((40, 1003, 1024), (1, 32), (1, 32), True),  # 1x32 power-of-two scales (decode kernel)
 ]
 
 
