@@ -531,7 +531,8 @@ def tiny_latency(torch, rt, wl, keep):
            "step_us_scrubbed": float(time_op(torch, step, reps=50, warmup=3, scrub=scrub)),
            "quantize_us_warm": float(time_op(torch, q, reps=200, warmup=10)),
            "gemm_us_warm": float(time_op(torch, gm, reps=200, warmup=10)),
-           "kernels": "k_tensor_amax + k_tensor_cast + k_finish; k_gemm_skinny (exact products, a workgroup per 16-row tile of A)"}
+           "kernels": "k_tensor_amax + k_tensor_cast (counters added by atomics: a small grid); "
+                      "k_gemm_skinny (exact products, a workgroup per 16-row tile of A)"}
     step()
     torch.cuda.synchronize()
     keep["tiny"] = {"x": d["x"], "w": d["w"], "xq": xq.cpu().numpy(), "wq": wq.cpu().numpy(),

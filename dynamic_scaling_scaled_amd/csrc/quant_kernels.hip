@@ -112,7 +112,10 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tensor_amax(const T* __restrict__ x, int64_t rows,
                                                         int64_t opr, int64_t ldx,
                                                         int64_t segs_per_row,
-                                                        BlockPartial* __restrict__ part) {
+                                                        BlockPartial* __restrict__ part,
+                                                        unsigned long long* zero_counts) {
+  // the cast pass of a small grid adds its counts straight into these
+  if (zero_counts && blockIdx.x == 0 && threadIdx.x < 2) zero_counts[threadIdx.x] = 0ull;
   constexpr int U = oct_unroll<T>();
   __shared__ uint32_t sh[kWaves];
   uint32_t m = 0;
@@ -175,7 +178,8 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
     const T* __restrict__ x, int64_t rows, int64_t opr, int64_t ldx, int64_t segs_per_row,
     uint8_t* __restrict__ q, int64_t ldq, int64_t img, const BlockPartial* __restrict__ part1, int nparts,
     float eps, int pow2, const float* __restrict__ s_in, const float* __restrict__ r_in,
-    float* s_out, float* r_out, float* amax_out, BlockPartial* __restrict__ part2) {
+    float* s_out, float* r_out, float* amax_out, BlockPartial* __restrict__ part2,
+    unsigned long long* acc_counts) {
   constexpr int U = oct_unroll<T>();
   __shared__ uint32_t sh[kWaves];
   const int64_t nseg = rows * segs_per_row;
@@ -237,6 +241,29 @@ __global__ __launch_bounds__(kBlock) void k_tensor_cast(
         if constexpr (IMG) store_codes(q, code_off(rr, o * 8, ldq, img), c, img);
         else __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(qr + o * 8));
       }
+    }
+  }
+  if constexpr (STATS && !GIVEN) {
+    if (acc_counts) {
+      // a small grid: one device-scope add per block and counter instead of
+      // a finisher launch (the amax pass zeroed the counters)
+      __shared__ unsigned long long sh_s[kWaves], sh_u[kWaves];
+      const unsigned long long sw = wave_sum_u64(sat_l), uw = wave_sum_u64(under_l);
+      if ((threadIdx.x & 63) == 0) {
+        sh_s[threadIdx.x >> 6] = sw;
+        sh_u[threadIdx.x >> 6] = uw;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        unsigned long long st = 0, ut = 0;
+        for (int i = 0; i < kWaves; ++i) {
+          st += sh_s[i];
+          ut += sh_u[i];
+        }
+        atomicAdd(&acc_counts[0], st);
+        atomicAdd(&acc_counts[1], ut);
+      }
+      return;
     }
   }
   if constexpr (STATS || AMAX) store_block_partial(part2, mb, sat_l, under_l);
@@ -838,6 +865,10 @@ __global__ __launch_bounds__(256) void k_image_pad_rows(uint8_t* __restrict__ q,
 
 namespace {
 
+// Largest cast grid whose counters go straight to the output by atomics:
+// 2 x 128 device-scope adds cost less than a finisher launch.
+constexpr int kSmallCountGrid = 128;
+
 // Image mode: a grid-stride grid rounded down to a multiple of 8 (the
 // kernels' per-XCD order of work items needs it).
 int img_grid(const QuantArgs& a, int grid) { return (a.img != 0 && grid >= 8) ? grid & ~7 : grid; }
@@ -866,22 +897,25 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   hipError_t e = get_workspace(st, &ws);
   if (e != hipSuccess) return e;
   const T* x = static_cast<const T*>(a.x);
+  // DYNAMIC with counters on a small grid: the cast pass adds its counts
+  // into the output (zeroed by the amax pass), no finisher launch
+  const bool small_counts = !given && stats && !a.amax_only && grid <= kSmallCountGrid;
   if (a.amax_only) {
     hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid1), dim3(kBlock), 0, st, x, rows, opr, a.ldx, spr,
-                       ws->pass1);
+                       ws->pass1, nullptr);
     hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass1, grid1, a.amax_out, nullptr);
     return hipGetLastError();
   }
 #define FP8RT_CAST_I(GV, ST, AM, IM)                                                                      \
   hipLaunchKernelGGL((k_tensor_cast<T, F, GV, ST, AM, IM>), dim3(grid), dim3(kBlock), 0, st, x, rows, opr, \
                      a.ldx, spr, a.q, a.ldq, a.img, ws->pass1, grid1, a.eps, a.pow2, a.scale, a.inv_scale,   \
-                     a.scale, a.inv_scale, a.amax_out, ws->pass2)
+                     a.scale, a.inv_scale, a.amax_out, ws->pass2, small_counts ? a.counts : nullptr)
 #define FP8RT_CAST(GV, ST, AM)                     \
   if (a.img != 0) FP8RT_CAST_I(GV, ST, AM, true); \
   else FP8RT_CAST_I(GV, ST, AM, false)
   if (!given) {
     hipLaunchKernelGGL(k_tensor_amax<T>, dim3(grid1), dim3(kBlock), 0, st, x, rows, opr, a.ldx, spr,
-                       ws->pass1);
+                       ws->pass1, small_counts ? a.counts : nullptr);
     if (stats) FP8RT_CAST(false, true, false);
     else FP8RT_CAST(false, false, false);
   } else {
@@ -892,7 +926,7 @@ hipError_t quant_tensor(const QuantArgs& a, hipStream_t st) {
   }
 #undef FP8RT_CAST
 #undef FP8RT_CAST_I
-  if (stats || (given && am))
+  if ((stats && !small_counts) || (given && am))
     hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinThreads), 0, st, ws->pass2, grid,
                        given ? a.amax_out : nullptr, a.counts);
   return hipGetLastError();
@@ -1065,7 +1099,7 @@ hipError_t quant_image_rows(const QuantArgs& a, hipStream_t st) {
     const int64_t spr = ceil_div(opr, static_cast<int64_t>(kBlock) * oct_unroll<T>());
     nparts = static_cast<int>(std::min<int64_t>({rows * spr, int64_t(4) * device_cus(), int64_t(kMaxBlocks)}));
     hipLaunchKernelGGL(k_tensor_amax<T>, dim3(nparts), dim3(kBlock), 0, st, static_cast<const T*>(a.x), rows, opr,
-                       a.ldx, spr, ws->pass1);
+                       a.ldx, spr, ws->pass1, nullptr);
   }
   bool ok = false;
   switch (ceil_div(a.img, int64_t(kImgWaves))) {
