@@ -35,20 +35,34 @@ def rt():
     return rt
 
 
-def make_input(seed, rows, cols, dtype):
+def make_input(seed, rows, cols, dtype, special=False):
     """Normal values with a per-row magnitude spread, an all-zero row, a few
-    outliers and values that underflow."""
+    outliers and values that underflow; with `special`, a NaN in one row and
+    an Inf in another (codes bit for bit; NaN scales and amax by position)."""
     g = np.random.default_rng(seed)
     x = g.standard_normal((rows, cols)).astype(np.float32)
     x *= np.exp(g.uniform(-4, 4, (rows, 1))).astype(np.float32)
     x[g.integers(0, rows), :] = 0.0
     x.reshape(-1)[g.integers(0, rows * cols, 5)] *= 300.0
     x.reshape(-1)[g.integers(0, rows * cols, 7)] = 1e-30
+    if special:
+        x[1, g.integers(0, cols)] = np.nan
+        x[rows - 2, g.integers(0, cols)] = -np.inf
     return to_bf16_bits(x) if dtype == "bf16" else x
 
 
 def same_f32(a, b):
     return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+def same_nan(a, b):
+    """Bit for bit except NaN payloads: the oracle writes the canonical quiet
+    NaN, the kernels carry the input's payload through the integer max of
+    |x| (a bf16 0xFFFF gives amax bits 0x7FFF0000); NaN in the same places."""
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    na, nb = np.isnan(a), np.isnan(b)
+    return np.array_equal(na, nb) and same_f32(a[~na], b[~nb])
+
 
 
 CASES = [  # (N, K, gran, dtype, fmt, mode, counters)
@@ -66,21 +80,26 @@ CASES = [  # (N, K, gran, dtype, fmt, mode, counters)
     (33, 8192, (0, 0), "bf16", 1, DYN, False),     # per tensor: amax pass, then the image kernel
     (48, 4096, (1, 0), "f32", 0, GIVEN, False),
     (48, 8192, (1, 0), "f32", 0, DYN, False),      # fp32 past the register budget
+    (40, 8192, (1, 0), "bf16", 0, DYN, False, True),   # NaN and Inf rows, the image kernel
+    (40, 8192, (1, 0), "bf16", 1, DYN, True, True),    # the same, the general kernel
+    (64, 2048, (0, 0), "bf16", 0, GIVEN, True, True),  # per tensor, given scale
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
 def test_quantize_into_image_matches_oracle(rt, orc, case):
-    N, K, gran, dtype, fmt, mode, counters = case
-    x = make_input(case_seed("image", case), N, K, dtype)
+    N, K, gran, dtype, fmt, mode, counters = case[:7]
+    special = len(case) > 7 and case[7]
+    x = make_input(case_seed("image", case), N, K, dtype, special)
     G = rt.scale_shape((N, K), gran)
     if mode == DYN:
         oq, os_, or_, oam, ocnt = orc.quantize(x, fmt, gran)
         S = torch.full(G, -1.0, device="cuda")
         R = torch.full(G, -1.0, device="cuda")
     else:
-        _, s0, _, _, _ = orc.quantize(x, fmt, gran)
-        s_given = (s0 * 0.5).astype(np.float32)          # half the dynamic scale: some codes saturate
+        # half the dynamic scale of the finite values: some codes saturate
+        _, s0, _, _, _ = orc.quantize(make_input(case_seed("image", case), N, K, dtype), fmt, gran)
+        s_given = (s0 * 0.5).astype(np.float32)
         oq, os_, or_, oam, ocnt = orc.quantize(x, fmt, gran, mode=GIVEN, scale=s_given)
         S = dev(s_given)
         R = None
@@ -95,9 +114,10 @@ def test_quantize_into_image_matches_oracle(rt, orc, case):
     ref = orc.pack_weights16(oq)
     bad = np.flatnonzero(got != ref)
     assert bad.size == 0, "%d image bytes differ, first at %d" % (bad.size, bad[0])
-    assert same_f32(host(am), oam)
+    same = same_nan if special else same_f32
+    assert same(host(am), oam)
     if mode == DYN:
-        assert same_f32(host(S), os_) and same_f32(host(R), or_)
+        assert same(host(S), os_) and same(host(R), or_)
     if counters:
         assert host(cnt).view(np.uint64).tolist() == ocnt.tolist()
     if mode == GIVEN:
