@@ -36,6 +36,12 @@
 //    per element; the step's scales are cached loads), so the epilogue only
 //    adds the bias.  The stream of B is the same, so such decode GEMMs cost
 //    what per-channel ones do.
+//  - 1 x 32 power-of-two scales ("Per-channel and block scaling", with
+//    the scales' exponents as E8M0): v_mfma_scale_f32_16x16x128_f8f6f4 takes
+//    one exponent per lane and operand, its row's scale for the 32-deep K
+//    block of its lane quarter; the lanes then load bytes [16 g, +16) and
+//    [64 + 16 g, +16) of each step, the matrix core's own K order, so those
+//    blocks are the memory's.  Row-major B only.
 //  - Exact products (a template flag): each 128-deep step becomes four
 //    v_mfma_f32_16x16x32_bf16, instruction j taking bytes [8 j, 8 j + 8) of
 //    every lane's 32 on both operands, widened exactly to bf16 in registers
