@@ -613,6 +613,11 @@ __global__ __launch_bounds__(kImgWaves * 64) void k_image_rows(
       for (int u = 0; u < 4; ++u) {
         const bool nan_path = !(fabsf(r[u]) <= FLT_MAX) || v[j][u].absmax_bits() > kInfBits;
         const u32x2 c = cast_octet<T, F, STATS>(v[j][u], r[u], nan_path, sat_l, under_l);
+        // the counters pass through an opaque copy per octet: otherwise the
+        // increments of the unrolled octets are reassociated into one tree
+        // that keeps every product live (126 instead of 104 VGPRs at three
+        // steps per wave; spills at four)
+        if constexpr (STATS) asm volatile("" : "+v"(sat_l), "+v"(under_l));
         *reinterpret_cast<u32x2*>(wt + (4 * u + rq) * kImgPitch + 8 * seg) = c;
       }
       // the wave's own tile: its LDS operations complete in order
@@ -1029,9 +1034,9 @@ hipError_t quant_blocktile(const QuantArgs& a, hipStream_t st) {
 // Into the weight image with per-row or per-tensor scales: k_image_rows,
 // when a row's steps fit its registers (NS per wave) and the 16-row groups
 // one grid of partials.
-// (With counters one step less: the per-element counting would spill.)
+// (fp32 with counters one step less: the per-element counting would spill.)
 template <typename T> constexpr int img_max_ns(bool stats) {
-  return sizeof(T) == 2 ? (stats ? 3 : 4) : (stats ? 1 : 2);
+  return sizeof(T) == 2 ? 4 : (stats ? 1 : 2);
 }
 
 template <typename T>

@@ -8,9 +8,9 @@ the fragment-ordered weight image.
   GIVEN), per row, 1 x 32 and 1 x 128 groups, 128 x 128 blocks and a 16 x 48
   grid of groups, fp32 and bf16 inputs, E4M3 and E5M2.
 - Per-row and per-tensor scales take a kernel of their own when a row fits
-  its registers (up to 4 steps of 128 per wave for bf16, 2 for fp32, one
-  less with counters), the general kernels otherwise: cases on both sides
-  of each limit.
+  its registers (up to 4 steps of 128 per wave for bf16; 2 for fp32, 1
+  with counters), the row-wise kernels otherwise: cases on both sides of
+  each limit.
 - At the weights' own sizes (8192 x 8192 per channel, 18432 x 7168 in
   128 x 128 blocks, 29568 x 8192 per tensor GIVEN, 4096 x 8192 per tensor
   DYNAMIC): the image equals the library's row-major quantize followed by
@@ -76,7 +76,9 @@ CASES = [  # (N, K, gran, dtype, fmt, mode, counters)
     (64, 4096, (1, 0), "bf16", 1, GIVEN, True),
     (40, 6144, (1, 0), "bf16", 0, DYN, True),      # three steps per wave
     (40, 8192, (1, 0), "bf16", 0, DYN, False),     # four steps per wave (no counters)
-    (40, 8192, (1, 0), "bf16", 0, DYN, True),      # with counters: the general kernel
+    (40, 8192, (1, 0), "bf16", 0, DYN, True),      # four steps per wave, with counters
+    (24, 8320, (1, 0), "bf16", 0, DYN, True),      # 65 steps: past the image kernel, the row kernel
+    (33, 4096, (0, 0), "f32", 0, DYN, True),       # fp32 with counters past one step: the tensor kernel
     (33, 8192, (0, 0), "bf16", 1, DYN, False),     # per tensor: amax pass, then the image kernel
     (48, 4096, (1, 0), "f32", 0, GIVEN, False),
     (48, 8192, (1, 0), "f32", 0, DYN, False),      # fp32 past the register budget
