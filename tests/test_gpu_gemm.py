@@ -250,3 +250,40 @@ def test_gemm_special_codes_other_kernels(rt, orc, route):
     t_hw = orc.dot_truncation_bound_full(a, 1, sa, ga, b, 0, sb, gb)
     ok, st = check_gemm(y[rows], yref[rows], S[rows], False, orc, t_hw=t_hw[rows])
     assert ok, st
+
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_decode_mx32_full_size(rt, orc, M):
+    """The decode kernel with 1x32 power-of-two scales at the decode layer's
+    size (M x 8192 x 8192, bf16 out, bias): A and W quantized on the device
+    (1x32 groups, power-of-two round-up), then every row on a column sample
+    (the first and last 256 columns and 512 random ones) against the oracle
+    under the one acceptance rule."""
+    N = K = 8192
+    print("decode mx32 full size, M =", M, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(case_seed("decode-mx32-full", M))
+    x = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    bias = (torch.randn(N, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+    A = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    B = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 32), device="cuda")
+    sb = torch.empty((N, K // 32), device="cuda")
+    rt.fp8_quantize(x, (1, 32), 0, rt.DYNAMIC, 1e-12, True, sa, None, A)
+    rt.fp8_quantize(w, (1, 32), 0, rt.DYNAMIC, 1e-12, True, sb, None, B)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    rt.fp8_scaled_gemm(A, 0, (1, 32), sa, B, 0, (1, 32), sb, y, bias=bias, flags=rt.POW2_SCALES)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    cols = np.unique(np.concatenate([np.arange(256), np.arange(N - 256, N), rng.integers(256, N - 256, 512)]))
+    m = np.repeat(np.arange(M), len(cols))
+    n = np.tile(cols, M)
+    a, b, ha, hb = host(A), host(B), host(sa), host(sb)
+    bias_bits = host(bias)
+    yref, S = orc.gemm_points(a, 0, ha, (1, 32), b, 0, hb, (1, 32), m, n, bias=bias_bits)
+    thw = orc.dot_truncation_bound(a, 0, ha, (1, 32), b, 0, hb, (1, 32), m, n)
+    bias_f = orc.bf16_bits_to_f32(bias_bits).astype(np.float64)[n]
+    ok, st = check_gemm(host(y)[m, n], yref, S, True, orc, t_hw=thw, bias=bias_f)
+    print("decode mx32", M, st)
+    assert ok, st
