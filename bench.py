@@ -44,6 +44,12 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                         "times: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    p.add_argument("--calibrate-mfma", action="store_true",
+                   help="run only the register-only FP8 MFMA rate (32x32x64 and 16x16x128, zero and random "
+                        "operands): the matrix cores' ceiling at the clock the chip holds for them")
+    p.add_argument("--library-comparison", action="store_true",
+                   help="run only a comparison of fp8_scaled_gemm with hipBLASLt (torch._scaled_mm) on "
+                        "identical E4M3 codes and per-tensor scales at the large shapes, bf16 out")
     return p.parse_args()
 
 
@@ -906,6 +912,109 @@ def extra_components(torch, rt, wl, keep):
     return comp
 
 
+def calibrate_mfma(torch):
+    """FP8 MFMA rate with operands in registers (libfp8rt_calib.so): 16 MFMAs
+    per wave and iteration, 4 waves per workgroup, 2048 workgroups, median of
+    5 event-timed launches after 2 untimed ones, for each instruction shape on
+    zero operands and on random bytes (finite E4M3 codes)."""
+    import ctypes as C
+
+    path = os.path.join(ROOT, "dynamic_scaling_scaled_amd", "libfp8rt_calib.so")
+    if not os.path.exists(path):
+        raise ImportError("libfp8rt_calib.so is not built: run __graft_entry__.build()")
+    L = C.CDLL(path)
+    L.fp8rt_calib_mfma_rate.restype = C.c_int
+    L.fp8rt_calib_mfma_rate.argtypes = [C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    nops = L.fp8rt_calib_mfma_operand_ints()
+    blocks, iters = 2048, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    g = np.random.default_rng(7)
+    codes = g.integers(0, 256, nops * 4, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E          # no NaN codes
+    operands = {"zero": torch.zeros(nops, dtype=torch.int32, device="cuda"),
+                "random_e4m3": torch.from_numpy(codes.view(np.int32).copy()).cuda()}
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows = []
+    for shape, flop in ((32, 2 * 32 * 32 * 64), (16, 2 * 16 * 16 * 128)):
+        for name, ops in operands.items():
+            run = lambda: L.fp8rt_calib_mfma_rate(shape, C.c_void_p(ops.data_ptr()), blocks, iters,
+                                                  C.c_void_p(out.data_ptr()), st)
+            ts = []
+            for rep in range(7):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                rc = run()
+                e1.record()
+                e1.synchronize()
+                if rc != 0:
+                    raise RuntimeError("fp8rt_calib_mfma_rate returned %d" % rc)
+                if rep >= 2:
+                    ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = float(np.median(ts))
+            pf = blocks * 4 * iters * 16 * flop / t / 1e15
+            rows.append({"instruction": "v_mfma_f32_%s_f8f6f4" % ("32x32x64" if shape == 32 else "16x16x128"),
+                         "operands": name, "ms": t * 1e3, "PFLOP_s": pf, "frac_fp8_peak": pf * 1e3 / FP8_PEAK_TFLOPS})
+    return {"mfma_rate_registers_only": rows}
+
+
+LIBRARY_SHAPES = [(4096, 29568, 8192), (4096, 28672, 8192), (8192, 8192, 8192), (8192, 18432, 7168)]
+
+
+def library_comparison(torch, rt):
+    """fp8_scaled_gemm against hipBLASLt (reached through torch._scaled_mm) on
+    the same E4M3 codes (N(0,1)-shaped values cast by torch), per-tensor scales,
+    bf16 out: median of 20 event-timed calls, caches scrubbed, interleaved so
+    that both see the same clock; the largest |difference| relative to the
+    output's scale.  Context for the kernels' rates, not part of the step."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261204)
+    junk = torch.empty(2**28, dtype=torch.float32, device="cuda")
+    rows = []
+    for M, N, K in LIBRARY_SHAPES:
+        a8 = torch.randn((M, K), device="cuda", generator=g).to(torch.float8_e4m3fn)
+        b8 = (torch.randn((N, K), device="cuda", generator=g) * 4).to(torch.float8_e4m3fn)
+        sa = torch.tensor([[0.01]], device="cuda")
+        sb = torch.tensor([[0.005]], device="cuda")
+        y_rt = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        held = [None]
+
+        def lib():
+            held[0] = torch._scaled_mm(a8, b8.t(), scale_a=sa.view(()), scale_b=sb.view(()),
+                                       out_dtype=torch.bfloat16)
+
+        ours = lambda: rt.fp8_scaled_gemm(a8.view(torch.uint8), rt.E4M3, (0, 0), sa, b8.view(torch.uint8),
+                                          rt.E4M3, (0, 0), sb, y_rt)
+        t_lib, t_rt = [], []
+        for _ in range(3):
+            lib()
+            ours()
+        for _ in range(20):
+            for fn, acc in ((lib, t_lib), (ours, t_rt)):
+                junk.fill_(1.0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                acc.append(e0.elapsed_time(e1) * 1e3)
+        y_lib = held[0]
+        d = (y_lib.float() - y_rt.float()).abs().max().item() / max(y_lib.float().abs().max().item(), 1e-30)
+        flops = 2.0 * M * N * K
+        rows.append({"shape_MxNxK": [M, N, K], "hipblaslt_us": float(np.median(t_lib)),
+                     "fp8_scaled_gemm_us": float(np.median(t_rt)),
+                     "hipblaslt_frac_fp8_peak": flops / (np.median(t_lib) * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+                     "fp8_scaled_gemm_frac_fp8_peak": flops / (np.median(t_rt) * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+                     "max_abs_diff_over_max_abs_y": d})
+        print("library comparison %dx%dx%d done" % (M, N, K), file=sys.stderr, flush=True)
+        held[0] = None
+        del a8, b8, y_lib, y_rt
+        torch.cuda.empty_cache()
+    return {"library_comparison": rows, "note": "hipBLASLt through torch._scaled_mm; same codes and scales; "
+                                                "median of 20 scrubbed calls each, interleaved"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -929,6 +1038,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "repeats": 3}), flush=True)
+        return
+    if args.calibrate_mfma:
+        print(json.dumps(calibrate_mfma(torch)), flush=True)
+        return
+    if args.library_comparison:
+        print(json.dumps(library_comparison(torch, rt)), flush=True)
         return
     keep = {}
     out = bench_prefill(args, torch, rt, wl, keep)

@@ -11,6 +11,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8rt.so")
+# measurement aids beside the library (csrc/calib): the matrix cores' rate with
+# register-held operands, used by bench.py --calibrate-mfma; never linked into
+# libfp8rt.so
+CALIB_LIB = os.path.join(PKG, "libfp8rt_calib.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -62,7 +66,22 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_calib(verbose)
     return LIB
+
+
+def build_calib(verbose: bool = False) -> str:
+    srcs = sorted(os.path.join(CSRC, "calib", f) for f in os.listdir(os.path.join(CSRC, "calib"))
+                  if f.endswith(".hip"))
+    tmp = CALIB_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, *srcs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the calibration library:\n%s\n%s" % (r.stdout, r.stderr))
+    os.replace(tmp, CALIB_LIB)
+    if verbose:
+        print("built", CALIB_LIB)
+    return CALIB_LIB
 
 
 # Host-side AddressSanitizer + UndefinedBehaviorSanitizer build for CPU checks
