@@ -455,7 +455,7 @@ def bench_prefill(args, torch, rt, wl, keep):
         "roofline": {"bound": "mfma", "achieved": g_tflops, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": g_tflops / FP8_PEAK_TFLOPS,
                      "traffic": traffic_from_profile("gemm_prefill_traffic.json"),
-                     "kernel": "k_gemm_big + k_split_reduce (one GEMM call: fp8 E4M3xE4M3, per-tensor scales, bf16 out)",
+                     "kernel": "k_gemm_big16 + k_split_reduce (one GEMM call: fp8 E4M3xE4M3, per-tensor scales, bf16 out)",
                      "avg_launch_us": g_ms * 1e3},
         "components": {
             "quantize_x_dynamic_per_tensor": {

@@ -32,6 +32,9 @@
 //  - Tile order: blocks are dealt round-robin to the 8 XCDs; each XCD gets a
 //    contiguous range of a grouped (GROUP_M M-tiles x all N-tiles) order, so
 //    the 32 CUs of an XCD share A and B slices in their own L2.
+//  - Per-tensor / per-row scales with BF16 or FP32 output run k_gemm_big16,
+//    the same tiling on v_mfma_f32_16x16x128_f8f6f4 (described with it);
+//    1x32 scales and FP8 output run k_gemm_big below.
 //  - The MFMA computes the transposed tile (B as the first operand), so a
 //    lane ends with 4 consecutive output columns of one row: the epilogue
 //    applies the scales and bias with 4-wide LDS reads of the block's column
@@ -511,6 +514,306 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     if (!unit) block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
 }
 
+// ---- 16x16x128 kernel (per-tensor / per-row scales, BF16 or FP32 output).
+// The same 256 x 256 tile, 4 waves of 128 x 128, LDS stages, DMA and tile
+// order as k_gemm_big; each wave issues 8 x 8 v_mfma_f32_16x16x128_f8f6f4
+// per 128-deep stage (one instruction consumes the whole stage).  On random
+// operands this instruction sustains a higher rate than 32x32x64 (the chip
+// holds a higher clock for it).  Registers: 64 four-wide accumulators (256
+// AGPRs, updated in place by inline MFMAs), B's 8 fragments of the current
+// and of the next stage (2 x 64 VGPRs) and A's 8 fragments (64 VGPRs).  Two
+// barriers per stage: one after the stage's last LDS read (row tile 1), after
+// which the stage after next is loaded into its arrays, and one at row tile 5
+// for the next stage's loads, so each stage's loads fly for 1.4 stages (with
+// a single barrier per stage, 1 stage, the kernel ran 5-10% slower).
+constexpr int MI16 = WTM / 16, NJ16 = WTN / 16;  // 8 x 8 tiles of 16 x 16
+
+// 16x16x128 operand: lane l holds row l % 16; the matrix core reads its first
+// 16 bytes as K [16 g, +16) and its last 16 as K [64 + 16 g, +16) of the
+// stage, g = l / 16 (A and B use the same map, so each product pairs equal K).
+__device__ __forceinline__ i32x8 frag16(const uint8_t* lds, int row, int g) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz(row, g));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, g + 4));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Epilogue of one wave: lane l holds output row 16 i + (l % 16) and columns
+// 16 j + 4 (l / 16) + (0..3) of its 128 x 128 tile (the MFMA computed the
+// transposed tile).  Scaled, converted, staged in the wave's 32 KB of LDS
+// (16-byte chunks XOR-swizzled by row) and stored as 16-byte row chunks;
+// rows and columns at or past (M, N) are skipped.
+template <int OUT>
+__device__ __forceinline__ void store16(const f32x4 (&acc)[MI16][NJ16], uint8_t* stage, const float* scol,
+                                      const float* sbias, const float (&sav)[MI16], int64_t wrow0, int64_t wcol0,
+                                      int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store, int wn,
+                                      int fr, int fg, int lane) {
+  constexpr int ESZ = OUT == kOutF32 ? 4 : 2;
+  constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
+  constexpr int SWM = 15;                       // chunk swizzle mask
+  constexpr int ROWS = kStageA / RB;            // rows per pass: 128 or 64
+  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass: 8 or 4
+  constexpr int EPC = 16 / ESZ;
+#pragma unroll
+  for (int pass = 0; pass < MI16 / IPP; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < IPP; ++ii) {
+      const int i = pass * IPP + ii;
+      const int lrow = ii * 16 + fr;
+#pragma unroll
+      for (int j = 0; j < NJ16; ++j) {
+        const int c = j * 16 + 4 * fg;
+        const f32x4 scv = *reinterpret_cast<const f32x4*>(&scol[wn * WTN + c]);
+        const f32x4 biv = *reinterpret_cast<const f32x4*>(&sbias[wn * WTN + c]);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sav[i] * scv[r]) + biv[r];
+        const int byte = c * ESZ;
+        const int chunk = (byte >> 4) ^ (lrow & SWM);
+        uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
+        if constexpr (OUT == kOutBF16)
+          *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+        else
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+      }
+    }
+    __syncthreads();
+    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
+      const int lrow = ch / CPR, cc = ch % CPR;
+      const int64_t row = wrow0 + pass * ROWS + lrow;
+      const int64_t col = wcol0 + cc * EPC;
+      if (row >= M || col >= N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & SWM)) << 4));
+      char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
+      if (vec_store && col + EPC <= N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const char* src = reinterpret_cast<const char*>(&v);
+        for (int e = 0; e < EPC && col + e < N; ++e)
+          for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+
+// One 16x16x128 MFMA, acc += B-fragment x A-fragment (the transposed tile),
+// written inline with the accumulator as one tied operand, so it stays in
+// the same AGPRs from stage to stage (the builtin's untied form made the
+// register allocator rotate the 64 accumulators between the two unrolled
+// stages and copy them back, about 100 moves per stage).  A E5M2 (FA = 1) is
+// the instruction's second source: blgp:1.
+template <int FA>
+__device__ __forceinline__ void mfma16(f32x4& acc, const i32x8& b, const i32x8& a) {
+  if constexpr (FA == 0)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 blgp:1" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// Wait states between VALU accesses of the accumulators and the inline MFMAs
+// (which the compiler's hazard recognizer does not see): 24, more than the
+// 8-pass MFMA's write-to-VALU-read distance and the VALU-write-to-MFMA one.
+__device__ __forceinline__ void acc_fence(f32x4 (&acc)[MI16][NJ16]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[0][4]),
+                 "+a"(acc[0][5]), "+a"(acc[0][6]), "+a"(acc[0][7]), "+a"(acc[1][0]), "+a"(acc[1][1]),
+                 "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[1][4]), "+a"(acc[1][5]), "+a"(acc[1][6]),
+                 "+a"(acc[1][7]), "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                 "+a"(acc[2][4]), "+a"(acc[2][5]), "+a"(acc[2][6]), "+a"(acc[2][7]), "+a"(acc[3][0]),
+                 "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]), "+a"(acc[3][4]), "+a"(acc[3][5]),
+                 "+a"(acc[3][6]), "+a"(acc[3][7]), "+a"(acc[4][0]), "+a"(acc[4][1]), "+a"(acc[4][2]),
+                 "+a"(acc[4][3]), "+a"(acc[4][4]), "+a"(acc[4][5]), "+a"(acc[4][6]), "+a"(acc[4][7]),
+                 "+a"(acc[5][0]), "+a"(acc[5][1]), "+a"(acc[5][2]), "+a"(acc[5][3]), "+a"(acc[5][4]),
+                 "+a"(acc[5][5]), "+a"(acc[5][6]), "+a"(acc[5][7]), "+a"(acc[6][0]), "+a"(acc[6][1]),
+                 "+a"(acc[6][2]), "+a"(acc[6][3]), "+a"(acc[6][4]), "+a"(acc[6][5]), "+a"(acc[6][6]),
+                 "+a"(acc[6][7]), "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                 "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7]));
+}
+
+// Wait for this wave's LDS reads (its vector-memory loads keep flying) and
+// join the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt at their maximum
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One DMA instruction of a stage: 1 KB (8 rows of 128 bytes) into slot k.
+__device__ __forceinline__ void dma1(__amdgpu_buffer_rsrc_t rs, int soff, uint32_t voff, uint8_t* lds, int k) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + k * 1024), 16, static_cast<int>(voff), soff, 0, 0);
+}
+
+// Row tile at which the 16x16x128 kernel's second barrier sits (the next
+// stage's fragments are read from there to row 7): rows 4, 5 and 6 measured
+// within 1-3% of each other at the large shapes, 5 the best or equal.
+constexpr int kRowB16 = 5;
+
+template <int FA, int FB, int OUT, int RB>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
+    const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
+    void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store, int t_main, int split,
+    int ns_part, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
+  __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
+  __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
+
+  // Whole tiles below t_main, split-K units above it (as in k_gemm_big).
+  const int bid = blockIdx.x;
+  const bool unit = bid >= t_main;
+  int logical, s0 = 0;
+  if (!unit) {
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int q = t_main >> 3, rem = t_main & 7;
+    logical = xcd * q + min(xcd, rem) + loc;
+  } else {
+    const int u = bid - t_main;
+    logical = t_main + u / split;
+    s0 = (u % split) * ns_part;
+  }
+  int tile_m, tile_n;
+  tile_of(logical, tiles_m, tiles_n, tile_m, tile_n);
+  const int64_t m0 = static_cast<int64_t>(tile_m) * TM, n0 = static_cast<int64_t>(tile_n) * TN;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int fr = lane & 15, fg = lane >> 4;
+
+  uint32_t voa[kDmaA], vob[kDmaB];
+#pragma unroll
+  for (int j = 0; j < kDmaA; ++j) {
+    const int r = (wave * kDmaA + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    voa[j] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * lda + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < kDmaB; ++j) {
+    const int r = (wave * kDmaB + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(A + m0 * lda + static_cast<int64_t>(s0) * TKS), 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(B + n0 * ldb + static_cast<int64_t>(s0) * TKS), 0, -1, 0x00020000);
+
+  f32x4 acc[MI16][NJ16];
+#pragma unroll
+  for (int i = 0; i < MI16; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ16; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // the zeros are written to the accumulators by VALU moves, which the first
+  // (inline) MFMAs read: wait states between them
+  acc_fence(acc);
+
+  constexpr int kDmaStage = kDmaA + kDmaB;
+  const int ns = unit ? ns_part : static_cast<int>(K / TKS);  // even
+  const int ra0 = wm * WTM + fr, rb0 = wn * WTN + fr;         // the lane's first A / B fragment row
+
+  dma_buf<kDmaA>(ra, 0, voa, sA0, wave);
+  dma_buf<kDmaB>(rb, 0, vob, sB0, wave);
+  dma_buf<kDmaA>(ra, TKS, voa, sA1, wave);
+  dma_buf<kDmaB>(rb, TKS, vob, sB1, wave);
+  step_barrier<kDmaStage>();  // stage 0 landed
+  i32x8 bx[NJ16], by[NJ16], af[MI16];
+#pragma unroll
+  for (int j = 0; j < NJ16; ++j) bx[j] = frag16(sB0, rb0 + j * 16, fg);
+  af[0] = frag16(sA0, ra0, fg);
+
+  // One stage s (arrays LA / LB), row tiles 0-7 with A fragment i in af[i]:
+  //  - rows 0-1 read A row tiles 1-7 of stage s, the last reads of this
+  //    stage's arrays;
+  //  - a barrier (every wave has read stage s), then rows 2-3 issue the DMA
+  //    of stage s + 2 into stage s's arrays (one load after each MFMA; two
+  //    after each MFMA of row 2 alone ran 10% slower);
+  //  - a second barrier at row RB (every wave's loads of stage s + 1 have
+  //    landed; stage s + 2's stay in flight), then rows RB-7 read stage
+  //    s + 1's B fragments 0-7 and A row tile 0 (9 fragments, evenly).
+  // A stage's loads are in flight from row 2 of one stage to row RB of the
+  // next.  The MFMAs are inline and volatile, so every memory operation
+  // keeps its place between them as written here.
+  constexpr int kNR = MI16 - RB;                     // rows that read the next stage
+  constexpr int kPer = (NJ16 + 1 + kNR - 1) / kNR;   // fragments per such row
+#define FP8RT_STAGE16(LA, LB, NA, NB, BC, BN, KS)                                                              \
+  {                                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                                             \
+      _Pragma("unroll") for (int j = 0; j < NJ16; ++j) {                                                        \
+        mfma16<FA>(acc[i][j], BC[j], af[i]);                                                                   \
+        const int t2 = 4 * i + j + 1;  /* A row tile read after this MFMA */                                   \
+        if (j < 4 && t2 < MI16) af[t2] = frag16(LA, ra0 + t2 * 16, fg);                                        \
+      }                                                                                                        \
+    }                                                                                                          \
+    lds_barrier();                                                                                             \
+    const int kn = min(KS, ns - 1);                                                                            \
+    _Pragma("unroll") for (int i = 2; i < RB; ++i) {                                                            \
+      _Pragma("unroll") for (int j = 0; j < NJ16; ++j) {                                                        \
+        mfma16<FA>(acc[i][j], BC[j], af[i]);                                                                   \
+        if (i < 4) {   /* 16 DMA instructions, one after each MFMA of rows 2-3: A's 8, then B's 8 */        \
+          const int d = (i - 2) * NJ16 + j;                                                                    \
+          if (d < kDmaA) dma1(ra, kn * TKS, voa[d], LA, wave * kDmaA + d);                                      \
+          else dma1(rb, kn * TKS, vob[d - kDmaA], LB, wave * kDmaB + d - kDmaA);                                \
+        }                                                                                                      \
+      }                                                                                                        \
+    }                                                                                                          \
+    step_barrier<kDmaStage>();                                                                                 \
+    _Pragma("unroll") for (int i = RB; i < MI16; ++i) {                                                         \
+      _Pragma("unroll") for (int j = 0; j < NJ16; ++j) {                                                        \
+        mfma16<FA>(acc[i][j], BC[j], af[i]);                                                                   \
+        const int k = (i - RB) * kPer + j;  /* item k: B 0, A 0, B 1 .. B 7 */                                 \
+        if (j < kPer && k <= NJ16) {                                                                           \
+          if (k == 1) af[0] = frag16(NA, ra0, fg);                                                             \
+          else { const int jb = k == 0 ? 0 : k - 1; BN[jb] = frag16(NB, rb0 + jb * 16, fg); }                  \
+        }                                                                                                      \
+      }                                                                                                        \
+    }                                                                                                          \
+  }
+  for (int s = 0; s < ns; s += 2) {
+    FP8RT_STAGE16(sA0, sB0, sA1, sB1, bx, by, s + 2)
+    FP8RT_STAGE16(sA1, sB1, sA0, sB0, by, bx, s + 3)
+  }
+#undef FP8RT_STAGE16
+  // the last MFMAs' results are read by VALU instructions below: wait states
+  acc_fence(acc);
+  step_barrier<0>();  // the clamped extra loads finish before the arrays are reused
+
+  __shared__ __attribute__((aligned(16))) float sCol[2][TN];
+  if (unit) {
+    sCol[0][t] = 1.0f;
+    sCol[1][t] = 0.0f;
+  } else {
+    const int64_t col = min(n0 + t, N - 1);
+    sCol[0][t] = sb[erb == 1 ? col : 0];
+    float bvv = 0.0f;
+    if (bias)
+      bvv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
+                      : static_cast<const float*>(bias)[col];
+    sCol[1][t] = bvv;
+  }
+  __syncthreads();
+  uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  float sav[MI16];
+  if (unit) {
+#pragma unroll
+    for (int i = 0; i < MI16; ++i) sav[i] = 1.0f;
+    float* dst = part + static_cast<int64_t>(bid - t_main) * (TM * TN);
+    store16<kOutF32>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1, wn, fr, fg,
+                   lane);
+  } else {
+    const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
+#pragma unroll
+    for (int i = 0; i < MI16; ++i) sav[i] = sa[era == 1 ? min(wrow0 + i * 16 + fr, M - 1) : 0];
+    store16<OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr, fg, lane);
+  }
+}
+
 // Finishes the split-K tiles: tile t_main + k sums its `split` FP32 partials
 // part[k split + p] in the order p = 0, 1, ..., applies s_a(row) s_b(col) and
 // the bias, rounds and stores.  A block covers kRedQ x 256 quads (4
@@ -707,7 +1010,20 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
     case kOutE5M2: FP8RT_BIG(FA, FB, kOutE5M2, MXV); break;         \
     default: FP8RT_BIG(FA, FB, kOutF32, MXV); break;                \
   }
-  if (g.fa == FP8RT_E4M3) {
+  // per-tensor / per-row scales with BF16 or FP32 output: the 16x16x128
+  // kernel; 1x32 scales and FP8 output: the 32x32x64 one
+  if (!g.pow2_mx && (okind == kOutBF16 || okind == kOutF32)) {
+#define FP8RT_BIG16(FA, FB, OUT)                                                                              \
+  hipLaunchKernelGGL((k_gemm_big16<FA, FB, OUT, kRowB16>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
+                     g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec,  \
+                     t_main, split, ns_part, part)
+    if (g.fa == FP8RT_E4M3) {
+      if (okind == kOutBF16) FP8RT_BIG16(0, 0, kOutBF16); else FP8RT_BIG16(0, 0, kOutF32);
+    } else {
+      if (okind == kOutBF16) FP8RT_BIG16(1, 0, kOutBF16); else FP8RT_BIG16(1, 0, kOutF32);
+    }
+#undef FP8RT_BIG16
+  } else if (g.fa == FP8RT_E4M3) {
     if (g.pow2_mx) { FP8RT_BIG_OUT(0, 0, true) } else { FP8RT_BIG_OUT(0, 0, false) }
   } else {
     if (g.pow2_mx) { FP8RT_BIG_OUT(1, 0, true) } else { FP8RT_BIG_OUT(1, 0, false) }
