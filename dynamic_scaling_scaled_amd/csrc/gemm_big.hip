@@ -32,9 +32,9 @@
 //  - Tile order: blocks are dealt round-robin to the 8 XCDs; each XCD gets a
 //    contiguous range of a grouped (GROUP_M M-tiles x all N-tiles) order, so
 //    the 32 CUs of an XCD share A and B slices in their own L2.
-//  - Per-tensor / per-row scales with BF16 or FP32 output run k_gemm_big16,
-//    the same tiling on v_mfma_f32_16x16x128_f8f6f4 (described with it);
-//    1x32 scales and FP8 output run k_gemm_big below.
+//  - Per-tensor / per-row scales run k_gemm_big16, the same tiling on
+//    v_mfma_f32_16x16x128_f8f6f4 (described with it); 1x32 scales run
+//    k_gemm_big below.
 //  - The MFMA computes the transposed tile (B as the first operand), so a
 //    lane ends with 4 consecutive output columns of one row: the epilogue
 //    applies the scales and bias with 4-wide LDS reads of the block's column
@@ -175,9 +175,11 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
   tile_n = within / gm;
 }
 
-// Epilogue of one block: lane l holds output row 32 i + (l % 32) and, per
-// group g = e / 4, the 4 consecutive columns 32 j + 8 g + 4 (l / 32) + (e % 4)
-// of its wave tile (the MFMA computed the transposed tile).  Values are
+// Epilogue of one block.  32x32 MFMA tiles (T = 32, f32x16 accumulators):
+// lane l holds output row 32 i + (l % 32) and, per group g = e / 4, the 4
+// consecutive columns 32 j + 8 g + 4 (l / 32) + (e % 4) of its wave tile;
+// 16x16 tiles (T = 16, f32x4): row 16 i + (l % 16), columns 16 j + 4 (l / 16)
+// + e (the MFMA computed the transposed tile).  Values are
 // scaled (row factor sav, column vectors scol / bias from LDS), converted,
 // staged in the wave's 32 KB of LDS (16-byte chunks XOR-swizzled by row) and
 // stored as 16-byte row chunks; rows / columns at or past (M, N) are skipped.
@@ -188,9 +190,9 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
 // thresholds, one unordered compare per pair) and the exact per-element work
 // runs only for a group that may need it.  EDGE: the wave tile may reach past
 // (M, N), so elements are tested before they count.
-template <int OUT, bool EDGE = true>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t* stage, const float* scol,
-                                           const float* sbias, const float (&sav)[MI], int64_t wrow0, int64_t wcol0,
+template <int OUT, bool EDGE = true, int T = 32, typename Acc = f32x16>
+__device__ __forceinline__ void store_tile(const Acc (&acc)[WTM / T][WTN / T], uint8_t* stage, const float* scol,
+                                           const float* sbias, const float (&sav)[WTM / T], int64_t wrow0, int64_t wcol0,
                                            int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
                                            int wn, int fr, int fg, int lane, float rq, uint32_t& mb, uint32_t& sat_l,
                                            uint32_t& under_l) {
@@ -214,19 +216,21 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], uint8_t*
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8, 16 or 32
   constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // chunk swizzle mask
   constexpr int ROWS = kStageA / RB < WTM ? kStageA / RB : WTM;  // rows per pass: 128 or 64
-  constexpr int IPP = ROWS / 32;                // MFMA row tiles per pass: 4 or 2
+  constexpr int IPP = ROWS / T;                 // MFMA row tiles per pass
+  constexpr int TMI = WTM / T, TNJ = WTN / T;   // MFMA tiles of the wave
+  constexpr int G = T == 32 ? 4 : 1;            // groups of 4 columns a lane holds per tile
   constexpr int EPC = 16 / ESZ;                 // elements per chunk
 #pragma unroll
-  for (int pass = 0; pass < MI / IPP; ++pass) {
+  for (int pass = 0; pass < TMI / IPP; ++pass) {
 #pragma unroll
     for (int ii = 0; ii < IPP; ++ii) {
       const int i = pass * IPP + ii;
-      const int lrow = ii * 32 + fr;            // row within the pass
+      const int lrow = ii * T + fr;             // row within the pass
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < TNJ; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = j * 32 + g * 8 + 4 * fg;  // first of 4 columns within the wave tile
+        for (int g = 0; g < G; ++g) {
+          const int c = j * T + g * 8 + 4 * fg;   // first of 4 columns within the wave tile
           const f32x4 scv = *reinterpret_cast<const f32x4*>(&scol[wn * WTN + c]);
           const f32x4 biv = *reinterpret_cast<const f32x4*>(&sbias[wn * WTN + c]);
           float v[4];
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
     if (!unit) block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
 }
 
-// ---- 16x16x128 kernel (per-tensor / per-row scales, BF16 or FP32 output).
+// ---- 16x16x128 kernel (per-tensor / per-row scales; BF16, FP32 or FP8 output).
 // The same 256 x 256 tile, 4 waves of 128 x 128, LDS stages, DMA and tile
 // order as k_gemm_big; each wave issues 8 x 8 v_mfma_f32_16x16x128_f8f6f4
 // per 128-deep stage (one instruction consumes the whole stage).  On random
@@ -536,67 +540,6 @@ __device__ __forceinline__ i32x8 frag16(const uint8_t* lds, int row, int g) {
   const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, g + 4));
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
-
-// Epilogue of one wave: lane l holds output row 16 i + (l % 16) and columns
-// 16 j + 4 (l / 16) + (0..3) of its 128 x 128 tile (the MFMA computed the
-// transposed tile).  Scaled, converted, staged in the wave's 32 KB of LDS
-// (16-byte chunks XOR-swizzled by row) and stored as 16-byte row chunks;
-// rows and columns at or past (M, N) are skipped.
-template <int OUT>
-__device__ __forceinline__ void store16(const f32x4 (&acc)[MI16][NJ16], uint8_t* stage, const float* scol,
-                                      const float* sbias, const float (&sav)[MI16], int64_t wrow0, int64_t wcol0,
-                                      int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store, int wn,
-                                      int fr, int fg, int lane) {
-  constexpr int ESZ = OUT == kOutF32 ? 4 : 2;
-  constexpr int RB = WTN * ESZ;                 // staged row bytes: 256 or 512
-  constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 16 or 32
-  constexpr int SWM = 15;                       // chunk swizzle mask
-  constexpr int ROWS = kStageA / RB;            // rows per pass: 128 or 64
-  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass: 8 or 4
-  constexpr int EPC = 16 / ESZ;
-#pragma unroll
-  for (int pass = 0; pass < MI16 / IPP; ++pass) {
-#pragma unroll
-    for (int ii = 0; ii < IPP; ++ii) {
-      const int i = pass * IPP + ii;
-      const int lrow = ii * 16 + fr;
-#pragma unroll
-      for (int j = 0; j < NJ16; ++j) {
-        const int c = j * 16 + 4 * fg;
-        const f32x4 scv = *reinterpret_cast<const f32x4*>(&scol[wn * WTN + c]);
-        const f32x4 biv = *reinterpret_cast<const f32x4*>(&sbias[wn * WTN + c]);
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sav[i] * scv[r]) + biv[r];
-        const int byte = c * ESZ;
-        const int chunk = (byte >> 4) ^ (lrow & SWM);
-        uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
-        if constexpr (OUT == kOutBF16)
-          *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
-        else
-          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-      }
-    }
-    __syncthreads();
-    for (int ch = lane; ch < ROWS * CPR; ch += 64) {
-      const int lrow = ch / CPR, cc = ch % CPR;
-      const int64_t row = wrow0 + pass * ROWS + lrow;
-      const int64_t col = wcol0 + cc * EPC;
-      if (row >= M || col >= N) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * RB + ((cc ^ (lrow & SWM)) << 4));
-      char* dst = static_cast<char*>(Y) + (row * ldy + col) * ESZ;
-      if (vec_store && col + EPC <= N) {
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
-        const char* src = reinterpret_cast<const char*>(&v);
-        for (int e = 0; e < EPC && col + e < N; ++e)
-          for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
-      }
-    }
-    __syncthreads();
-  }
-}
-
 
 // One 16x16x128 MFMA, acc += B-fragment x A-fragment (the transposed tile),
 // written inline with the accumulator as one tied operand, so it stays in
@@ -659,7 +602,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
     int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
     void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store, int t_main, int split,
-    int ns_part, float* __restrict__ part) {
+    int ns_part, float* __restrict__ part, const float* __restrict__ sy, const float* __restrict__ ry,
+    BlockPartial* __restrict__ ypart) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
@@ -800,18 +744,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
   __syncthreads();
   uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
   float sav[MI16];
+  uint32_t mb = 0, sat_l = 0, under_l = 0;
   if (unit) {
 #pragma unroll
     for (int i = 0; i < MI16; ++i) sav[i] = 1.0f;
     float* dst = part + static_cast<int64_t>(bid - t_main) * (TM * TN);
-    store16<kOutF32>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1, wn, fr, fg,
-                   lane);
+    store_tile<kOutF32, true, 16>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1,
+                                  wn, fr, fg, lane, 1.0f, mb, sat_l, under_l);
   } else {
     const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
 #pragma unroll
     for (int i = 0; i < MI16; ++i) sav[i] = sa[era == 1 ? min(wrow0 + i * 16 + fr, M - 1) : 0];
-    store16<OUT>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn, fr, fg, lane);
+    float rq = 1.0f;
+    if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
+    // the whole block tile inside (M, N): every wave takes the same branch
+    // (store_tile holds barriers)
+    if (OUT >= kOutE4M3 && m0 + TM <= M && n0 + TN <= N)
+      store_tile<OUT, false, 16>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store,
+                                 wn, fr, fg, lane, rq, mb, sat_l, under_l);
+    else
+      store_tile<OUT, true, 16>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store,
+                                wn, fr, fg, lane, rq, mb, sat_l, under_l);
   }
+  // FP8 output: a whole tile's max |y| and counters (split-K units hold raw
+  // partial sums; k_split_reduce takes the statistics of their tiles)
+  if constexpr (OUT >= kOutE4M3)
+    if (!unit) block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
 }
 
 // Finishes the split-K tiles: tile t_main + k sums its `split` FP32 partials
@@ -1010,23 +968,27 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
     case kOutE5M2: FP8RT_BIG(FA, FB, kOutE5M2, MXV); break;         \
     default: FP8RT_BIG(FA, FB, kOutF32, MXV); break;                \
   }
-  // per-tensor / per-row scales with BF16 or FP32 output: the 16x16x128
-  // kernel; 1x32 scales and FP8 output: the 32x32x64 one
-  if (!g.pow2_mx && (okind == kOutBF16 || okind == kOutF32)) {
+  // per-tensor / per-row scales: the 16x16x128 kernel; 1x32 scales: the
+  // 32x32x64 one (its scaled MFMA takes the E8M0 exponents)
+  if (!g.pow2_mx) {
 #define FP8RT_BIG16(FA, FB, OUT)                                                                              \
   hipLaunchKernelGGL((k_gemm_big16<FA, FB, OUT, kRowB16>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
                      g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec,  \
-                     t_main, split, ns_part, part)
-    if (g.fa == FP8RT_E4M3) {
-      if (okind == kOutBF16) FP8RT_BIG16(0, 0, kOutBF16); else FP8RT_BIG16(0, 0, kOutF32);
-    } else {
-      if (okind == kOutBF16) FP8RT_BIG16(1, 0, kOutBF16); else FP8RT_BIG16(1, 0, kOutF32);
-    }
+                     t_main, split, ns_part, part, g.sy, g.ry, g.part)
+#define FP8RT_BIG16_OUT(FA, FB)                                     \
+  switch (okind) {                                                  \
+    case kOutBF16: FP8RT_BIG16(FA, FB, kOutBF16); break;            \
+    case kOutE4M3: FP8RT_BIG16(FA, FB, kOutE4M3); break;            \
+    case kOutE5M2: FP8RT_BIG16(FA, FB, kOutE5M2); break;            \
+    default: FP8RT_BIG16(FA, FB, kOutF32); break;                   \
+  }
+    if (g.fa == FP8RT_E4M3) { FP8RT_BIG16_OUT(0, 0) } else { FP8RT_BIG16_OUT(1, 0) }
+#undef FP8RT_BIG16_OUT
 #undef FP8RT_BIG16
   } else if (g.fa == FP8RT_E4M3) {
-    if (g.pow2_mx) { FP8RT_BIG_OUT(0, 0, true) } else { FP8RT_BIG_OUT(0, 0, false) }
+    FP8RT_BIG_OUT(0, 0, true)
   } else {
-    if (g.pow2_mx) { FP8RT_BIG_OUT(1, 0, true) } else { FP8RT_BIG_OUT(1, 0, false) }
+    FP8RT_BIG_OUT(1, 0, true)
   }
 #undef FP8RT_BIG_OUT
 #undef FP8RT_BIG
