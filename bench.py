@@ -433,7 +433,7 @@ def bench_prefill(args, torch, rt, wl, keep):
     torch.cuda.synchronize()
     go_ms = float(np.mean(timer.ms("gemm_fp8out")))
     fp8out = mfma_entry(go_ms * 1e3, 2.0 * M * N * K, M * K + N * K + M * N + 8)
-    fp8out["kernels"] = "k_gemm_big (E4M3 out) + k_split_reduce (last wave) + k_finish"
+    fp8out["kernels"] = "k_gemm_big16 (E4M3 out) + k_split_reduce (last wave) + k_finish"
     q_ms = float(np.mean(timer.ms("quant_x")))
     g_ms = float(np.mean(timer.ms("gemm")))
     qw_ms = float(np.mean(timer.ms("quant_w")))

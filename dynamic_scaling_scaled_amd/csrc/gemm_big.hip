@@ -1,5 +1,6 @@
 // gemm_big.hip -- the large-shape scaled FP8 GEMM for gfx950 (per-tensor and
-// per-row / per-output-channel scales applied in the epilogue).
+// per-row / per-output-channel scales applied in the epilogue, 1x32
+// power-of-two scales inside the MFMA).
 //
 // Method: "FP8 formats and scaling for LLM inference", section "The full
 // precision contract of one FP8 GEMM": Y ~ s_x s_w (X8 W8) with FP32
@@ -8,8 +9,9 @@
 //
 // Design for MI355X:
 //  - 256 x 256 output tile per workgroup of 4 waves (one per SIMD); each wave
-//    owns a 128 x 128 sub-tile: 4 x 4 v_mfma_f32_32x32x64_f8f6f4 per 64-deep
-//    K sub-step, 256 FP32 accumulators per lane held in AGPRs.
+//    owns a 128 x 128 sub-tile: 8 x 8 v_mfma_f32_16x16x128_f8f6f4 per 128-deep
+//    K stage (one instruction consumes a whole stage), 64 four-wide FP32
+//    accumulators per lane held in AGPRs.
 //  - Two LDS stages of 128 K bytes (64 KB each).  A stage row is 128 bytes,
 //    a whole cache line, so every vector-memory request moves a full line
 //    (64-byte half rows doubled the L1->L2 request count and stalled the
@@ -20,26 +22,21 @@
 //    lane picks the global chunk that belongs at its LDS slot, an XOR swizzle
 //    of the 8 chunks of a row by (row / 2) that makes the ds_read_b128
 //    fragment reads conflict-free on the 64-bank LDS.
-//  - Software pipeline over sub-steps, with two fragment register sets P/Q:
-//    even sub-step 2j multiplies P (stage j, K bytes 0-63) while it reads
-//    stage j, K bytes 64-127 into Q, then joins a barrier (every wave has
-//    read stage j: its arrays are free); odd sub-step 2j+1 refills them with
-//    stage j+2 during its first 8 MFMAs on Q, waits for stage j+1 (issued
-//    one odd sub-step earlier, so 2.5 sub-steps in flight) and joins a
-//    second barrier, then reads stage j+1 into P during its last 8 MFMAs.
-//    Scheduling groups interleave the LDS reads and the loads between the
-//    MFMAs.
+//  - The schedule inside a stage and its two barriers are described with the
+//    kernel (k_gemm_big16).
+//  - 1x32 power-of-two scales: the scaled form of the same MFMA applies one
+//    E8M0 exponent per row and 32-element K block of each operand, repacked
+//    once per call (k_pack_e8m0_16).
 //  - Tile order: blocks are dealt round-robin to the 8 XCDs; each XCD gets a
 //    contiguous range of a grouped (GROUP_M M-tiles x all N-tiles) order, so
 //    the 32 CUs of an XCD share A and B slices in their own L2.
-//  - Per-tensor / per-row scales run k_gemm_big16, the same tiling on
-//    v_mfma_f32_16x16x128_f8f6f4 (described with it); 1x32 scales run
-//    k_gemm_big below.
 //  - The MFMA computes the transposed tile (B as the first operand), so a
 //    lane ends with 4 consecutive output columns of one row: the epilogue
 //    applies the scales and bias with 4-wide LDS reads of the block's column
 //    vectors, converts with the hardware bf16 conversion (round to nearest
-//    even), stages 8- or 16-byte pieces in LDS and stores 16-byte row chunks.
+//    even) or the FP8 cast, stages pieces in LDS and stores 16-byte row chunks.
+//  - A ragged last wave, or a grid of at most half the CUs, is split along K
+//    (k_split_reduce adds the parts).
 #include <float.h>
 
 #include <algorithm>
@@ -52,7 +49,6 @@ namespace fp8rt {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -60,12 +56,11 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 
 constexpr int TM = 256, TN = 256;
 constexpr int TKS = 128;                          // K bytes per LDS stage (full 128-byte rows)
-constexpr int TK = 64;                            // K per MFMA sub-step
 constexpr int kWaves = 4, WAVES_N = 2;            // 2 x 2 waves
 constexpr int kThreads = kWaves * 64;
 constexpr int WTM = TM / (kWaves / WAVES_N);      // 128 rows per wave
 constexpr int WTN = TN / WAVES_N;                 // 128 columns per wave
-constexpr int MI = WTM / 32, NJ = WTN / 32;       // 4 x 4 MFMA tiles of 32 x 32
+constexpr int MI16 = WTM / 16, NJ16 = WTN / 16;   // 8 x 8 MFMA tiles of 16 x 16 per wave
 constexpr int kStageA = TM * TKS, kStageB = TN * TKS;  // 32 KB + 32 KB per stage
 constexpr int kDmaA = kStageA / 1024 / kWaves;    // 8 DMA instructions per wave
 constexpr int kDmaB = kStageB / 1024 / kWaves;    // 8
@@ -73,48 +68,6 @@ constexpr int GROUP_M = 4;
 
 // Byte offset of 16-byte chunk c (0..7) of stage row r (128-byte rows).
 __device__ __forceinline__ int swz(int r, int c) { return r * TKS + ((c ^ ((r >> 1) & 7)) << 4); }
-
-// 32x32x64 operand of sub-step h: lane l holds row (l % 32); the matrix
-// core reads the lane's first 16 bytes as K [16 g, 16 g + 16) and the last 16
-// as K [32 + 16 g, 48 + 16 g) of the sub-step, g = l / 32, so the lane loads
-// chunks 4 h + g and 4 h + g + 2 and K order in LDS equals the hardware's
-// (which the 32-element scale blocks of the MX path rely on).
-__device__ __forceinline__ i32x8 frag(const uint8_t* lds, int row, int c0) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz(row, c0));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, c0 + 2));
-  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
-struct Frags {
-  i32x8 a[MI];
-  i32x8 b[NJ];
-};
-
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* la, const uint8_t* lb, int wm, int wn,
-                                           int fr, int c0) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i) f.a[i] = frag(la, wm * WTM + i * 32 + fr, c0);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) f.b[j] = frag(lb, wn * WTN + j * 32 + fr, c0);
-}
-
-// One 64-deep sub-step of MFMAs.  The first operand is B, so the result is
-// the transposed tile.  With MX, each lane passes the E8M0 scales of its own
-// row and 32-element K block; OPSEL picks the byte of the sub-step.
-template <int FA, int FB, bool MX, int OPSEL>
-__device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[MI][NJ], const uint32_t (&xa)[MI],
-                                          const uint32_t (&xb)[NJ]) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if constexpr (MX)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, OPSEL,
-                                                                    xb[j], OPSEL, xa[i]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
-    }
-}
 
 template <int NDMA>
 __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, int soff, const uint32_t (&voff)[NDMA], uint8_t* lds,
@@ -130,22 +83,6 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
   return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Half of a sub-step's MFMAs: row tiles 2 H and 2 H + 1.
-template <int FA, int FB, bool MX, int OPSEL, int H>
-__device__ __forceinline__ void mfma_step_half(const Frags& f, f32x16 (&acc)[MI][NJ], const uint32_t (&xa)[MI],
-                                               const uint32_t (&xb)[NJ]) {
-#pragma unroll
-  for (int i = 2 * H; i < 2 * H + 2; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if constexpr (MX)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, OPSEL,
-                                                                    xb[j], OPSEL, xa[i]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
-    }
 }
 
 // Wait until at most N of this wave's vector-memory operations (the loads of
@@ -175,11 +112,9 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
   tile_n = within / gm;
 }
 
-// Epilogue of one block.  32x32 MFMA tiles (T = 32, f32x16 accumulators):
-// lane l holds output row 32 i + (l % 32) and, per group g = e / 4, the 4
-// consecutive columns 32 j + 8 g + 4 (l / 32) + (e % 4) of its wave tile;
-// 16x16 tiles (T = 16, f32x4): row 16 i + (l % 16), columns 16 j + 4 (l / 16)
-// + e (the MFMA computed the transposed tile).  Values are
+// Epilogue of one block: lane l holds output row 16 i + (l % 16) and
+// columns 16 j + 4 (l / 16) + e of its wave tile (the MFMA computed the
+// transposed tile, accumulator acc[i][j][e]).  Values are
 // scaled (row factor sav, column vectors scol / bias from LDS), converted,
 // staged in the wave's 32 KB of LDS (16-byte chunks XOR-swizzled by row) and
 // stored as 16-byte row chunks; rows / columns at or past (M, N) are skipped.
@@ -190,9 +125,9 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
 // thresholds, one unordered compare per pair) and the exact per-element work
 // runs only for a group that may need it.  EDGE: the wave tile may reach past
 // (M, N), so elements are tested before they count.
-template <int OUT, bool EDGE = true, int T = 32, typename Acc = f32x16>
-__device__ __forceinline__ void store_tile(const Acc (&acc)[WTM / T][WTN / T], uint8_t* stage, const float* scol,
-                                           const float* sbias, const float (&sav)[WTM / T], int64_t wrow0, int64_t wcol0,
+template <int OUT, bool EDGE = true>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[MI16][NJ16], uint8_t* stage, const float* scol,
+                                           const float* sbias, const float (&sav)[MI16], int64_t wrow0, int64_t wcol0,
                                            int64_t M, int64_t N, void* __restrict__ Y, int64_t ldy, int vec_store,
                                            int wn, int fr, int fg, int lane, float rq, uint32_t& mb, uint32_t& sat_l,
                                            uint32_t& under_l) {
@@ -216,26 +151,22 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[WTM / T][WTN / T], u
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row: 8, 16 or 32
   constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // chunk swizzle mask
   constexpr int ROWS = kStageA / RB < WTM ? kStageA / RB : WTM;  // rows per pass: 128 or 64
-  constexpr int IPP = ROWS / T;                 // MFMA row tiles per pass
-  constexpr int TMI = WTM / T, TNJ = WTN / T;   // MFMA tiles of the wave
-  constexpr int G = T == 32 ? 4 : 1;            // groups of 4 columns a lane holds per tile
+  constexpr int IPP = ROWS / 16;                // MFMA row tiles per pass
   constexpr int EPC = 16 / ESZ;                 // elements per chunk
 #pragma unroll
-  for (int pass = 0; pass < TMI / IPP; ++pass) {
+  for (int pass = 0; pass < MI16 / IPP; ++pass) {
 #pragma unroll
     for (int ii = 0; ii < IPP; ++ii) {
       const int i = pass * IPP + ii;
-      const int lrow = ii * T + fr;             // row within the pass
+      const int lrow = ii * 16 + fr;            // row within the pass
 #pragma unroll
-      for (int j = 0; j < TNJ; ++j)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const int c = j * T + g * 8 + 4 * fg;   // first of 4 columns within the wave tile
+      for (int j = 0; j < NJ16; ++j) {
+          const int c = j * 16 + 4 * fg;          // first of 4 columns within the wave tile
           const f32x4 scv = *reinterpret_cast<const f32x4*>(&scol[wn * WTN + c]);
           const f32x4 biv = *reinterpret_cast<const f32x4*>(&sbias[wn * WTN + c]);
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * (sav[i] * scv[r]) + biv[r];
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sav[i] * scv[r]) + biv[r];
           const int byte = c * ESZ;               // byte offset of the 4 values in the row
           const int chunk = (byte >> 4) ^ (lrow & SWM);
           uint8_t* dst = stage + lrow * RB + (chunk << 4) + (byte & 15);
@@ -297,230 +228,9 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[WTM / T][WTN / T], u
   }
 }
 
-// MX: power-of-two 1x32 scales applied inside the MFMA.  xpa / xpb hold the
-// E8M0 exponents repacked by k_pack_e8m0 as [row / 32][stage][row % 32] dwords
-// (byte b = K block 4 stage + b).
-template <int FA, int FB, int OUT, bool MX>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
-    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
-    const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
-    void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store,
-    const uint32_t* __restrict__ xpa, const uint32_t* __restrict__ xpb, int t_main, int split, int ns_part,
-    float* __restrict__ part, const float* __restrict__ sy, const float* __restrict__ ry,
-    BlockPartial* __restrict__ ypart) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
-  __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
-  __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
-
-  // Blocks below t_main take whole tiles [0, t_main) of the grouped order;
-  // the rest are split-K units: unit u computes K stages
-  // [(u % split) ns_part, +ns_part) of tile t_main + u / split and writes its
-  // raw FP32 sums to part[u] (k_split_reduce finishes those tiles).
-  const int bid = blockIdx.x;
-  const bool unit = bid >= t_main;
-  int logical, s0 = 0;
-  if (!unit) {
-    const int xcd = bid & 7, loc = bid >> 3;
-    const int q = t_main >> 3, rem = t_main & 7;
-    logical = xcd * q + min(xcd, rem) + loc;
-  } else {
-    const int u = bid - t_main;
-    logical = t_main + u / split;
-    s0 = (u % split) * ns_part;
-  }
-  int tile_m, tile_n;
-  tile_of(logical, tiles_m, tiles_n, tile_m, tile_n);
-  const int64_t m0 = static_cast<int64_t>(tile_m) * TM, n0 = static_cast<int64_t>(tile_n) * TN;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int fr = lane & 31, fg = lane >> 5;
-
-  // DMA j of a wave fills stage rows (wave * NDMA + j) * 8 + (lane / 8); the
-  // lane's LDS slot is chunk lane % 8 of that row, which holds global chunk
-  // slot ^ ((row >> 1) & 7).
-  uint32_t voa[kDmaA], vob[kDmaB];
-#pragma unroll
-  for (int j = 0; j < kDmaA; ++j) {
-    const int r = (wave * kDmaA + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    voa[j] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * lda + c * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < kDmaB; ++j) {
-    const int r = (wave * kDmaB + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    vob[j] = static_cast<uint32_t>((min(n0 + r, N - 1) - n0) * ldb + c * 16);
-  }
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(A + m0 * lda + static_cast<int64_t>(s0) * TKS), 0, -1, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(B + n0 * ldb + static_cast<int64_t>(s0) * TKS), 0, -1, 0x00020000);
-
-  f32x16 acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  constexpr int kDmaStage = kDmaA + kDmaB;  // 16
-  const int ns_all = static_cast<int>(K / TKS);  // even
-  const int ns = unit ? ns_part : ns_all;         // stages this block runs (even)
-  const int c_lo = fg, c_hi = 4 + fg;  // first chunk of sub-step 0 / 1
-  // MX: per stage the workgroup needs the E8M0 dwords of 8 A and 8 B row
-  // groups (256 bytes each, 4 KB): each wave copies 1 KB of them into LDS
-  // with one DMA (waves 0/1: A groups 0-3 / 4-7, waves 2/3: B).  Lane l of
-  // an MFMA reads the dword of its row and K-half l / 32, whose bytes 0 and 2
-  // are the blocks of sub-steps 0 and 1.
-  __shared__ __attribute__((aligned(16))) uint32_t sX0[2][8 * 64];
-  __shared__ __attribute__((aligned(16))) uint32_t sX1[2][8 * 64];
-  uint32_t xa0[MI] = {}, xb0[NJ] = {}, xa1[MI] = {}, xb1[NJ] = {};  // even / odd stages
-  const uint32_t* xsrc = nullptr;
-  uint32_t xoff = 0;
-  if constexpr (MX) {
-    // lane l copies 16 bytes of row group 4 (wave & 1) + l / 16
-    const bool opb = wave >= 2;
-    const int64_t gmax = (opb ? (N - 1) : (M - 1)) / 32;
-    const int64_t g = min((opb ? n0 : m0) / 32 + 4 * (wave & 1) + (lane >> 4), gmax);
-    xsrc = opb ? xpb : xpa;
-    xoff = static_cast<uint32_t>((g * ns_all + s0) * 64 + (lane & 15) * 4);
-  }
-  auto sc_dma = [&](int st, uint32_t (&dst)[2][8 * 64]) {
-    if constexpr (MX) {
-      const int64_t stc = min(st, ns - 1);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(xsrc + xoff + stc * 64),
-                                       (lds_void*)(&dst[wave >> 1][(wave & 1) * 256]), 16, 0, 0);
-    }
-  };
-  auto sc_read = [&](const uint32_t (&src)[2][8 * 64], uint32_t (&xa)[MI], uint32_t (&xb)[NJ]) {
-    if constexpr (MX) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) xa[i] = src[0][(wm * MI + i) * 64 + fg * 32 + fr];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) xb[j] = src[1][(wn * NJ + j) * 64 + fg * 32 + fr];
-    }
-  };
-  sc_dma(0, sX0);
-  sc_dma(1, sX1);
-  dma_buf<kDmaA>(ra, 0, voa, sA0, wave);
-  dma_buf<kDmaB>(rb, 0, vob, sB0, wave);
-  dma_buf<kDmaA>(ra, TKS, voa, sA1, wave);
-  dma_buf<kDmaB>(rb, TKS, vob, sB1, wave);
-  step_barrier<kDmaStage>();  // stage 0 (and the scales, issued first) landed
-  Frags fp, fq;
-  read_frags(fp, sA0, sB0, wm, wn, fr, c_lo);
-  sc_read(sX0, xa0, xb0);
-  // Sub-step 2j: MFMAs on P (stage j, first half), read stage j second half
-  // into Q; then the barrier after which stage j's arrays are free (stage
-  // j+1's loads stay in flight).  Sub-step 2j+1: refill stage j's arrays with
-  // stage j+2 during the first half of the MFMAs on Q, wait for stage j+1
-  // and join the barrier, then read its first half into P during the second.
-  constexpr int kVmStage = kDmaStage + (MX ? 1 : 0);  // vector-memory ops per stage and wave
-#define FP8RT_EVEN(LA, LB, XA, XB)                                            \
-  {                                                                           \
-    read_frags(fq, LA, LB, wm, wn, fr, c_hi);                                 \
-    mfma_step<FA, FB, MX, 0>(fp, acc, XA, XB);                                \
-    for (int s = 0; s < 4; ++s) {                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
-    }                                                                         \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                        \
-    step_barrier<kVmStage>();                                                 \
-  }
-#define FP8RT_ODD(DA, DB, DX, KS, LA, LB, LX, XA, XB, NXA, NXB)              \
-  {                                                                           \
-    const int kn = min(KS, ns - 1);                                           \
-    dma_buf<kDmaA>(ra, kn * TKS, voa, DA, wave);                              \
-    dma_buf<kDmaB>(rb, kn * TKS, vob, DB, wave);                              \
-    sc_dma(KS, DX);                                                           \
-    mfma_step_half<FA, FB, MX, 2, 0>(fq, acc, XA, XB);                        \
-    for (int s = 0; s < 8; ++s) {                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                      \
-    }                                                                         \
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                        \
-    step_barrier<kVmStage>();                                                 \
-    sc_read(LX, NXA, NXB);                                                    \
-    read_frags(fp, LA, LB, wm, wn, fr, c_lo);                                 \
-    mfma_step_half<FA, FB, MX, 2, 1>(fq, acc, XA, XB);                        \
-    for (int s = 0; s < 8; ++s) {                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      \
-    }                                                                         \
-    __builtin_amdgcn_sched_barrier(0);                                        \
-  }
-  for (int j = 0; j < ns; j += 2) {
-    FP8RT_EVEN(sA0, sB0, xa0, xb0)
-    FP8RT_ODD(sA0, sB0, sX0, j + 2, sA1, sB1, sX1, xa0, xb0, xa1, xb1)
-    FP8RT_EVEN(sA1, sB1, xa1, xb1)
-    FP8RT_ODD(sA1, sB1, sX1, j + 3, sA0, sB0, sX0, xa1, xb1, xa0, xb0)
-  }
-#undef FP8RT_EVEN
-#undef FP8RT_ODD
-  step_barrier<0>();  // the clamped extra loads finish before the arrays are reused
-
-  // ---- epilogue.  The MFMA computed the transposed tile, so lane l holds
-  // output row 32 i + (l % 32) and, per group g = e / 4, the 4 consecutive
-  // columns 32 j + 8 g + 4 (l / 32) + (e % 4).  Column scales and bias go
-  // through LDS once per block; each wave converts its 128 x 128 result,
-  // stages it in its own 32 KB of LDS (16-byte chunks XOR-swizzled by row)
-  // and stores 16-byte row chunks.
-  __shared__ __attribute__((aligned(16))) float sCol[2][TN];
-  if (unit) {
-    sCol[0][t] = 1.0f;
-    sCol[1][t] = 0.0f;
-  } else {
-    const int64_t col = min(n0 + t, N - 1);
-    sCol[0][t] = MX ? 1.0f : sb[erb == 1 ? col : 0];  // MX scales were applied by the MFMA
-    float bvv = 0.0f;
-    if (bias)
-      bvv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
-                      : static_cast<const float*>(bias)[col];
-    sCol[1][t] = bvv;
-  }
-  __syncthreads();
-  uint8_t* stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
-  float sav[MI];
-  uint32_t mb = 0, sat_l = 0, under_l = 0;
-  if (unit) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sav[i] = 1.0f;
-    float* dst = part + static_cast<int64_t>(bid - t_main) * (TM * TN);
-    store_tile<kOutF32>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1, wn, fr,
-                        fg, lane, 1.0f, mb, sat_l, under_l);
-  } else {
-    const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 32 + fr, M - 1) : 0];
-    float rq = 1.0f;
-    if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
-    // the whole block tile inside (M, N): every wave takes the same branch
-    // (store_tile holds barriers)
-    if (OUT >= kOutE4M3 && m0 + TM <= M && n0 + TN <= N)
-      store_tile<OUT, false>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn,
-                             fr, fg, lane, rq, mb, sat_l, under_l);
-    else
-      store_tile<OUT, true>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store, wn,
-                            fr, fg, lane, rq, mb, sat_l, under_l);
-  }
-  // FP8 output: a whole tile's max |y| and counters (split-K units hold raw
-  // partial sums; k_split_reduce takes the statistics of their tiles)
-  if constexpr (OUT >= kOutE4M3)
-    if (!unit) block_stats_store<kWaves>(reinterpret_cast<u32x4*>(&ypart[bid]), mb, sat_l, under_l);
-}
-
 // ---- 16x16x128 kernel (per-tensor / per-row scales; BF16, FP32 or FP8 output).
 // The same 256 x 256 tile, 4 waves of 128 x 128, LDS stages, DMA and tile
-// order as k_gemm_big; each wave issues 8 x 8 v_mfma_f32_16x16x128_f8f6f4
+// order as described at the top; each wave issues 8 x 8 v_mfma_f32_16x16x128_f8f6f4
 // per 128-deep stage (one instruction consumes the whole stage).  On random
 // operands this instruction sustains a higher rate than 32x32x64 (the chip
 // holds a higher clock for it).  Registers: 64 four-wide accumulators (256
@@ -530,7 +240,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big(
 // which the stage after next is loaded into its arrays, and one at row tile 5
 // for the next stage's loads, so each stage's loads fly for 1.4 stages (with
 // a single barrier per stage, 1 stage, the kernel ran 5-10% slower).
-constexpr int MI16 = WTM / 16, NJ16 = WTN / 16;  // 8 x 8 tiles of 16 x 16
 
 // 16x16x128 operand: lane l holds row l % 16; the matrix core reads its first
 // 16 bytes as K [16 g, +16) and its last 16 as K [64 + 16 g, +16) of the
@@ -554,6 +263,52 @@ __device__ __forceinline__ void mfma16(f32x4& acc, const i32x8& b, const i32x8& 
   else
     asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 blgp:1" : "+a"(acc) : "v"(b), "v"(a));
 }
+
+// The same with 1x32 power-of-two scales: E8M0 exponent bytes, byte OB of
+// sb for the B operand (the instruction's first source) and byte OA of sa
+// for A; each lane supplies the exponent of its row and of K block
+// (lane / 16) of the stage, the block its lane group's bytes belong to.
+#define FP8RT_MFMA16X(ALO, AHI, BLO, BHI, FMT)                                                                \
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #BLO "," #ALO              \
+               ",0] op_sel_hi:[" #BHI "," #AHI ",0]" FMT                                                      \
+               : "+a"(acc)                                                                                     \
+               : "v"(b), "v"(a), "v"(sb), "v"(sa))
+template <int FA, int OA, int OB>
+__device__ __forceinline__ void mfma16x(f32x4& acc, const i32x8& b, const i32x8& a, uint32_t sb, uint32_t sa) {
+  if constexpr (FA == 0 && OA == 0 && OB == 0) FP8RT_MFMA16X(0, 0, 0, 0, "");
+  else if constexpr (FA == 0 && OA == 0 && OB == 1) FP8RT_MFMA16X(0, 0, 1, 0, "");
+  else if constexpr (FA == 0 && OA == 0 && OB == 2) FP8RT_MFMA16X(0, 0, 0, 1, "");
+  else if constexpr (FA == 0 && OA == 0 && OB == 3) FP8RT_MFMA16X(0, 0, 1, 1, "");
+  else if constexpr (FA == 0 && OA == 1 && OB == 0) FP8RT_MFMA16X(1, 0, 0, 0, "");
+  else if constexpr (FA == 0 && OA == 1 && OB == 1) FP8RT_MFMA16X(1, 0, 1, 0, "");
+  else if constexpr (FA == 0 && OA == 1 && OB == 2) FP8RT_MFMA16X(1, 0, 0, 1, "");
+  else if constexpr (FA == 0 && OA == 1 && OB == 3) FP8RT_MFMA16X(1, 0, 1, 1, "");
+  else if constexpr (FA == 0 && OA == 2 && OB == 0) FP8RT_MFMA16X(0, 1, 0, 0, "");
+  else if constexpr (FA == 0 && OA == 2 && OB == 1) FP8RT_MFMA16X(0, 1, 1, 0, "");
+  else if constexpr (FA == 0 && OA == 2 && OB == 2) FP8RT_MFMA16X(0, 1, 0, 1, "");
+  else if constexpr (FA == 0 && OA == 2 && OB == 3) FP8RT_MFMA16X(0, 1, 1, 1, "");
+  else if constexpr (FA == 0 && OA == 3 && OB == 0) FP8RT_MFMA16X(1, 1, 0, 0, "");
+  else if constexpr (FA == 0 && OA == 3 && OB == 1) FP8RT_MFMA16X(1, 1, 1, 0, "");
+  else if constexpr (FA == 0 && OA == 3 && OB == 2) FP8RT_MFMA16X(1, 1, 0, 1, "");
+  else if constexpr (FA == 0 && OA == 3 && OB == 3) FP8RT_MFMA16X(1, 1, 1, 1, "");
+  else if constexpr (FA == 1 && OA == 0 && OB == 0) FP8RT_MFMA16X(0, 0, 0, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 0 && OB == 1) FP8RT_MFMA16X(0, 0, 1, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 0 && OB == 2) FP8RT_MFMA16X(0, 0, 0, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 0 && OB == 3) FP8RT_MFMA16X(0, 0, 1, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 1 && OB == 0) FP8RT_MFMA16X(1, 0, 0, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 1 && OB == 1) FP8RT_MFMA16X(1, 0, 1, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 1 && OB == 2) FP8RT_MFMA16X(1, 0, 0, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 1 && OB == 3) FP8RT_MFMA16X(1, 0, 1, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 2 && OB == 0) FP8RT_MFMA16X(0, 1, 0, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 2 && OB == 1) FP8RT_MFMA16X(0, 1, 1, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 2 && OB == 2) FP8RT_MFMA16X(0, 1, 0, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 2 && OB == 3) FP8RT_MFMA16X(0, 1, 1, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 3 && OB == 0) FP8RT_MFMA16X(1, 1, 0, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 3 && OB == 1) FP8RT_MFMA16X(1, 1, 1, 0, " blgp:1");
+  else if constexpr (FA == 1 && OA == 3 && OB == 2) FP8RT_MFMA16X(1, 1, 0, 1, " blgp:1");
+  else if constexpr (FA == 1 && OA == 3 && OB == 3) FP8RT_MFMA16X(1, 1, 1, 1, " blgp:1");
+}
+#undef FP8RT_MFMA16X
 
 // Wait states between VALU accesses of the accumulators and the inline MFMAs
 // (which the compiler's hazard recognizer does not see): 24, more than the
@@ -591,25 +346,58 @@ __device__ __forceinline__ void dma1(__amdgpu_buffer_rsrc_t rs, int soff, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + k * 1024), 16, static_cast<int>(voff), soff, 0, 0);
 }
 
+// One MFMA of row tile I, column tile J: plain, or with the exponent bytes
+// I % 4 of xa and J % 4 of xb (1x32 scales).
+template <int FA, bool MX>
+__device__ __forceinline__ void mf16(f32x4& acc, const i32x8& b, const i32x8& a, uint32_t xb, uint32_t xa, int i,
+                                     int j) {
+  if constexpr (!MX) {
+    mfma16<FA>(acc, b, a);
+  } else {
+    // i and j are constants after unrolling: one asm form each
+    switch (((i & 3) << 2) | (j & 3)) {
+      case 0: mfma16x<FA, 0, 0>(acc, b, a, xb, xa); break;
+      case 1: mfma16x<FA, 0, 1>(acc, b, a, xb, xa); break;
+      case 2: mfma16x<FA, 0, 2>(acc, b, a, xb, xa); break;
+      case 3: mfma16x<FA, 0, 3>(acc, b, a, xb, xa); break;
+      case 4: mfma16x<FA, 1, 0>(acc, b, a, xb, xa); break;
+      case 5: mfma16x<FA, 1, 1>(acc, b, a, xb, xa); break;
+      case 6: mfma16x<FA, 1, 2>(acc, b, a, xb, xa); break;
+      case 7: mfma16x<FA, 1, 3>(acc, b, a, xb, xa); break;
+      case 8: mfma16x<FA, 2, 0>(acc, b, a, xb, xa); break;
+      case 9: mfma16x<FA, 2, 1>(acc, b, a, xb, xa); break;
+      case 10: mfma16x<FA, 2, 2>(acc, b, a, xb, xa); break;
+      case 11: mfma16x<FA, 2, 3>(acc, b, a, xb, xa); break;
+      case 12: mfma16x<FA, 3, 0>(acc, b, a, xb, xa); break;
+      case 13: mfma16x<FA, 3, 1>(acc, b, a, xb, xa); break;
+      case 14: mfma16x<FA, 3, 2>(acc, b, a, xb, xa); break;
+      default: mfma16x<FA, 3, 3>(acc, b, a, xb, xa); break;
+    }
+  }
+}
+
 // Row tile at which the 16x16x128 kernel's second barrier sits (the next
 // stage's fragments are read from there to row 7): rows 4, 5 and 6 measured
 // within 1-3% of each other at the large shapes, 5 the best or equal.
 constexpr int kRowB16 = 5;
 
-template <int FA, int FB, int OUT, int RB>
+template <int FA, int FB, int OUT, bool MX, int RB>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ sa, int64_t era,
     const float* __restrict__ sb, int64_t erb, const void* __restrict__ bias, int bias_bf16,
     void* __restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_store, int t_main, int split,
     int ns_part, float* __restrict__ part, const float* __restrict__ sy, const float* __restrict__ ry,
-    BlockPartial* __restrict__ ypart) {
+    BlockPartial* __restrict__ ypart, const u32x2* __restrict__ xpa, const u32x2* __restrict__ xpb) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[kStageA];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kStageB];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[kStageB];
 
-  // Whole tiles below t_main, split-K units above it (as in k_gemm_big).
+  // Blocks below t_main take whole tiles [0, t_main) of the grouped order;
+  // the rest are split-K units: unit u computes K stages
+  // [(u % split) ns_part, +ns_part) of tile t_main + u / split and writes its
+  // raw FP32 sums to part[u] (k_split_reduce finishes those tiles).
   const int bid = blockIdx.x;
   const bool unit = bid >= t_main;
   int logical, s0 = 0;
@@ -662,11 +450,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
   const int ns = unit ? ns_part : static_cast<int>(K / TKS);  // even
   const int ra0 = wm * WTM + fr, rb0 = wn * WTN + fr;         // the lane's first A / B fragment row
 
+  // 1x32 scales: the lane's 8 exponent bytes of A (one per row tile) and of
+  // B for a stage, repacked by k_pack_e8m0_16 as [128-row block][stage]
+  // [lane]; x0 / x1 hold the even / odd stage's, loaded one stage ahead
+  // (issued before the DMA of the stage after next, so the second barrier's
+  // wait covers them).
+  const int ns_all = static_cast<int>(K / TKS);
+  const u32x2* xra = nullptr;
+  const u32x2* xrb = nullptr;
+  u32x2 xa0 = {}, xb0 = {}, xa1 = {}, xb1 = {};
+  if constexpr (MX) {
+    xra = xpa + ((m0 / WTM + wm) * ns_all + s0) * 64 + lane;
+    xrb = xpb + ((n0 / WTN + wn) * ns_all + s0) * 64 + lane;
+    xa0 = xra[0];
+    xb0 = xrb[0];
+  }
   dma_buf<kDmaA>(ra, 0, voa, sA0, wave);
   dma_buf<kDmaB>(rb, 0, vob, sB0, wave);
   dma_buf<kDmaA>(ra, TKS, voa, sA1, wave);
   dma_buf<kDmaB>(rb, TKS, vob, sB1, wave);
-  step_barrier<kDmaStage>();  // stage 0 landed
+  step_barrier<kDmaStage>();  // stage 0 landed (and stage 0's exponents, loaded before it)
+  if constexpr (MX) asm volatile("" : "+v"(xa0), "+v"(xb0));
   i32x8 bx[NJ16], by[NJ16], af[MI16];
 #pragma unroll
   for (int j = 0; j < NJ16; ++j) bx[j] = frag16(sB0, rb0 + j * 16, fg);
@@ -686,20 +490,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
   // keeps its place between them as written here.
   constexpr int kNR = MI16 - RB;                     // rows that read the next stage
   constexpr int kPer = (NJ16 + 1 + kNR - 1) / kNR;   // fragments per such row
-#define FP8RT_STAGE16(LA, LB, NA, NB, BC, BN, KS)                                                              \
+#define FP8RT_STAGE16(LA, LB, NA, NB, BC, BN, XA, XB, NXA, NXB, KS)                                                              \
   {                                                                                                            \
     _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                                             \
       _Pragma("unroll") for (int j = 0; j < NJ16; ++j) {                                                        \
-        mfma16<FA>(acc[i][j], BC[j], af[i]);                                                                   \
+        mf16<FA, MX>(acc[i][j], BC[j], af[i], XB[j >> 2], XA[i >> 2], i, j);                                                                   \
         const int t2 = 4 * i + j + 1;  /* A row tile read after this MFMA */                                   \
         if (j < 4 && t2 < MI16) af[t2] = frag16(LA, ra0 + t2 * 16, fg);                                        \
       }                                                                                                        \
     }                                                                                                          \
     lds_barrier();                                                                                             \
     const int kn = min(KS, ns - 1);                                                                            \
+    if constexpr (MX) {                                                                                        \
+      const int kx = min(KS - 1, ns - 1);  /* the next stage's exponents */                                    \
+      NXA = xra[kx * 64];                                                                                      \
+      NXB = xrb[kx * 64];                                                                                      \
+    }                                                                                                          \
     _Pragma("unroll") for (int i = 2; i < RB; ++i) {                                                            \
       _Pragma("unroll") for (int j = 0; j < NJ16; ++j) {                                                        \
-        mfma16<FA>(acc[i][j], BC[j], af[i]);                                                                   \
+        mf16<FA, MX>(acc[i][j], BC[j], af[i], XB[j >> 2], XA[i >> 2], i, j);                                                                   \
         if (i < 4) {   /* 16 DMA instructions, one after each MFMA of rows 2-3: A's 8, then B's 8 */        \
           const int d = (i - 2) * NJ16 + j;                                                                    \
           if (d < kDmaA) dma1(ra, kn * TKS, voa[d], LA, wave * kDmaA + d);                                      \
@@ -708,9 +517,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
       }                                                                                                        \
     }                                                                                                          \
     step_barrier<kDmaStage>();                                                                                 \
+    /* the next stage's exponents have landed (the wait above covers them): an \
+       opaque use here keeps the compiler from waiting for every load at the \
+       loop head, where it would otherwise meet them still marked in flight */ \
+    if constexpr (MX) asm volatile("" : "+v"(NXA), "+v"(NXB));                                                  \
     _Pragma("unroll") for (int i = RB; i < MI16; ++i) {                                                         \
       _Pragma("unroll") for (int j = 0; j < NJ16; ++j) {                                                        \
-        mfma16<FA>(acc[i][j], BC[j], af[i]);                                                                   \
+        mf16<FA, MX>(acc[i][j], BC[j], af[i], XB[j >> 2], XA[i >> 2], i, j);                                                                   \
         const int k = (i - RB) * kPer + j;  /* item k: B 0, A 0, B 1 .. B 7 */                                 \
         if (j < kPer && k <= NJ16) {                                                                           \
           if (k == 1) af[0] = frag16(NA, ra0, fg);                                                             \
@@ -720,8 +533,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
     }                                                                                                          \
   }
   for (int s = 0; s < ns; s += 2) {
-    FP8RT_STAGE16(sA0, sB0, sA1, sB1, bx, by, s + 2)
-    FP8RT_STAGE16(sA1, sB1, sA0, sB0, by, bx, s + 3)
+    FP8RT_STAGE16(sA0, sB0, sA1, sB1, bx, by, xa0, xb0, xa1, xb1, s + 2)
+    FP8RT_STAGE16(sA1, sB1, sA0, sB0, by, bx, xa1, xb1, xa0, xb0, s + 3)
   }
 #undef FP8RT_STAGE16
   // the last MFMAs' results are read by VALU instructions below: wait states
@@ -734,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
     sCol[1][t] = 0.0f;
   } else {
     const int64_t col = min(n0 + t, N - 1);
-    sCol[0][t] = sb[erb == 1 ? col : 0];
+    sCol[0][t] = MX ? 1.0f : sb[erb == 1 ? col : 0];  // 1x32 scales were applied by the MFMA
     float bvv = 0.0f;
     if (bias)
       bvv = bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col]) << 16)
@@ -749,21 +562,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big16(
 #pragma unroll
     for (int i = 0; i < MI16; ++i) sav[i] = 1.0f;
     float* dst = part + static_cast<int64_t>(bid - t_main) * (TM * TN);
-    store_tile<kOutF32, true, 16>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1,
+    store_tile<kOutF32, true>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wm * WTM, wn * WTN, TM, TN, dst, TN, 1,
                                   wn, fr, fg, lane, 1.0f, mb, sat_l, under_l);
   } else {
     const int64_t wrow0 = m0 + wm * WTM, wcol0 = n0 + wn * WTN;
 #pragma unroll
-    for (int i = 0; i < MI16; ++i) sav[i] = sa[era == 1 ? min(wrow0 + i * 16 + fr, M - 1) : 0];
+    for (int i = 0; i < MI16; ++i) sav[i] = MX ? 1.0f : sa[era == 1 ? min(wrow0 + i * 16 + fr, M - 1) : 0];
     float rq = 1.0f;
     if constexpr (OUT >= kOutE4M3) rq = ry ? ry[0] : 1.0f / sy[0];
     // the whole block tile inside (M, N): every wave takes the same branch
     // (store_tile holds barriers)
     if (OUT >= kOutE4M3 && m0 + TM <= M && n0 + TN <= N)
-      store_tile<OUT, false, 16>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store,
+      store_tile<OUT, false>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store,
                                  wn, fr, fg, lane, rq, mb, sat_l, under_l);
     else
-      store_tile<OUT, true, 16>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store,
+      store_tile<OUT, true>(acc, stage, &sCol[0][0], &sCol[1][0], sav, wrow0, wcol0, M, N, Y, ldy, vec_store,
                                 wn, fr, fg, lane, rq, mb, sat_l, under_l);
   }
   // FP8 output: a whole tile's max |y| and counters (split-K units hold raw
@@ -856,25 +669,27 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
                          under_l);
 }
 
-// Repack power-of-two 1x32 scales (fp32, [rows][K / 32]) as E8M0 exponent
-// bytes for the MFMA: dword [row / 32][stage][half][row % 32] holds in bytes 0
-// and 2 the exponents of K blocks 4 stage + half and 4 stage + half + 2 (the
-// blocks that lane half `half` of an MFMA covers in the stage's two
-// sub-steps).  Rows past the end get exponent 127 (scale 1); their products
-// are never stored.
-__global__ __launch_bounds__(256) void k_pack_e8m0(const float* __restrict__ s, int64_t rows, int64_t nblk,
-                                                   int64_t ngroups, int64_t nstage, uint32_t* __restrict__ out) {
+// 1x32 power-of-two scales (fp32, [rows][K / 32]) as the exponent bytes that
+// k_gemm_big16 reads: u32x2 [row / 128][stage][lane], byte i (0-7) the
+// exponent of row 128 (row / 128) + 16 i + lane % 16 and K block
+// 4 stage + lane / 16.  Rows past the end get exponent 127 (scale 1); their
+// products are never stored.
+__global__ __launch_bounds__(256) void k_pack_e8m0_16(const float* __restrict__ s, int64_t rows, int64_t nblk,
+                                                      int64_t nrb, int64_t nstage, u32x2* __restrict__ out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= ngroups * nstage * 64) return;
-  const int64_t rr = idx & 31, half = (idx >> 5) & 1, gs = idx >> 6;
-  const int64_t st = gs % nstage, g = gs / nstage;
-  const int64_t row = g * 32 + rr;
-  uint32_t w = 0x007F007Fu;
-  if (row < rows) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(s + row * nblk + st * 4 + half);
-    w = ((src[0] >> 23) & 0xFFu) | (((src[2] >> 23) & 0xFFu) << 16);
+  if (idx >= nrb * nstage * 64) return;
+  const int64_t lane = idx & 63, rs = idx >> 6;
+  const int64_t st = rs % nstage, rb = rs / nstage;
+  const int64_t kb = st * 4 + (lane >> 4);
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = rb * WTM + 16 * i + (lane & 15);
+    const uint32_t e = row < rows ? (reinterpret_cast<const uint32_t*>(s)[row * nblk + kb] >> 23) & 0xFFu : 127u;
+    if (i < 4) w0 |= e << (8 * i);
+    else w1 |= e << (8 * (i - 4));
   }
-  out[idx] = w;
+  out[idx] = u32x2{w0, w1};
 }
 
 }  // namespace
@@ -892,8 +707,9 @@ bool gemm_big_eligible(const GemmArgs& g) {
 
 size_t gemm_big_required_scratch(const GemmArgs& g) {
   if (!g.pow2_mx) return 0;
-  const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
-  return (static_cast<size_t>((ga + gb) * ns * 64) * 4 + 255) & ~size_t(255);  // E8M0 exponent dwords
+  // whole 256-row tiles: a last tile's second wave reads its own (padding) block
+  const int64_t ns = g.K / TKS, ra = (g.M + TM - 1) / TM * (TM / WTM), rb = (g.N + TN - 1) / TN * (TN / WTN);
+  return (static_cast<size_t>((ra + rb) * ns * 64) * 8 + 255) & ~size_t(255);  // E8M0 exponent bytes
 }
 
 hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
@@ -946,52 +762,36 @@ hipError_t launch_gemm_big(const GemmArgs& g, hipStream_t st, int* nparts) {
   }
   float* part = split > 1 ? reinterpret_cast<float*>(scratch + mx_bytes) : nullptr;
   const dim3 grid(static_cast<unsigned>(t_main + (T - t_main) * split));
-  uint32_t* xpa = nullptr;
-  uint32_t* xpb = nullptr;
+  u32x2* xpa16 = nullptr;
+  u32x2* xpb16 = nullptr;
   if (g.pow2_mx) {
-    const int64_t ns = g.K / TKS, ga = (g.M + 31) / 32, gb = (g.N + 31) / 32;
-    xpa = reinterpret_cast<uint32_t*>(scratch);
-    xpb = xpa + ga * ns * 64;
-    hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((ga * ns * 64 + 255) / 256)), dim3(256), 0, st,
-                       g.sa, g.M, g.K / 32, ga, ns, xpa);
-    hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((gb * ns * 64 + 255) / 256)), dim3(256), 0, st,
-                       g.sb, g.N, g.K / 32, gb, ns, xpb);
+    // whole 256-row tiles: a last tile's second wave reads its own (padding) block
+    const int64_t ns = g.K / TKS, ra = (g.M + TM - 1) / TM * (TM / WTM), rb = (g.N + TN - 1) / TN * (TN / WTN);
+    xpa16 = reinterpret_cast<u32x2*>(scratch);
+    xpb16 = xpa16 + ra * ns * 64;
+    hipLaunchKernelGGL(k_pack_e8m0_16, dim3(static_cast<unsigned>((ra * ns * 64 + 255) / 256)), dim3(256), 0, st,
+                       g.sa, g.M, g.K / 32, ra, ns, xpa16);
+    hipLaunchKernelGGL(k_pack_e8m0_16, dim3(static_cast<unsigned>((rb * ns * 64 + 255) / 256)), dim3(256), 0, st,
+                       g.sb, g.N, g.K / 32, rb, ns, xpb16);
   }
-#define FP8RT_BIG(FA, FB, OUT, MXV)                                                                         \
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT, MXV>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
-                     g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec, \
-                     xpa, xpb, t_main, split, ns_part, part, g.sy, g.ry, g.part)
-#define FP8RT_BIG_OUT(FA, FB, MXV)                                  \
+#define FP8RT_BIG16(FA, FB, OUT, MXV)                                                                         \
+  hipLaunchKernelGGL((k_gemm_big16<FA, FB, OUT, MXV, kRowB16>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b,  \
+                     g.ldb, g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n,  \
+                     vec, t_main, split, ns_part, part, g.sy, g.ry, g.part, xpa16, xpb16)
+#define FP8RT_BIG16_OUT(FA, FB, MXV)                                \
   switch (okind) {                                                  \
-    case kOutBF16: FP8RT_BIG(FA, FB, kOutBF16, MXV); break;         \
-    case kOutE4M3: FP8RT_BIG(FA, FB, kOutE4M3, MXV); break;         \
-    case kOutE5M2: FP8RT_BIG(FA, FB, kOutE5M2, MXV); break;         \
-    default: FP8RT_BIG(FA, FB, kOutF32, MXV); break;                \
+    case kOutBF16: FP8RT_BIG16(FA, FB, kOutBF16, MXV); break;       \
+    case kOutE4M3: FP8RT_BIG16(FA, FB, kOutE4M3, MXV); break;       \
+    case kOutE5M2: FP8RT_BIG16(FA, FB, kOutE5M2, MXV); break;       \
+    default: FP8RT_BIG16(FA, FB, kOutF32, MXV); break;              \
   }
-  // per-tensor / per-row scales: the 16x16x128 kernel; 1x32 scales: the
-  // 32x32x64 one (its scaled MFMA takes the E8M0 exponents)
-  if (!g.pow2_mx) {
-#define FP8RT_BIG16(FA, FB, OUT)                                                                              \
-  hipLaunchKernelGGL((k_gemm_big16<FA, FB, OUT, kRowB16>), grid, dim3(kThreads), 0, st, g.a, g.lda, g.b, g.ldb, \
-                     g.M, g.N, g.K, g.sa, g.era, g.sb, g.erb, g.bias, bb, g.y, g.ldy, tiles_m, tiles_n, vec,  \
-                     t_main, split, ns_part, part, g.sy, g.ry, g.part)
-#define FP8RT_BIG16_OUT(FA, FB)                                     \
-  switch (okind) {                                                  \
-    case kOutBF16: FP8RT_BIG16(FA, FB, kOutBF16); break;            \
-    case kOutE4M3: FP8RT_BIG16(FA, FB, kOutE4M3); break;            \
-    case kOutE5M2: FP8RT_BIG16(FA, FB, kOutE5M2); break;            \
-    default: FP8RT_BIG16(FA, FB, kOutF32); break;                   \
+  if (g.fa == FP8RT_E4M3) {
+    if (g.pow2_mx) { FP8RT_BIG16_OUT(0, 0, true) } else { FP8RT_BIG16_OUT(0, 0, false) }
+  } else {
+    if (g.pow2_mx) { FP8RT_BIG16_OUT(1, 0, true) } else { FP8RT_BIG16_OUT(1, 0, false) }
   }
-    if (g.fa == FP8RT_E4M3) { FP8RT_BIG16_OUT(0, 0) } else { FP8RT_BIG16_OUT(1, 0) }
 #undef FP8RT_BIG16_OUT
 #undef FP8RT_BIG16
-  } else if (g.fa == FP8RT_E4M3) {
-    FP8RT_BIG_OUT(0, 0, true)
-  } else {
-    FP8RT_BIG_OUT(1, 0, true)
-  }
-#undef FP8RT_BIG_OUT
-#undef FP8RT_BIG
   if (split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -12,7 +12,7 @@
 namespace fp8rt {
 
 // kNoAllocScratchBytes = 16 MiB: the repacked 1x32 exponents of a
-// 8192 x 18432 x 7168 GEMM take 11.9 MB and its transposed 1x128 A scales
+// 8192 x 18432 x 7168 GEMM take 6.0 MB and its transposed 1x128 A scales
 // 1.8 MB; a split last wave takes as many K parts as fit (256 KB per part and
 // split tile).
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];

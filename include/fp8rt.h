@@ -17,8 +17,8 @@
  *    synchronizes the device or the stream:
  *      * a workspace of 256 KB for the per-block partial results of the
  *        quantize kernels and of the FP8-output GEMM;
- *      * a scratch buffer for the GEMM's repacked 1x32 exponents ((ceil(M/32)
- *        + ceil(N/32)) * K/128 * 256 bytes) and transposed 1x128 A scales
+ *      * a scratch buffer for the GEMM's repacked 1x32 exponents ((ceil(M/256)
+ *        + ceil(N/256)) * K/128 * 1024 bytes) and transposed 1x128 A scales
  *        (ceil(M/256) * 256 * K/128 * 4 bytes), the FP32 parts of a last wave
  *        split along K (up to 4 parts x 256 KB per split 256 x 256 tile), the
  *        cast-transpose's per-group arrays and the ledger's partials.  When a
@@ -261,7 +261,7 @@ fp8rt_status fp8_scaled_gemm(const uint8_t* a, fp8rt_format fa, int64_t lda, fp8
  * until the process ends; its address is looked up on the first call on each
  * device.
  *  - A call whose kernel needs more scratch than that (repacked 1x32
- *    exponents: (ceil(M/32) + ceil(N/32)) * K/128 * 256 bytes; transposed
+ *    exponents: (ceil(M/256) + ceil(N/256)) * K/128 * 1024 bytes; transposed
  *    1x128 A scales on large shapes: ceil(M/256) * 256 * K/128 * 4 bytes)
  *    returns FP8RT_ESCRATCH before anything is enqueued.
  *  - A ragged last wave of tiles, or a grid of tiles that fills at most half

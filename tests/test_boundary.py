@@ -343,10 +343,10 @@ def test_quant_error_and_ledger_validation(rt):
 
 def test_gemm_noalloc_refuses_shapes_beyond_its_scratch(rt):
     """The allocation-free GEMM checks its fixed scratch (16 MiB) on the host:
-    1x32 exponent tables of (ceil(M/32) + ceil(N/32)) * K/128 * 256 bytes fit
-    at M = N = 16384, K = 8192 (exactly 16 MiB) and not at N = 16416."""
+    1x32 exponent tables of (ceil(M/256) + ceil(N/256)) * K/128 * 1024 bytes fit
+    at M = 16384, N = 49152, K = 8192 (exactly 16 MiB) and not at N = 49408."""
     big = dict(M=16384, K=8192, lda=8192, ldb=8192, ga=(1, 32), gb=(1, 32), flags=rt.POW2_SCALES)
-    assert g(rt, "fp8_scaled_gemm_noalloc", N=16416, ldy=16416, **big) == rt.ESCRATCH
+    assert g(rt, "fp8_scaled_gemm_noalloc", N=49408, ldy=49408, **big) == rt.ESCRATCH
     # 128 x 128 B blocks with 1x128 A groups on a large shape: ceil(M/256)*256 * K/128 * 4 bytes
     assert g(rt, "fp8_scaled_gemm_noalloc", M=65536 * 2, N=256, K=65536 // 2, lda=32768, ldb=32768,
              ldy=256, ga=(1, 128), gb=(128, 128)) == rt.ESCRATCH

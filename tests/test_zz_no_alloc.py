@@ -91,11 +91,11 @@ def test_noalloc_unsplit_last_wave(rt, orc):
 
 
 def test_noalloc_refuses_oversized_scratch(rt):
-    """1x32 exponents of a 16384 x N x 8192 GEMM take (ceil(M/32) + ceil(N/32)) *
-    64 * 256 bytes: exactly 16 MiB at N = 16384, more at N = 16416, which is
+    """1x32 exponents of a 16384 x N x 8192 GEMM take (ceil(M/256) + ceil(N/256))
+    * 64 * 1024 bytes: exactly 16 MiB at N = 49152, more at N = 49408, which is
     refused with FP8RT_ESCRATCH before anything is enqueued."""
     M, K = 16384, 8192
-    for N, expect in [(16416, rt.ESCRATCH)]:
+    for N, expect in [(49408, rt.ESCRATCH)]:
         A = torch.empty((M, K), dtype=torch.uint8, device="cuda")
         B = torch.empty((N, K), dtype=torch.uint8, device="cuda")
         sa = torch.ones((M, K // 32), device="cuda")
