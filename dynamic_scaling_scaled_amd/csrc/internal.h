@@ -31,14 +31,16 @@ struct DevWorkspace {
   BlockPartial pass2[kMaxBlocks];  // per-block counters / observed amax of a cast pass
 };
 
-// Returns the workspace of (current device, stream), allocating and zeroing
-// it on first use (hipMalloc + hipMemset, outside any graph capture).
+// Returns the workspace of (current device, stream), allocating it on first
+// use (hipMalloc; nothing in it is zeroed: every partial is written before it
+// is read).
 hipError_t get_workspace(hipStream_t stream, DevWorkspace** ws);
 
 // Returns a scratch buffer of at least `bytes` for (current device, stream).
-// It grows on demand (the stream is synchronized before an old buffer is
-// freed) and is kept for the life of the process; its contents do not
-// persist between calls.
+// It grows on demand: a larger buffer replaces it and the old one is kept,
+// never freed, so an address a captured graph holds stays valid; buffers live
+// for the life of the process and their contents do not persist between
+// calls.
 hipError_t get_scratch(hipStream_t stream, size_t bytes, void** ptr);
 
 // Compute units of the current device (256 on MI355X).
