@@ -121,13 +121,19 @@ def _check(fn, status):
 
 
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtypes convert it, no object per argument
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return C.c_void_p(stream.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:  # the current stream's handle, without a Stream object
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -139,9 +145,11 @@ def _dtype(t: torch.Tensor) -> int:
 
 
 def _mat(t: torch.Tensor):
-    if t.dim() != 2 or t.stride(1) != 1:
+    st = t.stride()
+    if len(st) != 2 or st[1] != 1:
         raise ValueError("expected a 2-D row-major tensor with unit column stride")
-    return t.shape[0], t.shape[1], t.stride(0)
+    rows, cols = t.shape
+    return rows, cols, st[0]
 
 
 def ngroups(n: int, g: int) -> int:
