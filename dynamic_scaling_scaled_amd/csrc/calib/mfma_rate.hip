@@ -5,9 +5,10 @@
 // measured against on this chip: the instruction rate at the clock the chip
 // holds for the operands' switching activity (zero bytes against random ones).
 //
-// Each wave keeps 16 independent accumulators (as the large GEMM does: 4 x 4
-// 32x32x64 tiles, 256 FP32 registers; or 4 x 4 16x16x128 tiles) and issues 16
-// MFMAs per iteration on 4 A and 4 B operand registers loaded once.  The sum
+// Each wave keeps 16 independent accumulators (4 x 4 tiles: 256 FP32
+// registers of 32x32x64, or 64 of 16x16x128; far more independent chains than
+// either instruction's latency needs) and issues 16 MFMAs per iteration on 4 A
+// and 4 B operand registers loaded once.  The sum
 // of the accumulators is written per thread so the work cannot be dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
